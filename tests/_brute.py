@@ -1,0 +1,162 @@
+"""Naive pure-Python loop implementations for tiny shapes.
+
+Written independently of oracle/ (no imports from it, scalar loops only) so
+that the vectorised oracle can be checked against them. Every formula below is
+restated from the pages: RMSNorm / LayerNorm, the textbook rotation form of
+RoPE (complex multiplication), written-out softmax, GQA head mapping through
+repeat_interleave expansion, SwiGLU, pre-LN ViT block.
+"""
+import math
+
+
+def matvec(W, x):
+    """W [n][k] times x [k]."""
+    return [sum(W[i][j] * x[j] for j in range(len(x))) for i in range(len(W))]
+
+
+def rmsnorm(x, g, eps):
+    ms = sum(v * v for v in x) / len(x)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [x[i] * r * g[i] for i in range(len(x))]
+
+
+def layernorm(x, g, b, eps):
+    n = len(x)
+    mu = sum(x) / n
+    var = sum((v - mu) ** 2 for v in x) / n
+    r = 1.0 / math.sqrt(var + eps)
+    return [(x[i] - mu) * r * g[i] + b[i] for i in range(n)]
+
+
+def rope_complex(u, angles):
+    """Rotate consecutive-half pairs (u[j], u[j+h]) as the complex number
+    u[j] + i u[j+h] multiplied by exp(i angle_j)."""
+    h = len(u) // 2
+    out = [0.0] * len(u)
+    for j in range(h):
+        a, b = u[j], u[j + h]
+        c, s = math.cos(angles[j]), math.sin(angles[j])
+        out[j] = a * c - b * s
+        out[j + h] = a * s + b * c
+    return out
+
+
+def text_angles(pos, d, theta):
+    return [pos * theta ** (-2.0 * j / d) for j in range(d // 2)]
+
+
+def silu(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def gelu_tanh(z):
+    return 0.5 * z * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def attention_rows(qs, ks, vs, visible):
+    """qs [Sq][d]; ks, vs [Sk][d]; visible(i, j) -> bool. Softmax written out."""
+    d = len(qs[0])
+    out = []
+    for i, q in enumerate(qs):
+        scores = []
+        for j, k in enumerate(ks):
+            if visible(i, j):
+                scores.append((j, sum(q[t] * k[t] for t in range(d)) / math.sqrt(d)))
+        m = max(s for _, s in scores)
+        e = [(j, math.exp(s - m)) for j, s in scores]
+        tot = sum(v for _, v in e)
+        o = [0.0] * len(vs[0])
+        for j, p in e:
+            for t in range(len(o)):
+                o[t] += p / tot * vs[j][t]
+        out.append(o)
+    return out
+
+
+def expand_kv_rows(W, n_kv, head_dim, rep):
+    """Repeat each KV head's block of rows `rep` times consecutively
+    (repeat_interleave over heads), as the GQA-to-MHA weight expansion does."""
+    out = []
+    for g in range(n_kv):
+        block = W[g * head_dim:(g + 1) * head_dim]
+        for _ in range(rep):
+            out.extend([list(r) for r in block])
+    return out
+
+
+def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v):
+    """One decoder layer written as MHA over expanded K/V weights.
+
+    xs: list of rows at positions pos0..; w: dict of nested lists with wk/wv
+    already expanded to nq heads; cache_k/cache_v: lists (per position) of
+    [nq][d] rows, extended in place.
+    """
+    outs = []
+    for s, x in enumerate(xs):
+        pos = pos0 + s
+        h = rmsnorm(x, w["attn_norm"], eps)
+        q = matvec(w["wq"], h)
+        k = matvec(w["wk"], h)
+        v = matvec(w["wv"], h)
+        qh, kh, vh = [], [], []
+        for hd in range(nq):
+            qq = q[hd * d:(hd + 1) * d]
+            kk = k[hd * d:(hd + 1) * d]
+            if qk_norm:
+                qq = rmsnorm(qq, w["q_norm"], eps)
+                kk = rmsnorm(kk, w["k_norm"], eps)
+            ang = text_angles(pos, d, theta)
+            qh.append(rope_complex(qq, ang))
+            kh.append(rope_complex(kk, ang))
+            vh.append(v[hd * d:(hd + 1) * d])
+        cache_k.append(kh)
+        cache_v.append(vh)
+        o = []
+        for hd in range(nq):
+            ks = [cache_k[j][hd] for j in range(pos + 1)]
+            vs = [cache_v[j][hd] for j in range(pos + 1)]
+            o.extend(attention_rows([qh[hd]], ks, vs, lambda i, j: True)[0])
+        att = matvec(w["wo"], o)
+        x = [x[i] + att[i] for i in range(len(x))]
+        h2 = rmsnorm(x, w["mlp_norm"], eps)
+        g = matvec(w["wg"], h2)
+        u = matvec(w["wu"], h2)
+        a = [silu(g[i]) * u[i] for i in range(len(g))]
+        dn = matvec(w["wd"], a)
+        outs.append([x[i] + dn[i] for i in range(len(x))])
+    return outs
+
+
+def vit_layer(xs, w, nh, d, eps, pos_hw, theta, visible):
+    """Pre-LN ViT block; 2D RoPE: first half of each head by h, second by w."""
+    S = len(xs)
+    q_all, k_all, v_all = [], [], []
+    for s in range(S):
+        h = layernorm(xs[s], w["attn_norm"], w["attn_norm_b"], eps)
+        q = [a + b for a, b in zip(matvec(w["wq"], h), w["bq"])]
+        k = [a + b for a, b in zip(matvec(w["wk"], h), w["bk"])]
+        v = [a + b for a, b in zip(matvec(w["wv"], h), w["bv"])]
+        qr, kr = [], []
+        for hd in range(nh):
+            qq, kk = q[hd * d:(hd + 1) * d], k[hd * d:(hd + 1) * d]
+            half = d // 2
+            ah = text_angles(pos_hw[0][s], half, theta)
+            aw = text_angles(pos_hw[1][s], half, theta)
+            qr.append(rope_complex(qq[:half], ah) + rope_complex(qq[half:], aw))
+            kr.append(rope_complex(kk[:half], ah) + rope_complex(kk[half:], aw))
+        q_all.append(qr)
+        k_all.append(kr)
+        v_all.append([v[hd * d:(hd + 1) * d] for hd in range(nh)])
+    outs = []
+    for s in range(S):
+        o = []
+        for hd in range(nh):
+            o.extend(attention_rows([q_all[s][hd]], [k_all[j][hd] for j in range(S)],
+                                    [v_all[j][hd] for j in range(S)], lambda i, j: visible(s, j))[0])
+        att = [a + b for a, b in zip(matvec(w["wo"], o), w["bo"])]
+        x = [xs[s][i] + att[i] for i in range(len(att))]
+        h2 = layernorm(x, w["mlp_norm"], w["mlp_norm_b"], eps)
+        f = [gelu_tanh(a + b) for a, b in zip(matvec(w["w1"], h2), w["b1"])]
+        dn = [a + b for a, b in zip(matvec(w["w2"], f), w["b2"])]
+        outs.append([x[i] + dn[i] for i in range(len(x))])
+    return outs
