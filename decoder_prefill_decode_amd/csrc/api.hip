@@ -1,0 +1,675 @@
+// C ABI of the decoder hot path: argument validation, workspace carving, the
+// KV-cache handle, the per-layer launch sequences of prefill and decode, and
+// the HIP-graph decode loop. All checks run before anything is enqueued, so a
+// failed call changes nothing (HunyuanOCR v1.5 ncnn port §3.6 and §3.7: strict
+// checks at load, the cache committed only after success).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "vlm.h"
+
+using namespace vlm;
+
+namespace {
+
+thread_local std::string g_err;
+
+vlm_status fail(vlm_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+vlm_status ok() {
+    g_err.clear();
+    return VLM_OK;
+}
+
+#define HIP_TRY(expr)                                                                   \
+    do {                                                                                \
+        hipError_t e_ = (expr);                                                         \
+        if (e_ != hipSuccess) return fail(VLM_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr size_t kHeader = 256;
+
+size_t esize(int dtype) { return dtype == VLM_BF16 ? 2 : 4; }
+size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+vlm_status check_desc(const vlm_model_desc* d) {
+    if (!d) return fail(VLM_ERR_ARG, "desc is NULL");
+    if (d->block_kind != VLM_BLOCK_DECODER && d->block_kind != VLM_BLOCK_VIT)
+        return fail(VLM_ERR_ARG, "block_kind %d invalid", d->block_kind);
+    if (d->dtype != VLM_F32 && d->dtype != VLM_BF16) return fail(VLM_ERR_DTYPE, "dtype %d invalid", d->dtype);
+    if (d->n_layers < 1) return fail(VLM_ERR_SHAPE, "n_layers %d < 1", d->n_layers);
+    if (d->hidden < 8 || d->hidden % 8) return fail(VLM_ERR_SHAPE, "hidden %d must be a positive multiple of 8", d->hidden);
+    if (d->hidden > 16384) return fail(VLM_ERR_UNSUPPORTED, "hidden %d > 16384", d->hidden);
+    if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads)
+        return fail(VLM_ERR_SHAPE, "n_q_heads %d must be a multiple of n_kv_heads %d", d->n_q_heads, d->n_kv_heads);
+    const int grp = d->n_q_heads / d->n_kv_heads;
+    if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
+        return fail(VLM_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}", grp);
+    if (d->head_dim != 64 && d->head_dim != 72 && d->head_dim != 80 && d->head_dim != 128)
+        return fail(VLM_ERR_UNSUPPORTED, "head_dim %d not in {64,72,80,128}", d->head_dim);
+    if (d->dtype == VLM_BF16 && d->head_dim % 16)
+        return fail(VLM_ERR_UNSUPPORTED, "bf16 attention needs head_dim %% 16 == 0 (got %d)", d->head_dim);
+    if (d->rope_segments != 1 && d->rope_segments != 2) return fail(VLM_ERR_ARG, "rope_segments %d", d->rope_segments);
+    if ((d->head_dim / d->rope_segments) % 2) return fail(VLM_ERR_SHAPE, "rope segment length must be even");
+    if (d->qk_norm != 0 && d->qk_norm != 1) return fail(VLM_ERR_UNSUPPORTED, "qk_norm %d", d->qk_norm);
+    if (d->ffn < 8 || d->ffn % 8) return fail(VLM_ERR_SHAPE, "ffn %d must be a positive multiple of 8", d->ffn);
+    if (d->ffn > 16384) return fail(VLM_ERR_UNSUPPORTED, "ffn %d > 16384", d->ffn);
+    if (d->block_kind == VLM_BLOCK_DECODER && d->ffn % 32)
+        return fail(VLM_ERR_SHAPE, "decoder ffn %d must be a multiple of 32 (gate/up groups)", d->ffn);
+    if (d->n_q_heads * d->head_dim > 16384) return fail(VLM_ERR_UNSUPPORTED, "n_q_heads*head_dim too large");
+    if (d->vocab < 0) return fail(VLM_ERR_SHAPE, "vocab %d < 0", d->vocab);
+    if (!(d->norm_eps >= 0.f)) return fail(VLM_ERR_ARG, "norm_eps must be >= 0");
+    if (d->block_kind == VLM_BLOCK_VIT && (d->n_kv_heads != d->n_q_heads || d->qk_norm))
+        return fail(VLM_ERR_UNSUPPORTED, "ViT blocks need n_kv_heads == n_q_heads and no QK-Norm");
+    return VLM_OK;
+}
+
+int qkv_rows(const vlm_model_desc* d) { return (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim; }
+
+struct Ws {
+    size_t h, qkv, q, kv, o, a, xrow, qkvrow, qrow, part, orow, arow, lm, total;
+};
+
+Ws ws_layout(const vlm_model_desc* d, int max_rows) {
+    const size_t E = esize(d->dtype), R = std::max(max_rows, 1);
+    const size_t H = d->hidden, F = d->ffn, nq = d->n_q_heads, nkv = d->n_kv_heads, hd = d->head_dim;
+    Ws w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += al256(bytes);
+        return o;
+    };
+    w.h = take(R * H * E);
+    w.qkv = take(R * qkv_rows(d) * 4);
+    w.q = take(nq * R * hd * E);
+    w.kv = d->block_kind == VLM_BLOCK_VIT ? take(2 * nkv * R * hd * E) : off;
+    w.o = take(R * nq * hd * E);
+    w.a = take(R * F * E);
+    w.xrow = take(H * 4);
+    w.qkvrow = take(qkv_rows(d) * 4);
+    w.qrow = take(nq * hd * E);
+    w.part = take(nq * 32 * (hd + 2) * 4);
+    w.orow = take(nq * hd * E);
+    w.arow = take(F * E);
+    w.lm = take(d->vocab > 0 ? (size_t)lmhead_blocks(d->vocab) * 8 : 8);
+    w.total = off;
+    return w;
+}
+
+vlm_status check_ws(const vlm_model_desc* d, int rows, const void* ws, size_t bytes, Ws* out) {
+    if (!ws) return fail(VLM_ERR_ARG, "workspace is NULL");
+    if ((uintptr_t)ws & 255) return fail(VLM_ERR_ARG, "workspace must be 256-byte aligned");
+    *out = ws_layout(d, rows);
+    if (bytes < out->total)
+        return fail(VLM_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", bytes, out->total);
+    return VLM_OK;
+}
+
+char* P(void* base, size_t off) { return (char*)base + off; }
+
+vlm_status need(const void* p, const char* name, int layer) {
+    if (!p) return fail(VLM_ERR_ARG, "layer %d: %s is NULL", layer, name);
+    if (!aligned16(p)) return fail(VLM_ERR_ARG, "layer %d: %s not 16-byte aligned", layer, name);
+    return VLM_OK;
+}
+
+vlm_status check_layers(const vlm_model_desc* d, const vlm_layer* L) {
+    if (!L) return fail(VLM_ERR_ARG, "layers is NULL");
+    for (int l = 0; l < d->n_layers; l++) {
+        const vlm_layer& y = L[l];
+        vlm_status s;
+        if ((s = need(y.attn_norm, "attn_norm", l)) || (s = need(y.wqkv, "wqkv", l)) || (s = need(y.wo, "wo", l)) ||
+            (s = need(y.mlp_norm, "mlp_norm", l)) || (s = need(y.w1, "w1", l)) || (s = need(y.w2, "w2", l)))
+            return s;
+        if (d->qk_norm && ((s = need(y.q_norm, "q_norm", l)) || (s = need(y.k_norm, "k_norm", l)))) return s;
+        if (d->block_kind == VLM_BLOCK_VIT) {
+            if ((s = need(y.attn_norm_b, "attn_norm_b", l)) || (s = need(y.bqkv, "bqkv", l)) ||
+                (s = need(y.bo, "bo", l)) || (s = need(y.mlp_norm_b, "mlp_norm_b", l)) || (s = need(y.b1, "b1", l)) ||
+                (s = need(y.b2, "b2", l)))
+                return s;
+        }
+    }
+    return VLM_OK;
+}
+
+}  // namespace
+
+// =============================================================================== KV cache
+struct GraphKey {
+    vlm_model_desc desc;
+    std::vector<vlm_layer> layers;
+    const void *embed, *fnorm, *table;
+    int32_t* tok;
+    const float *cos, *sin;
+    int table_rows;
+    int32_t* hist;
+    void* ws;
+    size_t ws_bytes;
+    bool operator==(const GraphKey& o) const {
+        return memcmp(&desc, &o.desc, sizeof(desc)) == 0 && layers.size() == o.layers.size() &&
+               memcmp(layers.data(), o.layers.data(), layers.size() * sizeof(vlm_layer)) == 0 && embed == o.embed &&
+               fnorm == o.fnorm && table == o.table && tok == o.tok && cos == o.cos && sin == o.sin &&
+               table_rows == o.table_rows && hist == o.hist && ws == o.ws && ws_bytes == o.ws_bytes;
+    }
+};
+
+struct vlm_kv {
+    vlm_model_desc desc;
+    int capacity;
+    void* buf;
+    size_t bytes;
+    int len;  // host mirror
+    hipStream_t cap_stream = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    bool has_key = false;
+    GraphKey key;
+    int32_t* dlen() const { return (int32_t*)buf; }
+    size_t layer_bytes() const { return 2 * (size_t)desc.n_kv_heads * capacity * desc.head_dim * esize(desc.dtype); }
+    char* kptr(int l) const { return (char*)buf + kHeader + (size_t)l * layer_bytes(); }
+    char* vptr(int l) const { return kptr(l) + layer_bytes() / 2; }
+    void drop_graph() {
+        if (exec) hipGraphExecDestroy(exec);
+        if (graph) hipGraphDestroy(graph);
+        exec = nullptr;
+        graph = nullptr;
+        has_key = false;
+    }
+};
+
+extern "C" {
+
+const char* vlm_last_error(void) { return g_err.c_str(); }
+
+vlm_status vlm_kv_bytes(const vlm_model_desc* desc, int32_t capacity, size_t* bytes) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "KV cache is for decoder stacks");
+    if (capacity < 1) return fail(VLM_ERR_SHAPE, "capacity %d < 1", capacity);
+    if (!bytes) return fail(VLM_ERR_ARG, "bytes is NULL");
+    *bytes = kHeader + (size_t)desc->n_layers * 2 * desc->n_kv_heads * capacity * desc->head_dim * esize(desc->dtype);
+    return ok();
+}
+
+vlm_status vlm_kv_alloc(const vlm_model_desc* desc, int32_t capacity, void* d_buf, size_t bytes, hipStream_t stream,
+                        vlm_kv** out) {
+    size_t need_b = 0;
+    vlm_status s = vlm_kv_bytes(desc, capacity, &need_b);
+    if (s) return s;
+    if (!out) return fail(VLM_ERR_ARG, "out is NULL");
+    if (!d_buf || ((uintptr_t)d_buf & 255)) return fail(VLM_ERR_ARG, "KV buffer NULL or not 256-byte aligned");
+    if (bytes < need_b) return fail(VLM_ERR_CAPACITY, "KV buffer %zu bytes < %zu needed", bytes, need_b);
+    HIP_TRY(launch_set_len((int32_t*)d_buf, 0, stream));
+    vlm_kv* kv = new vlm_kv();
+    kv->desc = *desc;
+    kv->capacity = capacity;
+    kv->buf = d_buf;
+    kv->bytes = bytes;
+    kv->len = 0;
+    *out = kv;
+    return ok();
+}
+
+vlm_status vlm_kv_free(vlm_kv* kv) {
+    if (!kv) return fail(VLM_ERR_ARG, "kv is NULL");
+    kv->drop_graph();
+    if (kv->cap_stream) hipStreamDestroy(kv->cap_stream);
+    delete kv;
+    return ok();
+}
+
+vlm_status vlm_kv_len(const vlm_kv* kv, int32_t* len) {
+    if (!kv || !len) return fail(VLM_ERR_ARG, "NULL argument");
+    *len = kv->len;
+    return ok();
+}
+
+vlm_status vlm_kv_truncate(vlm_kv* kv, int32_t new_len, hipStream_t stream) {
+    if (!kv) return fail(VLM_ERR_ARG, "kv is NULL");
+    if (new_len < 0 || new_len > kv->len)
+        return fail(VLM_ERR_CAPACITY, "new length %d outside [0, %d]", new_len, kv->len);
+    HIP_TRY(launch_set_len(kv->dlen(), new_len, stream));
+    kv->len = new_len;
+    return ok();
+}
+
+vlm_status vlm_workspace_bytes(const vlm_model_desc* desc, int32_t max_rows, size_t* bytes) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (max_rows < 0) return fail(VLM_ERR_SHAPE, "max_rows %d < 0", max_rows);
+    if (!bytes) return fail(VLM_ERR_ARG, "bytes is NULL");
+    *bytes = ws_layout(desc, max_rows).total;
+    return ok();
+}
+
+// =============================================================================== packing
+vlm_status vlm_pack_qkv(const void* d_wq, const void* d_wk, const void* d_wv, int32_t q_rows, int32_t kv_rows,
+                        int32_t hidden, int32_t dtype, void* d_out, hipStream_t stream) {
+    if (!d_wq || !d_wk || !d_wv || !d_out) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (dtype != VLM_F32 && dtype != VLM_BF16) return fail(VLM_ERR_DTYPE, "dtype %d", dtype);
+    if (q_rows < 1 || kv_rows < 1 || hidden < 1) return fail(VLM_ERR_SHAPE, "bad sizes");
+    const size_t E = esize(dtype), qb = (size_t)q_rows * hidden * E, kb = (size_t)kv_rows * hidden * E;
+    HIP_TRY(hipMemcpyAsync(d_out, d_wq, qb, hipMemcpyDeviceToDevice, stream));
+    HIP_TRY(hipMemcpyAsync((char*)d_out + qb, d_wk, kb, hipMemcpyDeviceToDevice, stream));
+    HIP_TRY(hipMemcpyAsync((char*)d_out + qb + kb, d_wv, kb, hipMemcpyDeviceToDevice, stream));
+    return ok();
+}
+
+vlm_status vlm_pack_gate_up(const void* d_wg, const void* d_wu, int32_t ffn, int32_t hidden, int32_t dtype,
+                            void* d_out, hipStream_t stream) {
+    if (!d_wg || !d_wu || !d_out) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (dtype != VLM_F32 && dtype != VLM_BF16) return fail(VLM_ERR_DTYPE, "dtype %d", dtype);
+    if (ffn < 32 || ffn % 32 || hidden < 1) return fail(VLM_ERR_SHAPE, "ffn must be a positive multiple of 32");
+    HIP_TRY(launch_pack_gate_up(dtype, d_wg, d_wu, ffn, hidden, d_out, stream));
+    return ok();
+}
+
+// =============================================================================== RoPE table
+vlm_status vlm_rope_table(const int32_t* d_pos, int32_t n_axes, int32_t n_rows, const int32_t* h_axis_of_pair,
+                          int32_t rope_segments, int32_t head_dim, double theta, float* d_cos, float* d_sin,
+                          hipStream_t stream) {
+    if (!d_pos || !h_axis_of_pair || !d_cos || !d_sin) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (n_axes < 1 || n_rows < 0) return fail(VLM_ERR_SHAPE, "n_axes %d / n_rows %d", n_axes, n_rows);
+    if (head_dim < 2 || head_dim > 128) return fail(VLM_ERR_UNSUPPORTED, "head_dim %d not in [2, 128]", head_dim);
+    if (rope_segments != 1 && rope_segments != 2) return fail(VLM_ERR_ARG, "rope_segments %d", rope_segments);
+    if (head_dim % (2 * rope_segments)) return fail(VLM_ERR_SHAPE, "segment length must be even");
+    if (!(theta > 0.0)) return fail(VLM_ERR_ARG, "theta must be > 0");
+    for (int i = 0; i < head_dim / 2; i++)
+        if (h_axis_of_pair[i] < 0 || h_axis_of_pair[i] >= n_axes)
+            return fail(VLM_ERR_ARG, "axis_of_pair[%d] = %d outside [0, %d)", i, h_axis_of_pair[i], n_axes);
+    HIP_TRY(launch_rope_table(d_pos, n_axes, n_rows, h_axis_of_pair, rope_segments, head_dim, theta, d_cos, d_sin, stream));
+    return ok();
+}
+
+// =============================================================================== embed / inject
+vlm_status vlm_embed(const vlm_model_desc* desc, const void* d_embed, const int32_t* d_ids, int32_t S, float* d_x,
+                     hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->vocab < 1) return fail(VLM_ERR_SHAPE, "model has no embedding table (vocab 0)");
+    if (S < 0) return fail(VLM_ERR_SHAPE, "S %d < 0", S);
+    if (S == 0) return ok();
+    if (!d_embed || !d_ids || !d_x) return fail(VLM_ERR_ARG, "NULL pointer");
+    HIP_TRY(launch_embed(desc->dtype, d_embed, desc->vocab, desc->hidden, d_ids, S, d_x, stream));
+    return ok();
+}
+
+vlm_status vlm_inject_image_embeds(const vlm_model_desc* desc, float* d_x, int32_t S, const int32_t* h_ids,
+                                   const int32_t* d_ids, int32_t placeholder_id, const void* d_img, int32_t n_img,
+                                   int32_t img_dtype, hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (S < 0 || n_img < 0) return fail(VLM_ERR_SHAPE, "S %d / n_img %d negative", S, n_img);
+    if (img_dtype != VLM_F32 && img_dtype != VLM_BF16) return fail(VLM_ERR_DTYPE, "img_dtype %d", img_dtype);
+    if (S > 0 && (!h_ids || !d_ids || !d_x)) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (n_img > 0 && !d_img) return fail(VLM_ERR_ARG, "d_img is NULL");
+    int count = 0;
+    for (int i = 0; i < S; i++) count += h_ids[i] == placeholder_id;
+    if (count != n_img)
+        return fail(VLM_ERR_COUNT_MISMATCH, "%d placeholder rows (id %d) but %d image rows", count, placeholder_id, n_img);
+    if (n_img == 0) return ok();
+    HIP_TRY(launch_inject(img_dtype, d_x, S, desc->hidden, d_ids, placeholder_id, d_img, n_img, stream));
+    return ok();
+}
+
+// =============================================================================== prefill
+vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, float* d_x, int32_t S, int32_t pos0,
+                       const float* d_cos, const float* d_sin, int32_t table_rows, const vlm_mask* h_masks,
+                       int32_t n_masks, vlm_kv* kv, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    const bool vit = desc->block_kind == VLM_BLOCK_VIT;
+    if (S < 0 || pos0 < 0) return fail(VLM_ERR_SHAPE, "S %d / pos0 %d negative", S, pos0);
+    if (vit) {
+        if (kv) return fail(VLM_ERR_ARG, "ViT prefill takes no KV cache");
+        if (pos0 != 0) return fail(VLM_ERR_ARG, "ViT prefill needs pos0 == 0");
+    } else {
+        if (!kv) return fail(VLM_ERR_ARG, "decoder prefill needs a KV cache");
+        if (memcmp(&kv->desc, desc, sizeof(*desc)) != 0) return fail(VLM_ERR_ARG, "KV cache bound to another model desc");
+        if (pos0 > kv->len) return fail(VLM_ERR_CAPACITY, "pos0 %d beyond the cache length %d", pos0, kv->len);
+        if ((long)pos0 + S > kv->capacity)
+            return fail(VLM_ERR_CAPACITY, "sequence end %d exceeds the KV window %d", pos0 + S, kv->capacity);
+    }
+    if ((long)pos0 + S > table_rows)
+        return fail(VLM_ERR_CAPACITY, "sequence end %d exceeds the RoPE table rows %d", pos0 + S, table_rows);
+    if (!d_x || !aligned16(d_x) || !d_cos || !d_sin) return fail(VLM_ERR_ARG, "x/cos/sin NULL or x misaligned");
+    if ((s = check_layers(desc, h_layers))) return s;
+    if (!h_masks || (n_masks != 1 && n_masks != desc->n_layers))
+        return fail(VLM_ERR_ARG, "masks: need 1 or n_layers entries (got %d)", n_masks);
+    for (int i = 0; i < n_masks; i++) {
+        const vlm_mask& m = h_masks[i];
+        if (m.kind < VLM_MASK_CAUSAL || m.kind > VLM_MASK_SEGMENT) return fail(VLM_ERR_ARG, "mask %d kind %d", i, m.kind);
+        if (m.kind == VLM_MASK_ADDITIVE && (!m.add || m.ld_add < pos0 + S))
+            return fail(VLM_ERR_ARG, "mask %d: additive mask NULL or ld_add %d < %d", i, m.ld_add, pos0 + S);
+        if (m.kind == VLM_MASK_SEGMENT && (!m.seg || pos0 != 0))
+            return fail(VLM_ERR_ARG, "mask %d: segment mask needs seg ids and pos0 == 0", i);
+    }
+    Ws w;
+    if ((s = check_ws(desc, S, d_ws, ws_bytes, &w))) return s;
+    if (S == 0) {
+        if (!vit && kv->len != pos0) {
+            HIP_TRY(launch_set_len(kv->dlen(), pos0, stream));
+            kv->len = pos0;
+        }
+        return ok();
+    }
+
+    const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
+    const int hd = desc->head_dim, QKV = qkv_rows(desc);
+    const size_t E = esize(dt);
+    void* hbuf = P(d_ws, w.h);
+    float* qkv = (float*)P(d_ws, w.qkv);
+    void* qb = P(d_ws, w.q);
+    void* ob = P(d_ws, w.o);
+    void* ab = P(d_ws, w.a);
+    for (int l = 0; l < desc->n_layers; l++) {
+        const vlm_layer& y = h_layers[l];
+        const vlm_mask& mk = h_masks[n_masks == 1 ? 0 : l];
+        void *kd, *vd;
+        int ldkv;
+        if (vit) {
+            kd = P(d_ws, w.kv);
+            vd = (char*)kd + (size_t)nkv * S * hd * E;
+            ldkv = S;
+        } else {
+            kd = kv->kptr(l);
+            vd = kv->vptr(l);
+            ldkv = kv->capacity;
+        }
+        HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.attn_norm, y.attn_norm_b, desc->norm_eps, hbuf, stream));
+        GemmArgs g{};
+        g.A = hbuf; g.B = y.wqkv; g.bias = vit ? y.bqkv : nullptr; g.out = qkv; g.M = S; g.N = QKV; g.K = H; g.ldo = QKV;
+        HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
+        RopeArgs r{};
+        r.qkv = qkv; r.S = S; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
+        r.qn = desc->qk_norm ? y.q_norm : nullptr; r.kn = desc->qk_norm ? y.k_norm : nullptr; r.eps = desc->norm_eps;
+        r.cos = d_cos; r.sin = d_sin; r.q = qb; r.ldq = S; r.kdst = kd; r.vdst = vd; r.ldkv = ldkv;
+        r.pos0 = pos0; r.pos_dev = nullptr;
+        HIP_TRY(launch_rope_qkv(dt, r, stream));
+        AttnArgs at{};
+        at.q = qb; at.ldq = S; at.k = kd; at.v = vd; at.ldkv = ldkv; at.out = ob;
+        at.S = S; at.nq = nq; at.nkv = nkv; at.d = hd; at.pos0 = pos0; at.nkeys = pos0 + S;
+        at.mask_kind = mk.kind; at.add = mk.add; at.ld_add = mk.ld_add; at.seg = mk.seg;
+        HIP_TRY(launch_attn_prefill(dt, at, stream));
+        g = GemmArgs{};
+        g.A = ob; g.B = y.wo; g.bias = vit ? y.bo : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = nq * hd; g.ldo = H;
+        HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
+        HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.mlp_norm, y.mlp_norm_b, desc->norm_eps, hbuf, stream));
+        g = GemmArgs{};
+        g.A = hbuf; g.B = y.w1; g.out = ab; g.M = S; g.K = H; g.ldo = F;
+        if (vit) {
+            g.bias = y.b1; g.N = F;
+            HIP_TRY(launch_gemm(dt, Epi::Gelu, g, stream));
+        } else {
+            g.N = 2 * F;
+            HIP_TRY(launch_gemm(dt, Epi::SwiGLU, g, stream));
+        }
+        g = GemmArgs{};
+        g.A = ab; g.B = y.w2; g.bias = vit ? y.b2 : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = F; g.ldo = H;
+        HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
+    }
+    if (!vit) {
+        HIP_TRY(launch_set_len(kv->dlen(), pos0 + S, stream));
+        kv->len = pos0 + S;
+    }
+    return ok();
+}
+
+// =============================================================================== head
+vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
+                             const float* d_x_row, int32_t* d_token_out, float* d_logits, void* d_ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->vocab < 1) return fail(VLM_ERR_SHAPE, "model has no lm_head table (vocab 0)");
+    if (!d_final_norm || !d_table || !aligned16(d_table) || !d_x_row || !d_token_out)
+        return fail(VLM_ERR_ARG, "NULL or misaligned pointer");
+    Ws w;
+    if ((s = check_ws(desc, 0, d_ws, ws_bytes, &w))) return s;
+    auto* part = (unsigned long long*)P(d_ws, w.lm);
+    HIP_TRY(launch_lmhead(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab, desc->hidden, part,
+                          d_logits, stream));
+    HIP_TRY(launch_argmax_final(part, lmhead_blocks(desc->vocab), d_token_out, nullptr, nullptr, stream));
+    return ok();
+}
+
+// =============================================================================== decode
+static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L, const void* embed, const void* fnorm,
+                                 const void* table, vlm_kv* kv, const int32_t* tok_in, const float* x_in,
+                                 const float* cosv, const float* sinv, int32_t* tok_out, float* x_out, int32_t* hist,
+                                 void* ws, const Ws& w, hipStream_t st) {
+    const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
+    const int hd = desc->head_dim, QKV = qkv_rows(desc), W = kv->capacity;
+    float* x = (float*)P(ws, w.xrow);
+    float* qkv = (float*)P(ws, w.qkvrow);
+    void* qr = P(ws, w.qrow);
+    float* part = (float*)P(ws, w.part);
+    void* orow = P(ws, w.orow);
+    void* arow = P(ws, w.arow);
+    const int nsplit = attn_decode_splits(W);
+    HIP_TRY(launch_embed_or_copy(dt, embed, desc->vocab, H, tok_in, x_in, x, st));
+    for (int l = 0; l < desc->n_layers; l++) {
+        const vlm_layer& y = L[l];
+        GemvArgs g{};
+        g.W = y.wqkv; g.vec = x; g.gain = y.attn_norm; g.eps = desc->norm_eps; g.out = qkv; g.N = QKV; g.K = H;
+        HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
+        RopeArgs r{};
+        r.qkv = qkv; r.S = 1; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
+        r.qn = desc->qk_norm ? y.q_norm : nullptr; r.kn = desc->qk_norm ? y.k_norm : nullptr; r.eps = desc->norm_eps;
+        r.cos = cosv; r.sin = sinv; r.q = qr; r.ldq = 1; r.kdst = kv->kptr(l); r.vdst = kv->vptr(l); r.ldkv = W;
+        r.pos0 = 0; r.pos_dev = kv->dlen();
+        HIP_TRY(launch_rope_qkv(dt, r, st));
+        HIP_TRY(launch_attn_decode(dt, qr, kv->kptr(l), kv->vptr(l), W, nq, nkv, hd, kv->dlen(), nsplit, part, orow, st));
+        g = GemvArgs{};
+        g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * hd;
+        HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
+        g = GemvArgs{};
+        g.W = y.w1; g.vec = x; g.gain = y.mlp_norm; g.eps = desc->norm_eps; g.out = arow; g.N = 2 * F; g.K = H;
+        HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::SwiGLU, g, st));
+        g = GemvArgs{};
+        g.W = y.w2; g.vec = arow; g.out = x; g.N = H; g.K = F;
+        HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
+    }
+    if (x_out) HIP_TRY(launch_copy_f32(x, x_out, H, st));
+    if (table) {
+        auto* lm = (unsigned long long*)P(ws, w.lm);
+        HIP_TRY(launch_lmhead(dt, table, x, fnorm, desc->norm_eps, desc->vocab, H, lm, nullptr, st));
+        HIP_TRY(launch_argmax_final(lm, lmhead_blocks(desc->vocab), tok_out, hist, kv->dlen(), st));
+    } else {
+        HIP_TRY(launch_inc_len(kv->dlen(), st));
+    }
+    return VLM_OK;
+}
+
+static vlm_status check_decode(const vlm_model_desc* desc, const vlm_layer* L, const void* embed, const void* fnorm,
+                               const void* table, vlm_kv* kv, const int32_t* tok_in, const float* x_in,
+                               const float* cosv, const float* sinv, int32_t table_rows, const int32_t* tok_out,
+                               void* ws, size_t ws_bytes, int steps, Ws* w) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decode needs a decoder stack");
+    if (!kv) return fail(VLM_ERR_ARG, "kv is NULL");
+    if (memcmp(&kv->desc, desc, sizeof(*desc)) != 0) return fail(VLM_ERR_ARG, "KV cache bound to another model desc");
+    if ((long)kv->len + steps > kv->capacity)
+        return fail(VLM_ERR_CAPACITY, "decode to length %d exceeds the KV window %d", kv->len + steps, kv->capacity);
+    if ((long)kv->len + steps > table_rows)
+        return fail(VLM_ERR_CAPACITY, "decode to length %d exceeds the RoPE table rows %d", kv->len + steps, table_rows);
+    if (!cosv || !sinv) return fail(VLM_ERR_ARG, "cos/sin NULL");
+    if ((s = check_layers(desc, L))) return s;
+    if (!x_in) {
+        if (desc->vocab < 1 || !embed || !aligned16(embed) || !tok_in)
+            return fail(VLM_ERR_ARG, "token input needs an embedding table and d_token_in");
+    }
+    if (table) {
+        if (desc->vocab < 1 || !aligned16(table) || !fnorm || !tok_out)
+            return fail(VLM_ERR_ARG, "lm_head needs vocab > 0, final norm and d_token_out");
+    }
+    return check_ws(desc, 1, ws, ws_bytes, w);
+}
+
+vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                           const void* d_final_norm, const void* d_table, vlm_kv* kv, const int32_t* d_token_in,
+                           const float* d_x_in, const float* d_cos, const float* d_sin, int32_t table_rows,
+                           int32_t* d_token_out, float* d_x_out, int32_t* d_token_hist, void* d_ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    Ws w;
+    vlm_status s = check_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_in, d_x_in, d_cos, d_sin,
+                                table_rows, d_token_out, d_ws, ws_bytes, 1, &w);
+    if (s) return s;
+    if ((s = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_in, d_x_in, d_cos, d_sin,
+                            d_token_out, d_x_out, d_token_hist, d_ws, w, stream)))
+        return s;
+    kv->len += 1;
+    return ok();
+}
+
+vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                           const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
+                           const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
+                           int32_t n_steps, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (n_steps < 0) return fail(VLM_ERR_SHAPE, "n_steps %d < 0", n_steps);
+    Ws w;
+    vlm_status s = check_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos, d_sin,
+                                table_rows, d_token_io, d_ws, ws_bytes, n_steps, &w);
+    if (s) return s;
+    if (!d_table) return fail(VLM_ERR_ARG, "decode loop needs the lm_head table");
+    if (n_steps == 0) return ok();
+    GraphKey key;
+    key.desc = *desc;
+    key.layers.assign(h_layers, h_layers + desc->n_layers);
+    key.embed = d_embed; key.fnorm = d_final_norm; key.table = d_table; key.tok = d_token_io;
+    key.cos = d_cos; key.sin = d_sin; key.table_rows = table_rows; key.hist = d_token_hist;
+    key.ws = d_ws; key.ws_bytes = ws_bytes;
+    if (!kv->has_key || !(kv->key == key)) {
+        kv->drop_graph();
+        if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
+        HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
+        vlm_status es = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos,
+                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, kv->cap_stream);
+        hipGraph_t graph = nullptr;
+        hipError_t ee = hipStreamEndCapture(kv->cap_stream, &graph);
+        if (es) {
+            if (graph) hipGraphDestroy(graph);
+            return es;
+        }
+        if (ee != hipSuccess) return fail(VLM_ERR_HIP, "graph capture: %s", hipGetErrorString(ee));
+        hipGraphExec_t exec = nullptr;
+        hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        if (ie != hipSuccess) {
+            hipGraphDestroy(graph);
+            return fail(VLM_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ie));
+        }
+        kv->graph = graph;
+        kv->exec = exec;
+        kv->key = key;
+        kv->has_key = true;
+    }
+    for (int i = 0; i < n_steps; i++) HIP_TRY(hipGraphLaunch(kv->exec, stream));
+    kv->len += n_steps;
+    return ok();
+}
+
+// =============================================================================== vision helpers
+vlm_status vlm_vit_window_index(int32_t grid_h, int32_t grid_w, int32_t merge, int32_t window, int32_t* h_unit_perm,
+                                int32_t* h_row_perm, int32_t* h_row_seg, int32_t* h_pos) {
+    if (grid_h < 1 || grid_w < 1 || merge < 1 || window < 1) return fail(VLM_ERR_SHAPE, "sizes must be positive");
+    if (grid_h % merge || grid_w % merge) return fail(VLM_ERR_SHAPE, "grid not divisible by merge");
+    const int gh = grid_h / merge, gw = grid_w / merge, m2 = merge * merge, n_rows = grid_h * grid_w;
+    int p = 0, wid = 0;
+    for (int wr = 0; wr < gh; wr += window)
+        for (int wc = 0; wc < gw; wc += window, wid++)
+            for (int r = wr; r < std::min(wr + window, gh); r++)
+                for (int c = wc; c < std::min(wc + window, gw); c++, p++) {
+                    const int u = r * gw + c;
+                    if (h_unit_perm) h_unit_perm[p] = u;
+                    for (int sI = 0; sI < m2; sI++) {
+                        const int row = p * m2 + sI;
+                        if (h_row_perm) h_row_perm[row] = u * m2 + sI;
+                        if (h_row_seg) h_row_seg[row] = wid;
+                        if (h_pos) {
+                            h_pos[row] = r * merge + sI / merge;
+                            h_pos[n_rows + row] = c * merge + sI % merge;
+                        }
+                    }
+                }
+    return ok();
+}
+
+vlm_status vlm_gather_rows(const float* d_src, int32_t n_src, const int32_t* d_idx, int32_t n_rows, int32_t row_len,
+                           float* d_dst, hipStream_t stream) {
+    if (n_rows < 0 || row_len < 0 || n_src < 0) return fail(VLM_ERR_SHAPE, "negative size");
+    if (n_rows == 0) return ok();
+    if (!d_src || !d_idx || !d_dst) return fail(VLM_ERR_ARG, "NULL pointer");
+    HIP_TRY(launch_gather_rows(d_src, n_src, d_idx, n_rows, row_len, d_dst, stream));
+    return ok();
+}
+
+static vlm_status check_merger(const vlm_merger* m, int N) {
+    if (!m) return fail(VLM_ERR_ARG, "merger desc NULL");
+    if (m->dtype != VLM_F32 && m->dtype != VLM_BF16) return fail(VLM_ERR_DTYPE, "dtype %d", m->dtype);
+    if (m->hidden < 8 || m->hidden % 8 || m->merge < 1 || m->merger_hidden < 8 || m->merger_hidden % 8 ||
+        m->out_dim < 1)
+        return fail(VLM_ERR_SHAPE, "merger sizes invalid");
+    if (N < 0 || N % (m->merge * m->merge)) return fail(VLM_ERR_SHAPE, "N %d not a multiple of merge^2", N);
+    if (!m->post_ln || !m->post_ln_b || !m->w1 || !m->b1 || !m->w2 || !m->b2) return fail(VLM_ERR_ARG, "NULL weight");
+    if (!aligned16(m->w1) || !aligned16(m->w2)) return fail(VLM_ERR_ARG, "weights not 16-byte aligned");
+    return VLM_OK;
+}
+
+static size_t merger_ws(const vlm_merger* m, int N, size_t* z_off) {
+    const size_t E = esize(m->dtype);
+    const size_t a = al256((size_t)N * m->hidden * E);
+    *z_off = a;
+    return a + al256((size_t)(N / (m->merge * m->merge)) * m->merger_hidden * E);
+}
+
+vlm_status vlm_vit_merger_workspace_bytes(const vlm_merger* m, int32_t N, size_t* bytes) {
+    vlm_status s = check_merger(m, N);
+    if (s) return s;
+    if (!bytes) return fail(VLM_ERR_ARG, "bytes NULL");
+    size_t z;
+    *bytes = merger_ws(m, N, &z);
+    return ok();
+}
+
+vlm_status vlm_vit_merger(const vlm_merger* m, const float* d_x, int32_t N, const int32_t* d_unit_perm, float* d_out,
+                          void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    vlm_status s = check_merger(m, N);
+    if (s) return s;
+    if (!d_x || !d_unit_perm || !d_out || !d_ws || ((uintptr_t)d_ws & 255)) return fail(VLM_ERR_ARG, "NULL pointer");
+    size_t zoff;
+    const size_t need_b = merger_ws(m, N, &zoff);
+    if (ws_bytes < need_b) return fail(VLM_ERR_WORKSPACE, "workspace %zu < %zu", ws_bytes, need_b);
+    if (N == 0) return ok();
+    const int m2 = m->merge * m->merge, U = N / m2;
+    void* hp = d_ws;
+    void* z = P(d_ws, zoff);
+    HIP_TRY(launch_norm_rows(m->dtype, true, d_x, N, m->hidden, m->post_ln, m->post_ln_b, m->norm_eps, hp, stream));
+    GemmArgs g{};
+    g.A = hp; g.B = m->w1; g.bias = m->b1; g.out = z; g.M = U; g.N = m->merger_hidden; g.K = m2 * m->hidden;
+    g.ldo = m->merger_hidden;
+    HIP_TRY(launch_gemm(m->dtype, Epi::Gelu, g, stream));
+    g = GemmArgs{};
+    g.A = z; g.B = m->w2; g.bias = m->b2; g.out = d_out; g.rowmap = d_unit_perm; g.M = U; g.N = m->out_dim;
+    g.K = m->merger_hidden; g.ldo = m->out_dim;
+    HIP_TRY(launch_gemm(m->dtype, Epi::StoreRowMap, g, stream));
+    return ok();
+}
+
+}  // extern "C"

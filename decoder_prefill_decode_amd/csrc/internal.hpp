@@ -1,0 +1,103 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+// Launchers enqueue on `st` and return the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vlm {
+
+// vlm_mask_kind values of the C ABI
+constexpr int VLM_MASK_CAUSAL_ID = 0, VLM_MASK_NONE_ID = 1, VLM_MASK_ADDITIVE_ID = 2, VLM_MASK_SEGMENT_ID = 3;
+
+enum class Epi : int {
+    StoreF32 = 0,    // out_f32[m][n] = acc (+ bias[n])
+    Resid = 1,       // x[m][n] += acc (+ bias[n])
+    SwiGLU = 2,      // out_T[m][n/2] = silu(gate) * up over 32-row interleaved groups
+    Gelu = 3,        // out_T[m][n] = gelu_tanh(acc + bias[n])
+    StoreRowMap = 4  // out_f32[rowmap[m]][n] = acc + bias[n]
+};
+
+struct GemmArgs {
+    const void* A;     // [M][K] operand rows, element type of the model (bf16 or f32)
+    const void* B;     // [N][K] weights
+    const void* bias;  // [N] or null (model element type)
+    void* out;         // epilogue target
+    const int32_t* rowmap;
+    int M, N, K;
+    int ldo;           // row stride of `out` in elements
+};
+
+// dtype: 0 = f32, 1 = bf16 (vlm_dtype values)
+hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t st);
+
+enum class Pro : int { RmsNorm = 0, Plain = 1 };
+struct GemvArgs {
+    const void* W;          // [N][K]
+    const void* vec;        // Pro::RmsNorm: fp32 x [K]; Pro::Plain: model-type vector [K]
+    const void* gain;       // RmsNorm gain [K] (model type)
+    float eps;
+    void* out;              // StoreF32: f32 [N]; Resid: f32 x [N]; SwiGLU: model type [N/2]
+    int N, K;
+};
+hipError_t launch_gemv(int dtype, Pro pro, Epi epi, const GemvArgs& a, hipStream_t st);
+
+// lm_head: logits of final-normed x against table [V][K]; block partials of the argmax
+// into `partials` (u64 per block), optional logits; then a final reduction.
+int lmhead_blocks(int V);
+hipError_t launch_lmhead(int dtype, const void* table, const float* x, const void* gain, float eps, int V, int K,
+                         unsigned long long* partials, float* logits, hipStream_t st);
+// token_out[0] = argmax (or -1); when kv_len != null: hist[len+1] = token (if hist), *kv_len += 1.
+hipError_t launch_argmax_final(const unsigned long long* partials, int nblocks, int32_t* token_out, int32_t* hist,
+                               int32_t* kv_len, hipStream_t st);
+
+// Row norms producing the GEMM operand (model type): RMSNorm (shift == null, layer == false)
+// or LayerNorm (layer == true, shift may be null).
+hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H, const void* gain, const void* shift,
+                            float eps, void* out, hipStream_t st);
+
+// qkv fp32 [S][(nq+2nkv)*d] -> q' [nq][ldq][d] (model type), K/V rows written to
+// kdst/vdst [nkv][ldkv][d] at slot base+s, base = pos_dev ? *pos_dev : pos0.
+// cos/sin rows base+s. Optional per-head RMSNorm (qn/kn gains) before RoPE.
+struct RopeArgs {
+    const float* qkv;
+    int S, nq, nkv, d, segments;
+    const void* qn; const void* kn; float eps;
+    const float* cos; const float* sin;
+    void* q; int ldq;
+    void* kdst; void* vdst; int ldkv;
+    int pos0; const int32_t* pos_dev;
+};
+hipError_t launch_rope_qkv(int dtype, const RopeArgs& a, hipStream_t st);
+
+// Prefill flash attention. q [nq][ldq][d], k/v [nkv][ldkv][d]; keys 0..nkeys-1;
+// query row s has position pos0+s; out [S][nq*d] (model type).
+struct AttnArgs {
+    const void* q; int ldq;
+    const void* k; const void* v; int ldkv;
+    void* out;
+    int S, nq, nkv, d, pos0, nkeys;
+    int mask_kind; const float* add; int ld_add; const int32_t* seg;
+};
+hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st);
+
+// Decode attention over slots 0..*len (inclusive) of k/v [nkv][W][d]; q [nq][d].
+int attn_decode_splits(int capacity);
+hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
+                              const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st);
+
+hipError_t launch_embed(int dtype, const void* table, int V, int H, const int32_t* ids, int S, float* x,
+                        hipStream_t st);
+hipError_t launch_embed_or_copy(int dtype, const void* table, int V, int H, const int32_t* tok, const float* xin,
+                                float* x, hipStream_t st);
+hipError_t launch_inject(int img_dtype, float* x, int S, int H, const int32_t* ids, int pid, const void* img,
+                         int n_img, hipStream_t st);
+hipError_t launch_set_len(int32_t* len, int value, hipStream_t st);
+hipError_t launch_inc_len(int32_t* len, hipStream_t st);
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st);
+hipError_t launch_rope_table(const int32_t* pos, int n_axes, int n_rows, const int32_t* axis_of_pair, int segments,
+                             int d, double theta, float* cos, float* sin, hipStream_t st);
+hipError_t launch_gather_rows(const float* src, int n_src, const int32_t* idx, int n_rows, int row_len, float* dst,
+                              hipStream_t st);
+hipError_t launch_pack_gate_up(int dtype, const void* wg, const void* wu, int F, int H, void* out, hipStream_t st);
+
+}  // namespace vlm

@@ -1,0 +1,561 @@
+// Attention kernels.
+//
+// Prefill: fused (flash-style) attention — scores, mask, softmax and the
+// product with V in one kernel with the intermediates in registers and LDS
+// (MNN llm_demo Omni article §5.1), over the KV cache the same call just wrote
+// (Youtu-VL-4B ncnn port, 实现流程 §7). GQA: query head h reads KV head
+// h / (nq/nkv) (Penguin-VL ncnn port §3). Softmax as max, subtract, exp, sum,
+// divide (Youtu-VL-4B ncnn port, 实现难点 §3), done online per key tile.
+//
+// gfx950 mapping of the prefill kernel: one block = one query head x 128
+// query rows, 4 wavefronts x 32 rows; 64-key K/V tiles staged in LDS.
+// Each wavefront computes S^T = K Q^T with 32x32 MFMAs, so a lane holds all
+// scores of ONE query (column) and the row max / sum need a single cross-half
+// shuffle; P^T is then already in the B-operand layout of O^T = V^T P^T, and
+// the rescaling of O^T by the running max is lane-local. The 32-key MFMA
+// block permutes keys inside a 16-key step the same way for P and V, which
+// leaves the contraction unchanged. bf16 uses 32x32x16 (V transposed in LDS
+// so each lane reads two 8-byte runs) and feeds P as a hi + lo pair of bf16
+// values; f32 uses 32x32x2.
+//
+// Decode: split-K over the valid slots 0..t of the fixed window (Youtu-VL-4B
+// ncnn port, 实现流程 §7: slots beyond t carry -1e9 in the mask, i.e. they
+// are skipped), each block covering one KV head and a slice of slots for all
+// query heads of its group; 16 lanes share a key row (coalesced 16-byte
+// loads), softmax statistics merge across lanes, wavefronts and blocks by
+// log-sum-exp.
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace vlm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ============================================================== prefill, bf16
+template <int D, int MASK>
+__global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
+    constexpr int BQ = 128, BKEY = 64;
+    constexpr int DK = D / 16, NB = (D + 31) / 32, DP = NB * 32;
+    constexpr int LDK = D + 8, LDV = BKEY + 8;
+    constexpr int CH = D / 8;  // 16-byte chunks per key row
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[BKEY * LDK];
+    __shared__ __attribute__((aligned(16))) bf16_t Vt[DP * LDV];
+
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, hh = lane / 32, l32 = lane % 32;
+    const int hq = blockIdx.y, g = hq / (a.nq / a.nkv);
+    const int q0 = blockIdx.x * BQ + w * 32;
+    const int qrow = q0 + l32;
+    const int S = a.S;
+    const bf16_t* Q = (const bf16_t*)a.q + (size_t)hq * a.ldq * D;
+    const bf16_t* Kg = (const bf16_t*)a.k + (size_t)g * a.ldkv * D;
+    const bf16_t* Vg = (const bf16_t*)a.v + (size_t)g * a.ldkv * D;
+
+    for (int i = tid; i < (DP - D) * LDV; i += 256) Vt[D * LDV + i] = 0;
+
+    bf16x8 Qf[DK];
+#pragma unroll
+    for (int kk = 0; kk < DK; kk++) {
+        if (qrow < S) {
+            Qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + kk * 16 + hh * 8);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) Qf[kk][i] = (__bf16)0.0f;
+        }
+    }
+    f32x16 oacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) oacc[nb][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float scale = kLog2e / sqrtf((float)D);
+
+    int kend = a.nkeys;
+    if (MASK == VLM_MASK_CAUSAL_ID) {
+        const int last = min(S, (int)(blockIdx.x + 1) * BQ) - 1;
+        kend = min(kend, a.pos0 + last + 1);
+    }
+    const int seg_q = (MASK == VLM_MASK_SEGMENT_ID && qrow < S) ? a.seg[qrow] : 0;
+    const int nkt = (kend + BKEY - 1) / BKEY;
+
+    for (int kt = 0; kt < nkt; kt++) {
+        const int key0 = kt * BKEY;
+        for (int c = tid; c < BKEY * CH; c += 256) {
+            const int r = c / CH, d0 = (c % CH) * 8;
+            const int key = key0 + r;
+            u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+            if (key < a.nkeys) {
+                kv = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + d0);
+                vv = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + d0);
+            }
+            *reinterpret_cast<u32x4*>(Ks + r * LDK + d0) = kv;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                Vt[(d0 + 2 * i) * LDV + r] = (bf16_t)(vv[i] & 0xffffu);
+                Vt[(d0 + 2 * i + 1) * LDV + r] = (bf16_t)(vv[i] >> 16);
+            }
+        }
+        __syncthreads();
+        bool active = true;
+        if (MASK == VLM_MASK_CAUSAL_ID) active = key0 <= a.pos0 + q0 + 31;
+        if (active) {
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < DK; kk++) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * LDK + kk * 16 + hh * 8);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[kk], sacc[kb], 0, 0, 0);
+                }
+            }
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = key0 + kb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+                    float s = sacc[kb][r] * scale;
+                    bool vis = key < a.nkeys;
+                    if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
+                    if (MASK == VLM_MASK_SEGMENT_ID) vis = vis && qrow < S && a.seg[key] == seg_q;
+                    if (MASK == VLM_MASK_ADDITIVE_ID && vis && qrow < S)
+                        s += a.add[(size_t)qrow * a.ld_add + key] * kLog2e;
+                    s = vis ? s : -INFINITY;
+                    sacc[kb][r] = s;
+                    mt = fmaxf(mt, s);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+            const float mn = fmaxf(m, mt);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float alpha = exp2f(m - mu);
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float p = exp2f(sacc[kb][r] - mu);
+                    sacc[kb][r] = p;
+                    rs += p;
+                }
+            rs += __shfl_xor(rs, 32, kWave);
+            l = l * alpha + rs;
+            m = mn;
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) oacc[nb][r] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                for (int hs = 0; hs < 2; hs++) {
+                    // P = hi + lo with both parts bf16: the product with V keeps ~16
+                    // significant bits of P instead of 8.
+                    bf16x8 phi, plo;
+#pragma unroll
+                    for (int i = 0; i < 8; i++) {
+                        const float p = sacc[kb][hs * 8 + i];
+                        const bf16_t b = f2bf(p);
+                        phi[i] = __builtin_bit_cast(__bf16, b);
+                        plo[i] = __builtin_bit_cast(__bf16, f2bf(p - bf2f(b)));
+                    }
+                    const int kofs = kb * 32 + hs * 16 + hh * 4;
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        const bf16_t* vp = Vt + (nb * 32 + l32) * LDV + kofs;
+                        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+                        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+                        u32x4 raw = {lo.x, lo.y, hi.x, hi.y};
+                        const bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
+                        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, phi, oacc[nb], 0, 0, 0);
+                        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plo, oacc[nb], 0, 0, 0);
+                    }
+                }
+        }
+        __syncthreads();
+    }
+    if (qrow < S) {
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        bf16_t* O = (bf16_t*)a.out + (size_t)qrow * a.nq * D + (size_t)hq * D;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int n = nb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+                if (n < D) O[n] = f2bf(oacc[nb][r] * inv);
+            }
+    }
+}
+
+// ============================================================== prefill, f32
+template <int D, int MASK>
+__global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
+    constexpr int BQ = 128, KB = D >= 128 ? 1 : 2, BKEY = 32 * KB;
+    constexpr int NB = (D + 31) / 32, DP = NB * 32;
+    constexpr int LDK = D + 4, LDV = DP + 4;
+    constexpr int CH = D / 4;
+    __shared__ __attribute__((aligned(16))) float Ks[BKEY * LDK];
+    __shared__ __attribute__((aligned(16))) float Vs[BKEY * LDV];
+
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, hh = lane / 32, l32 = lane % 32;
+    const int hq = blockIdx.y, g = hq / (a.nq / a.nkv);
+    const int q0 = blockIdx.x * BQ + w * 32;
+    const int qrow = q0 + l32;
+    const int S = a.S;
+    const float* Q = (const float*)a.q + (size_t)hq * a.ldq * D;
+    const float* Kg = (const float*)a.k + (size_t)g * a.ldkv * D;
+    const float* Vg = (const float*)a.v + (size_t)g * a.ldkv * D;
+
+    if constexpr (DP > D) {
+        for (int i = tid; i < BKEY * (DP - D); i += 256) Vs[(i / (DP - D)) * LDV + D + i % (DP - D)] = 0.f;
+    }
+
+    float Qf[D / 2];
+#pragma unroll
+    for (int kk = 0; kk < D / 2; kk++) Qf[kk] = qrow < S ? Q[(size_t)qrow * D + kk * 2 + hh] : 0.f;
+    f32x16 oacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) oacc[nb][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float scale = kLog2e / sqrtf((float)D);
+
+    int kend = a.nkeys;
+    if (MASK == VLM_MASK_CAUSAL_ID) {
+        const int last = min(S, (int)(blockIdx.x + 1) * BQ) - 1;
+        kend = min(kend, a.pos0 + last + 1);
+    }
+    const int seg_q = (MASK == VLM_MASK_SEGMENT_ID && qrow < S) ? a.seg[qrow] : 0;
+    const int nkt = (kend + BKEY - 1) / BKEY;
+
+    for (int kt = 0; kt < nkt; kt++) {
+        const int key0 = kt * BKEY;
+        for (int c = tid; c < BKEY * CH; c += 256) {
+            const int r = c / CH, d0 = (c % CH) * 4;
+            const int key = key0 + r;
+            f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+            if (key < a.nkeys) {
+                kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)key * D + d0);
+                vv = *reinterpret_cast<const f32x4*>(Vg + (size_t)key * D + d0);
+            }
+            *reinterpret_cast<f32x4*>(Ks + r * LDK + d0) = kv;
+            *reinterpret_cast<f32x4*>(Vs + r * LDV + d0) = vv;
+        }
+        __syncthreads();
+        bool active = true;
+        if (MASK == VLM_MASK_CAUSAL_ID) active = key0 <= a.pos0 + q0 + 31;
+        if (active) {
+            f32x16 sacc[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
+                const float* kr = Ks + (kb * 32 + l32) * LDK + hh;
+#pragma unroll
+                for (int kk = 0; kk < D / 2; kk++)
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[kk * 2], Qf[kk], sacc[kb], 0, 0, 0);
+            }
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = key0 + kb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+                    float s = sacc[kb][r] * scale;
+                    bool vis = key < a.nkeys;
+                    if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
+                    if (MASK == VLM_MASK_SEGMENT_ID) vis = vis && qrow < S && a.seg[key] == seg_q;
+                    if (MASK == VLM_MASK_ADDITIVE_ID && vis && qrow < S)
+                        s += a.add[(size_t)qrow * a.ld_add + key] * kLog2e;
+                    s = vis ? s : -INFINITY;
+                    sacc[kb][r] = s;
+                    mt = fmaxf(mt, s);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+            const float mn = fmaxf(m, mt);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float alpha = exp2f(m - mu);
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float p = exp2f(sacc[kb][r] - mu);
+                    sacc[kb][r] = p;
+                    rs += p;
+                }
+            rs += __shfl_xor(rs, 32, kWave);
+            l = l * alpha + rs;
+            m = mn;
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) oacc[nb][r] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int kl = kb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+                    const float* vr = Vs + kl * LDV + l32;
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++)
+                        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[nb * 32], sacc[kb][r], oacc[nb], 0, 0, 0);
+                }
+        }
+        __syncthreads();
+    }
+    if (qrow < S) {
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        float* O = (float*)a.out + (size_t)qrow * a.nq * D + (size_t)hq * D;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int n = nb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+                if (n < D) O[n] = oacc[nb][r] * inv;
+            }
+    }
+}
+
+template <int D, int MASK>
+static hipError_t run_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
+    dim3 grid((a.S + 127) / 128, a.nq);
+    if (dtype == 1) {
+        if constexpr (D % 16 == 0) {
+            attn_prefill_bf16<D, MASK><<<grid, 256, 0, st>>>(a);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+        attn_prefill_f32<D, MASK><<<grid, 256, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t prefill_mask(int dtype, const AttnArgs& a, hipStream_t st) {
+    switch (a.mask_kind) {
+        case VLM_MASK_CAUSAL_ID: return run_prefill<D, VLM_MASK_CAUSAL_ID>(dtype, a, st);
+        case VLM_MASK_NONE_ID: return run_prefill<D, VLM_MASK_NONE_ID>(dtype, a, st);
+        case VLM_MASK_ADDITIVE_ID: return run_prefill<D, VLM_MASK_ADDITIVE_ID>(dtype, a, st);
+        case VLM_MASK_SEGMENT_ID: return run_prefill<D, VLM_MASK_SEGMENT_ID>(dtype, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
+    if (a.S <= 0) return hipSuccess;
+    switch (a.d) {
+        case 64: return prefill_mask<64>(dtype, a, st);
+        case 72: return prefill_mask<72>(dtype, a, st);
+        case 80: return prefill_mask<80>(dtype, a, st);
+        case 128: return prefill_mask<128>(dtype, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ============================================================== decode
+// partial layout: [nq][nsplit][D + 2]: o[0..D) (unnormalised), then m (log2 units), l.
+template <class T, int D, int G>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                                                          const T* __restrict__ vc, int W, int nkv,
+                                                          const int32_t* __restrict__ len, int nsplit,
+                                                          float* __restrict__ partial) {
+    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16;
+    __shared__ float sm_m[4][G], sm_l[4][G];
+    __shared__ float sm_o[4][G][D];
+    const int g = blockIdx.x, sp = blockIdx.y;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
+    const int T_ = len[0] + 1;
+    const int chunk = (T_ + nsplit - 1) / nsplit;
+    const int k0 = sp * chunk, k1 = min(T_, k0 + chunk);
+    const float scale = kLog2e / sqrtf((float)D);
+
+    float qf[G][CPL][VEC];
+#pragma unroll
+    for (int gg = 0; gg < G; gg++)
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+            const int ch = sub + 16 * c;
+            if (ch < CH) {
+                ld16(q + (size_t)(g * G + gg) * D + ch * VEC, qf[gg][c]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VEC; i++) qf[gg][c][i] = 0.f;
+            }
+        }
+    float mrun[G], lrun[G], o[G][CPL][VEC];
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+        mrun[gg] = -INFINITY;
+        lrun[gg] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; c++)
+#pragma unroll
+            for (int i = 0; i < VEC; i++) o[gg][c][i] = 0.f;
+    }
+    const T* Kg = kc + (size_t)g * W * D;
+    const T* Vg = vc + (size_t)g * W * D;
+    for (int j = k0 + w * 4 + kq; j < k1; j += 16) {
+        float kf[CPL][VEC], vf[CPL][VEC];
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+            const int ch = sub + 16 * c;
+            if (ch < CH) {
+                ld16(Kg + (size_t)j * D + ch * VEC, kf[c]);
+                ld16(Vg + (size_t)j * D + ch * VEC, vf[c]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VEC; i++) kf[c][i] = vf[c][i] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+                for (int i = 0; i < VEC; i++) s = fmaf(qf[gg][c][i], kf[c][i], s);
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
+            s *= scale;
+            const float mn = fmaxf(mrun[gg], s);
+            const float alpha = exp2f(mrun[gg] - mn);
+            const float p = exp2f(s - mn);
+            lrun[gg] = lrun[gg] * alpha + p;
+            mrun[gg] = mn;
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+                for (int i = 0; i < VEC; i++) o[gg][c][i] = o[gg][c][i] * alpha + p * vf[c][i];
+        }
+    }
+    // merge the four 16-lane groups of the wavefront (lanes sub, sub+16, sub+32, sub+48)
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            const float mo = __shfl_xor(mrun[gg], off, kWave);
+            const float lo = __shfl_xor(lrun[gg], off, kWave);
+            const float mn = fmaxf(mrun[gg], mo);
+            const float fa = mn == -INFINITY ? 0.f : exp2f(mrun[gg] - mn);
+            const float fb = mn == -INFINITY ? 0.f : exp2f(mo - mn);
+            lrun[gg] = lrun[gg] * fa + lo * fb;
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+                for (int i = 0; i < VEC; i++) {
+                    const float ov = __shfl_xor(o[gg][c][i], off, kWave);
+                    o[gg][c][i] = o[gg][c][i] * fa + ov * fb;
+                }
+            mrun[gg] = mn;
+        }
+        if (kq == 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                const int ch = sub + 16 * c;
+                if (ch < CH)
+#pragma unroll
+                    for (int i = 0; i < VEC; i++) sm_o[w][gg][ch * VEC + i] = o[gg][c][i];
+            }
+            if (sub == 0) {
+                sm_m[w][gg] = mrun[gg];
+                sm_l[w][gg] = lrun[gg];
+            }
+        }
+    }
+    __syncthreads();
+    // merge the four wavefronts and write the block partial
+    for (int idx = tid; idx < G * (D + 2); idx += 256) {
+        const int gg = idx / (D + 2), e = idx % (D + 2);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) mx = fmaxf(mx, sm_m[ww][gg]);
+        float v = 0.f;
+        if (e == D) {
+            v = mx;
+        } else {
+#pragma unroll
+            for (int ww = 0; ww < 4; ww++) {
+                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[ww][gg] - mx);
+                v += f * (e < D ? sm_o[ww][gg][e] : sm_l[ww][gg]);
+            }
+        }
+        partial[((size_t)(g * G + gg) * nsplit + sp) * (D + 2) + e] = v;
+    }
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ partial, int nsplit,
+                                                           T* __restrict__ out) {
+    const int h = blockIdx.x;
+    const float* p = partial + (size_t)h * nsplit * (D + 2);
+    float mx = -INFINITY;
+    for (int s = 0; s < nsplit; s++) mx = fmaxf(mx, p[s * (D + 2) + D]);
+    float lsum = 0.f;
+    for (int s = 0; s < nsplit; s++) {
+        const float ms = p[s * (D + 2) + D];
+        lsum += ms == -INFINITY ? 0.f : exp2f(ms - mx) * p[s * (D + 2) + D + 1];
+    }
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    for (int e = threadIdx.x; e < D; e += 128) {
+        float v = 0.f;
+        for (int s = 0; s < nsplit; s++) {
+            const float ms = p[s * (D + 2) + D];
+            if (ms != -INFINITY) v += exp2f(ms - mx) * p[s * (D + 2) + e];
+        }
+        Elt<T>::st(out, (size_t)h * D + e, v * inv);
+    }
+}
+
+int attn_decode_splits(int capacity) {
+    int n = (capacity + 63) / 64;
+    return n < 1 ? 1 : (n > 32 ? 32 : n);
+}
+
+template <class T, int D, int G>
+static hipError_t run_decode(const void* q, const void* k, const void* v, int W, int nq, int nkv, const int32_t* len,
+                             int nsplit, float* partial, void* out, hipStream_t st) {
+    attn_decode_kernel<T, D, G><<<dim3(nkv, nsplit), 256, 0, st>>>((const T*)q, (const T*)k, (const T*)v, W, nkv,
+                                                                   len, nsplit, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_combine_kernel<T, D><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out);
+    return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t decode_group(const void* q, const void* k, const void* v, int W, int nq, int nkv,
+                               const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st) {
+    switch (nq / nkv) {
+        case 1: return run_decode<T, D, 1>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+        case 2: return run_decode<T, D, 2>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+        case 4: return run_decode<T, D, 4>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+        case 8: return run_decode<T, D, 8>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+static hipError_t decode_dim(const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
+                             const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st) {
+    switch (d) {
+        case 64: return decode_group<T, 64>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+        case 72: return decode_group<T, 72>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+        case 80: return decode_group<T, 80>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+        case 128: return decode_group<T, 128>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
+                              const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st) {
+    return dtype == 1 ? decode_dim<bf16_t>(q, k, v, W, nq, nkv, d, len, nsplit, partial, out, st)
+                      : decode_dim<float>(q, k, v, W, nq, nkv, d, len, nsplit, partial, out, st);
+}
+
+}  // namespace vlm

@@ -1,0 +1,300 @@
+// Memory-bound helper kernels: embedding lookup and image-row injection
+// (Youtu-VL-4B ncnn port, 实现流程 §5), row norms feeding the GEMMs, QK-Norm +
+// rotate-half RoPE + KV-cache write (Youtu-VL-4B ncnn port, 实现难点 §2 and
+// 实现流程 §7; Penguin-VL ncnn port §2.3 for the two-segment form), RoPE table
+// construction, row gathers and weight packing.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace vlm {
+
+// ---------------------------------------------------------------- embedding
+template <class T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ table, int V, int H,
+                                                    const int32_t* __restrict__ ids, float* __restrict__ x) {
+    const int s = blockIdx.x;
+    const int id = ids[s];
+    float* row = x + (size_t)s * H;
+    if (id < 0 || id >= V) {
+        for (int j = threadIdx.x; j < H; j += 256) row[j] = __uint_as_float(0x7fc00000u);
+        return;
+    }
+    const T* src = table + (size_t)id * H;
+    for (int j = threadIdx.x; j < H; j += 256) row[j] = Elt<T>::ld(src, j);
+}
+
+// One row: the embedding of tok[0], or a copy of xin when xin != null.
+template <class T>
+__global__ __launch_bounds__(256) void embed_row_kernel(const T* __restrict__ table, int V, int H,
+                                                        const int32_t* __restrict__ tok, const float* __restrict__ xin,
+                                                        float* __restrict__ x) {
+    if (xin) {
+        for (int j = threadIdx.x; j < H; j += 256) x[j] = xin[j];
+        return;
+    }
+    const int id = tok[0];
+    if (id < 0 || id >= V) {
+        for (int j = threadIdx.x; j < H; j += 256) x[j] = __uint_as_float(0x7fc00000u);
+        return;
+    }
+    const T* src = table + (size_t)id * H;
+    for (int j = threadIdx.x; j < H; j += 256) x[j] = Elt<T>::ld(src, j);
+}
+
+// ---------------------------------------------------------------- injection
+// Row s with ids[s] == pid gets image row rank(s) = #{j < s : ids[j] == pid}.
+template <class T>
+__global__ __launch_bounds__(256) void inject_kernel(float* __restrict__ x, int H, const int32_t* __restrict__ ids,
+                                                     int pid, const T* __restrict__ img, int n_img) {
+    __shared__ int red[4];
+    const int s = blockIdx.x;
+    if (ids[s] != pid) return;
+    int c = 0;
+    for (int j = threadIdx.x; j < s; j += 256) c += (ids[j] == pid);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, kWave);
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = c;
+    __syncthreads();
+    const int rank = red[0] + red[1] + red[2] + red[3];
+    if (rank >= n_img) return;
+    const T* src = img + (size_t)rank * H;
+    float* dst = x + (size_t)s * H;
+    for (int j = threadIdx.x; j < H; j += 256) dst[j] = Elt<T>::ld(src, j);
+}
+
+__global__ void set_len_kernel(int32_t* len, int v) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) len[0] = v;
+}
+
+__global__ void inc_len_kernel(int32_t* len) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) len[0] = len[0] + 1;
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ s, float* __restrict__ d, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------- row norms
+// RMSNorm: y = x * rsqrt(mean(x^2) + eps) * g. LayerNorm: y = (x - mu) * rsqrt(var + eps) * g + b.
+// Output rounded to the operand type. One block per row.
+template <class T, bool LAYER>
+__global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict__ x, int H, const T* __restrict__ g,
+                                                        const T* __restrict__ b, float eps, T* __restrict__ out) {
+    __shared__ float red[4];
+    const float* row = x + (size_t)blockIdx.x * H;
+    float mu = 0.f;
+    if (LAYER) {
+        float s = 0.f;
+        for (int j = threadIdx.x; j < H; j += 256) s += row[j];
+        mu = block_sum<256>(s, red) / (float)H;
+    }
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < H; j += 256) {
+        const float v = row[j] - mu;
+        ss += v * v;
+    }
+    const float r = rsqrtf(block_sum<256>(ss, red) / (float)H + eps);
+    T* o = out + (size_t)blockIdx.x * H;
+    for (int j = threadIdx.x; j < H; j += 256) {
+        float y = (row[j] - mu) * r * Elt<T>::ld(g, j);
+        if (LAYER && b) y += Elt<T>::ld(b, j);
+        Elt<T>::st(o, j, y);
+    }
+}
+
+// ---------------------------------------------------------------- QK-Norm + RoPE + cache write
+// One wavefront per (row, head); lane p < d/2 owns rotation pair p, i.e. the
+// elements i0 = g*sd + j and i1 = i0 + sd/2 of segment g (sd = d/segments).
+// rotate_half(a, b) = (-b, a): y[i0] = a cos - b sin, y[i1] = b cos + a sin.
+template <class T>
+__global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
+    const int wave = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int nh = a.nq + 2 * a.nkv;
+    if (wave >= a.S * nh) return;
+    const int s = wave / nh, h = wave % nh;
+    const int d = a.d, half = d / 2;
+    const int base = a.pos_dev ? a.pos_dev[0] : a.pos0;
+    const int pos = base + s;
+    const float* src = a.qkv + (size_t)s * nh * d + (size_t)h * d;
+    const bool on = lane < half;
+    const int sd = d / a.segments, sh = sd / 2;
+    const int g = on ? lane / sh : 0, j = on ? lane % sh : 0;
+    const int i0 = g * sd + j, i1 = i0 + sh;
+    float x0 = on ? src[i0] : 0.f, x1 = on ? src[i1] : 0.f;
+    if (h >= a.nq + a.nkv) {  // V head: plain copy (rounded to the cache type)
+        if (on) {
+            T* dst = (T*)a.vdst + ((size_t)(h - a.nq - a.nkv) * a.ldkv + pos) * d;
+            Elt<T>::st(dst, i0, x0);
+            Elt<T>::st(dst, i1, x1);
+        }
+        return;
+    }
+    const bool isq = h < a.nq;
+    const T* gn = (const T*)(isq ? a.qn : a.kn);
+    if (gn) {
+        const float ms = wave_sum(x0 * x0 + x1 * x1) / (float)d;
+        const float r = rsqrtf(ms + a.eps);
+        if (on) {
+            x0 = x0 * r * Elt<T>::ld(gn, i0);
+            x1 = x1 * r * Elt<T>::ld(gn, i1);
+        }
+    }
+    if (!on) return;
+    const float* cr = a.cos + (size_t)pos * d;
+    const float* sr = a.sin + (size_t)pos * d;
+    const float y0 = x0 * cr[i0] - x1 * sr[i0];
+    const float y1 = x1 * cr[i1] + x0 * sr[i1];
+    T* dst = isq ? (T*)a.q + ((size_t)h * a.ldq + s) * d : (T*)a.kdst + ((size_t)(h - a.nq) * a.ldkv + pos) * d;
+    Elt<T>::st(dst, i0, y0);
+    Elt<T>::st(dst, i1, y1);
+}
+
+// ---------------------------------------------------------------- RoPE tables
+struct AxisMap { int32_t ax[64]; };
+__global__ __launch_bounds__(64) void rope_table_kernel(const int32_t* __restrict__ pos, int n_rows, AxisMap am,
+                                                        int segments, int d, double theta, float* __restrict__ cosv,
+                                                        float* __restrict__ sinv) {
+    const int row = blockIdx.x;
+    const int p = threadIdx.x;
+    if (p >= d / 2) return;
+    const int sd = d / segments, sh = sd / 2;
+    const int g = p / sh, j = p % sh;
+    const double inv = pow(theta, -2.0 * (double)j / (double)sd);
+    const double ang = (double)pos[(size_t)am.ax[p] * n_rows + row] * inv;
+    const float c = (float)cos(ang), s = (float)sin(ang);
+    const size_t o = (size_t)row * d + g * sd + j;
+    cosv[o] = c;
+    cosv[o + sh] = c;
+    sinv[o] = s;
+    sinv[o + sh] = s;
+}
+
+// ---------------------------------------------------------------- gathers / packing
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ src, int n_src,
+                                                          const int32_t* __restrict__ idx, int row_len,
+                                                          float* __restrict__ dst) {
+    const int r = blockIdx.x;
+    const int i = idx[r];
+    float* o = dst + (size_t)r * row_len;
+    if (i < 0 || i >= n_src) {
+        for (int j = threadIdx.x; j < row_len; j += 256) o[j] = __uint_as_float(0x7fc00000u);
+        return;
+    }
+    const float* s = src + (size_t)i * row_len;
+    for (int j = threadIdx.x; j < row_len; j += 256) o[j] = s[j];
+}
+
+// out row 64g + r (r < 32) = wg row 32g + r; out row 64g + 32 + r = wu row 32g + r.
+template <class T>
+__global__ __launch_bounds__(256) void pack_gate_up_kernel(const T* __restrict__ wg, const T* __restrict__ wu, int H,
+                                                           T* __restrict__ out) {
+    const int orow = blockIdx.x;
+    const int g = orow / 64, r = orow % 64;
+    const T* src = (r < 32 ? wg : wu) + (size_t)(32 * g + (r % 32)) * H;
+    T* o = out + (size_t)orow * H;
+    for (int j = threadIdx.x; j < H; j += 256) o[j] = src[j];
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_embed(int dtype, const void* table, int V, int H, const int32_t* ids, int S, float* x,
+                        hipStream_t st) {
+    if (S <= 0) return hipSuccess;
+    if (dtype == 1)
+        embed_kernel<bf16_t><<<S, 256, 0, st>>>((const bf16_t*)table, V, H, ids, x);
+    else
+        embed_kernel<float><<<S, 256, 0, st>>>((const float*)table, V, H, ids, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_or_copy(int dtype, const void* table, int V, int H, const int32_t* tok, const float* xin,
+                                float* x, hipStream_t st) {
+    if (dtype == 1)
+        embed_row_kernel<bf16_t><<<1, 256, 0, st>>>((const bf16_t*)table, V, H, tok, xin, x);
+    else
+        embed_row_kernel<float><<<1, 256, 0, st>>>((const float*)table, V, H, tok, xin, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_inject(int img_dtype, float* x, int S, int H, const int32_t* ids, int pid, const void* img,
+                         int n_img, hipStream_t st) {
+    if (S <= 0 || n_img <= 0) return hipSuccess;
+    if (img_dtype == 1)
+        inject_kernel<bf16_t><<<S, 256, 0, st>>>(x, H, ids, pid, (const bf16_t*)img, n_img);
+    else
+        inject_kernel<float><<<S, 256, 0, st>>>(x, H, ids, pid, (const float*)img, n_img);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_len(int32_t* len, int value, hipStream_t st) {
+    set_len_kernel<<<1, 64, 0, st>>>(len, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_inc_len(int32_t* len, hipStream_t st) {
+    inc_len_kernel<<<1, 64, 0, st>>>(len);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    copy_f32_kernel<<<blocks, 256, 0, st>>>(src, dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H, const void* gain, const void* shift,
+                            float eps, void* out, hipStream_t st) {
+    if (R <= 0) return hipSuccess;
+    if (dtype == 1) {
+        if (layer)
+            norm_rows_kernel<bf16_t, true><<<R, 256, 0, st>>>(x, H, (const bf16_t*)gain, (const bf16_t*)shift, eps, (bf16_t*)out);
+        else
+            norm_rows_kernel<bf16_t, false><<<R, 256, 0, st>>>(x, H, (const bf16_t*)gain, nullptr, eps, (bf16_t*)out);
+    } else {
+        if (layer)
+            norm_rows_kernel<float, true><<<R, 256, 0, st>>>(x, H, (const float*)gain, (const float*)shift, eps, (float*)out);
+        else
+            norm_rows_kernel<float, false><<<R, 256, 0, st>>>(x, H, (const float*)gain, nullptr, eps, (float*)out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_qkv(int dtype, const RopeArgs& a, hipStream_t st) {
+    const int waves = a.S * (a.nq + 2 * a.nkv);
+    if (waves <= 0) return hipSuccess;
+    const int blocks = (waves + 3) / 4;
+    if (dtype == 1)
+        rope_qkv_kernel<bf16_t><<<blocks, 256, 0, st>>>(a);
+    else
+        rope_qkv_kernel<float><<<blocks, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const int32_t* pos, int n_axes, int n_rows, const int32_t* axis_of_pair, int segments,
+                             int d, double theta, float* cos, float* sin, hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    AxisMap am;
+    for (int i = 0; i < 64; i++) am.ax[i] = i < d / 2 ? axis_of_pair[i] : 0;
+    (void)n_axes;
+    rope_table_kernel<<<n_rows, 64, 0, st>>>(pos, n_rows, am, segments, d, theta, cos, sin);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const float* src, int n_src, const int32_t* idx, int n_rows, int row_len, float* dst,
+                              hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    gather_rows_kernel<<<n_rows, 256, 0, st>>>(src, n_src, idx, row_len, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_gate_up(int dtype, const void* wg, const void* wu, int F, int H, void* out, hipStream_t st) {
+    if (dtype == 1)
+        pack_gate_up_kernel<bf16_t><<<2 * F, 256, 0, st>>>((const bf16_t*)wg, (const bf16_t*)wu, H, (bf16_t*)out);
+    else
+        pack_gate_up_kernel<float><<<2 * F, 256, 0, st>>>((const float*)wg, (const float*)wu, H, (float*)out);
+    return hipGetLastError();
+}
+
+}  // namespace vlm

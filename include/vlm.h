@@ -1,0 +1,299 @@
+/*
+ * vlm.h — C ABI of the MI355X (gfx950) VLM decoder hot path.
+ *
+ * The library runs, on one GPU, the decoder stack that a vision-language
+ * model executes after its vision tower: embedding lookup, injection of
+ * projected image rows into the placeholder positions, parallel causal
+ * prefill that fills a per-layer fixed-window KV cache, one-token KV-cache
+ * decode, final RMSNorm, lm_head and greedy argmax; plus the window/full
+ * attention ViT stack with its 2x2 patch merger.
+ *
+ * Sources (page title, section) cited below:
+ *   [Youtu]   Youtu-VL-4B ncnn port (ncnn discussion #6850)
+ *   [Penguin] Penguin-VL ncnn port (ncnn discussion #6868)
+ *   [HyOCR15] HunyuanOCR v1.5 ncnn port, technical report (ncnn discussion #6846)
+ *   [HyOCR10] HunyuanOCR v1.0 ncnn port (ncnn discussion #6847)
+ *   [MNN]     MNN llm_demo Omni article (hmyw.cn news 148174)
+ *
+ * Conventions for every entry point:
+ *   - Pointers prefixed d_ are device pointers, h_ are host pointers. Every
+ *     device buffer belongs to the caller; the library never allocates or
+ *     frees device memory. Pointers are borrowed: they must stay valid until
+ *     the work enqueued on `stream` has completed. Host arrays are read during
+ *     the call only.
+ *   - All device work is enqueued asynchronously on the caller's `stream`.
+ *   - Every argument, shape, count and capacity check runs before anything is
+ *     enqueued, so a call that returns an error has changed nothing (the KV
+ *     length included). A HIP launch failure returns VLM_ERR_HIP; faults of
+ *     earlier asynchronous work surface at the caller's next synchronisation.
+ *   - vlm_last_error() returns a thread-local description of the last error.
+ *   - A vlm_kv handle and a workspace must not be used by two streams at once.
+ *   - Weight element type: desc->dtype (VLM_F32 -> float, VLM_BF16 -> bfloat16
+ *     bits). All matrices are row-major, [out_features][in_features].
+ */
+#ifndef VLM_H
+#define VLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VLM_OK = 0,
+    VLM_ERR_ARG = -1,            /* NULL / misaligned pointer, bad enum value */
+    VLM_ERR_SHAPE = -2,          /* sizes inconsistent or unsupported by the kernels */
+    VLM_ERR_CAPACITY = -3,       /* sequence would exceed the KV window or the RoPE table */
+    VLM_ERR_COUNT_MISMATCH = -4, /* placeholder count != image rows */
+    VLM_ERR_DTYPE = -5,          /* dtype not valid for this call */
+    VLM_ERR_NONFINITE = -6,      /* reserved for host wrappers: argmax over non-finite logits */
+    VLM_ERR_HIP = -7,            /* a HIP runtime call failed */
+    VLM_ERR_UNSUPPORTED = -8,    /* valid request that this build has no kernel for */
+    VLM_ERR_WORKSPACE = -9       /* workspace too small */
+} vlm_status;
+
+typedef enum { VLM_F32 = 0, VLM_BF16 = 1 } vlm_dtype;
+typedef enum { VLM_BLOCK_DECODER = 0, VLM_BLOCK_VIT = 1 } vlm_block_kind;
+
+/* Attention masks of the prefill ([Youtu] 实现流程 §3 and §7; [HyOCR10] 五.6).
+ * CAUSAL:   query row s (position pos0+s) sees cache slots 0..pos0+s.
+ * NONE:     every query row sees slots 0..pos0+S-1.
+ * ADDITIVE: every query row sees slots 0..pos0+S-1 and add[s*ld_add + j] is
+ *           added to the scaled score of slot j (the pages' finite 0 / -1e9
+ *           form; any finite values are allowed).
+ * SEGMENT:  non-causal, pos0 must be 0: row s sees row j iff seg[s] == seg[j]
+ *           (the block-diagonal window mask of the vision tower). */
+typedef enum { VLM_MASK_CAUSAL = 0, VLM_MASK_NONE = 1, VLM_MASK_ADDITIVE = 2, VLM_MASK_SEGMENT = 3 } vlm_mask_kind;
+
+typedef struct {
+    int32_t kind;          /* vlm_mask_kind */
+    int32_t ld_add;        /* ADDITIVE: row stride of add in floats, >= pos0+S */
+    const float* add;      /* ADDITIVE: d_ [S][ld_add] fp32; else NULL */
+    const int32_t* seg;    /* SEGMENT: d_ [S] segment ids; else NULL */
+} vlm_mask;
+
+/* Model shape ([Penguin] §2.1 for the Qwen3 fields; [Youtu] 实现流程 §3 for the ViT).
+ * Kernels exist for head_dim in {64, 72, 80, 128}; hidden, ffn and
+ * n_q_heads*head_dim must be multiples of 8; a decoder's ffn a multiple of 32;
+ * n_q_heads a multiple of n_kv_heads (GQA: query head h reads KV head
+ * h / (n_q_heads / n_kv_heads), [Penguin] §3). */
+typedef struct {
+    int32_t block_kind;    /* vlm_block_kind */
+    int32_t n_layers;
+    int32_t hidden;        /* H */
+    int32_t n_q_heads;     /* nq */
+    int32_t n_kv_heads;    /* nkv (ViT: equal to nq) */
+    int32_t head_dim;      /* d */
+    int32_t ffn;           /* F */
+    int32_t vocab;         /* V rows of the embedding / lm_head table; 0 = none */
+    int32_t dtype;         /* vlm_dtype of weights, gains, table, KV cache and GEMM operands */
+    int32_t qk_norm;       /* 1: per-head RMSNorm of q and k before RoPE (Qwen3 order, [Penguin] §5.4) */
+    int32_t rope_segments; /* 1: rotate-half over the whole head; 2: each half rotated on its own (2D vision RoPE, [Penguin] §2.3) */
+    float norm_eps;        /* RMSNorm / LayerNorm epsilon (1e-6) */
+} vlm_model_desc;
+
+/* Per-layer weights (device pointers, element type desc->dtype).
+ * Decoder ([Penguin] §2.1, §4.2): RMSNorm gains attn_norm, mlp_norm [H];
+ *   wqkv [(nq+2*nkv)*d][H] = rows of Wq, then Wk, then Wv (see vlm_pack_qkv);
+ *   q_norm, k_norm [d] (qk_norm only); wo [H][nq*d];
+ *   w1 [2F][H] = gate and up rows interleaved in groups of 32 rows: rows
+ *   64g..64g+31 are gate rows 32g..32g+31 and rows 64g+32..64g+63 the up rows
+ *   32g..32g+31 (see vlm_pack_gate_up); w2 = down [H][F]. Biases NULL.
+ * ViT ([Youtu] 实现流程 §3): LayerNorm gain/shift attn_norm/attn_norm_b and
+ *   mlp_norm/mlp_norm_b [H]; wqkv [3*nq*d][H] + bqkv; wo [H][nq*d] + bo;
+ *   w1 = fc1 [F][H] + b1; w2 = fc2 [H][F] + b2. GELU (tanh form) after fc1. */
+typedef struct {
+    const void* attn_norm;
+    const void* attn_norm_b;
+    const void* wqkv;
+    const void* bqkv;
+    const void* q_norm;
+    const void* k_norm;
+    const void* wo;
+    const void* bo;
+    const void* mlp_norm;
+    const void* mlp_norm_b;
+    const void* w1;
+    const void* b1;
+    const void* w2;
+    const void* b2;
+} vlm_layer;
+
+/* ------------------------------------------------------------------------- */
+/* KV cache ([Youtu] 实现流程 §7: fixed window per layer, runtime-owned slots;
+ * [HyOCR15] §3.7: cache stays resident on the device).
+ * The caller provides one device buffer of vlm_kv_bytes() bytes. Layout:
+ *   bytes [0, 256): device header (int32 length at offset 0, rest reserved);
+ *   then K/V elements of type desc->dtype as [L][2][nkv][W][d] (index 0 = K,
+ *   1 = V; d contiguous), so one decode split reads a contiguous run of slots
+ *   of one KV head.
+ * The handle keeps a host mirror of the length; kernels use the device copy,
+ * which lets a captured decode step replay unchanged. */
+typedef struct vlm_kv vlm_kv;
+
+/* Bytes needed for a cache of `capacity` slots per layer. */
+vlm_status vlm_kv_bytes(const vlm_model_desc* desc, int32_t capacity, size_t* bytes);
+/* Binds caller memory (256-byte aligned, >= vlm_kv_bytes) to a new host
+ * handle and enqueues a kernel that sets the device length to 0. */
+vlm_status vlm_kv_alloc(const vlm_model_desc* desc, int32_t capacity, void* d_buf, size_t bytes,
+                        hipStream_t stream, vlm_kv** out);
+/* Frees the host handle (and its cached decode graph), not the device memory. */
+vlm_status vlm_kv_free(vlm_kv* kv);
+/* Host mirror of the number of valid slots. */
+vlm_status vlm_kv_len(const vlm_kv* kv, int32_t* len);
+/* Shrinks the valid length to new_len <= current length (host mirror and,
+ * through an enqueued kernel, the device copy); slots >= new_len are then
+ * treated as empty. Used to commit only an accepted prefix after a
+ * multi-token verify ([HyOCR15] §3.8). */
+vlm_status vlm_kv_truncate(vlm_kv* kv, int32_t new_len, hipStream_t stream);
+
+/* Bytes of scratch needed by vlm_prefill (S <= max_rows), vlm_decode_step,
+ * vlm_decode_loop and vlm_lmhead_argmax for this model. */
+vlm_status vlm_workspace_bytes(const vlm_model_desc* desc, int32_t max_rows, size_t* bytes);
+
+/* ------------------------------------------------------------------------- */
+/* Weight packing (device to device copies, element type dtype).
+ * vlm_pack_qkv: out [(nq+2nkv)*d][H] = concat(wq [nq*d][H], wk [nkv*d][H], wv [nkv*d][H]).
+ * vlm_pack_gate_up: out [2F][H] interleaved in 32-row groups as vlm_layer.w1 states; F % 32 == 0. */
+vlm_status vlm_pack_qkv(const void* d_wq, const void* d_wk, const void* d_wv, int32_t q_rows, int32_t kv_rows,
+                        int32_t hidden, int32_t dtype, void* d_out, hipStream_t stream);
+vlm_status vlm_pack_gate_up(const void* d_wg, const void* d_wu, int32_t ffn, int32_t hidden, int32_t dtype,
+                            void* d_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* RoPE tables ([Youtu] 实现难点 §2 and 实现流程 §6: q*cos + rotate_half(q)*sin
+ * with cos/sin fed from the runtime; [Penguin] §2.3: 2D split of the head;
+ * [HyOCR15] §3.3: several position-id axes select frequencies).
+ * d_pos: [n_axes][n_rows] int32 positions. The head is split into
+ * rope_segments segments of length s = head_dim/rope_segments; rotation pair j
+ * of segment g (elements g*s+j and g*s+j+s/2) turns by
+ * pos[h_axis_of_pair[g*s/2 + j]][row] * theta^(-2j/s), computed in float64 and
+ * rounded to float. Writes d_cos, d_sin [n_rows][head_dim] fp32. */
+vlm_status vlm_rope_table(const int32_t* d_pos, int32_t n_axes, int32_t n_rows, const int32_t* h_axis_of_pair,
+                          int32_t rope_segments, int32_t head_dim, double theta, float* d_cos, float* d_sin,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Embedding lookup ([Youtu] 实现流程 §5 and §6: tied [V][H] table, looked up
+ * by the runtime). d_x[s][:] = float(d_embed[d_ids[s]][:]) for s < S.
+ * An id outside [0, V) is not read: its row is written as NaN, which a later
+ * argmax reports as non-finite. */
+vlm_status vlm_embed(const vlm_model_desc* desc, const void* d_embed, const int32_t* d_ids, int32_t S,
+                     float* d_x, hipStream_t stream);
+
+/* Image-row injection ([Youtu] 实现流程 §5; [HyOCR15] §3.2): the rows whose
+ * id equals placeholder_id are, in increasing position order, overwritten by
+ * d_img rows 0..n_img-1 (exact copies, img_dtype VLM_F32 or VLM_BF16).
+ * The count of placeholders in h_ids (host copy of the ids) must equal n_img,
+ * else VLM_ERR_COUNT_MISMATCH and nothing is enqueued. d_ids is the device
+ * copy of the same ids, which the kernel ranks; a placeholder whose rank is
+ * >= n_img (ids differing from h_ids) is skipped, so no read goes out of bounds. */
+vlm_status vlm_inject_image_embeds(const vlm_model_desc* desc, float* d_x, int32_t S, const int32_t* h_ids,
+                                   const int32_t* d_ids, int32_t placeholder_id, const void* d_img, int32_t n_img,
+                                   int32_t img_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Parallel prefill over all layers ([Youtu] 实现流程 §6-§7; [HyOCR10] 四.3:
+ * per layer (x, cos, sin, mask) -> hidden and K/V for the cache).
+ * d_x [S][H] fp32: input rows on entry, hidden state after the last layer
+ * (before the final norm) on return. Row s has position pos0+s and uses row
+ * pos0+s of d_cos/d_sin ([table_rows][d] fp32).
+ * masks: n_masks == 1 (same mask for every layer) or n_layers.
+ * Decoder: kv must be bound; requires pos0 <= current length and
+ *   pos0+S <= capacity (else VLM_ERR_CAPACITY: an over-long sequence is
+ *   rejected, [Youtu] 已知限制); K/V of the rows go to slots pos0..pos0+S-1;
+ *   afterwards the length is pos0+S. A CAUSAL prefill with pos0 > 0 is a
+ *   chunked prefill / multi-token verify over the existing cache.
+ * ViT: kv must be NULL, pos0 == 0; K/V live in the workspace.
+ * Workspace: d_ws of ws_bytes >= vlm_workspace_bytes(desc, S). */
+vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, float* d_x, int32_t S, int32_t pos0,
+                       const float* d_cos, const float* d_sin, int32_t table_rows, const vlm_mask* h_masks,
+                       int32_t n_masks, vlm_kv* kv, void* d_ws, size_t ws_bytes, hipStream_t stream);
+
+/* Final RMSNorm + lm_head + greedy argmax of one row ([Youtu] 实现流程 §6 and
+ * 解码与采样说明; [HyOCR15] §3.4: a single [V][H] table, one weight copy).
+ * d_token_out[0] = index of the largest logit (lowest index on ties); -1 if any
+ * logit is NaN or infinite. d_logits ([V] fp32) receives the logits when
+ * non-NULL. The table may alias the embedding (tied weights). */
+vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
+                             const float* d_x_row, int32_t* d_token_out, float* d_logits, void* d_ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* One-token decode step ([Youtu] 实现流程 §8; [HyOCR10] 四.4: q/k/v of the new
+ * token, K/V written into slot t, attention over the window with slots > t
+ * masked; [HyOCR15] §3.7: one submission per token, cache committed on success).
+ * t = device length. The input row is d_x_in ([H] fp32) when non-NULL, else
+ * the embedding row of d_token_in[0]. Runs every layer at position t (RoPE row
+ * t), then, when d_table is non-NULL, final norm + lm_head + argmax into
+ * d_token_out[0] (may alias d_token_in) and, when d_token_hist is non-NULL,
+ * into d_token_hist[t+1] (array of capacity+1 ints). d_x_out ([H]) receives the
+ * hidden row after the last layer when non-NULL. Device length becomes t+1.
+ * Requires host length < capacity and < table_rows. */
+vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                           const void* d_final_norm, const void* d_table, vlm_kv* kv, const int32_t* d_token_in,
+                           const float* d_x_in, const float* d_cos, const float* d_sin, int32_t table_rows,
+                           int32_t* d_token_out, float* d_x_out, int32_t* d_token_hist, void* d_ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* n_steps greedy decode steps with each step's token feeding the next
+ * (d_token_io is read and written by every step). The first call captures one
+ * step into a HIP graph, cached on the kv handle and re-captured when any
+ * argument changes; each step is then one graph launch on `stream`, and the
+ * host never synchronises inside the loop. Requires vocab > 0 and
+ * length + n_steps <= min(capacity, table_rows). */
+vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                           const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
+                           const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
+                           int32_t n_steps, void* d_ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Vision tower helpers ([Youtu] 实现流程 §3: window grouping is a permutation
+ * built by the runtime, the mask block-diagonal, 2x2 neighbours concatenated).
+ * Input rows are 2x2-group-major: rows 4u..4u+3 are the merge*merge patches of
+ * merge unit u (units in raster order of the merged grid, patches in raster
+ * order inside the unit). Windows tile the merged grid in window x window
+ * cells; units are permuted window by window (raster inside a window).
+ * Host-only; writes h_unit_perm [n_units] (raster unit at permuted slot p),
+ * h_row_perm [n_rows] (input row at permuted row r), h_row_seg [n_rows]
+ * (window id of permuted row r) and h_pos [2][n_rows] (patch row h, then patch
+ * column w, of permuted row r). Any output pointer may be NULL. */
+vlm_status vlm_vit_window_index(int32_t grid_h, int32_t grid_w, int32_t merge, int32_t window,
+                                int32_t* h_unit_perm, int32_t* h_row_perm, int32_t* h_row_seg, int32_t* h_pos);
+
+/* d_dst[r][:] = d_src[d_idx[r]][:] for r < n_rows (fp32 rows of row_len);
+ * an index outside [0, n_src) yields a NaN row. */
+vlm_status vlm_gather_rows(const float* d_src, int32_t n_src, const int32_t* d_idx, int32_t n_rows,
+                           int32_t row_len, float* d_dst, hipStream_t stream);
+
+typedef struct {
+    int32_t hidden;        /* H of the tower */
+    int32_t merge;         /* 2: 2x2 neighbours */
+    int32_t merger_hidden; /* width of the first merger layer */
+    int32_t out_dim;       /* language-model width */
+    int32_t dtype;         /* vlm_dtype (VLM_F32) */
+    float norm_eps;
+    const void* post_ln;   /* [H] */
+    const void* post_ln_b; /* [H] */
+    const void* w1;        /* [merger_hidden][merge*merge*H] */
+    const void* b1;
+    const void* w2;        /* [out_dim][merger_hidden] */
+    const void* b2;
+} vlm_merger;
+
+/* post_layernorm -> view [N/m^2][m^2*H] (2x2 concat of the permuted rows) ->
+ * Linear + GELU -> Linear -> rows written in raster unit order:
+ * d_out[d_unit_perm[p]][:] = result row p. d_x [N][H] fp32 (permuted order). */
+vlm_status vlm_vit_merger(const vlm_merger* m, const float* d_x, int32_t N, const int32_t* d_unit_perm,
+                          float* d_out, void* d_ws, size_t ws_bytes, hipStream_t stream);
+vlm_status vlm_vit_merger_workspace_bytes(const vlm_merger* m, int32_t N, size_t* bytes);
+
+/* Thread-local description of the last error. */
+const char* vlm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VLM_H */

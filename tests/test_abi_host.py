@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/vlm.h declares, and rejects bad arguments before any
+device work (no compute calls are made here)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decoder_prefill_decode_amd import native as N
+from oracle import vit as ov
+import vlm_synth as vs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "vlm.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vlm_[a-z0-9_]+)\s*\(", src)))
+
+
+def desc(**kw):
+    base = dict(block_kind=0, n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=768, vocab=4096,
+                dtype=N.VLM_F32, qk_norm=0, rope_segments=1, norm_eps=1e-6)
+    base.update(kw)
+    return N.ModelDesc(**base)
+
+
+def test_library_exports_every_declared_symbol():
+    L = N.lib()
+    names = declared()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(names) == set(N._SIG), "binding signatures out of sync with the header"
+
+
+def test_kv_and_workspace_sizes():
+    d = desc()
+    n = C.c_size_t()
+    N.call("vlm_kv_bytes", C.byref(d), 64, C.byref(n))
+    assert n.value == N.KV_HEADER_BYTES + 2 * 2 * 2 * 64 * 64 * 4
+    d = desc(dtype=N.VLM_BF16)
+    N.call("vlm_kv_bytes", C.byref(d), 64, C.byref(n))
+    assert n.value == N.KV_HEADER_BYTES + 2 * 2 * 2 * 64 * 64 * 2
+    N.call("vlm_workspace_bytes", C.byref(d), 512, C.byref(n))
+    assert n.value > 512 * 256 * 2
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n_q_heads=5), N.VLM_ERR_SHAPE),            # nq % nkv != 0
+    (dict(head_dim=96), N.VLM_ERR_UNSUPPORTED),
+    (dict(dtype=7), N.VLM_ERR_DTYPE),
+    (dict(ffn=770), N.VLM_ERR_SHAPE),
+    (dict(ffn=776), N.VLM_ERR_SHAPE),                 # decoder ffn not a multiple of 32
+    (dict(dtype=N.VLM_BF16, head_dim=72), N.VLM_ERR_UNSUPPORTED),
+    (dict(n_q_heads=6, n_kv_heads=2), N.VLM_ERR_UNSUPPORTED),  # group of 3
+    (dict(block_kind=1, n_kv_heads=2), N.VLM_ERR_UNSUPPORTED),
+    (dict(rope_segments=3), N.VLM_ERR_ARG),
+])
+def test_desc_validation(bad, status):
+    d = desc(**bad)
+    n = C.c_size_t()
+    assert N.lib().vlm_workspace_bytes(C.byref(d), 16, C.byref(n)) == status
+    assert N.last_error()
+
+
+def test_inject_count_mismatch_rejected_before_launch():
+    d = desc()
+    ids = np.array([1, 4095, 4095, 3], np.int32)
+    fake = C.c_void_p(0x1000)        # never dereferenced: the check fails first
+    st = N.lib().vlm_inject_image_embeds(C.byref(d), fake, 4, ids.ctypes.data_as(C.POINTER(C.c_int32)), fake, 4095,
+                                         fake, 3, N.VLM_F32, None)
+    assert st == N.VLM_ERR_COUNT_MISMATCH
+    assert "2 placeholder" in N.last_error()
+
+
+def test_rope_table_argument_checks():
+    axes = np.zeros(32, np.int32)
+    P = C.POINTER(C.c_int32)
+    fake = C.c_void_p(0x1000)
+    L = N.lib()
+    assert L.vlm_rope_table(fake, 1, 8, axes.ctypes.data_as(P), 1, 256, 1e6, fake, fake, None) == N.VLM_ERR_UNSUPPORTED
+    axes[3] = 2
+    assert L.vlm_rope_table(fake, 2, 8, axes.ctypes.data_as(P), 1, 64, 1e6, fake, fake, None) == N.VLM_ERR_ARG
+    axes[3] = 0
+    assert L.vlm_rope_table(fake, 1, 8, axes.ctypes.data_as(P), 1, 64, -1.0, fake, fake, None) == N.VLM_ERR_ARG
+
+
+def test_window_index_matches_oracle():
+    """Integer bookkeeping of the vision window permutation: bit-exact vs the oracle."""
+    from decoder_prefill_decode_amd.pipeline import window_index
+    for cfg in (vs.C5, vs.scaled_vit(vs.C5, grid_h=6, grid_w=10, window=2)):
+        up, rp, sg, pos = window_index(cfg.grid_h, cfg.grid_w, cfg.merge, cfg.window)
+        perm, seg = ov.vit_window_order(cfg)
+        assert np.array_equal(up, perm)
+        row_perm = (perm[:, None] * 4 + np.arange(4)).reshape(-1)
+        assert np.array_equal(rp, row_perm)
+        assert np.array_equal(sg, np.repeat(seg, 4))
+        assert np.array_equal(pos, ov.vit_positions(cfg)[:, row_perm])
+
+
+def test_window_index_rejects_bad_grid():
+    assert N.lib().vlm_vit_window_index(13, 92, 2, 8, None, None, None, None) == N.VLM_ERR_SHAPE
+
+
+def test_merger_validation():
+    m = N.Merger(1152, 2, 4608, 2560, N.VLM_F32, 1e-6)
+    n = C.c_size_t()
+    assert N.lib().vlm_vit_merger_workspace_bytes(C.byref(m), 1288, C.byref(n)) == N.VLM_ERR_ARG  # NULL weights
+    for f in ("post_ln", "post_ln_b", "w1", "b1", "w2", "b2"):
+        setattr(m, f, 0x1000)
+    assert N.lib().vlm_vit_merger_workspace_bytes(C.byref(m), 1287, C.byref(n)) == N.VLM_ERR_SHAPE
+    N.call("vlm_vit_merger_workspace_bytes", C.byref(m), 1288, C.byref(n))
+    assert n.value >= 1288 * 1152 * 4 + 322 * 4608 * 4
