@@ -672,4 +672,56 @@ vlm_status vlm_vit_merger(const vlm_merger* m, const float* d_x, int32_t N, cons
     return ok();
 }
 
+// =============================================================================== measurement
+vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_final_norm,
+                             const void* d_table, int32_t which, int32_t n_launches, const float* d_x_row,
+                             void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decoder kernels only");
+    if (which < VLM_KERNEL_LMHEAD || which > VLM_KERNEL_DOWN) return fail(VLM_ERR_ARG, "which %d", which);
+    if (n_launches < 0) return fail(VLM_ERR_SHAPE, "n_launches < 0");
+    if (!d_x_row) return fail(VLM_ERR_ARG, "d_x_row is NULL");
+    if (which == VLM_KERNEL_LMHEAD) {
+        if (desc->vocab < 1 || !d_table || !aligned16(d_table) || !d_final_norm)
+            return fail(VLM_ERR_ARG, "lm_head needs vocab > 0, table and final norm");
+    } else if ((s = check_layers(desc, h_layers))) {
+        return s;
+    }
+    Ws w;
+    if ((s = check_ws(desc, 1, d_ws, ws_bytes, &w))) return s;
+    const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, hd = desc->head_dim;
+    float* x = (float*)P(d_ws, w.xrow);
+    HIP_TRY(launch_copy_f32(d_x_row, x, H, stream));
+    for (int i = 0; i < n_launches; i++) {
+        const vlm_layer& y = h_layers ? h_layers[i % desc->n_layers] : vlm_layer{};
+        GemvArgs g{};
+        switch (which) {
+            case VLM_KERNEL_LMHEAD:
+                HIP_TRY(launch_lmhead(dt, d_table, x, d_final_norm, desc->norm_eps, desc->vocab, H,
+                                      (unsigned long long*)P(d_ws, w.lm), nullptr, stream));
+                break;
+            case VLM_KERNEL_QKV:
+                g.W = y.wqkv; g.vec = x; g.gain = y.attn_norm; g.eps = desc->norm_eps; g.out = P(d_ws, w.qkvrow);
+                g.N = qkv_rows(desc); g.K = H;
+                HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, stream));
+                break;
+            case VLM_KERNEL_O:
+                g.W = y.wo; g.vec = P(d_ws, w.orow); g.out = P(d_ws, w.qkvrow); g.N = H; g.K = nq * hd;
+                HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, stream));
+                break;
+            case VLM_KERNEL_GATE_UP:
+                g.W = y.w1; g.vec = x; g.gain = y.mlp_norm; g.eps = desc->norm_eps; g.out = P(d_ws, w.arow);
+                g.N = 2 * F; g.K = H;
+                HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::SwiGLU, g, stream));
+                break;
+            default:
+                g.W = y.w2; g.vec = P(d_ws, w.arow); g.out = P(d_ws, w.qkvrow); g.N = H; g.K = F;
+                HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, stream));
+                break;
+        }
+    }
+    return ok();
+}
+
 }  // extern "C"

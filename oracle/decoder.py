@@ -40,6 +40,8 @@ Readings where the pages are silent (listed with the design notes):
   attention output, SwiGLU product, final-norm row), q and the cached k/v are
   rounded to bf16 (ties to even), the softmax P stays unrounded.
 """
+import time
+
 import numpy as np
 
 MASK_NEG = -1.0e9          # finite "minus infinity" of the fixed-window mask
@@ -305,6 +307,7 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
             rows = decoder_layer(rows, ws[l], cfg, kc[l], vc[l], pos0, cos, sin, prec)
         return rows
 
+    t_start = time.perf_counter()
     t0 = S if prefill_split is None else prefill_split
     out = stack(x, 0) if t0 == S else stack(x[:t0], 0)
     if t0 < S:
@@ -319,6 +322,8 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
         res["logits0"] = lg
         ids.append(greedy_argmax(lg))
         margins.append(_top2_margin(lg))
+    res["t_prefill_s"] = time.perf_counter() - t_start
+    t_start = time.perf_counter()
     for i in range(steps):
         pos = S + i
         if pos >= W:
@@ -333,6 +338,7 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
             margins.append(_top2_margin(lg))
             if keep_logits:
                 all_logits.append(lg)
+    res["t_decode_s"] = time.perf_counter() - t_start
     res["ids"] = np.asarray(ids, np.int64)
     res["margins"] = np.asarray(margins)
     res["decode_x"] = np.asarray(dec_x).reshape(steps, cfg.hidden)
