@@ -41,7 +41,10 @@ vlm_status ok() {
         if (e_ != hipSuccess) return fail(VLM_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
 
+// KV buffer header (int32 words): [0] length; the rest is zeroed at bind time
+// and reserved.
 constexpr size_t kHeader = 256;
+constexpr int kHdrWords = 64;
 
 size_t esize(int dtype) { return dtype == VLM_BF16 ? 2 : 4; }
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -107,7 +110,7 @@ Ws ws_layout(const vlm_model_desc* d, int max_rows) {
     w.part = take(nq * 32 * (hd + 2) * 4);
     w.orow = take(nq * hd * E);
     w.arow = take(F * E);
-    w.lm = take(d->vocab > 0 ? (size_t)lmhead_blocks(d->vocab) * 8 : 8);
+    w.lm = take(d->vocab > 0 ? (size_t)lmhead_partials_max(d->vocab) * 8 : 8);
     w.total = off;
     return w;
 }
@@ -215,7 +218,7 @@ vlm_status vlm_kv_alloc(const vlm_model_desc* desc, int32_t capacity, void* d_bu
     if (!out) return fail(VLM_ERR_ARG, "out is NULL");
     if (!d_buf || ((uintptr_t)d_buf & 255)) return fail(VLM_ERR_ARG, "KV buffer NULL or not 256-byte aligned");
     if (bytes < need_b) return fail(VLM_ERR_CAPACITY, "KV buffer %zu bytes < %zu needed", bytes, need_b);
-    HIP_TRY(launch_set_len((int32_t*)d_buf, 0, stream));
+    HIP_TRY(launch_zero_i32((int32_t*)d_buf, kHdrWords, stream));
     vlm_kv* kv = new vlm_kv();
     kv->desc = *desc;
     kv->capacity = capacity;
@@ -443,9 +446,8 @@ vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_nor
     Ws w;
     if ((s = check_ws(desc, 0, d_ws, ws_bytes, &w))) return s;
     auto* part = (unsigned long long*)P(d_ws, w.lm);
-    HIP_TRY(launch_lmhead(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab, desc->hidden, part,
-                          d_logits, stream));
-    HIP_TRY(launch_argmax_final(part, lmhead_blocks(desc->vocab), d_token_out, nullptr, nullptr, stream));
+    HIP_TRY(launch_lmhead_argmax(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab,
+                                 desc->hidden, part, d_logits, d_token_out, nullptr, nullptr, stream));
     return ok();
 }
 
@@ -458,7 +460,6 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
     const int hd = desc->head_dim, QKV = qkv_rows(desc), W = kv->capacity;
     float* x = (float*)P(ws, w.xrow);
     float* qkv = (float*)P(ws, w.qkvrow);
-    void* qr = P(ws, w.qrow);
     float* part = (float*)P(ws, w.part);
     void* orow = P(ws, w.orow);
     void* arow = P(ws, w.arow);
@@ -469,13 +470,13 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         GemvArgs g{};
         g.W = y.wqkv; g.vec = x; g.gain = y.attn_norm; g.eps = desc->norm_eps; g.out = qkv; g.N = QKV; g.K = H;
         HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
-        RopeArgs r{};
-        r.qkv = qkv; r.S = 1; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
-        r.qn = desc->qk_norm ? y.q_norm : nullptr; r.kn = desc->qk_norm ? y.k_norm : nullptr; r.eps = desc->norm_eps;
-        r.cos = cosv; r.sin = sinv; r.q = qr; r.ldq = 1; r.kdst = kv->kptr(l); r.vdst = kv->vptr(l); r.ldkv = W;
-        r.pos0 = 0; r.pos_dev = kv->dlen();
-        HIP_TRY(launch_rope_qkv(dt, r, st));
-        HIP_TRY(launch_attn_decode(dt, qr, kv->kptr(l), kv->vptr(l), W, nq, nkv, hd, kv->dlen(), nsplit, part, orow, st));
+        DecAttnArgs at{};
+        at.qkv = qkv; at.qn = desc->qk_norm ? y.q_norm : nullptr; at.kn = desc->qk_norm ? y.k_norm : nullptr;
+        at.eps = desc->norm_eps; at.cos = cosv; at.sin = sinv; at.segments = desc->rope_segments;
+        at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
+        at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
+        at.out = orow;
+        HIP_TRY(launch_attn_decode_fused(dt, at, st));
         g = GemvArgs{};
         g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * hd;
         HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
@@ -489,8 +490,8 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
     if (x_out) HIP_TRY(launch_copy_f32(x, x_out, H, st));
     if (table) {
         auto* lm = (unsigned long long*)P(ws, w.lm);
-        HIP_TRY(launch_lmhead(dt, table, x, fnorm, desc->norm_eps, desc->vocab, H, lm, nullptr, st));
-        HIP_TRY(launch_argmax_final(lm, lmhead_blocks(desc->vocab), tok_out, hist, kv->dlen(), st));
+        HIP_TRY(launch_lmhead_argmax(dt, table, x, fnorm, desc->norm_eps, desc->vocab, H, lm, nullptr, tok_out, hist,
+                                     kv->dlen(), st));
     } else {
         HIP_TRY(launch_inc_len(kv->dlen(), st));
     }
@@ -698,8 +699,9 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
         GemvArgs g{};
         switch (which) {
             case VLM_KERNEL_LMHEAD:
-                HIP_TRY(launch_lmhead(dt, d_table, x, d_final_norm, desc->norm_eps, desc->vocab, H,
-                                      (unsigned long long*)P(d_ws, w.lm), nullptr, stream));
+                HIP_TRY(launch_lmhead_argmax(dt, d_table, x, d_final_norm, desc->norm_eps, desc->vocab, H,
+                                             (unsigned long long*)P(d_ws, w.lm), nullptr, nullptr, nullptr, nullptr,
+                                             stream));
                 break;
             case VLM_KERNEL_QKV:
                 g.W = y.wqkv; g.vec = x; g.gain = y.attn_norm; g.eps = desc->norm_eps; g.out = P(d_ws, w.qkvrow);

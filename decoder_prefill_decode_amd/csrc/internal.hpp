@@ -14,7 +14,8 @@ enum class Epi : int {
     Resid = 1,       // x[m][n] += acc (+ bias[n])
     SwiGLU = 2,      // out_T[m][n/2] = silu(gate) * up over 32-row interleaved groups
     Gelu = 3,        // out_T[m][n] = gelu_tanh(acc + bias[n])
-    StoreRowMap = 4  // out_f32[rowmap[m]][n] = acc + bias[n]
+    StoreRowMap = 4, // out_f32[rowmap[m]][n] = acc + bias[n]
+    Argmax = 5       // GEMV only: per-block argmax key of the row results (+ optional logits)
 };
 
 struct GemmArgs {
@@ -36,8 +37,9 @@ struct GemvArgs {
     const void* vec;        // Pro::RmsNorm: fp32 x [K]; Pro::Plain: model-type vector [K]
     const void* gain;       // RmsNorm gain [K] (model type)
     float eps;
-    void* out;              // StoreF32: f32 [N]; Resid: f32 x [N]; SwiGLU: model type [N/2]
+    void* out;              // StoreF32: f32 [N]; Resid: f32 x [N]; SwiGLU: model type [N/2]; Argmax: f32 logits or null
     int N, K;
+    unsigned long long* partials = nullptr;  // Argmax only: one key per block
 };
 hipError_t launch_gemv(int dtype, Pro pro, Epi epi, const GemvArgs& a, hipStream_t st);
 
@@ -82,6 +84,31 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 
 // Decode attention over slots 0..*len (inclusive) of k/v [nkv][W][d]; q [nq][d].
 int attn_decode_splits(int capacity);
+
+// Decode attention of one layer: QK-Norm + RoPE of the new token's q and k
+// (position t = *len), K/V written into slot t, split-K attention over slots
+// 0..t, then a second kernel merging the splits into `out`.
+struct DecAttnArgs {
+    const float* qkv;  // [nq + 2*nkv][d] fp32 projections of the token
+    const void* qn; const void* kn; float eps;
+    const float* cos; const float* sin; int segments;
+    void* kc; void* vc;  // layer K and V, [nkv][W][d]
+    int W, nq, nkv, d;
+    const int32_t* len;
+    int nsplit;
+    float* partial;      // [nq][nsplit][d + 2]
+    void* out;           // [nq * d] model type
+};
+hipError_t launch_attn_decode_fused(int dtype, const DecAttnArgs& a, hipStream_t st);
+
+// Final RMSNorm + lm_head GEMV + argmax. Writes per-block argmax keys to
+// `partials` (lmhead_partials_max(V) entries) and the logits when non-null.
+// token_out == null: partials only; otherwise a second kernel reduces the
+// token, then hist[len+1] = token (if hist) and *kv_len += 1 (if kv_len).
+int lmhead_partials_max(int V);
+hipError_t launch_lmhead_argmax(int dtype, const void* table, const float* x, const void* gain, float eps, int V,
+                                int K, unsigned long long* partials, float* logits, int32_t* token_out, int32_t* hist,
+                                int32_t* kv_len, hipStream_t st);
 hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
                               const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st);
 
@@ -93,6 +120,7 @@ hipError_t launch_inject(int img_dtype, float* x, int S, int H, const int32_t* i
                          int n_img, hipStream_t st);
 hipError_t launch_set_len(int32_t* len, int value, hipStream_t st);
 hipError_t launch_inc_len(int32_t* len, hipStream_t st);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st);
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st);
 hipError_t launch_rope_table(const int32_t* pos, int n_axes, int n_rows, const int32_t* axis_of_pair, int segments,
                              int d, double theta, float* cos, float* sin, hipStream_t st);

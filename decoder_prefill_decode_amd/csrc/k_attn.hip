@@ -558,4 +558,273 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const voi
                       : decode_dim<float>(q, k, v, W, nq, nkv, d, len, nsplit, partial, out, st);
 }
 
+
+// ============================================================== decode, fused
+// One block per (KV head g, split sp). Phases:
+//  1. the block's K/V slots are requested first (they do not depend on q);
+//  2. wavefronts normalise + rotate the G query heads of g (and, in the block
+//     owning slot t, the new k and v, which are also written to the cache);
+//  3. online softmax over the block's slots, merged across lanes and
+//     wavefronts into one (m, l, o) partial per query head.
+// attn_combine_fast_kernel then merges the nsplit partials of each head.
+// (A last-block merge through a ticket counter needs agent-scope fences,
+// which write back the whole L2 of each XCD and measured ~4x slower.)
+constexpr int kDecPrefetch = 4;  // key iterations whose K/V rows are requested up front
+
+template <class T, int D, int G>
+__global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
+    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16;
+    __shared__ float qs[G][D];
+    __shared__ __attribute__((aligned(16))) T knew[D];
+    __shared__ __attribute__((aligned(16))) T vnew[D];
+    __shared__ float sm_m[4][G], sm_l[4][G];
+    __shared__ float sm_o[4][G][D];
+    const int g = blockIdx.x, sp = blockIdx.y;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
+    const int t = a.len[0];
+    const int T_ = t + 1;
+    const int chunk = (T_ + a.nsplit - 1) / a.nsplit;
+    const int k0 = sp * chunk, k1 = min(T_, k0 + chunk);
+    const bool own = k0 <= t && t < k1;
+    const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
+    const T* Vg = (const T*)a.vc + (size_t)g * a.W * D;
+
+    // (1) first key batch in flight
+    float kf[kDecPrefetch][CPL][VEC], vf[kDecPrefetch][CPL][VEC];
+    auto load_batch = [&](int jb) {
+#pragma unroll
+        for (int b = 0; b < kDecPrefetch; b++) {
+            const int j = jb + b * 16;
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                const int ch = sub + 16 * c;
+                if (j < k1 && j != t && ch < CH) {
+                    ld16(Kg + (size_t)j * D + ch * VEC, kf[b][c]);
+                    ld16(Vg + (size_t)j * D + ch * VEC, vf[b][c]);
+                }
+            }
+        }
+    };
+    int jb = k0 + w * 4 + kq;
+    load_batch(jb);
+
+    // (2) rotations of q (G heads) and, in the owner block, of the new k / v
+    {
+        const int half = D / 2, sd = D / a.segments, sh = sd / 2;
+        const bool on = lane < half;
+        const int gs = on ? lane / sh : 0, js = on ? lane % sh : 0;
+        const int i0 = gs * sd + js, i1 = i0 + sh;
+        const float* cr = a.cos + (size_t)t * D;
+        const float* sr = a.sin + (size_t)t * D;
+        const int nitems = G + (own ? 2 : 0);
+        for (int it = w; it < nitems; it += 4) {
+            const bool isq = it < G, isk = it == G;
+            const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
+            const float* src = a.qkv + (size_t)row * D;
+            float x0 = on ? src[i0] : 0.f, x1 = on ? src[i1] : 0.f;
+            if (isq || isk) {
+                const T* gn = (const T*)(isq ? a.qn : a.kn);
+                if (gn) {
+                    const float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + a.eps);
+                    if (on) {
+                        x0 = x0 * r * Elt<T>::ld(gn, i0);
+                        x1 = x1 * r * Elt<T>::ld(gn, i1);
+                    }
+                }
+                const float y0 = x0 * cr[i0] - x1 * sr[i0];
+                const float y1 = x1 * cr[i1] + x0 * sr[i1];
+                x0 = y0;
+                x1 = y1;
+            }
+            if (!on) continue;
+            if (isq) {
+                qs[it][i0] = Elt<T>::rnd(x0);
+                qs[it][i1] = Elt<T>::rnd(x1);
+            } else {
+                T* cache = (T*)(isk ? a.kc : a.vc) + ((size_t)g * a.W + t) * D;
+                T* lds = isk ? knew : vnew;
+                Elt<T>::st(lds, i0, x0);
+                Elt<T>::st(lds, i1, x1);
+                Elt<T>::st(cache, i0, x0);
+                Elt<T>::st(cache, i1, x1);
+            }
+        }
+    }
+    __syncthreads();
+
+    float qf[G][CPL][VEC];
+#pragma unroll
+    for (int gg = 0; gg < G; gg++)
+#pragma unroll
+        for (int c = 0; c < CPL; c++) {
+            const int ch = sub + 16 * c;
+#pragma unroll
+            for (int i = 0; i < VEC; i++) qf[gg][c][i] = ch < CH ? qs[gg][ch * VEC + i] : 0.f;
+        }
+    const float scale = kLog2e / sqrtf((float)D);
+    float mrun[G], lrun[G], o[G][CPL][VEC];
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+        mrun[gg] = -INFINITY;
+        lrun[gg] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; c++)
+#pragma unroll
+            for (int i = 0; i < VEC; i++) o[gg][c][i] = 0.f;
+    }
+    // (3) online softmax over this block's slots
+    for (; jb < k1; jb += 16 * kDecPrefetch) {
+#pragma unroll
+        for (int b = 0; b < kDecPrefetch; b++) {
+            const int j = jb + b * 16;
+            if (j >= k1) break;
+            if (j == t) {
+#pragma unroll
+                for (int c = 0; c < CPL; c++) {
+                    const int ch = sub + 16 * c;
+                    if (ch < CH) {
+                        ld16(knew + ch * VEC, kf[b][c]);
+                        ld16(vnew + ch * VEC, vf[b][c]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int gg = 0; gg < G; gg++) {
+                float s = 0.f;
+#pragma unroll
+                for (int c = 0; c < CPL; c++)
+                    if (sub + 16 * c < CH)
+#pragma unroll
+                        for (int i = 0; i < VEC; i++) s = fmaf(qf[gg][c][i], kf[b][c][i], s);
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
+                s *= scale;
+                const float mn = fmaxf(mrun[gg], s);
+                const float alpha = exp2f(mrun[gg] - mn);
+                const float p = exp2f(s - mn);
+                lrun[gg] = lrun[gg] * alpha + p;
+                mrun[gg] = mn;
+#pragma unroll
+                for (int c = 0; c < CPL; c++)
+                    if (sub + 16 * c < CH)
+#pragma unroll
+                        for (int i = 0; i < VEC; i++) o[gg][c][i] = o[gg][c][i] * alpha + p * vf[b][c][i];
+            }
+        }
+        if (jb + 16 * kDecPrefetch < k1) load_batch(jb + 16 * kDecPrefetch);
+    }
+    // merge the four 16-lane groups of the wavefront, then the wavefronts
+#pragma unroll
+    for (int gg = 0; gg < G; gg++) {
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            const float mo = __shfl_xor(mrun[gg], off, kWave);
+            const float lo = __shfl_xor(lrun[gg], off, kWave);
+            const float mn = fmaxf(mrun[gg], mo);
+            const float fa = mn == -INFINITY ? 0.f : exp2f(mrun[gg] - mn);
+            const float fb = mn == -INFINITY ? 0.f : exp2f(mo - mn);
+            lrun[gg] = lrun[gg] * fa + lo * fb;
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+                for (int i = 0; i < VEC; i++) {
+                    const float ov = __shfl_xor(o[gg][c][i], off, kWave);
+                    o[gg][c][i] = o[gg][c][i] * fa + ov * fb;
+                }
+            mrun[gg] = mn;
+        }
+        if (kq == 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                const int ch = sub + 16 * c;
+                if (ch < CH)
+#pragma unroll
+                    for (int i = 0; i < VEC; i++) sm_o[w][gg][ch * VEC + i] = o[gg][c][i];
+            }
+            if (sub == 0) {
+                sm_m[w][gg] = mrun[gg];
+                sm_l[w][gg] = lrun[gg];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * (D + 2); idx += 256) {
+        const int gg = idx / (D + 2), e = idx % (D + 2);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) mx = fmaxf(mx, sm_m[ww][gg]);
+        float v = 0.f;
+        if (e == D) {
+            v = mx;
+        } else {
+#pragma unroll
+            for (int ww = 0; ww < 4; ww++) {
+                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[ww][gg] - mx);
+                v += f * (e < D ? sm_o[ww][gg][e] : sm_l[ww][gg]);
+            }
+        }
+        a.partial[((size_t)(g * G + gg) * a.nsplit + sp) * (D + 2) + e] = v;
+    }
+}
+
+// Merge of the split partials: one block per query head, one thread per
+// element; all (m, l, o) loads of a thread are issued before any is used.
+template <class T, int D>
+__global__ __launch_bounds__(128) void attn_combine_fast_kernel(const float* __restrict__ partial, int nsplit,
+                                                                T* __restrict__ out) {
+    constexpr int NS = 32;
+    const int h = blockIdx.x, e = threadIdx.x;
+    const float* p = partial + (size_t)h * nsplit * (D + 2);
+    float m[NS], l[NS], o[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        const bool on = s < nsplit;
+        m[s] = on ? p[s * (D + 2) + D] : -INFINITY;
+        l[s] = on ? p[s * (D + 2) + D + 1] : 0.f;
+        o[s] = (on && e < D) ? p[s * (D + 2) + e] : 0.f;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; s++) mx = fmaxf(mx, m[s]);
+    float lsum = 0.f, v = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+        const float f = m[s] == -INFINITY ? 0.f : exp2f(m[s] - mx);
+        lsum += f * l[s];
+        v += f * o[s];
+    }
+    if (e < D) Elt<T>::st(out, (size_t)h * D + e, lsum > 0.f ? v / lsum : 0.f);
+}
+
+template <class T, int D>
+static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
+    const dim3 grid(a.nkv, a.nsplit);
+    switch (a.nq / a.nkv) {
+        case 1: attn_decode_fused_kernel<T, D, 1><<<grid, 256, 0, st>>>(a); break;
+        case 2: attn_decode_fused_kernel<T, D, 2><<<grid, 256, 0, st>>>(a); break;
+        case 4: attn_decode_fused_kernel<T, D, 4><<<grid, 256, 0, st>>>(a); break;
+        case 8: attn_decode_fused_kernel<T, D, 8><<<grid, 256, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_combine_fast_kernel<T, D><<<a.nq, 128, 0, st>>>(a.partial, a.nsplit, (T*)a.out);
+    return hipGetLastError();
+}
+
+template <class T>
+static hipError_t fused_dim(const DecAttnArgs& a, hipStream_t st) {
+    switch (a.d) {
+        case 64: return fused_group<T, 64>(a, st);
+        case 72: return fused_group<T, 72>(a, st);
+        case 80: return fused_group<T, 80>(a, st);
+        case 128: return fused_group<T, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_decode_fused(int dtype, const DecAttnArgs& a, hipStream_t st) {
+    return dtype == 1 ? fused_dim<bf16_t>(a, st) : fused_dim<float>(a, st);
+}
+
 }  // namespace vlm

@@ -128,6 +128,227 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
 }
 
+// Latency-hiding variant used when K fits the register plan: the operand
+// vector (and its gain) is requested first, then every weight chunk this
+// wavefront needs, and only then is the vector normalised. Vector-memory loads
+// complete in issue order, so waiting for the small vector leaves the weight
+// stream in flight while the block reduction runs.
+constexpr int kMaxVecChunks = 12;  // 16-byte chunks of the operand vector per thread
+
+template <class T> __device__ __forceinline__ void ld4(const T* p, float* o);
+template <> __device__ __forceinline__ void ld4<float>(const float* p, float* o) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+}
+template <> __device__ __forceinline__ void ld4<bf16_t>(const bf16_t* p, float* o) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void unpack16(const u32x4& v, const bf16_t*, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        o[2 * i] = __uint_as_float(v[i] << 16);
+        o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack16(const u32x4& v, const float*, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) o[i] = __uint_as_float(v[i]);
+}
+
+template <class T, Pro PRO, Epi EPI, int NR, int KCH>
+__global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
+    constexpr int VEC = 16 / sizeof(T), STEP = kWave * VEC;
+    extern __shared__ float vs[];
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = blockIdx.x * 4 + tid / kWave;
+    const int K = a.K;
+    const T* W = (const T*)a.W;
+
+    // (1) operand vector (+ gain) chunks
+    float xv[kMaxVecChunks][4], gv[kMaxVecChunks][4];
+    u32x4 pv[kMaxVecChunks];
+    const int nx = PRO == Pro::RmsNorm ? K / 4 : K / VEC;
+#pragma unroll
+    for (int i = 0; i < kMaxVecChunks; i++) {
+        const int c = tid + 256 * i;
+        if (c < nx) {
+            if constexpr (PRO == Pro::RmsNorm) {
+                ld4<float>((const float*)a.vec + 4 * c, xv[i]);
+                ld4<T>((const T*)a.gain + 4 * c, gv[i]);
+            } else {
+                pv[i] = *reinterpret_cast<const u32x4*>((const T*)a.vec + VEC * c);
+            }
+        }
+    }
+    // (2) weight rows of this wavefront
+    int rows[NR];
+    if constexpr (EPI == Epi::SwiGLU) {
+        const int nout = a.N / 2;
+#pragma unroll
+        for (int r = 0; r < NR / 2; r++) {
+            int o = wave * (NR / 2) + r;
+            o = o < nout ? o : nout - 1;
+            rows[r] = 64 * (o / 32) + (o % 32);
+            rows[NR / 2 + r] = rows[r] + 32;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const int n = wave * NR + r;
+            rows[r] = n < a.N ? n : a.N - 1;
+        }
+    }
+    u32x4 wr[NR][KCH];
+#pragma unroll
+    for (int c = 0; c < KCH; c++) {
+        const int k = lane * VEC + c * STEP;
+#pragma unroll
+        for (int r = 0; r < NR; r++)
+            wr[r][c] = k < K ? *reinterpret_cast<const u32x4*>(W + (size_t)rows[r] * K + k) : u32x4{0, 0, 0, 0};
+    }
+    // (3) operand row into LDS (normalised and rounded for RmsNorm)
+    if constexpr (PRO == Pro::RmsNorm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxVecChunks; i++)
+            if (tid + 256 * i < nx)
+#pragma unroll
+                for (int e = 0; e < 4; e++) ss += xv[i][e] * xv[i][e];
+        const float rs = rsqrtf(block_sum<256>(ss, red) / (float)K + a.eps);
+#pragma unroll
+        for (int i = 0; i < kMaxVecChunks; i++) {
+            const int c = tid + 256 * i;
+            if (c < nx)
+#pragma unroll
+                for (int e = 0; e < 4; e++) vs[4 * c + e] = Elt<T>::rnd(xv[i][e] * rs * gv[i][e]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kMaxVecChunks; i++) {
+            const int c = tid + 256 * i;
+            if (c < nx) {
+                float f[VEC];
+                unpack16(pv[i], (const T*)nullptr, f);
+#pragma unroll
+                for (int e = 0; e < VEC; e++) vs[VEC * c + e] = f[e];
+            }
+        }
+    }
+    __syncthreads();
+    // (4) dot products
+    float acc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; r++) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KCH; c++) {
+        const int k = lane * VEC + c * STEP;
+        if (k < K) {
+            float v[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e++) v[e] = vs[k + e];
+#pragma unroll
+            for (int r = 0; r < NR; r++) {
+                float wf[VEC];
+                unpack16(wr[r][c], (const T*)nullptr, wf);
+#pragma unroll
+                for (int e = 0; e < VEC; e++) acc[r] = fmaf(wf[e], v[e], acc[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; r++) acc[r] = wave_sum(acc[r]);
+    // (5) epilogue: lane r stores row r
+    if constexpr (EPI == Epi::Argmax) {
+        __shared__ unsigned long long bk[4];
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const int n = wave * NR + r;
+            if (n < a.N) {
+                const float v = acc[r];
+                const unsigned long long key = isfinite(v)
+                    ? (((unsigned long long)ordered_key(v)) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n)
+                    : ~0ull;
+                best = key > best ? key : best;
+                if (a.out && lane == r) ((float*)a.out)[n] = v;
+            }
+        }
+        if (lane == 0) bk[tid / kWave] = best;
+        __syncthreads();
+        if (tid == 0) {
+            unsigned long long b = bk[0];
+            for (int i = 1; i < 4; i++) b = bk[i] > b ? bk[i] : b;
+            a.partials[blockIdx.x] = b;
+        }
+    } else if constexpr (EPI == Epi::SwiGLU) {
+#pragma unroll
+        for (int r = 0; r < NR / 2; r++) {
+            const int o = wave * (NR / 2) + r;
+            if (lane == r && o < a.N / 2) Elt<T>::st((T*)a.out, o, silu_f(acc[r]) * acc[NR / 2 + r]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const int n = wave * NR + r;
+            if (lane == r && n < a.N) {
+                float* o = (float*)a.out;
+                if constexpr (EPI == Epi::Resid)
+                    o[n] += acc[r];
+                else
+                    o[n] = acc[r];
+            }
+        }
+    }
+}
+
+template <class T, Pro PRO, Epi EPI, int NR, int KCH>
+static hipError_t run_gemv2(const GemvArgs& a, hipStream_t st) {
+    const int nrows = a.N;  // SwiGLU: NR counts gate + up rows
+    const int waves = (nrows + NR - 1) / NR;
+    const int blocks = (waves + 3) / 4;
+    gemv2_kernel<T, PRO, EPI, NR, KCH><<<blocks, 256, (size_t)a.K * sizeof(float), st>>>(a);
+    return hipGetLastError();
+}
+
+// Rows per wavefront: as many as the register plan allows (NR*KCH <= 24 chunks)
+// while keeping >= 1024 wavefronts in flight.
+template <class T, Pro PRO, Epi EPI, int KCH>
+static hipError_t pick_nr(const GemvArgs& a, hipStream_t st) {
+    constexpr int cap = 24 / KCH;
+    const int n = a.N;
+    if constexpr (cap >= 8) if (n / 8 >= 1024) return run_gemv2<T, PRO, EPI, 8, KCH>(a, st);
+    if constexpr (cap >= 4) if (n / 4 >= 1024) return run_gemv2<T, PRO, EPI, 4, KCH>(a, st);
+    if constexpr (cap >= 2) if (n / 2 >= 1024 || EPI == Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 2, KCH>(a, st);
+    if constexpr (EPI != Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 1, KCH>(a, st);
+    return hipErrorNotSupported;
+}
+
+// Returns hipErrorNotSupported when K has no register plan (caller falls back).
+template <class T, Pro PRO, Epi EPI>
+static hipError_t try_gemv2(const GemvArgs& a, hipStream_t st) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int nx = PRO == Pro::RmsNorm ? a.K / 4 : a.K / VEC;
+    if (nx > 256 * kMaxVecChunks) return hipErrorNotSupported;
+    const int kch = (a.K + kWave * VEC - 1) / (kWave * VEC);
+    switch (kch) {
+        case 1: return pick_nr<T, PRO, EPI, 1>(a, st);
+        case 2: return pick_nr<T, PRO, EPI, 2>(a, st);
+        case 3: return pick_nr<T, PRO, EPI, 3>(a, st);
+        case 4: return pick_nr<T, PRO, EPI, 4>(a, st);
+        case 5: return pick_nr<T, PRO, EPI, 5>(a, st);
+        case 6: return pick_nr<T, PRO, EPI, 6>(a, st);
+        case 8: return pick_nr<T, PRO, EPI, 8>(a, st);
+        case 12: return pick_nr<T, PRO, EPI, 12>(a, st);
+        case 19: return pick_nr<T, PRO, EPI, 19>(a, st);
+        case 20: return pick_nr<T, PRO, EPI, 20>(a, st);
+    }
+    return hipErrorNotSupported;
+}
+
 template <class T, Pro PRO, Epi EPI, int ROWS>
 static hipError_t run_gemv(const GemvArgs& a, hipStream_t st) {
     const int nrows = EPI == Epi::SwiGLU ? a.N / 2 : a.N;
@@ -140,6 +361,10 @@ static hipError_t run_gemv(const GemvArgs& a, hipStream_t st) {
 
 template <class T, Pro PRO, Epi EPI>
 static hipError_t pick_rows(const GemvArgs& a, hipStream_t st) {
+    {
+        const hipError_t e = try_gemv2<T, PRO, EPI>(a, st);
+        if (e != hipErrorNotSupported) return e;
+    }
     const int nrows = EPI == Epi::SwiGLU ? a.N / 2 : a.N;
     if (nrows >= 8192) return run_gemv<T, PRO, EPI, 4>(a, st);
     if (nrows >= 4096) return run_gemv<T, PRO, EPI, 2>(a, st);
@@ -236,6 +461,49 @@ __global__ __launch_bounds__(1024) void argmax_final_kernel(const unsigned long 
 }
 
 int lmhead_blocks(int V) { return (V + 4 * kLmRows - 1) / (4 * kLmRows); }
+
+template <class T, int NR, int KCH>
+static hipError_t run_lm2(const GemvArgs& a, int* nblocks, hipStream_t st) {
+    *nblocks = (((a.N + NR - 1) / NR) + 3) / 4;
+    return run_gemv2<T, Pro::RmsNorm, Epi::Argmax, NR, KCH>(a, st);
+}
+
+// lm_head on the latency-hiding GEMV; hipErrorNotSupported when K has no register plan.
+template <class T>
+static hipError_t lm2_dispatch(const GemvArgs& a, int* nb, hipStream_t st) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int kch = (a.K + kWave * VEC - 1) / (kWave * VEC);
+    if (a.K / 4 > 256 * kMaxVecChunks || a.K < 512) return hipErrorNotSupported;
+    switch (kch) {
+        case 1: return run_lm2<T, 8, 1>(a, nb, st);
+        case 2: return run_lm2<T, 8, 2>(a, nb, st);
+        case 3: return run_lm2<T, 8, 3>(a, nb, st);
+        case 4: return run_lm2<T, 4, 4>(a, nb, st);
+        case 5: return run_lm2<T, 4, 5>(a, nb, st);
+        case 6: return run_lm2<T, 4, 6>(a, nb, st);
+        case 8: return run_lm2<T, 2, 8>(a, nb, st);
+        case 12: return run_lm2<T, 2, 12>(a, nb, st);
+    }
+    return hipErrorNotSupported;
+}
+
+int lmhead_partials_max(int V) { return (V + 3) / 4 + 1; }
+
+hipError_t launch_lmhead_argmax(int dtype, const void* table, const float* x, const void* gain, float eps, int V,
+                                int K, unsigned long long* partials, float* logits, int32_t* token_out, int32_t* hist,
+                                int32_t* kv_len, hipStream_t st) {
+    GemvArgs a{};
+    a.W = table; a.vec = x; a.gain = gain; a.eps = eps; a.out = logits; a.N = V; a.K = K; a.partials = partials;
+    int nb = 0;
+    hipError_t e = dtype == 1 ? lm2_dispatch<bf16_t>(a, &nb, st) : lm2_dispatch<float>(a, &nb, st);
+    if (e == hipErrorNotSupported) {
+        e = launch_lmhead(dtype, table, x, gain, eps, V, K, partials, logits, st);
+        nb = lmhead_blocks(V);
+    }
+    if (e != hipSuccess) return e;
+    if (token_out) return launch_argmax_final(partials, nb, token_out, hist, kv_len, st);
+    return hipSuccess;
+}
 
 hipError_t launch_lmhead(int dtype, const void* table, const float* x, const void* gain, float eps, int V, int K,
                          unsigned long long* partials, float* logits, hipStream_t st) {

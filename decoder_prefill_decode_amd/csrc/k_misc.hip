@@ -66,6 +66,10 @@ __global__ void set_len_kernel(int32_t* len, int v) {
     if (threadIdx.x == 0 && blockIdx.x == 0) len[0] = v;
 }
 
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 __global__ void inc_len_kernel(int32_t* len) {
     if (threadIdx.x == 0 && blockIdx.x == 0) len[0] = len[0] + 1;
 }
@@ -228,6 +232,11 @@ hipError_t launch_inject(int img_dtype, float* x, int S, int H, const int32_t* i
 
 hipError_t launch_set_len(int32_t* len, int value, hipStream_t st) {
     set_len_kernel<<<1, 64, 0, st>>>(len, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t st) {
+    zero_i32_kernel<<<1, 256, 0, st>>>(p, n);
     return hipGetLastError();
 }
 

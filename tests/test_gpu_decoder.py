@@ -162,3 +162,17 @@ def test_scaled_bf16_stacks(rt, cfg):
     eps = 8 * float(np.abs(lg - ref["logits0"]).max())
     flips, div = check_ids(free, forced, ref["ids"], ref["margins"], eps)
     print(f"{cfg.name}: logit err {eps / 8:.2e}, tie eps {eps:.2e}, first divergence {div}, tie flips {flips}")
+
+
+def test_generic_gemv_fallback_shapes(rt):
+    """FFN 3584 gives the down projection K = 3584 (7 chunks per lane), which
+    has no register plan in the latency-hiding GEMV and runs the generic one."""
+    pipeline, _ = rt
+    cfg = vs.scaled(vs.C2_BF16, ffn=3584, seq=64, decode_steps=6, capacity=128)
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    run = gpu_run(pipeline, cfg, glob, layers)
+    x = run.prefill()
+    assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["bf16"]
+    out = run.decode_hidden(run.dec_x).cpu().numpy()
+    assert rel(out, ref["decode_x"]) <= TOL["bf16"]
