@@ -85,7 +85,7 @@ vlm_status check_desc(const vlm_model_desc* d) {
 int qkv_rows(const vlm_model_desc* d) { return (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim; }
 
 struct Ws {
-    size_t h, qkv, q, kv, o, a, xrow, qkvrow, qrow, part, orow, arow, lm, total;
+    size_t h, qkv, q, kv, o, a, gpart, gpart_floats, xrow, qkvrow, qrow, part, orow, arow, lm, total;
 };
 
 Ws ws_layout(const vlm_model_desc* d, int max_rows) {
@@ -104,6 +104,9 @@ Ws ws_layout(const vlm_model_desc* d, int max_rows) {
     w.kv = d->block_kind == VLM_BLOCK_VIT ? take(2 * nkv * R * hd * E) : off;
     w.o = take(R * nq * hd * E);
     w.a = take(R * F * E);
+    // split-K partials of the narrow prefill GEMMs: up to 4 splits of [R][max(QKV, H, F)] fp32
+    w.gpart_floats = 4 * R * std::max({(size_t)qkv_rows(d), H, F});
+    w.gpart = take(w.gpart_floats * 4);
     w.xrow = take(H * 4);
     w.qkvrow = take(qkv_rows(d) * 4);
     w.qrow = take(nq * hd * E);
@@ -396,8 +399,10 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
             ldkv = kv->capacity;
         }
         HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.attn_norm, y.attn_norm_b, desc->norm_eps, hbuf, stream));
+        float* gpart = (float*)P(d_ws, w.gpart);
         GemmArgs g{};
         g.A = hbuf; g.B = y.wqkv; g.bias = vit ? y.bqkv : nullptr; g.out = qkv; g.M = S; g.N = QKV; g.K = H; g.ldo = QKV;
+        g.part = gpart; g.part_cap = w.gpart_floats;
         HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
         RopeArgs r{};
         r.qkv = qkv; r.S = S; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
@@ -412,10 +417,12 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
         HIP_TRY(launch_attn_prefill(dt, at, stream));
         g = GemmArgs{};
         g.A = ob; g.B = y.wo; g.bias = vit ? y.bo : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = nq * hd; g.ldo = H;
+        g.part = gpart; g.part_cap = w.gpart_floats;
         HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
         HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.mlp_norm, y.mlp_norm_b, desc->norm_eps, hbuf, stream));
         g = GemmArgs{};
         g.A = hbuf; g.B = y.w1; g.out = ab; g.M = S; g.K = H; g.ldo = F;
+        g.part = gpart; g.part_cap = w.gpart_floats;
         if (vit) {
             g.bias = y.b1; g.N = F;
             HIP_TRY(launch_gemm(dt, Epi::Gelu, g, stream));
@@ -425,6 +432,7 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
         }
         g = GemmArgs{};
         g.A = ab; g.B = y.w2; g.bias = vit ? y.b2 : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = F; g.ldo = H;
+        g.part = gpart; g.part_cap = w.gpart_floats;
         HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
     }
     if (!vit) {
@@ -475,8 +483,8 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         at.eps = desc->norm_eps; at.cos = cosv; at.sin = sinv; at.segments = desc->rope_segments;
         at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
         at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
-        at.out = orow;
         HIP_TRY(launch_attn_decode_fused(dt, at, st));
+        HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, hd, orow, st));
         g = GemvArgs{};
         g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * hd;
         HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));

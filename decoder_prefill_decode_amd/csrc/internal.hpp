@@ -26,6 +26,8 @@ struct GemmArgs {
     const int32_t* rowmap;
     int M, N, K;
     int ldo;           // row stride of `out` in elements
+    float* part = nullptr;  // split-K scratch (fp32 [splits][M][N]); null: no split-K
+    size_t part_cap = 0;    // floats available at `part`
 };
 
 // dtype: 0 = f32, 1 = bf16 (vlm_dtype values)
@@ -87,7 +89,7 @@ int attn_decode_splits(int capacity);
 
 // Decode attention of one layer: QK-Norm + RoPE of the new token's q and k
 // (position t = *len), K/V written into slot t, split-K attention over slots
-// 0..t, then a second kernel merging the splits into `out`.
+// 0..t into `partial`; launch_attn_combine merges the splits into `out`.
 struct DecAttnArgs {
     const float* qkv;  // [nq + 2*nkv][d] fp32 projections of the token
     const void* qn; const void* kn; float eps;
@@ -97,9 +99,10 @@ struct DecAttnArgs {
     const int32_t* len;
     int nsplit;
     float* partial;      // [nq][nsplit][d + 2]
-    void* out;           // [nq * d] model type
 };
 hipError_t launch_attn_decode_fused(int dtype, const DecAttnArgs& a, hipStream_t st);
+hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
+                               hipStream_t st);
 
 // Final RMSNorm + lm_head GEMV + argmax. Writes per-block argmax keys to
 // `partials` (lmhead_partials_max(V) entries) and the logits when non-null.

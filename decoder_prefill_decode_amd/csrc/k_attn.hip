@@ -560,7 +560,7 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const voi
 
 
 // ============================================================== decode, fused
-// One block per (KV head g, split sp). Phases:
+// One block of 8 wavefronts per (KV head g, split sp). Phases:
 //  1. the block's K/V slots are requested first (they do not depend on q);
 //  2. wavefronts normalise + rotate the G query heads of g (and, in the block
 //     owning slot t, the new k and v, which are also written to the cache);
@@ -572,13 +572,13 @@ hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const voi
 constexpr int kDecPrefetch = 4;  // key iterations whose K/V rows are requested up front
 
 template <class T, int D, int G>
-__global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
-    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16;
+__global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
+    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16, NW = 8, KSTEP = NW * 4;
     __shared__ float qs[G][D];
     __shared__ __attribute__((aligned(16))) T knew[D];
     __shared__ __attribute__((aligned(16))) T vnew[D];
-    __shared__ float sm_m[4][G], sm_l[4][G];
-    __shared__ float sm_o[4][G][D];
+    __shared__ float sm_m[NW][G], sm_l[NW][G];
+    __shared__ float sm_o[NW][G][D];
     const int g = blockIdx.x, sp = blockIdx.y;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
     const int t = a.len[0];
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
     auto load_batch = [&](int jb) {
 #pragma unroll
         for (int b = 0; b < kDecPrefetch; b++) {
-            const int j = jb + b * 16;
+            const int j = jb + b * KSTEP;
 #pragma unroll
             for (int c = 0; c < CPL; c++) {
                 const int ch = sub + 16 * c;
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
         const float* cr = a.cos + (size_t)t * D;
         const float* sr = a.sin + (size_t)t * D;
         const int nitems = G + (own ? 2 : 0);
-        for (int it = w; it < nitems; it += 4) {
+        for (int it = w; it < nitems; it += NW) {
             const bool isq = it < G, isk = it == G;
             const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
             const float* src = a.qkv + (size_t)row * D;
@@ -673,10 +673,10 @@ __global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
             for (int i = 0; i < VEC; i++) o[gg][c][i] = 0.f;
     }
     // (3) online softmax over this block's slots
-    for (; jb < k1; jb += 16 * kDecPrefetch) {
+    for (; jb < k1; jb += KSTEP * kDecPrefetch) {
 #pragma unroll
         for (int b = 0; b < kDecPrefetch; b++) {
-            const int j = jb + b * 16;
+            const int j = jb + b * KSTEP;
             if (j >= k1) break;
             if (j == t) {
 #pragma unroll
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
                         for (int i = 0; i < VEC; i++) o[gg][c][i] = o[gg][c][i] * alpha + p * vf[b][c][i];
             }
         }
-        if (jb + 16 * kDecPrefetch < k1) load_batch(jb + 16 * kDecPrefetch);
+        if (jb + KSTEP * kDecPrefetch < k1) load_batch(jb + KSTEP * kDecPrefetch);
     }
     // merge the four 16-lane groups of the wavefront, then the wavefronts
 #pragma unroll
@@ -748,17 +748,17 @@ __global__ __launch_bounds__(256) void attn_decode_fused_kernel(DecAttnArgs a) {
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * (D + 2); idx += 256) {
+    for (int idx = tid; idx < G * (D + 2); idx += NW * kWave) {
         const int gg = idx / (D + 2), e = idx % (D + 2);
         float mx = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < 4; ww++) mx = fmaxf(mx, sm_m[ww][gg]);
+        for (int ww = 0; ww < NW; ww++) mx = fmaxf(mx, sm_m[ww][gg]);
         float v = 0.f;
         if (e == D) {
             v = mx;
         } else {
 #pragma unroll
-            for (int ww = 0; ww < 4; ww++) {
+            for (int ww = 0; ww < NW; ww++) {
                 const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[ww][gg] - mx);
                 v += f * (e < D ? sm_o[ww][gg][e] : sm_l[ww][gg]);
             }
@@ -800,16 +800,31 @@ template <class T, int D>
 static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
     const dim3 grid(a.nkv, a.nsplit);
     switch (a.nq / a.nkv) {
-        case 1: attn_decode_fused_kernel<T, D, 1><<<grid, 256, 0, st>>>(a); break;
-        case 2: attn_decode_fused_kernel<T, D, 2><<<grid, 256, 0, st>>>(a); break;
-        case 4: attn_decode_fused_kernel<T, D, 4><<<grid, 256, 0, st>>>(a); break;
-        case 8: attn_decode_fused_kernel<T, D, 8><<<grid, 256, 0, st>>>(a); break;
+        case 1: attn_decode_fused_kernel<T, D, 1><<<grid, 512, 0, st>>>(a); break;
+        case 2: attn_decode_fused_kernel<T, D, 2><<<grid, 512, 0, st>>>(a); break;
+        case 4: attn_decode_fused_kernel<T, D, 4><<<grid, 512, 0, st>>>(a); break;
+        case 8: attn_decode_fused_kernel<T, D, 8><<<grid, 512, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    attn_combine_fast_kernel<T, D><<<a.nq, 128, 0, st>>>(a.partial, a.nsplit, (T*)a.out);
     return hipGetLastError();
+}
+
+template <class T>
+static hipError_t combine_dim(const float* partial, int nq, int nsplit, int d, void* out, hipStream_t st) {
+    switch (d) {
+        case 64: attn_combine_fast_kernel<T, 64><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
+        case 72: attn_combine_fast_kernel<T, 72><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
+        case 80: attn_combine_fast_kernel<T, 80><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
+        case 128: attn_combine_fast_kernel<T, 128><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
+                               hipStream_t st) {
+    return dtype == 1 ? combine_dim<bf16_t>(partial, nq, nsplit, d, out, st)
+                      : combine_dim<float>(partial, nq, nsplit, d, out, st);
 }
 
 template <class T>
