@@ -31,7 +31,8 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 METRIC = "prefill tok/s + decode tok/s per decoder stack; % of HBM / MFMA roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "decoder_prefill_decode_amd", "csrc", "k_gemv.hip")
+KERNEL_SOURCES = {k: os.path.join(ROOT, "decoder_prefill_decode_amd", "csrc", f)
+                  for k, f in (("gemv", "k_gemv.hip"), ("attn", "k_attn.hip"))}
 
 
 def parse():
@@ -43,18 +44,32 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-decode-steps", type=int, default=128)
     ap.add_argument("--kernel-only", default=None,
-                    help="launch one decode kernel (lmhead, qkv, o, gate_up, down) --launches times and exit")
+                    help="launch one decode kernel (lmhead, qkv, o, gate_up, down, attn) --launches times, then "
+                         "one plain copy of --copy-mib MiB (reference for HBM counters), and exit")
     ap.add_argument("--launches", type=int, default=200)
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --kernel-only run "
+                         "into profiles/traffic.json and exit")
     return ap.parse_args()
 
 
-KERNELS = ["lmhead", "qkv", "o", "gate_up", "down"]
+KERNELS = ["lmhead", "qkv", "o", "gate_up", "down", "attn"]
+# name fragments of each kernel in a --kernel-only run (the copy kernels are told apart by name too)
+KERNEL_NAME = {"lmhead": "Epi)5", "qkv": "Epi)0", "o": "Epi)1", "gate_up": "Epi)2", "down": "Epi)1",
+               "attn": "attn_decode_fused"}
 
 
-def kernel_bytes(cfg, name):
-    """Algorithmic HBM bytes of one launch: the weight matrix once plus its vector input/output."""
+def kernel_bytes(cfg, name, t=None):
+    """Algorithmic HBM bytes of one launch: the weight matrix once plus its vector input/output;
+    attention: the K/V slots 0..t-1 it reads, the slot t it writes, q/k/v in and the split partials out."""
     E = 2 if cfg.dtype == "bf16" else 4
     H, F, qd = cfg.hidden, cfg.ffn, cfg.n_q_heads * cfg.head_dim
+    if name == "attn":
+        from decoder_prefill_decode_amd.csrc_info import decode_splits
+        kvd = cfg.n_kv_heads * cfg.head_dim
+        return 2 * kvd * t * E + 2 * kvd * E + cfg.qkv_rows * 4 + \
+            cfg.n_q_heads * decode_splits(cfg.capacity) * (cfg.head_dim + 2) * 4
     if name == "lmhead":
         return cfg.vocab * H * E + H * 4
     if name == "qkv":
@@ -66,20 +81,62 @@ def kernel_bytes(cfg, name):
     return H * F * E + F * E + 2 * H * 4
 
 
+def source_sha(name):
+    return hashlib.sha256(open(KERNEL_SOURCES["attn" if name == "attn" else "gemv"], "rb").read()).hexdigest()
+
+
 def load_traffic(name):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        ent = t.get(name)
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-        if ent and ent.get("source_sha256") == sha:
+            ent = json.load(f).get(name)
+        if ent and ent.get("source_sha256") == source_sha(name):
             return ent.get("bytes_per_launch")
     except (OSError, ValueError):
         pass
     return None
 
 
+def traffic_from_csv(kernel, fetch_csv, write_csv, copy_mib):
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for the plain copy of copy_mib MiB in the same run."""
+    import csv
+
+    def rows(path, counter):
+        out = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rs = rows(path, counter)
+        copies = [v for n, v in rs if "gather_rows_kernel" in n]
+        mine = [v for n, v in rs if KERNEL_NAME[kernel] in n and "vlm::" in n]
+        if not copies or not mine:
+            raise SystemExit(f"{path}: no {counter} rows for the copy or for {kernel}")
+        scale = copy_mib * 1024.0 / max(copies)          # KiB the copy moves / KiB the counter reports
+        res[counter] = {"kib_per_launch": sum(mine) / len(mine), "copy_kib": max(copies), "scale": scale,
+                        "launches": len(mine)}
+    b = (res["FETCH_SIZE"]["kib_per_launch"] * res["FETCH_SIZE"]["scale"]
+         + res["WRITE_SIZE"]["kib_per_launch"] * res["WRITE_SIZE"]["scale"]) * 1024.0
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {}
+    allt[kernel] = {"bytes_per_launch": round(b), "source_sha256": source_sha(kernel), "counters": res,
+                    "copy_reference_mib": copy_mib}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allt, f, indent=1)
+    print(json.dumps(allt[kernel]))
+
+
 def time_kernel(run, name, launches):
+    """Average launch duration (us) of one decode kernel, from HIP events on the stream it runs on,
+    around `launches` back-to-back launches (attention at the mid-run cache length)."""
     import ctypes as C
 
     import torch
@@ -89,10 +146,12 @@ def time_kernel(run, name, launches):
     m = run.model
     which = KERNELS.index(name)
     x = run.x[run.cfg.seq - 1]
+    if name == "attn":
+        run.kv.truncate(run.cfg.seq + run.cfg.decode_steps // 2)
 
     def go(n):
-        N.call("vlm_launch_kernel", C.byref(m.desc), m.layers, ptr(m.final_norm), ptr(m.embed), which, n, ptr(x),
-               ptr(run.ws), run.ws.numel(), stream())
+        N.call("vlm_launch_kernel", C.byref(m.desc), m.layers, ptr(m.final_norm), ptr(m.embed), run.kv.handle,
+               ptr(run.cos), ptr(run.sin), which, n, ptr(x), ptr(run.ws), run.ws.numel(), stream())
     go(10)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -125,6 +184,9 @@ def cpu_baseline(cfg, glob, layers, n_dec):
 
 def main():
     args = parse()
+    if args.traffic:
+        traffic_from_csv(args.traffic[0], args.traffic[1], args.traffic[2], args.copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path; run with --gpus 1)", file=sys.stderr)
@@ -147,7 +209,23 @@ def main():
           flush=True)
 
     if args.kernel_only:
+        if args.kernel_only == "attn":   # a filled cache for the attention kernel to read (eager steps:
+            run.prefill()                 # counter collection does not handle graph launches)
+            run.first_token()
+            run.decode(cfg.decode_steps, loop=False)
         t = time_kernel(run, args.kernel_only, args.launches)
+        # the counters' reference: a plain row copy (the library's gather kernel with the identity
+        # index) reading and writing exactly copy_mib MiB
+        import ctypes as C
+        from decoder_prefill_decode_amd import native as N
+        from decoder_prefill_decode_amd.runtime import ptr, stream
+        rows = args.copy_mib * 256
+        src = torch.ones((rows, 1024), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        idx = torch.arange(rows, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        N.call("vlm_gather_rows", ptr(src), rows, ptr(idx), rows, 1024, ptr(dst), stream())
+        torch.cuda.synchronize()
         print(f"# {args.kernel_only}: {t:.2f} us per launch over {args.launches} launches", file=sys.stderr)
         return
 
@@ -183,14 +261,15 @@ def main():
 
     # per-kernel timing of the decode step; the dominant one carries the roofline
     per = {}
+    t_mid = S + N // 2
     for k in KERNELS:
         if k == "lmhead" and cfg.vocab == 0:
             continue
         us = time_kernel(run, k, 4 * cfg.n_layers if k != "lmhead" else 40)
         count = 1 if k == "lmhead" else cfg.n_layers
-        per[k] = {"us": us, "per_token_us": us * count, "gbs": kernel_bytes(cfg, k) / (us * 1e-6) / 1e9}
+        per[k] = {"us": us, "per_token_us": us * count, "gbs": kernel_bytes(cfg, k, t_mid) / (us * 1e-6) / 1e9}
     dom = max(per, key=lambda k: per[k]["per_token_us"])
-    b = kernel_bytes(cfg, dom)
+    b = kernel_bytes(cfg, dom, t_mid)
     achieved = b / (per[dom]["us"] * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom),

@@ -683,12 +683,13 @@ vlm_status vlm_vit_merger(const vlm_merger* m, const float* d_x, int32_t N, cons
 
 // =============================================================================== measurement
 vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_final_norm,
-                             const void* d_table, int32_t which, int32_t n_launches, const float* d_x_row,
-                             void* d_ws, size_t ws_bytes, hipStream_t stream) {
+                             const void* d_table, vlm_kv* kv, const float* d_cos, const float* d_sin,
+                             int32_t which, int32_t n_launches, const float* d_x_row, void* d_ws, size_t ws_bytes,
+                             hipStream_t stream) {
     vlm_status s = check_desc(desc);
     if (s) return s;
     if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decoder kernels only");
-    if (which < VLM_KERNEL_LMHEAD || which > VLM_KERNEL_DOWN) return fail(VLM_ERR_ARG, "which %d", which);
+    if (which < VLM_KERNEL_LMHEAD || which > VLM_KERNEL_ATTN) return fail(VLM_ERR_ARG, "which %d", which);
     if (n_launches < 0) return fail(VLM_ERR_SHAPE, "n_launches < 0");
     if (!d_x_row) return fail(VLM_ERR_ARG, "d_x_row is NULL");
     if (which == VLM_KERNEL_LMHEAD) {
@@ -697,13 +698,19 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
     } else if ((s = check_layers(desc, h_layers))) {
         return s;
     }
+    if (which == VLM_KERNEL_ATTN) {
+        if (!kv || !d_cos || !d_sin) return fail(VLM_ERR_ARG, "attention needs the KV cache and RoPE tables");
+        if (memcmp(&kv->desc, desc, sizeof(*desc)) != 0) return fail(VLM_ERR_ARG, "KV cache bound to another model");
+        if (kv->len >= kv->capacity) return fail(VLM_ERR_CAPACITY, "cache full");
+    }
     Ws w;
     if ((s = check_ws(desc, 1, d_ws, ws_bytes, &w))) return s;
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, hd = desc->head_dim;
     float* x = (float*)P(d_ws, w.xrow);
     HIP_TRY(launch_copy_f32(d_x_row, x, H, stream));
     for (int i = 0; i < n_launches; i++) {
-        const vlm_layer& y = h_layers ? h_layers[i % desc->n_layers] : vlm_layer{};
+        const int l = i % desc->n_layers;
+        const vlm_layer& y = h_layers ? h_layers[l] : vlm_layer{};
         GemvArgs g{};
         switch (which) {
             case VLM_KERNEL_LMHEAD:
@@ -725,10 +732,20 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
                 g.N = 2 * F; g.K = H;
                 HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::SwiGLU, g, stream));
                 break;
-            default:
+            case VLM_KERNEL_DOWN:
                 g.W = y.w2; g.vec = P(d_ws, w.arow); g.out = P(d_ws, w.qkvrow); g.N = H; g.K = F;
                 HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, stream));
                 break;
+            default: {
+                DecAttnArgs at{};
+                at.qkv = (const float*)P(d_ws, w.qkvrow); at.qn = desc->qk_norm ? y.q_norm : nullptr;
+                at.kn = desc->qk_norm ? y.k_norm : nullptr; at.eps = desc->norm_eps; at.cos = d_cos; at.sin = d_sin;
+                at.segments = desc->rope_segments; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = kv->capacity;
+                at.nq = nq; at.nkv = desc->n_kv_heads; at.d = hd; at.len = kv->dlen();
+                at.nsplit = attn_decode_splits(kv->capacity); at.partial = (float*)P(d_ws, w.part);
+                HIP_TRY(launch_attn_decode_fused(dt, at, stream));
+                break;
+            }
         }
     }
     return ok();

@@ -295,18 +295,24 @@ vlm_status vlm_vit_merger_workspace_bytes(const vlm_merger* m, int32_t N, size_t
  * of the decode step, exactly as vlm_decode_step launches it, cycling over the
  * layers so that consecutive launches read different weights. Inputs come from
  * d_x_row ([H] fp32, copied into the workspace first) and the workspace;
- * outputs go to the workspace only. Used to time one kernel with events on
- * `stream` (and under a profiler) without the rest of the step. */
+ * outputs go to the workspace only, except VLM_KERNEL_ATTN, which (like a
+ * decode step) writes the new token's K/V into slot t = current length of
+ * `kv` and reads slots 0..t; the length does not change. `kv`, d_cos and
+ * d_sin are needed for VLM_KERNEL_ATTN only (else may be NULL). Used to time
+ * one kernel with events on `stream`, and under a profiler, without the rest
+ * of the step. */
 typedef enum {
     VLM_KERNEL_LMHEAD = 0,   /* final RMSNorm + lm_head GEMV + block argmax partials */
     VLM_KERNEL_QKV = 1,      /* RMSNorm + fused QKV GEMV */
     VLM_KERNEL_O = 2,        /* O-projection GEMV + residual */
     VLM_KERNEL_GATE_UP = 3,  /* RMSNorm + gate/up GEMV + SwiGLU */
-    VLM_KERNEL_DOWN = 4      /* down GEMV + residual */
+    VLM_KERNEL_DOWN = 4,     /* down GEMV + residual */
+    VLM_KERNEL_ATTN = 5      /* QK-Norm + RoPE + slot write + split-K attention (without the split merge) */
 } vlm_kernel_id;
 vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_final_norm,
-                             const void* d_table, int32_t which, int32_t n_launches, const float* d_x_row,
-                             void* d_ws, size_t ws_bytes, hipStream_t stream);
+                             const void* d_table, vlm_kv* kv, const float* d_cos, const float* d_sin,
+                             int32_t which, int32_t n_launches, const float* d_x_row, void* d_ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* Thread-local description of the last error. */
 const char* vlm_last_error(void);
