@@ -2,11 +2,18 @@
 written by tests/golden/make_golden.py, which calls only the oracle).
 
 Decoder stacks (28-layer Qwen3-style and 36-layer 4B-class, bf16): sampled
-prefill rows, the top-64 first-token logits and sampled KV slots within the
-bf16 gate (2e-2 of the tensor's max), and greedy ids checked free-running and
-teacher-forced with near-tie attribution (see test_gpu_decoder.check_ids).
+prefill rows and the top-64 first-token logits within the bf16 gate (2e-2 of
+the tensor's max); sampled KV slots within twice the oracle's own noise
+floor at that depth; greedy ids checked free-running and teacher-forced, a
+disagreement allowed only at a step whose oracle top-2 margin is below the
+oracle's own first-token logit noise floor (see test_gpu_decoder.check_ids).
+The noise floors (tests/golden/noise_floor.json, written by
+tests/golden/noise_floor.py from the oracle alone) are the difference between
+the oracle with float32 BLAS and with float64 products of the same bf16
+operands: no result finer than that is fixed by the arithmetic.
 Vision tower (27 layers + merger, fp32): sampled merged rows within 1e-4.
 """
+import json
 import os
 
 import numpy as np
@@ -22,6 +29,11 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def load(name):
     return dict(np.load(os.path.join(GOLDEN, f"{name}.npz"), allow_pickle=False))
+
+
+def noise_floor(name):
+    with open(os.path.join(GOLDEN, "noise_floor.json")) as f:
+        return json.load(f)[name]
 
 
 @pytest.mark.parametrize("cfg", [vs.C3, vs.C4], ids=["c3_28layer", "c4_36layer"])
@@ -42,22 +54,26 @@ def test_decoder_stack_full_size(cfg):
     assert err_lg / g["logits0_absmax"] <= 2e-2, err_lg
     free = [tok0] + list(run.decode(cfg.decode_steps))
     L, slots = g["kv_layers"], g["kv_slots"]
+    kv_err = []
     for i, l in enumerate(L):
         k, v = run.kv.kv(int(l))
-        ks = k[:, torch.from_numpy(slots).to("cuda")].float().cpu().numpy()
-        vv = v[:, torch.from_numpy(slots).to("cuda")].float().cpu().numpy()
-        # slots after a free-running divergence hold different tokens: compare the prompt part always
-        pr = slots < cfg.seq
-        assert np.abs(ks[:, pr] - g["k_samples"][i][:, pr]).max() / np.abs(g["k_samples"][i]).max() <= 2e-2
-        assert np.abs(vv[:, pr] - g["v_samples"][i][:, pr]).max() / np.abs(g["v_samples"][i]).max() <= 2e-2
+        idx = torch.from_numpy(slots).to("cuda")
+        ks, vv = k[:, idx].float().cpu().numpy(), v[:, idx].float().cpu().numpy()
+        pr = slots < cfg.seq   # prompt slots; decode slots differ after a free-running divergence
+        kv_err.append(max(np.abs(ks[:, pr] - g["k_samples"][i][:, pr]).max() / np.abs(g["k_samples"][i]).max(),
+                          np.abs(vv[:, pr] - g["v_samples"][i][:, pr]).max() / np.abs(g["v_samples"][i]).max()))
     run.kv.truncate(cfg.seq)
     forced = [tok0] + list(run.decode_forced(g["ids"][:-1]))
-    eps = 8 * float(err_lg)
-    flips, div = check_ids(free, forced, g["ids"], g["margins"], eps)
+    nf = noise_floor(cfg.name)
+    eps = max(8 * float(err_lg), nf["logit_abs"])
     agree = sum(int(a == b) for a, b in zip(free, g["ids"]))
-    print(f"{cfg.name}: prefill err {err_x:.2e}, top-logit err {err_lg:.2e}, tie eps {eps:.2e}, "
-          f"free-running agreement {agree}/{len(free)} (first divergence {div}), tie flips {flips}, "
+    print(f"{cfg.name}: prefill err {err_x:.2e}, top-logit err {err_lg:.2e}, KV err {kv_err}, tie eps {eps:.2e}, "
+          f"free-running agreement {agree}/{len(free)}, "
           f"teacher-forced agreement {sum(int(a == b) for a, b in zip(forced, g['ids']))}/{len(forced)}")
+    floor = [nf["kv_rel"][str(int(l))] for l in L]
+    assert all(e <= 2 * f for e, f in zip(kv_err, floor)), (kv_err, floor)
+    flips, div = check_ids(free, forced, g["ids"], g["margins"], eps)
+    print(f"{cfg.name}: first divergence {div}, tie-ambiguous flips {flips}")
 
 
 def test_vit_full_size():
