@@ -85,7 +85,7 @@ vlm_status check_desc(const vlm_model_desc* d) {
 int qkv_rows(const vlm_model_desc* d) { return (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim; }
 
 struct Ws {
-    size_t h, qkv, q, kv, o, a, gpart, gpart_floats, xrow, qkvrow, qrow, part, orow, arow, lm, total;
+    size_t h, qkv, q, kv, o, a, gpart, gpart_floats, xrow, qkvrow, qrow, part, orow, arow, rope, lm, total;
 };
 
 Ws ws_layout(const vlm_model_desc* d, int max_rows) {
@@ -110,9 +110,10 @@ Ws ws_layout(const vlm_model_desc* d, int max_rows) {
     w.xrow = take(H * 4);
     w.qkvrow = take(qkv_rows(d) * 4);
     w.qrow = take(nq * hd * E);
-    w.part = take(nq * 32 * (hd + 2) * 4);
+    w.part = take(nq * kDecMaxSplits * (hd + 4) * 4);
     w.orow = take(nq * hd * E);
     w.arow = take(F * E);
+    w.rope = take(2 * hd * 4);  // cos/sin row of the decode position
     w.lm = take(d->vocab > 0 ? (size_t)lmhead_partials_max(d->vocab) * 8 : 8);
     w.total = off;
     return w;
@@ -472,7 +473,8 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
     void* orow = P(ws, w.orow);
     void* arow = P(ws, w.arow);
     const int nsplit = attn_decode_splits(W);
-    HIP_TRY(launch_embed_or_copy(dt, embed, desc->vocab, H, tok_in, x_in, x, st));
+    float* rope = (float*)P(ws, w.rope);
+    HIP_TRY(launch_embed_or_copy(dt, embed, desc->vocab, H, tok_in, x_in, x, kv->dlen(), cosv, sinv, hd, rope, st));
     for (int l = 0; l < desc->n_layers; l++) {
         const vlm_layer& y = L[l];
         GemvArgs g{};
@@ -480,7 +482,7 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
         DecAttnArgs at{};
         at.qkv = qkv; at.qn = desc->qk_norm ? y.q_norm : nullptr; at.kn = desc->qk_norm ? y.k_norm : nullptr;
-        at.eps = desc->norm_eps; at.cos = cosv; at.sin = sinv; at.segments = desc->rope_segments;
+        at.eps = desc->norm_eps; at.rope = rope; at.segments = desc->rope_segments;
         at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
         at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
         HIP_TRY(launch_attn_decode_fused(dt, at, st));
@@ -707,7 +709,12 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
     if ((s = check_ws(desc, 1, d_ws, ws_bytes, &w))) return s;
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, hd = desc->head_dim;
     float* x = (float*)P(d_ws, w.xrow);
-    HIP_TRY(launch_copy_f32(d_x_row, x, H, stream));
+    float* rope = (float*)P(d_ws, w.rope);
+    if (which == VLM_KERNEL_ATTN)  // the row copy also stages the RoPE row, as a decode step's embed kernel does
+        HIP_TRY(launch_embed_or_copy(desc->dtype, nullptr, 0, H, nullptr, d_x_row, x, kv->dlen(), d_cos, d_sin, hd,
+                                     rope, stream));
+    else
+        HIP_TRY(launch_copy_f32(d_x_row, x, H, stream));
     for (int i = 0; i < n_launches; i++) {
         const int l = i % desc->n_layers;
         const vlm_layer& y = h_layers ? h_layers[l] : vlm_layer{};
@@ -739,7 +746,7 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
             default: {
                 DecAttnArgs at{};
                 at.qkv = (const float*)P(d_ws, w.qkvrow); at.qn = desc->qk_norm ? y.q_norm : nullptr;
-                at.kn = desc->qk_norm ? y.k_norm : nullptr; at.eps = desc->norm_eps; at.cos = d_cos; at.sin = d_sin;
+                at.kn = desc->qk_norm ? y.k_norm : nullptr; at.eps = desc->norm_eps; at.rope = rope;
                 at.segments = desc->rope_segments; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = kv->capacity;
                 at.nq = nq; at.nkv = desc->n_kv_heads; at.d = hd; at.len = kv->dlen();
                 at.nsplit = attn_decode_splits(kv->capacity); at.partial = (float*)P(d_ws, w.part);

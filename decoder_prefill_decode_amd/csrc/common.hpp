@@ -55,17 +55,72 @@ __device__ __forceinline__ void ld16(const float* p, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; i++) out[i] = v[i];
 }
+
+// 16 raw bytes already in registers, widened to float (the type argument picks the layout).
+__device__ __forceinline__ void unpack16(const u32x4& v, const bf16_t*, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        o[2 * i] = __uint_as_float(v[i] << 16);
+        o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack16(const u32x4& v, const float*, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) o[i] = __uint_as_float(v[i]);
+}
 template <class T> struct Vec16 { static constexpr int n = 16 / sizeof(T); };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Cross-lane steps without the LDS crossbar (gfx950 DPP and permlane swaps).
+// A "row" is 16 consecutive lanes. dpp_f<CTRL> reads the lane selected by a
+// DPP16 control within the row: 0xB1 = quad_perm[1,0,3,2] (lane ^ 1),
+// 0x4E = quad_perm[2,3,0,1] (lane ^ 2), 0x141 = row_half_mirror (7 - i within
+// each 8 lanes), 0x140 = row_mirror (15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Pairs lanes l and l ^ 16 (swap16) or l and l ^ 32 (swap32): both lanes of a
+// pair get {value of the lower lane, value of the upper lane}, so any
+// symmetric combination of the two is bitwise identical in both lanes.
+struct LanePair { float lo, hi; };
+__device__ __forceinline__ LanePair swap16(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // {lower row's, upper row's}
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair swap32(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // {lower half's, upper half's}
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Sum / max over the 16 lanes of each row, in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
     return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    const LanePair a = swap16(v);
+    v = a.lo + a.hi;
+    const LanePair b = swap32(v);
+    return b.lo + b.hi;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = row16_max(v);
+    const LanePair a = swap16(v);
+    v = fmaxf(a.lo, a.hi);
+    const LanePair b = swap32(v);
+    return fmaxf(b.lo, b.hi);
 }
 
 // Block-wide sum for blockDim.x == NT (multiple of 64); `red` holds NT/64 floats.

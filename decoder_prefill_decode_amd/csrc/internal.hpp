@@ -85,6 +85,9 @@ struct AttnArgs {
 hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 
 // Decode attention over slots 0..*len (inclusive) of k/v [nkv][W][d]; q [nq][d].
+// Decode attention splits the valid slots over at most this many blocks per KV
+// head; each writes one partial row of d + 4 floats (o[d], m, l, pad) per query head.
+constexpr int kDecMaxSplits = 32;
 int attn_decode_splits(int capacity);
 
 // Decode attention of one layer: QK-Norm + RoPE of the new token's q and k
@@ -93,12 +96,12 @@ int attn_decode_splits(int capacity);
 struct DecAttnArgs {
     const float* qkv;  // [nq + 2*nkv][d] fp32 projections of the token
     const void* qn; const void* kn; float eps;
-    const float* cos; const float* sin; int segments;
+    const float* rope; int segments;  // cos[d] then sin[d] of position len (staged by the embed kernel)
     void* kc; void* vc;  // layer K and V, [nkv][W][d]
     int W, nq, nkv, d;
     const int32_t* len;
     int nsplit;
-    float* partial;      // [nq][nsplit][d + 2]
+    float* partial;      // [nq][nsplit][d + 4]
 };
 hipError_t launch_attn_decode_fused(int dtype, const DecAttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
@@ -112,13 +115,14 @@ int lmhead_partials_max(int V);
 hipError_t launch_lmhead_argmax(int dtype, const void* table, const float* x, const void* gain, float eps, int V,
                                 int K, unsigned long long* partials, float* logits, int32_t* token_out, int32_t* hist,
                                 int32_t* kv_len, hipStream_t st);
-hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
-                              const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st);
 
 hipError_t launch_embed(int dtype, const void* table, int V, int H, const int32_t* ids, int S, float* x,
                         hipStream_t st);
+// Decode input row: embedding of *tok (or a copy of xin); with rope != NULL also
+// stages the RoPE row of position *len: rope[0..D) = cos, rope[D..2D) = sin.
 hipError_t launch_embed_or_copy(int dtype, const void* table, int V, int H, const int32_t* tok, const float* xin,
-                                float* x, hipStream_t st);
+                                float* x, const int32_t* len, const float* cosv, const float* sinv, int D, float* rope,
+                                hipStream_t st);
 hipError_t launch_inject(int img_dtype, float* x, int S, int H, const int32_t* ids, int pid, const void* img,
                          int n_img, hipStream_t st);
 hipError_t launch_set_len(int32_t* len, int value, hipStream_t st);

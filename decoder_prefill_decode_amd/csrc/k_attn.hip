@@ -128,7 +128,10 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                     sacc[kb][r] = s;
                     mt = fmaxf(mt, s);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+            {
+                const LanePair h2 = swap32(mt);
+                mt = fmaxf(h2.lo, h2.hi);
+            }
             const float mn = fmaxf(m, mt);
             const float mu = mn == -INFINITY ? 0.f : mn;
             const float alpha = exp2f(m - mu);
@@ -141,7 +144,10 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                     sacc[kb][r] = p;
                     rs += p;
                 }
-            rs += __shfl_xor(rs, 32, kWave);
+            {
+                const LanePair h2 = swap32(rs);
+                rs = h2.lo + h2.hi;
+            }
             l = l * alpha + rs;
             m = mn;
 #pragma unroll
@@ -275,7 +281,10 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                     sacc[kb][r] = s;
                     mt = fmaxf(mt, s);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+            {
+                const LanePair h2 = swap32(mt);
+                mt = fmaxf(h2.lo, h2.hi);
+            }
             const float mn = fmaxf(m, mt);
             const float mu = mn == -INFINITY ? 0.f : mn;
             const float alpha = exp2f(m - mu);
@@ -288,7 +297,10 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                     sacc[kb][r] = p;
                     rs += p;
                 }
-            rs += __shfl_xor(rs, 32, kWave);
+            {
+                const LanePair h2 = swap32(rs);
+                rs = h2.lo + h2.hi;
+            }
             l = l * alpha + rs;
             m = mn;
 #pragma unroll
@@ -358,222 +370,38 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-// ============================================================== decode
-// partial layout: [nq][nsplit][D + 2]: o[0..D) (unnormalised), then m (log2 units), l.
-template <class T, int D, int G>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
-                                                          const T* __restrict__ vc, int W, int nkv,
-                                                          const int32_t* __restrict__ len, int nsplit,
-                                                          float* __restrict__ partial) {
-    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16;
-    __shared__ float sm_m[4][G], sm_l[4][G];
-    __shared__ float sm_o[4][G][D];
-    const int g = blockIdx.x, sp = blockIdx.y;
-    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
-    const int T_ = len[0] + 1;
-    const int chunk = (T_ + nsplit - 1) / nsplit;
-    const int k0 = sp * chunk, k1 = min(T_, k0 + chunk);
-    const float scale = kLog2e / sqrtf((float)D);
-
-    float qf[G][CPL][VEC];
-#pragma unroll
-    for (int gg = 0; gg < G; gg++)
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-            const int ch = sub + 16 * c;
-            if (ch < CH) {
-                ld16(q + (size_t)(g * G + gg) * D + ch * VEC, qf[gg][c]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < VEC; i++) qf[gg][c][i] = 0.f;
-            }
-        }
-    float mrun[G], lrun[G], o[G][CPL][VEC];
-#pragma unroll
-    for (int gg = 0; gg < G; gg++) {
-        mrun[gg] = -INFINITY;
-        lrun[gg] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; c++)
-#pragma unroll
-            for (int i = 0; i < VEC; i++) o[gg][c][i] = 0.f;
-    }
-    const T* Kg = kc + (size_t)g * W * D;
-    const T* Vg = vc + (size_t)g * W * D;
-    for (int j = k0 + w * 4 + kq; j < k1; j += 16) {
-        float kf[CPL][VEC], vf[CPL][VEC];
-#pragma unroll
-        for (int c = 0; c < CPL; c++) {
-            const int ch = sub + 16 * c;
-            if (ch < CH) {
-                ld16(Kg + (size_t)j * D + ch * VEC, kf[c]);
-                ld16(Vg + (size_t)j * D + ch * VEC, vf[c]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < VEC; i++) kf[c][i] = vf[c][i] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int gg = 0; gg < G; gg++) {
-            float s = 0.f;
-#pragma unroll
-            for (int c = 0; c < CPL; c++)
-#pragma unroll
-                for (int i = 0; i < VEC; i++) s = fmaf(qf[gg][c][i], kf[c][i], s);
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
-            s *= scale;
-            const float mn = fmaxf(mrun[gg], s);
-            const float alpha = exp2f(mrun[gg] - mn);
-            const float p = exp2f(s - mn);
-            lrun[gg] = lrun[gg] * alpha + p;
-            mrun[gg] = mn;
-#pragma unroll
-            for (int c = 0; c < CPL; c++)
-#pragma unroll
-                for (int i = 0; i < VEC; i++) o[gg][c][i] = o[gg][c][i] * alpha + p * vf[c][i];
-        }
-    }
-    // merge the four 16-lane groups of the wavefront (lanes sub, sub+16, sub+32, sub+48)
-#pragma unroll
-    for (int gg = 0; gg < G; gg++) {
-#pragma unroll
-        for (int off = 16; off < 64; off <<= 1) {
-            const float mo = __shfl_xor(mrun[gg], off, kWave);
-            const float lo = __shfl_xor(lrun[gg], off, kWave);
-            const float mn = fmaxf(mrun[gg], mo);
-            const float fa = mn == -INFINITY ? 0.f : exp2f(mrun[gg] - mn);
-            const float fb = mn == -INFINITY ? 0.f : exp2f(mo - mn);
-            lrun[gg] = lrun[gg] * fa + lo * fb;
-#pragma unroll
-            for (int c = 0; c < CPL; c++)
-#pragma unroll
-                for (int i = 0; i < VEC; i++) {
-                    const float ov = __shfl_xor(o[gg][c][i], off, kWave);
-                    o[gg][c][i] = o[gg][c][i] * fa + ov * fb;
-                }
-            mrun[gg] = mn;
-        }
-        if (kq == 0) {
-#pragma unroll
-            for (int c = 0; c < CPL; c++) {
-                const int ch = sub + 16 * c;
-                if (ch < CH)
-#pragma unroll
-                    for (int i = 0; i < VEC; i++) sm_o[w][gg][ch * VEC + i] = o[gg][c][i];
-            }
-            if (sub == 0) {
-                sm_m[w][gg] = mrun[gg];
-                sm_l[w][gg] = lrun[gg];
-            }
-        }
-    }
-    __syncthreads();
-    // merge the four wavefronts and write the block partial
-    for (int idx = tid; idx < G * (D + 2); idx += 256) {
-        const int gg = idx / (D + 2), e = idx % (D + 2);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < 4; ww++) mx = fmaxf(mx, sm_m[ww][gg]);
-        float v = 0.f;
-        if (e == D) {
-            v = mx;
-        } else {
-#pragma unroll
-            for (int ww = 0; ww < 4; ww++) {
-                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[ww][gg] - mx);
-                v += f * (e < D ? sm_o[ww][gg][e] : sm_l[ww][gg]);
-            }
-        }
-        partial[((size_t)(g * G + gg) * nsplit + sp) * (D + 2) + e] = v;
-    }
-}
-
-template <class T, int D>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ partial, int nsplit,
-                                                           T* __restrict__ out) {
-    const int h = blockIdx.x;
-    const float* p = partial + (size_t)h * nsplit * (D + 2);
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; s++) mx = fmaxf(mx, p[s * (D + 2) + D]);
-    float lsum = 0.f;
-    for (int s = 0; s < nsplit; s++) {
-        const float ms = p[s * (D + 2) + D];
-        lsum += ms == -INFINITY ? 0.f : exp2f(ms - mx) * p[s * (D + 2) + D + 1];
-    }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    for (int e = threadIdx.x; e < D; e += 128) {
-        float v = 0.f;
-        for (int s = 0; s < nsplit; s++) {
-            const float ms = p[s * (D + 2) + D];
-            if (ms != -INFINITY) v += exp2f(ms - mx) * p[s * (D + 2) + e];
-        }
-        Elt<T>::st(out, (size_t)h * D + e, v * inv);
-    }
-}
-
-int attn_decode_splits(int capacity) {
-    int n = (capacity + 63) / 64;
-    return n < 1 ? 1 : (n > 32 ? 32 : n);
-}
-
-template <class T, int D, int G>
-static hipError_t run_decode(const void* q, const void* k, const void* v, int W, int nq, int nkv, const int32_t* len,
-                             int nsplit, float* partial, void* out, hipStream_t st) {
-    attn_decode_kernel<T, D, G><<<dim3(nkv, nsplit), 256, 0, st>>>((const T*)q, (const T*)k, (const T*)v, W, nkv,
-                                                                   len, nsplit, partial);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    attn_combine_kernel<T, D><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out);
-    return hipGetLastError();
-}
-
-template <class T, int D>
-static hipError_t decode_group(const void* q, const void* k, const void* v, int W, int nq, int nkv,
-                               const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st) {
-    switch (nq / nkv) {
-        case 1: return run_decode<T, D, 1>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-        case 2: return run_decode<T, D, 2>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-        case 4: return run_decode<T, D, 4>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-        case 8: return run_decode<T, D, 8>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <class T>
-static hipError_t decode_dim(const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
-                             const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st) {
-    switch (d) {
-        case 64: return decode_group<T, 64>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-        case 72: return decode_group<T, 72>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-        case 80: return decode_group<T, 80>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-        case 128: return decode_group<T, 128>(q, k, v, W, nq, nkv, len, nsplit, partial, out, st);
-    }
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_attn_decode(int dtype, const void* q, const void* k, const void* v, int W, int nq, int nkv, int d,
-                              const int32_t* len, int nsplit, float* partial, void* out, hipStream_t st) {
-    return dtype == 1 ? decode_dim<bf16_t>(q, k, v, W, nq, nkv, d, len, nsplit, partial, out, st)
-                      : decode_dim<float>(q, k, v, W, nq, nkv, d, len, nsplit, partial, out, st);
-}
-
-
 // ============================================================== decode, fused
-// One block of 8 wavefronts per (KV head g, split sp). Phases:
-//  1. the block's K/V slots are requested first (they do not depend on q);
-//  2. wavefronts normalise + rotate the G query heads of g (and, in the block
-//     owning slot t, the new k and v, which are also written to the cache);
-//  3. online softmax over the block's slots, merged across lanes and
-//     wavefronts into one (m, l, o) partial per query head.
-// attn_combine_fast_kernel then merges the nsplit partials of each head.
-// (A last-block merge through a ticket counter needs agent-scope fences,
-// which write back the whole L2 of each XCD and measured ~4x slower.)
-constexpr int kDecPrefetch = 4;  // key iterations whose K/V rows are requested up front
+// One block of 8 wavefronts per (KV head g, split sp); split sp owns the
+// window slots [sp*chunk, (sp+1)*chunk), chunk = ceil(W / nsplit), of which
+// those below T = t+1 are valid. Each 16-lane quarter of a wavefront scores
+// one key per 32-key step. Phases:
+//  1. the block's K/V rows, the projections it rotates (q heads of g, the
+//     new k and v), their norm gains and the RoPE row of position t (staged
+//     once per token by the embed kernel) are requested first: none of these
+//     addresses depends on the device length t, so no request waits for it;
+//  2. QK-Norm + RoPE run while K/V are in flight; with t known, the block
+//     owning slot t writes the new k and v into the cache;
+//  3. softmax over the block's valid slots, one max/rescale per batch of
+//     steps, merged across the quarters and wavefronts into one (o, m, l)
+//     partial per query head; attn_combine_fast_kernel merges the splits.
+// Loads are unconditional within a step that exists (indices clamped into
+// range) and raw data is converted only after the batch is requested.
+constexpr int kDecSteps = 8;  // 32-key steps requested in one batch (fewer for 4 or 8 heads per KV head)
+
+// Splits: one per 64 window slots (up to kDecMaxSplits). A block streams at
+// most ~50 GB/s, so the KV read needs >= ~128 blocks in flight; the combine
+// then reads nsplit partials per query head.
+int attn_decode_splits(int capacity) {
+    const int n = (capacity + 63) / 64;
+    return n < 1 ? 1 : (n > kDecMaxSplits ? kDecMaxSplits : n);
+}
 
 template <class T, int D, int G>
 __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
     constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16, NW = 8, KSTEP = NW * 4;
+    constexpr int PS = D + 4;  // partial row: o[D], m, l, pad
+    constexpr int NB = G <= 2 ? kDecSteps : (G == 4 ? kDecSteps / 2 : kDecSteps / 4);  // steps per batch
+    constexpr int NI = (G + 2 + NW - 1) / NW;  // rotation items (G q heads, k, v) per wavefront
     __shared__ float qs[G][D];
     __shared__ __attribute__((aligned(16))) T knew[D];
     __shared__ __attribute__((aligned(16))) T vnew[D];
@@ -581,72 +409,86 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
     __shared__ float sm_o[NW][G][D];
     const int g = blockIdx.x, sp = blockIdx.y;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
-    const int t = a.len[0];
-    const int T_ = t + 1;
-    const int chunk = (T_ + a.nsplit - 1) / a.nsplit;
-    const int k0 = sp * chunk, k1 = min(T_, k0 + chunk);
-    const bool own = k0 <= t && t < k1;
+    const int chunk = (a.W + a.nsplit - 1) / a.nsplit;
+    const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
+    const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;  // 32-key steps of the slot range
     const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
     const T* Vg = (const T*)a.vc + (size_t)g * a.W * D;
+    const int jl = max(kend - 1, 0);  // a valid slot for clamped requests
 
-    // (1) first key batch in flight
-    float kf[kDecPrefetch][CPL][VEC], vf[kDecPrefetch][CPL][VEC];
-    auto load_batch = [&](int jb) {
+    // (1) K/V rows of the first batch, then the projections to rotate
+    u32x4 kr[NB][CPL], vr[NB][CPL];
+    const int jw = k0 + w * 4 + kq;  // this quarter's key in step 0
+    auto request = [&](int s0) {
 #pragma unroll
-        for (int b = 0; b < kDecPrefetch; b++) {
-            const int j = jb + b * KSTEP;
+        for (int b = 0; b < NB; b++) {
+            if (s0 + b < nst) {  // uniform over the block
+                const int j = min(jw + (s0 + b) * KSTEP, jl);
 #pragma unroll
-            for (int c = 0; c < CPL; c++) {
-                const int ch = sub + 16 * c;
-                if (j < k1 && j != t && ch < CH) {
-                    ld16(Kg + (size_t)j * D + ch * VEC, kf[b][c]);
-                    ld16(Vg + (size_t)j * D + ch * VEC, vf[b][c]);
+                for (int c = 0; c < CPL; c++) {
+                    const int ch = min(sub + 16 * c, CH - 1);
+                    kr[b][c] = *reinterpret_cast<const u32x4*>(Kg + (size_t)j * D + ch * VEC);
+                    vr[b][c] = *reinterpret_cast<const u32x4*>(Vg + (size_t)j * D + ch * VEC);
                 }
             }
         }
     };
-    int jb = k0 + w * 4 + kq;
-    load_batch(jb);
+    request(0);
+    const int half = D / 2, sd = D / a.segments, sh = sd / 2;
+    const bool on = lane < half;
+    const int lp = on ? lane : 0;
+    const int i0 = (lp / sh) * sd + lp % sh, i1 = i0 + sh;
+    float x0[NI], x1[NI], g0[NI], g1[NI];
+#pragma unroll
+    for (int ii = 0; ii < NI; ii++) {
+        const int it = min(w + ii * NW, G + 1);
+        const bool isq = it < G, isk = it == G;
+        const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
+        const float* src = a.qkv + (size_t)row * D;
+        const T* gn = (const T*)(isq ? a.qn : a.kn);
+        const T* gp = (it <= G && gn) ? gn : (const T*)a.kc;  // any valid address when unused
+        x0[ii] = src[i0];
+        x1[ii] = src[i1];
+        g0[ii] = Elt<T>::ld(gp, i0);
+        g1[ii] = Elt<T>::ld(gp, i1);
+    }
+    const float c0 = a.rope[i0], c1 = a.rope[i1], s0 = a.rope[D + i0], s1 = a.rope[D + i1];
+    __builtin_amdgcn_sched_barrier(0);
 
-    // (2) rotations of q (G heads) and, in the owner block, of the new k / v
+    // (2) the valid range, then QK-Norm + RoPE of q (G heads) and of the owner's new k / v
+    const int t = a.len[0];
+    const int k1 = min(t + 1, kend);
+    const bool own = k0 <= t && t < kend;
     {
-        const int half = D / 2, sd = D / a.segments, sh = sd / 2;
-        const bool on = lane < half;
-        const int gs = on ? lane / sh : 0, js = on ? lane % sh : 0;
-        const int i0 = gs * sd + js, i1 = i0 + sh;
-        const float* cr = a.cos + (size_t)t * D;
-        const float* sr = a.sin + (size_t)t * D;
-        const int nitems = G + (own ? 2 : 0);
-        for (int it = w; it < nitems; it += NW) {
+#pragma unroll
+        for (int ii = 0; ii < NI; ii++) {
+            const int it = w + ii * NW;
+            if (it >= G + (own ? 2 : 0)) continue;  // uniform per wavefront
             const bool isq = it < G, isk = it == G;
-            const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
-            const float* src = a.qkv + (size_t)row * D;
-            float x0 = on ? src[i0] : 0.f, x1 = on ? src[i1] : 0.f;
-            if (isq || isk) {
-                const T* gn = (const T*)(isq ? a.qn : a.kn);
-                if (gn) {
-                    const float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)D + a.eps);
-                    if (on) {
-                        x0 = x0 * r * Elt<T>::ld(gn, i0);
-                        x1 = x1 * r * Elt<T>::ld(gn, i1);
-                    }
-                }
-                const float y0 = x0 * cr[i0] - x1 * sr[i0];
-                const float y1 = x1 * cr[i1] + x0 * sr[i1];
-                x0 = y0;
-                x1 = y1;
+            const bool rot = isq || isk, norm = rot && (isq ? a.qn : a.kn) != nullptr;
+            float y0 = on ? x0[ii] : 0.f, y1 = on ? x1[ii] : 0.f;
+            if (norm) {
+                const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
+                y0 = y0 * r * g0[ii];
+                y1 = y1 * r * g1[ii];
+            }
+            if (rot) {
+                const float z0 = y0 * c0 - y1 * s0;
+                const float z1 = y1 * c1 + y0 * s1;
+                y0 = z0;
+                y1 = z1;
             }
             if (!on) continue;
             if (isq) {
-                qs[it][i0] = Elt<T>::rnd(x0);
-                qs[it][i1] = Elt<T>::rnd(x1);
+                qs[it][i0] = Elt<T>::rnd(y0);
+                qs[it][i1] = Elt<T>::rnd(y1);
             } else {
                 T* cache = (T*)(isk ? a.kc : a.vc) + ((size_t)g * a.W + t) * D;
                 T* lds = isk ? knew : vnew;
-                Elt<T>::st(lds, i0, x0);
-                Elt<T>::st(lds, i1, x1);
-                Elt<T>::st(cache, i0, x0);
-                Elt<T>::st(cache, i1, x1);
+                Elt<T>::st(lds, i0, y0);
+                Elt<T>::st(lds, i1, y1);
+                Elt<T>::st(cache, i0, y0);
+                Elt<T>::st(cache, i1, y1);
             }
         }
     }
@@ -657,9 +499,9 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
     for (int gg = 0; gg < G; gg++)
 #pragma unroll
         for (int c = 0; c < CPL; c++) {
-            const int ch = sub + 16 * c;
+            const int ch = min(sub + 16 * c, CH - 1);
 #pragma unroll
-            for (int i = 0; i < VEC; i++) qf[gg][c][i] = ch < CH ? qs[gg][ch * VEC + i] : 0.f;
+            for (int i = 0; i < VEC; i++) qf[gg][c][i] = sub + 16 * c < CH ? qs[gg][ch * VEC + i] : 0.f;
         }
     const float scale = kLog2e / sqrtf((float)D);
     float mrun[G], lrun[G], o[G][CPL][VEC];
@@ -672,64 +514,94 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
 #pragma unroll
             for (int i = 0; i < VEC; i++) o[gg][c][i] = 0.f;
     }
-    // (3) online softmax over this block's slots
-    for (; jb < k1; jb += KSTEP * kDecPrefetch) {
+    // (3) softmax over this block's slots, one batch of steps at a time; K/V
+    // stay packed in registers and are widened at use
+    for (int s0 = 0; s0 < nst; s0 += NB) {
+        if (s0 > 0) request(s0);
+        float sc[G][NB];
 #pragma unroll
-        for (int b = 0; b < kDecPrefetch; b++) {
-            const int j = jb + b * KSTEP;
-            if (j >= k1) break;
-            if (j == t) {
+        for (int b = 0; b < NB; b++) {
+            const int j = jw + (s0 + b) * KSTEP;
+            const bool valid = s0 + b < nst && j < k1;
+            if (s0 + b >= nst) {  // uniform: a step past the slot range
+#pragma unroll
+                for (int gg = 0; gg < G; gg++) sc[gg][b] = -INFINITY;
+#pragma unroll
+                for (int c = 0; c < CPL; c++) vr[b][c] = u32x4{0, 0, 0, 0};
+                continue;
+            }
+            float kf[CPL][VEC];
+#pragma unroll
+            for (int c = 0; c < CPL; c++) unpack16(kr[b][c], (const T*)nullptr, kf[c]);
+            if (j == t) {  // the new slot: this token's rotated k and v
 #pragma unroll
                 for (int c = 0; c < CPL; c++) {
-                    const int ch = sub + 16 * c;
-                    if (ch < CH) {
-                        ld16(knew + ch * VEC, kf[b][c]);
-                        ld16(vnew + ch * VEC, vf[b][c]);
-                    }
+                    const int ch = min(sub + 16 * c, CH - 1);
+                    ld16(knew + ch * VEC, kf[c]);
+                    vr[b][c] = *reinterpret_cast<const u32x4*>(vnew + ch * VEC);
                 }
+            }
+            if (!valid) {  // clamped or unrequested rows hold arbitrary bits: weight 0 must not meet NaN
+#pragma unroll
+                for (int c = 0; c < CPL; c++) vr[b][c] = u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int gg = 0; gg < G; gg++) {
-                float s = 0.f;
+                float sv = 0.f;
 #pragma unroll
                 for (int c = 0; c < CPL; c++)
-                    if (sub + 16 * c < CH)
 #pragma unroll
-                        for (int i = 0; i < VEC; i++) s = fmaf(qf[gg][c][i], kf[b][c][i], s);
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, kWave);
-                s *= scale;
-                const float mn = fmaxf(mrun[gg], s);
-                const float alpha = exp2f(mrun[gg] - mn);
-                const float p = exp2f(s - mn);
-                lrun[gg] = lrun[gg] * alpha + p;
-                mrun[gg] = mn;
-#pragma unroll
-                for (int c = 0; c < CPL; c++)
-                    if (sub + 16 * c < CH)
-#pragma unroll
-                        for (int i = 0; i < VEC; i++) o[gg][c][i] = o[gg][c][i] * alpha + p * vf[b][c][i];
+                    for (int i = 0; i < VEC; i++) sv = fmaf(qf[gg][c][i], kf[c][i], sv);
+                sv = row16_sum(sv);  // the 16 lanes of this quarter hold one key row
+                sc[gg][b] = valid ? sv * scale : -INFINITY;
             }
         }
-        if (jb + KSTEP * kDecPrefetch < k1) load_batch(jb + KSTEP * kDecPrefetch);
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+            float mb = sc[gg][0];
+#pragma unroll
+            for (int b = 1; b < NB; b++) mb = fmaxf(mb, sc[gg][b]);
+            if (mb == -INFINITY) continue;  // no valid key of this quarter in the batch
+            const float mn = fmaxf(mrun[gg], mb);
+            const float alpha = exp2f(mrun[gg] - mn);
+            lrun[gg] *= alpha;
+            mrun[gg] = mn;
+#pragma unroll
+            for (int c = 0; c < CPL; c++)
+#pragma unroll
+                for (int i = 0; i < VEC; i++) o[gg][c][i] *= alpha;
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                const float pb = exp2f(sc[gg][b] - mn);
+                lrun[gg] += pb;
+#pragma unroll
+                for (int c = 0; c < CPL; c++) {
+                    float vf[VEC];
+                    unpack16(vr[b][c], (const T*)nullptr, vf);
+#pragma unroll
+                    for (int i = 0; i < VEC; i++) o[gg][c][i] = fmaf(pb, vf[i], o[gg][c][i]);
+                }
+            }
+        }
     }
-    // merge the four 16-lane groups of the wavefront, then the wavefronts
+    // merge the four 16-lane quarters of the wavefront (lane pairs l, l^16 then
+    // l, l^32; each pair computes the same symmetric merge), then the wavefronts
 #pragma unroll
     for (int gg = 0; gg < G; gg++) {
 #pragma unroll
-        for (int off = 16; off < 64; off <<= 1) {
-            const float mo = __shfl_xor(mrun[gg], off, kWave);
-            const float lo = __shfl_xor(lrun[gg], off, kWave);
-            const float mn = fmaxf(mrun[gg], mo);
-            const float fa = mn == -INFINITY ? 0.f : exp2f(mrun[gg] - mn);
-            const float fb = mn == -INFINITY ? 0.f : exp2f(mo - mn);
-            lrun[gg] = lrun[gg] * fa + lo * fb;
+        for (int lvl = 0; lvl < 2; lvl++) {
+            const LanePair m2 = lvl ? swap32(mrun[gg]) : swap16(mrun[gg]);
+            const LanePair l2 = lvl ? swap32(lrun[gg]) : swap16(lrun[gg]);
+            const float mn = fmaxf(m2.lo, m2.hi);
+            const float fa = mn == -INFINITY ? 0.f : exp2f(m2.lo - mn);
+            const float fb = mn == -INFINITY ? 0.f : exp2f(m2.hi - mn);
+            lrun[gg] = l2.lo * fa + l2.hi * fb;
 #pragma unroll
             for (int c = 0; c < CPL; c++)
 #pragma unroll
                 for (int i = 0; i < VEC; i++) {
-                    const float ov = __shfl_xor(o[gg][c][i], off, kWave);
-                    o[gg][c][i] = o[gg][c][i] * fa + ov * fb;
+                    const LanePair o2 = lvl ? swap32(o[gg][c][i]) : swap16(o[gg][c][i]);
+                    o[gg][c][i] = o2.lo * fa + o2.hi * fb;
                 }
             mrun[gg] = mn;
         }
@@ -763,33 +635,34 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
                 v += f * (e < D ? sm_o[ww][gg][e] : sm_l[ww][gg]);
             }
         }
-        a.partial[((size_t)(g * G + gg) * a.nsplit + sp) * (D + 2) + e] = v;
+        a.partial[((size_t)(g * G + gg) * a.nsplit + sp) * PS + e] = v;
     }
 }
 
 // Merge of the split partials: one block per query head, one thread per
-// element; all (m, l, o) loads of a thread are issued before any is used.
+// element; all (o, m, l) loads of a thread are issued before any is used.
 template <class T, int D>
 __global__ __launch_bounds__(128) void attn_combine_fast_kernel(const float* __restrict__ partial, int nsplit,
                                                                 T* __restrict__ out) {
-    constexpr int NS = 32;
+    constexpr int NS = kDecMaxSplits, PS = D + 4;
     const int h = blockIdx.x, e = threadIdx.x;
-    const float* p = partial + (size_t)h * nsplit * (D + 2);
+    const float* p = partial + (size_t)h * nsplit * PS;
+    const int ee = e < D ? e : 0;
     float m[NS], l[NS], o[NS];
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-        const bool on = s < nsplit;
-        m[s] = on ? p[s * (D + 2) + D] : -INFINITY;
-        l[s] = on ? p[s * (D + 2) + D + 1] : 0.f;
-        o[s] = (on && e < D) ? p[s * (D + 2) + e] : 0.f;
+        const int ss = s < nsplit ? s : 0;
+        m[s] = p[ss * PS + D];
+        l[s] = p[ss * PS + D + 1];
+        o[s] = p[ss * PS + ee];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < NS; s++) mx = fmaxf(mx, m[s]);
+    for (int s = 0; s < NS; s++) mx = s < nsplit ? fmaxf(mx, m[s]) : mx;
     float lsum = 0.f, v = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-        const float f = m[s] == -INFINITY ? 0.f : exp2f(m[s] - mx);
+        const float f = (s >= nsplit || m[s] == -INFINITY) ? 0.f : exp2f(m[s] - mx);
         lsum += f * l[s];
         v += f * o[s];
     }

@@ -13,6 +13,8 @@
 // covering elements l*VEC + i*64*VEC, so one wavefront instruction reads 1 KiB
 // of contiguous row. Several rows and two K strides per iteration keep enough
 // loads in flight to cover HBM latency.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -128,39 +130,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
 }
 
-// Latency-hiding variant used when K fits the register plan: the operand
-// vector (and its gain) is requested first, then every weight chunk this
-// wavefront needs, and only then is the vector normalised. Vector-memory loads
-// complete in issue order, so waiting for the small vector leaves the weight
-// stream in flight while the block reduction runs.
-constexpr int kMaxVecChunks = 12;  // 16-byte chunks of the operand vector per thread
+// Latency-hiding variant used when K fits the register plan. Lane l of a
+// wavefront owns the elements k = l*VEC + c*64*VEC (+0..VEC-1) of every row
+// it reads. Requests go out in the order operand vector, weights, old output
+// (for a residual update); vector-memory loads complete in issue order, so
+// the operand is prepared while the weight stream is still in flight.
+//  * Plain operand (a bf16/fp32 row): each lane loads the vector at its own
+//    positions, so the wavefront needs no LDS and no barrier.
+//  * RMSNorm operand (fp32 x and a gain): the block loads x once, reduces the
+//    sum of squares and writes the normalised, rounded row into LDS (a
+//    per-lane copy would cost 12 registers per chunk and halve occupancy).
+// Every load is unconditional (indices are clamped into range, out-of-range
+// lanes are masked afterwards) and raw data is converted only after the last
+// request: a load under a branch, or arithmetic between loads, makes the
+// compiler wait for a memory round trip before the next request.
 
-template <class T> __device__ __forceinline__ void ld4(const T* p, float* o);
-template <> __device__ __forceinline__ void ld4<float>(const float* p, float* o) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
-}
-template <> __device__ __forceinline__ void ld4<bf16_t>(const bf16_t* p, float* o) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
-    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
-}
-
-__device__ __forceinline__ void unpack16(const u32x4& v, const bf16_t*, float* o) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        o[2 * i] = __uint_as_float(v[i] << 16);
-        o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+// Four gain values in their storage type, raw.
+template <class T> struct Raw4;
+template <> struct Raw4<float> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ float get(int e) const { return __uint_as_float(v[e]); }
+};
+template <> struct Raw4<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = e < 2 ? v.x : v.y;
+        return __uint_as_float(e % 2 ? (w & 0xffff0000u) : (w << 16));
     }
-}
-__device__ __forceinline__ void unpack16(const u32x4& v, const float*, float* o) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) o[i] = __uint_as_float(v[i]);
-}
+};
 
 template <class T, Pro PRO, Epi EPI, int NR, int KCH>
 __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
     constexpr int VEC = 16 / sizeof(T), STEP = kWave * VEC;
+    constexpr bool NORM = PRO == Pro::RmsNorm;
+    constexpr int VCH = NORM ? (KCH * STEP / 4 + 255) / 256 : 1;  // 4-float chunks of x per thread
     extern __shared__ float vs[];
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid % kWave;
@@ -168,22 +173,25 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
     const int K = a.K;
     const T* W = (const T*)a.W;
 
-    // (1) operand vector (+ gain) chunks
-    float xv[kMaxVecChunks][4], gv[kMaxVecChunks][4];
-    u32x4 pv[kMaxVecChunks];
-    const int nx = PRO == Pro::RmsNorm ? K / 4 : K / VEC;
+    // (1) operand: RMSNorm -> this thread's chunks of x and gain; Plain -> this lane's slice
+    u32x4 xr[NORM ? VCH : KCH];
+    Raw4<T> gr[VCH];
+    if constexpr (NORM) {
+        const int nx = K / 4;
 #pragma unroll
-    for (int i = 0; i < kMaxVecChunks; i++) {
-        const int c = tid + 256 * i;
-        if (c < nx) {
-            if constexpr (PRO == Pro::RmsNorm) {
-                ld4<float>((const float*)a.vec + 4 * c, xv[i]);
-                ld4<T>((const T*)a.gain + 4 * c, gv[i]);
-            } else {
-                pv[i] = *reinterpret_cast<const u32x4*>((const T*)a.vec + VEC * c);
-            }
+        for (int i = 0; i < VCH; i++) {
+            const int c = min(tid + 256 * i, nx - 1);
+            xr[i] = *reinterpret_cast<const u32x4*>((const float*)a.vec + 4 * c);
+            gr[i].load((const T*)a.gain + 4 * c);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < KCH; c++) {
+            const int k = lane * VEC + c * STEP;
+            xr[c] = *reinterpret_cast<const u32x4*>((const T*)a.vec + (k < K ? k : 0));
         }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the operand requests ahead of the weight stream
     // (2) weight rows of this wavefront
     int rows[NR];
     if constexpr (EPI == Epi::SwiGLU) {
@@ -206,39 +214,36 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < KCH; c++) {
         const int k = lane * VEC + c * STEP;
+        const int kk = k < K ? k : 0;
 #pragma unroll
-        for (int r = 0; r < NR; r++)
-            wr[r][c] = k < K ? *reinterpret_cast<const u32x4*>(W + (size_t)rows[r] * K + k) : u32x4{0, 0, 0, 0};
+        for (int r = 0; r < NR; r++) wr[r][c] = *reinterpret_cast<const u32x4*>(W + (size_t)rows[r] * K + kk);
     }
-    // (3) operand row into LDS (normalised and rounded for RmsNorm)
-    if constexpr (PRO == Pro::RmsNorm) {
+    // (2b) the value a residual update adds to: lane r holds row wave*NR + r
+    float old = 0.f;
+    if constexpr (EPI == Epi::Resid) {
+        const int n = min(wave * NR + min(lane, NR - 1), a.N - 1);
+        old = ((const float*)a.out)[n];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // no arithmetic is hoisted between the requests
+    // (3) RMSNorm: normalised, rounded row into LDS
+    if constexpr (NORM) {
+        const int nx = K / 4;
         float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < kMaxVecChunks; i++)
+        for (int i = 0; i < VCH; i++)
             if (tid + 256 * i < nx)
 #pragma unroll
-                for (int e = 0; e < 4; e++) ss += xv[i][e] * xv[i][e];
+                for (int e = 0; e < 4; e++) ss += __uint_as_float(xr[i][e]) * __uint_as_float(xr[i][e]);
         const float rs = rsqrtf(block_sum<256>(ss, red) / (float)K + a.eps);
 #pragma unroll
-        for (int i = 0; i < kMaxVecChunks; i++) {
+        for (int i = 0; i < VCH; i++) {
             const int c = tid + 256 * i;
             if (c < nx)
 #pragma unroll
-                for (int e = 0; e < 4; e++) vs[4 * c + e] = Elt<T>::rnd(xv[i][e] * rs * gv[i][e]);
+                for (int e = 0; e < 4; e++) vs[4 * c + e] = Elt<T>::rnd(__uint_as_float(xr[i][e]) * rs * gr[i].get(e));
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kMaxVecChunks; i++) {
-            const int c = tid + 256 * i;
-            if (c < nx) {
-                float f[VEC];
-                unpack16(pv[i], (const T*)nullptr, f);
-#pragma unroll
-                for (int e = 0; e < VEC; e++) vs[VEC * c + e] = f[e];
-            }
-        }
+        __syncthreads();
     }
-    __syncthreads();
     // (4) dot products
     float acc[NR];
 #pragma unroll
@@ -247,15 +252,19 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
     for (int c = 0; c < KCH; c++) {
         const int k = lane * VEC + c * STEP;
         if (k < K) {
-            float v[VEC];
+            float h[VEC];
+            if constexpr (NORM) {
 #pragma unroll
-            for (int e = 0; e < VEC; e++) v[e] = vs[k + e];
+                for (int e = 0; e < VEC; e++) h[e] = vs[k + e];
+            } else {
+                unpack16(xr[c], (const T*)nullptr, h);
+            }
 #pragma unroll
             for (int r = 0; r < NR; r++) {
                 float wf[VEC];
                 unpack16(wr[r][c], (const T*)nullptr, wf);
 #pragma unroll
-                for (int e = 0; e < VEC; e++) acc[r] = fmaf(wf[e], v[e], acc[r]);
+                for (int e = 0; e < VEC; e++) acc[r] = fmaf(wf[e], h[e], acc[r]);
             }
         }
     }
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
             if (lane == r && n < a.N) {
                 float* o = (float*)a.out;
                 if constexpr (EPI == Epi::Resid)
-                    o[n] += acc[r];
+                    o[n] = old + acc[r];
                 else
                     o[n] = acc[r];
             }
@@ -310,29 +319,49 @@ static hipError_t run_gemv2(const GemvArgs& a, hipStream_t st) {
     const int nrows = a.N;  // SwiGLU: NR counts gate + up rows
     const int waves = (nrows + NR - 1) / NR;
     const int blocks = (waves + 3) / 4;
-    gemv2_kernel<T, PRO, EPI, NR, KCH><<<blocks, 256, (size_t)a.K * sizeof(float), st>>>(a);
+    const size_t smem = PRO == Pro::RmsNorm ? (size_t)a.K * sizeof(float) : 0;
+    gemv2_kernel<T, PRO, EPI, NR, KCH><<<blocks, 256, smem, st>>>(a);
     return hipGetLastError();
+}
+
+// VLM_GEMV_ROWS (1, 2, 4 or 8) fixes the rows per wavefront of the decode
+// projections, for tuning; unset or 0 keeps the choice below.
+static int gemv_rows_override() {
+    static int v = [] {
+        const char* e = getenv("VLM_GEMV_ROWS");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
 }
 
 // Rows per wavefront: as many as the register plan allows (NR*KCH <= 24 chunks)
 // while keeping >= 1024 wavefronts in flight.
 template <class T, Pro PRO, Epi EPI, int KCH>
 static hipError_t pick_nr(const GemvArgs& a, hipStream_t st) {
-    constexpr int cap = 24 / KCH;
-    const int n = a.N;
-    if constexpr (cap >= 8) if (n / 8 >= 1024) return run_gemv2<T, PRO, EPI, 8, KCH>(a, st);
-    if constexpr (cap >= 4) if (n / 4 >= 1024) return run_gemv2<T, PRO, EPI, 4, KCH>(a, st);
-    if constexpr (cap >= 2) if (n / 2 >= 1024 || EPI == Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 2, KCH>(a, st);
-    if constexpr (EPI != Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 1, KCH>(a, st);
-    return hipErrorNotSupported;
+    // the RMSNorm operand is staged with at most 12 chunks per thread: wider rows take the generic path
+    if constexpr (PRO == Pro::RmsNorm && KCH > 12) {
+        return hipErrorNotSupported;
+    } else {
+        constexpr int cap = 24 / KCH;
+        const int n = a.N;
+        switch (gemv_rows_override()) {  // tuning override: rows per wavefront, if the plan allows it
+            case 8: if constexpr (cap >= 8) return run_gemv2<T, PRO, EPI, 8, KCH>(a, st); break;
+            case 4: if constexpr (cap >= 4) return run_gemv2<T, PRO, EPI, 4, KCH>(a, st); break;
+            case 2: if constexpr (cap >= 2) return run_gemv2<T, PRO, EPI, 2, KCH>(a, st); break;
+            case 1: if constexpr (EPI != Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 1, KCH>(a, st); break;
+        }
+        if constexpr (cap >= 8) if (n / 8 >= 1024) return run_gemv2<T, PRO, EPI, 8, KCH>(a, st);
+        if constexpr (cap >= 4) if (n / 4 >= 1024) return run_gemv2<T, PRO, EPI, 4, KCH>(a, st);
+        if constexpr (cap >= 2) if (n / 2 >= 1024 || EPI == Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 2, KCH>(a, st);
+        if constexpr (EPI != Epi::SwiGLU) return run_gemv2<T, PRO, EPI, 1, KCH>(a, st);
+        return hipErrorNotSupported;
+    }
 }
 
 // Returns hipErrorNotSupported when K has no register plan (caller falls back).
 template <class T, Pro PRO, Epi EPI>
 static hipError_t try_gemv2(const GemvArgs& a, hipStream_t st) {
     constexpr int VEC = 16 / sizeof(T);
-    const int nx = PRO == Pro::RmsNorm ? a.K / 4 : a.K / VEC;
-    if (nx > 256 * kMaxVecChunks) return hipErrorNotSupported;
     const int kch = (a.K + kWave * VEC - 1) / (kWave * VEC);
     switch (kch) {
         case 1: return pick_nr<T, PRO, EPI, 1>(a, st);
@@ -473,7 +502,6 @@ template <class T>
 static hipError_t lm2_dispatch(const GemvArgs& a, int* nb, hipStream_t st) {
     constexpr int VEC = 16 / sizeof(T);
     const int kch = (a.K + kWave * VEC - 1) / (kWave * VEC);
-    if (a.K / 4 > 256 * kMaxVecChunks || a.K < 512) return hipErrorNotSupported;
     switch (kch) {
         case 1: return run_lm2<T, 8, 1>(a, nb, st);
         case 2: return run_lm2<T, 8, 2>(a, nb, st);

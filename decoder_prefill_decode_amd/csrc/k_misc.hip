@@ -27,7 +27,17 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ table,
 template <class T>
 __global__ __launch_bounds__(256) void embed_row_kernel(const T* __restrict__ table, int V, int H,
                                                         const int32_t* __restrict__ tok, const float* __restrict__ xin,
-                                                        float* __restrict__ x) {
+                                                        float* __restrict__ x, const int32_t* __restrict__ len,
+                                                        const float* __restrict__ cosv, const float* __restrict__ sinv,
+                                                        int D, float* __restrict__ rope) {
+    // the RoPE row of this token's position (slot len), staged once for every layer's attention
+    if (rope) {
+        const int t = len[0];
+        for (int j = threadIdx.x; j < D; j += 256) {
+            rope[j] = cosv[(size_t)t * D + j];
+            rope[D + j] = sinv[(size_t)t * D + j];
+        }
+    }
     if (xin) {
         for (int j = threadIdx.x; j < H; j += 256) x[j] = xin[j];
         return;
@@ -212,11 +222,12 @@ hipError_t launch_embed(int dtype, const void* table, int V, int H, const int32_
 }
 
 hipError_t launch_embed_or_copy(int dtype, const void* table, int V, int H, const int32_t* tok, const float* xin,
-                                float* x, hipStream_t st) {
+                                float* x, const int32_t* len, const float* cosv, const float* sinv, int D, float* rope,
+                                hipStream_t st) {
     if (dtype == 1)
-        embed_row_kernel<bf16_t><<<1, 256, 0, st>>>((const bf16_t*)table, V, H, tok, xin, x);
+        embed_row_kernel<bf16_t><<<1, 256, 0, st>>>((const bf16_t*)table, V, H, tok, xin, x, len, cosv, sinv, D, rope);
     else
-        embed_row_kernel<float><<<1, 256, 0, st>>>((const float*)table, V, H, tok, xin, x);
+        embed_row_kernel<float><<<1, 256, 0, st>>>((const float*)table, V, H, tok, xin, x, len, cosv, sinv, D, rope);
     return hipGetLastError();
 }
 

@@ -5,3 +5,8 @@ def decode_splits(capacity: int) -> int:
     """Split count of decode attention for a KV window (attn_decode_splits in k_attn.hip)."""
     n = (capacity + 63) // 64
     return max(1, min(32, n))
+
+
+def partial_stride(head_dim: int) -> int:
+    """Floats per (query head, split) partial row of decode attention: o[d], m, l, pad."""
+    return head_dim + 4
