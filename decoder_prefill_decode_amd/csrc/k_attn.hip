@@ -371,10 +371,10 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
 }
 
 // ============================================================== decode, fused
-// One block of 8 wavefronts per (KV head g, split sp); split sp owns the
+// One block of kDecWaves wavefronts per (KV head g, split sp); split sp owns the
 // window slots [sp*chunk, (sp+1)*chunk), chunk = ceil(W / nsplit), of which
 // those below T = t+1 are valid. Each 16-lane quarter of a wavefront scores
-// one key per 32-key step. Phases:
+// one key per step (a step covers 4 keys per wavefront). Phases:
 //  1. the block's K/V rows, the projections it rotates (q heads of g, the
 //     new k and v), their norm gains and the RoPE row of position t (staged
 //     once per token by the embed kernel) are requested first: none of these
@@ -386,19 +386,22 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
 //     partial per query head; attn_combine_fast_kernel merges the splits.
 // Loads are unconditional within a step that exists (indices clamped into
 // range) and raw data is converted only after the batch is requested.
-constexpr int kDecSteps = 8;  // 32-key steps requested in one batch (fewer for 4 or 8 heads per KV head)
+constexpr int kDecWaves = 4;  // wavefronts per block
+constexpr int kDecSteps = 8;  // key steps requested in one batch (fewer for 4 or 8 heads per KV head)
 
-// Splits: one per 64 window slots (up to kDecMaxSplits). A block streams at
+// Splits: one per 32 window slots (up to kDecMaxSplits). A block streams at
 // most ~50 GB/s, so the KV read needs >= ~128 blocks in flight; the combine
-// then reads nsplit partials per query head.
+// then reads nsplit partials per query head. (Measured on the 28-layer
+// stack's shape at 624 valid slots: 4 wavefronts x 32 splits 5.1 us,
+// 8 x 16 5.6 us, 2 x 64 5.8 us.)
 int attn_decode_splits(int capacity) {
-    const int n = (capacity + 63) / 64;
+    const int n = (capacity + 31) / 32;
     return n < 1 ? 1 : (n > kDecMaxSplits ? kDecMaxSplits : n);
 }
 
-template <class T, int D, int G>
-__global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
-    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16, NW = 8, KSTEP = NW * 4;
+template <class T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs a) {
+    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16, KSTEP = NW * 4;
     constexpr int PS = D + 4;  // partial row: o[D], m, l, pad
     constexpr int NB = G <= 2 ? kDecSteps : (G == 4 ? kDecSteps / 2 : kDecSteps / 4);  // steps per batch
     constexpr int NI = (G + 2 + NW - 1) / NW;  // rotation items (G q heads, k, v) per wavefront
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
     const int chunk = (a.W + a.nsplit - 1) / a.nsplit;
     const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
-    const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;  // 32-key steps of the slot range
+    const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;  // key steps of the slot range
     const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
     const T* Vg = (const T*)a.vc + (size_t)g * a.W * D;
     const int jl = max(kend - 1, 0);  // a valid slot for clamped requests
@@ -560,7 +563,8 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
         for (int gg = 0; gg < G; gg++) {
             float mb = sc[gg][0];
 #pragma unroll
-            for (int b = 1; b < NB; b++) mb = fmaxf(mb, sc[gg][b]);
+            for (int b = 1; b < NB; b++)
+                if (s0 + b < nst) mb = fmaxf(mb, sc[gg][b]);
             if (mb == -INFINITY) continue;  // no valid key of this quarter in the batch
             const float mn = fmaxf(mrun[gg], mb);
             const float alpha = exp2f(mrun[gg] - mn);
@@ -572,6 +576,7 @@ __global__ __launch_bounds__(512) void attn_decode_fused_kernel(DecAttnArgs a) {
                 for (int i = 0; i < VEC; i++) o[gg][c][i] *= alpha;
 #pragma unroll
             for (int b = 0; b < NB; b++) {
+                if (s0 + b >= nst) break;  // uniform
                 const float pb = exp2f(sc[gg][b] - mn);
                 lrun[gg] += pb;
 #pragma unroll
@@ -673,10 +678,10 @@ template <class T, int D>
 static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
     const dim3 grid(a.nkv, a.nsplit);
     switch (a.nq / a.nkv) {
-        case 1: attn_decode_fused_kernel<T, D, 1><<<grid, 512, 0, st>>>(a); break;
-        case 2: attn_decode_fused_kernel<T, D, 2><<<grid, 512, 0, st>>>(a); break;
-        case 4: attn_decode_fused_kernel<T, D, 4><<<grid, 512, 0, st>>>(a); break;
-        case 8: attn_decode_fused_kernel<T, D, 8><<<grid, 512, 0, st>>>(a); break;
+        case 1: attn_decode_fused_kernel<T, D, 1, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
+        case 2: attn_decode_fused_kernel<T, D, 2, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
+        case 4: attn_decode_fused_kernel<T, D, 4, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
+        case 8: attn_decode_fused_kernel<T, D, 8, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -3,7 +3,7 @@
 
 def decode_splits(capacity: int) -> int:
     """Split count of decode attention for a KV window (attn_decode_splits in k_attn.hip)."""
-    n = (capacity + 63) // 64
+    n = (capacity + 31) // 32
     return max(1, min(32, n))
 
 
