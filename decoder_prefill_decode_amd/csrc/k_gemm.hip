@@ -30,6 +30,70 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return b;
 }
 
+// Epilogue of one wavefront's (TM*32) x (TN*32) accumulator tile at output
+// rows m0 + wm*WM, columns n0 + wn*WN. C layout of a 32x32 block: lane owns
+// column l32 and rows (r/4)*8 + h*4 + r%4, r = 0..15.
+template <class T, int WM, int WN, int TM, int TN, Epi EPI, bool SPLIT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x16 (&acc)[TM][TN], int m0, int n0, int wm,
+                                              int wn, int h, int l32) {
+    const int M = a.M, N = a.N;
+    const T* bias = (const T*)a.bias;
+    if constexpr (SPLIT) {  // raw partial sums; splitk_reduce_kernel applies the epilogue
+        float* part = a.part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int n = n0 + wn * WN + j * 32 + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+                    if (m < M) part[(size_t)m * N + n] = acc[i][j][r];
+                }
+        }
+    } else if constexpr (EPI == Epi::SwiGLU) {
+        static_assert(TN == 2, "SwiGLU needs a 64-column wave tile (gate block, up block)");
+        const int ncol = (n0 + wn * WN) / 2 + l32;
+        T* out = (T*)a.out;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+                if (m < M && n0 + wn * WN < N) {  // N = 2F is a multiple of 64: whole groups
+                    const float gt = acc[i][0][r], up = acc[i][1][r];
+                    Elt<T>::st(out, (size_t)m * a.ldo + ncol, silu_f(gt) * up);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int n = n0 + wn * WN + j * 32 + l32;
+            if (n >= N) continue;
+            const float bn = bias ? Elt<T>::ld(bias, n) : 0.f;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+                    if (m >= M) continue;
+                    const float v = acc[i][j][r] + bn;
+                    if constexpr (EPI == Epi::StoreF32) {
+                        ((float*)a.out)[(size_t)m * a.ldo + n] = v;
+                    } else if constexpr (EPI == Epi::Resid) {
+                        float* x = (float*)a.out + (size_t)m * a.ldo + n;
+                        *x = *x + v;
+                    } else if constexpr (EPI == Epi::Gelu) {
+                        Elt<T>::st((T*)a.out, (size_t)m * a.ldo + n, gelu_tanh_f(v));
+                    } else {  // StoreRowMap
+                        ((float*)a.out)[(size_t)a.rowmap[m] * a.ldo + n] = v;
+                    }
+                }
+        }
+    }
+}
+
 template <class T, int BM, int BN, Epi EPI, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     using Tr = GemmTraits<T>;
@@ -139,63 +203,126 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         __syncthreads();
     }
 
-    // Epilogue. C layout of a 32x32 block: lane owns column l32 and rows
-    // (r/4)*8 + h*4 + r%4, r = 0..15.
-    const T* bias = (const T*)a.bias;
-    if constexpr (SPLIT) {  // raw partial sums; splitk_reduce_kernel applies the epilogue
-        float* part = a.part + (size_t)blockIdx.y * M * N;
-#pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const int n = n0 + wn * WN + j * 32 + l32;
-            if (n >= N) continue;
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-                    if (m < M) part[(size_t)m * N + n] = acc[i][j][r];
-                }
+    gemm_epilogue<T, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32);
+}
+
+// ------------------------------------------------- bf16, direct-to-LDS pipeline
+// The prefill shapes (M ~ 500 rows) give each block little MFMA work per K
+// stage, so a stage is bound by the global-load round trip unless several
+// stages are in flight. Here the operands go straight from global memory into
+// a ring of P LDS stages (global_load_lds_dwordx4: lane L's 16 bytes land at
+// the wave-uniform base + 16*L), P-1 stages ahead of the MFMAs, with no
+// register staging. One load instruction fills 8 tile rows of 64 bf16; lane L
+// fetches row L/8, chunk (L%8) ^ (L/8), so a row's eight 16-byte chunks are
+// XOR-swizzled by the row index and the MFMA operand reads (32 rows, one
+// chunk) spread over the LDS banks. Requires K % 64 == 0.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int V>
+__device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(V), other counters untouched (gfx9 encoding)
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+// Waits until at most k * LPS of this wave's loads are outstanding, k in [0, KMAX] (wave-uniform).
+template <int LPS, int KMAX>
+__device__ __forceinline__ void wait_stages(int k) {
+    if constexpr (KMAX > 0) {
+        if (k >= KMAX) {
+            wait_vm<KMAX * LPS>();
+            return;
         }
-    } else if constexpr (EPI == Epi::SwiGLU) {
-        static_assert(TN == 2, "SwiGLU needs a 64-column wave tile (gate block, up block)");
-        const int ncol = (n0 + wn * WN) / 2 + l32;
-        T* out = (T*)a.out;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-                if (m < M && n0 + wn * WN < N) {  // N = 2F is a multiple of 64: whole groups
-                    const float gt = acc[i][0][r], up = acc[i][1][r];
-                    Elt<T>::st(out, (size_t)m * a.ldo + ncol, silu_f(gt) * up);
-                }
-            }
+        wait_stages<LPS, KMAX - 1>(k);
     } else {
+        wait_vm<0>();
+    }
+}
+
+template <int BM, int BN, int P, Epi EPI, bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_lds_kernel(GemmArgs a) {
+    constexpr int BK = 64, WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int AI = BM / 32, BI = BN / 32;  // load instructions per wave per stage (8 rows each, 4 waves)
+    constexpr int LPS = AI + BI, STAGE = (BM + BN) * BK;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
+
+    const int M = a.M, N = a.N, K = a.K;
+    const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
+    const int tile = xcd_remap(blockIdx.x, mt * nt);
+    const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int wm = w / 2, wn = w % 2, h = lane / 32, l32 = lane % 32;
+    const bf16_t* A = (const bf16_t*)a.A;
+    const bf16_t* B = (const bf16_t*)a.B;
+
+    // this lane's source row/chunk in each of the wave's load instructions (rows past M / N are clamped:
+    // their products land in output rows / columns the epilogue never stores)
+    const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+    const bf16_t* ga[AI];
+    const bf16_t* gb[BI];
 #pragma unroll
-        for (int j = 0; j < TN; j++) {
-            const int n = n0 + wn * WN + j * 32 + l32;
-            if (n >= N) continue;
-            const float bn = bias ? Elt<T>::ld(bias, n) : 0.f;
+    for (int i = 0; i < AI; i++) ga[i] = A + (size_t)min(m0 + (w * AI + i) * 8 + lr, M - 1) * K + lc * 8;
+#pragma unroll
+    for (int i = 0; i < BI; i++) gb[i] = B + (size_t)min(n0 + (w * BI + i) * 8 + lr, N - 1) * K + lc * 8;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    int kt0 = 0, nk = K / BK;
+    if constexpr (SPLIT) {
+        const int per = (nk + gridDim.y - 1) / gridDim.y;
+        kt0 = blockIdx.y * per;
+        nk = max(0, min(nk, kt0 + per) - kt0);
+    }
+    // one K stage of both tiles into LDS stage ST: instruction i of wavefront w fills 8 rows (1 KiB).
+    // (The source pointer is passed as const void*: the host pass silently drops the kernel otherwise.)
+#define VLM_LDS_STAGE(KOFF, ST)                                                                              \
+    do {                                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < AI; i++) __builtin_amdgcn_global_load_lds(                     \
+            (const void*)(ga[i] + (KOFF)), (lds_void*)((ST) + (w * AI + i) * 512), 16, 0, 0);                \
+        _Pragma("unroll") for (int i = 0; i < BI; i++) __builtin_amdgcn_global_load_lds(                     \
+            (const void*)(gb[i] + (KOFF)), (lds_void*)((ST) + BM * BK + (w * BI + i) * 512), 16, 0, 0);      \
+    } while (0)
+#pragma unroll
+    for (int s = 0; s < P - 1; s++)
+        if (s < nk) VLM_LDS_STAGE((kt0 + s) * BK, smem + s * STAGE);
+    // operand rows of this lane inside a stage; chunk c of row r sits at r*64 + ((c ^ (r & 7)) * 8)
+    int ra[TM], rb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++) ra[i] = wm * WM + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < TN; j++) rb[j] = BM + wn * WN + j * 32 + l32;
+    for (int kt = 0; kt < nk; kt++) {
+        wait_stages<LPS, P - 2>(nk - 1 - kt);  // this lane's loads of stage kt have landed
+        // ... and every lane's; stage kt-1 is free (its reads fed MFMAs already). A plain s_barrier:
+        // __syncthreads() would add a fence that waits for every load in flight, later stages included.
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + P - 1 < nk) VLM_LDS_STAGE((kt0 + kt + P - 1) * BK, smem + ((kt + P - 1) % P) * STAGE);
+        const bf16_t* st = smem + (kt % P) * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; kk++) {
+            const int c = kk * 2 + h;
+            bf16x8 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                fa[i] = *reinterpret_cast<const bf16x8*>(st + ra[i] * BK + ((c ^ (ra[i] & 7)) * 8));
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+                fb[j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ (rb[j] & 7)) * 8));
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-                    if (m >= M) continue;
-                    const float v = acc[i][j][r] + bn;
-                    if constexpr (EPI == Epi::StoreF32) {
-                        ((float*)a.out)[(size_t)m * a.ldo + n] = v;
-                    } else if constexpr (EPI == Epi::Resid) {
-                        float* x = (float*)a.out + (size_t)m * a.ldo + n;
-                        *x = *x + v;
-                    } else if constexpr (EPI == Epi::Gelu) {
-                        Elt<T>::st((T*)a.out, (size_t)m * a.ldo + n, gelu_tanh_f(v));
-                    } else {  // StoreRowMap
-                        ((float*)a.out)[(size_t)a.rowmap[m] * a.ldo + n] = v;
-                    }
-                }
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
     }
+#undef VLM_LDS_STAGE
+    gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32);
 }
 
 // Sums the split partials in split order (deterministic) and applies the epilogue.
@@ -256,6 +383,27 @@ static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int P, Epi EPI, bool SPLIT>
+static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
+    const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
+    const size_t smem = (size_t)P * (BM + BN) * 64 * sizeof(bf16_t);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, EPI, SPLIT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    gemm_lds_kernel<BM, BN, P, EPI, SPLIT><<<dim3(mt * nt, SPLIT ? splits : 1), 256, smem, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !SPLIT) return e;
+    const size_t total = (size_t)a.M * (EPI == Epi::SwiGLU ? a.N / 2 : a.N);
+    int blocks = (int)((total + 255) / 256);
+    blocks = blocks > 4096 ? 4096 : blocks;
+    splitk_reduce_kernel<bf16_t, EPI><<<blocks, 256, 0, st>>>(a, splits);
+    return hipGetLastError();
+}
+
 // Blocks a prefill GEMM aims for before it splits K (several blocks per CU
 // keep more loads in flight; the GEMMs here are latency-bound, not MFMA-bound).
 // VLM_GEMM_TARGET_BLOCKS overrides it for tuning.
@@ -282,6 +430,25 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
         while (sp > 1 && (nk / sp < 4 || (size_t)sp * a.M * a.N > a.part_cap)) sp--;
         return sp < 1 ? 1 : sp;
     };
+    if constexpr (sizeof(T) == 2) {
+        if (a.K % 64 == 0) {  // direct-to-LDS pipeline: 128 or 144 KiB of LDS stages, one block per CU
+            if (tiles(128, 128) >= 256) {
+                const int sp = splits_for(tiles(128, 128));
+                return sp > 1 ? run_gemm_lds<128, 128, 4, EPI, true>(a, sp, st)
+                              : run_gemm_lds<128, 128, 4, EPI, false>(a, 1, st);
+            }
+            if (tiles(64, 128) >= 256 || EPI == Epi::SwiGLU) {
+                const int sp = splits_for(tiles(64, 128));
+                return sp > 1 ? run_gemm_lds<64, 128, 6, EPI, true>(a, sp, st)
+                              : run_gemm_lds<64, 128, 6, EPI, false>(a, 1, st);
+            }
+            if constexpr (EPI != Epi::SwiGLU) {
+                const int sp = splits_for(tiles(64, 64));
+                return sp > 1 ? run_gemm_lds<64, 64, 8, EPI, true>(a, sp, st)
+                              : run_gemm_lds<64, 64, 8, EPI, false>(a, 1, st);
+            }
+        }
+    }
     if (tiles(128, 128) >= 256) {
         const int sp = splits_for(tiles(128, 128));
         return sp > 1 ? run_gemm<T, 128, 128, EPI, true>(a, sp, st) : run_gemm<T, 128, 128, EPI, false>(a, 1, st);
@@ -305,6 +472,7 @@ static hipError_t dispatch_epi(Epi epi, const GemmArgs& a, hipStream_t st) {
         case Epi::SwiGLU: return pick_tile<T, Epi::SwiGLU>(a, st);
         case Epi::Gelu: return pick_tile<T, Epi::Gelu>(a, st);
         case Epi::StoreRowMap: return pick_tile<T, Epi::StoreRowMap>(a, st);
+        default: break;
     }
     return hipErrorInvalidValue;
 }
