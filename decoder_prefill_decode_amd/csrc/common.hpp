@@ -17,13 +17,9 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+// float -> bfloat16, round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32, one instruction with no branch.
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // Round a float to the nearest bf16 value, kept as float.
 __device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }

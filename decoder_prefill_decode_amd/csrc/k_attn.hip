@@ -80,24 +80,58 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     const int seg_q = (MASK == VLM_MASK_SEGMENT_ID && qrow < S) ? a.seg[qrow] : 0;
     const int nkt = (kend + BKEY - 1) / BKEY;
 
+    // K/V tile kt+1 is requested into registers (unconditional, key index clamped; keys past nkeys
+    // are zeroed when stored) while tile kt runs on the matrix cores. K chunks are spread along rows
+    // (coalesced 16-byte row pieces into the row-major K tile); V is fetched as key pairs so that
+    // each transposed LDS store writes two keys of one dimension as a dword, 32 lanes to 32
+    // consecutive dwords.
+    constexpr int TCH = (BKEY * CH + 255) / 256;        // 16-byte chunks of the K tile per thread
+    constexpr int NVP = (BKEY / 2) * CH, VP = (NVP + 255) / 256;  // (key pair, chunk) items of the V tile
+    auto request = [&](int kt, u32x4 (&kreg)[TCH], u32x4 (&vreg)[VP][2]) {
+#pragma unroll
+        for (int i = 0; i < TCH; i++) {
+            const int c = min(tid + 256 * i, BKEY * CH - 1), r = c / CH, d0 = (c % CH) * 8;
+            const int key = min(kt * BKEY + r, a.nkeys - 1);
+            kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + d0);
+        }
+#pragma unroll
+        for (int i = 0; i < VP; i++) {
+            const int pi = min(tid + 256 * i, NVP - 1), kp = pi % (BKEY / 2), d0 = (pi / (BKEY / 2)) * 8;
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const int key = min(kt * BKEY + 2 * kp + u, a.nkeys - 1);
+                vreg[i][u] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + d0);
+            }
+        }
+    };
+    u32x4 kreg[TCH], vreg[VP][2];
+    if (nkt > 0) request(0, kreg, vreg);
     for (int kt = 0; kt < nkt; kt++) {
         const int key0 = kt * BKEY;
-        for (int c = tid; c < BKEY * CH; c += 256) {
-            const int r = c / CH, d0 = (c % CH) * 8;
-            const int key = key0 + r;
-            u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-            if (key < a.nkeys) {
-                kv = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + d0);
-                vv = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + d0);
-            }
-            *reinterpret_cast<u32x4*>(Ks + r * LDK + d0) = kv;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                Vt[(d0 + 2 * i) * LDV + r] = (bf16_t)(vv[i] & 0xffffu);
-                Vt[(d0 + 2 * i + 1) * LDV + r] = (bf16_t)(vv[i] >> 16);
+        for (int i = 0; i < TCH; i++) {
+            const int c = tid + 256 * i;
+            if (c < BKEY * CH) {
+                const int r = c / CH, d0 = (c % CH) * 8;
+                *reinterpret_cast<u32x4*>(Ks + r * LDK + d0) = key0 + r < a.nkeys ? kreg[i] : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VP; i++) {
+            const int pi = tid + 256 * i, kp = pi % (BKEY / 2), d0 = (pi / (BKEY / 2)) * 8;
+            if (pi >= NVP) break;
+            const u32x4 v0 = key0 + 2 * kp < a.nkeys ? vreg[i][0] : u32x4{0, 0, 0, 0};
+            const u32x4 v1 = key0 + 2 * kp + 1 < a.nkeys ? vreg[i][1] : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                uint32_t* row0 = reinterpret_cast<uint32_t*>(Vt + (d0 + 2 * e) * LDV + 2 * kp);
+                uint32_t* row1 = reinterpret_cast<uint32_t*>(Vt + (d0 + 2 * e + 1) * LDV + 2 * kp);
+                *row0 = (v0[e] & 0xffffu) | (v1[e] << 16);
+                *row1 = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
             }
         }
         __syncthreads();
+        if (kt + 1 < nkt) request(kt + 1, kreg, vreg);  // in flight during this tile's MFMAs
         bool active = true;
         if (MASK == VLM_MASK_CAUSAL_ID) active = key0 <= a.pos0 + q0 + 31;
         if (active) {
@@ -112,6 +146,10 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[kk], sacc[kb], 0, 0, 0);
                 }
             }
+            // a tile every key of which is visible to every query row of this wavefront skips the mask
+            const bool full = (MASK == VLM_MASK_NONE_ID ||
+                               (MASK == VLM_MASK_CAUSAL_ID && key0 + BKEY - 1 <= a.pos0 + q0)) &&
+                              key0 + BKEY <= a.nkeys;
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
@@ -119,6 +157,11 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                 for (int r = 0; r < 16; r++) {
                     const int key = key0 + kb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
                     float s = sacc[kb][r] * scale;
+                    if (full) {
+                        sacc[kb][r] = s;
+                        mt = fmaxf(mt, s);
+                        continue;
+                    }
                     bool vis = key < a.nkeys;
                     if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
                     if (MASK == VLM_MASK_SEGMENT_ID) vis = vis && qrow < S && a.seg[key] == seg_q;
@@ -134,13 +177,14 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
             }
             const float mn = fmaxf(m, mt);
             const float mu = mn == -INFINITY ? 0.f : mn;
-            const float alpha = exp2f(m - mu);
+            // arguments are <= 0 (or -inf): the bare v_exp_f32 needs no range reduction
+            const float alpha = __builtin_amdgcn_exp2f(m - mu);
             float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const float p = exp2f(sacc[kb][r] - mu);
+                    const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - mu);
                     sacc[kb][r] = p;
                     rs += p;
                 }
@@ -150,10 +194,12 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
             }
             l = l * alpha + rs;
             m = mn;
+            if (!__all(alpha == 1.f)) {  // the running max moved for some row of this wavefront
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++)
+                for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) oacc[nb][r] *= alpha;
+                    for (int r = 0; r < 16; r++) oacc[nb][r] *= alpha;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
