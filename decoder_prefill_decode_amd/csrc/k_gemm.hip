@@ -304,22 +304,27 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (kt + P - 1 < nk) VLM_LDS_STAGE((kt0 + kt + P - 1) * BK, smem + ((kt + P - 1) % P) * STAGE);
         const bf16_t* st = smem + (kt % P) * STAGE;
+        // every operand fragment of the stage is requested before the first MFMA, so the LDS
+        // latency is paid once per stage rather than once per 16-wide K step
+        bf16x8 fa[BK / 16][TM], fb[BK / 16][TN];
 #pragma unroll
         for (int kk = 0; kk < BK / 16; kk++) {
             const int c = kk * 2 + h;
-            bf16x8 fa[TM], fb[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                fa[i] = *reinterpret_cast<const bf16x8*>(st + ra[i] * BK + ((c ^ (ra[i] & 7)) * 8));
+                fa[kk][i] = *reinterpret_cast<const bf16x8*>(st + ra[i] * BK + ((c ^ (ra[i] & 7)) * 8));
 #pragma unroll
             for (int j = 0; j < TN; j++)
-                fb[j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ (rb[j] & 7)) * 8));
+                fb[kk][j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ (rb[j] & 7)) * 8));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; kk++)
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
     }
 #undef VLM_LDS_STAGE
     gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32);
@@ -431,21 +436,21 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
         return sp < 1 ? 1 : sp;
     };
     if constexpr (sizeof(T) == 2) {
-        if (a.K % 64 == 0) {  // direct-to-LDS pipeline: 128 or 144 KiB of LDS stages, one block per CU
+        if (a.K % 64 == 0) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
             if (tiles(128, 128) >= 256) {
                 const int sp = splits_for(tiles(128, 128));
-                return sp > 1 ? run_gemm_lds<128, 128, 4, EPI, true>(a, sp, st)
-                              : run_gemm_lds<128, 128, 4, EPI, false>(a, 1, st);
+                return sp > 1 ? run_gemm_lds<128, 128, 2, EPI, true>(a, sp, st)
+                              : run_gemm_lds<128, 128, 2, EPI, false>(a, 1, st);
             }
             if (tiles(64, 128) >= 256 || EPI == Epi::SwiGLU) {
                 const int sp = splits_for(tiles(64, 128));
-                return sp > 1 ? run_gemm_lds<64, 128, 6, EPI, true>(a, sp, st)
-                              : run_gemm_lds<64, 128, 6, EPI, false>(a, 1, st);
+                return sp > 1 ? run_gemm_lds<64, 128, 3, EPI, true>(a, sp, st)
+                              : run_gemm_lds<64, 128, 3, EPI, false>(a, 1, st);
             }
             if constexpr (EPI != Epi::SwiGLU) {
                 const int sp = splits_for(tiles(64, 64));
-                return sp > 1 ? run_gemm_lds<64, 64, 8, EPI, true>(a, sp, st)
-                              : run_gemm_lds<64, 64, 8, EPI, false>(a, 1, st);
+                return sp > 1 ? run_gemm_lds<64, 64, 4, EPI, true>(a, sp, st)
+                              : run_gemm_lds<64, 64, 4, EPI, false>(a, 1, st);
             }
         }
     }
