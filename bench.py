@@ -32,7 +32,7 @@ PEAK_F32_TFLOPS = 157.3
 METRIC = "prefill tok/s + decode tok/s per decoder stack; % of HBM / MFMA roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {k: os.path.join(ROOT, "decoder_prefill_decode_amd", "csrc", f)
-                  for k, f in (("gemv", "k_gemv.hip"), ("attn", "k_attn.hip"))}
+                  for k, f in (("gemv", "k_gemv.hip"), ("attn", "k_attn.hip"), ("common", "common.hpp"))}
 
 
 def parse():
@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c3_qwen3_28l")
+    ap.add_argument("--config", default="c4_llama_4b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-decode-steps", type=int, default=128)
     ap.add_argument("--kernel-only", default=None,
@@ -82,14 +82,20 @@ def kernel_bytes(cfg, name, t=None):
 
 
 def source_sha(name):
-    return hashlib.sha256(open(KERNEL_SOURCES["attn" if name == "attn" else "gemv"], "rb").read()).hexdigest()
+    """Hash of the sources the kernel is built from (its own file and the shared device helpers)."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SOURCES["attn" if name == "attn" else "gemv"], KERNEL_SOURCES["common"]):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def load_traffic(name):
-    """Counter-measured HBM bytes per launch, if taken on the current kernel source."""
+def load_traffic(cfg_name, name):
+    """Counter-measured HBM bytes per launch of kernel `name` on workload `cfg_name`, if taken on the
+    current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            ent = json.load(f).get(name)
+            ent = json.load(f).get(f"{cfg_name}:{name}")
         if ent and ent.get("source_sha256") == source_sha(name):
             return ent.get("bytes_per_launch")
     except (OSError, ValueError):
@@ -97,7 +103,7 @@ def load_traffic(name):
     return None
 
 
-def traffic_from_csv(kernel, fetch_csv, write_csv, copy_mib):
+def traffic_from_csv(cfg_name, kernel, fetch_csv, write_csv, copy_mib):
     """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
     what the same counter reads for the plain copy of copy_mib MiB in the same run."""
     import csv
@@ -126,12 +132,13 @@ def traffic_from_csv(kernel, fetch_csv, write_csv, copy_mib):
             allt = json.load(f)
     except (OSError, ValueError):
         allt = {}
-    allt[kernel] = {"bytes_per_launch": round(b), "source_sha256": source_sha(kernel), "counters": res,
-                    "copy_reference_mib": copy_mib}
+    key = f"{cfg_name}:{kernel}"
+    allt[key] = {"bytes_per_launch": round(b), "source_sha256": source_sha(kernel), "counters": res,
+                 "copy_reference_mib": copy_mib}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(allt, f, indent=1)
-    print(json.dumps(allt[kernel]))
+    print(json.dumps(allt[key]))
 
 
 def time_kernel(run, name, launches):
@@ -185,7 +192,7 @@ def cpu_baseline(cfg, glob, layers, n_dec):
 def main():
     args = parse()
     if args.traffic:
-        traffic_from_csv(args.traffic[0], args.traffic[1], args.traffic[2], args.copy_mib)
+        traffic_from_csv(args.config, args.traffic[0], args.traffic[1], args.traffic[2], args.copy_mib)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
@@ -272,12 +279,17 @@ def main():
     b = kernel_bytes(cfg, dom, t_mid)
     achieved = b / (per[dom]["us"] * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom),
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(cfg.name, dom),
             "kernel": dom, "bytes_per_launch": b, "avg_launch_us": round(per[dom]["us"], 3)}
     flops = 2.0 * (cfg.n_layers * (cfg.qkv_rows * cfg.hidden + cfg.hidden * cfg.n_q_heads * cfg.head_dim
                                    + 3 * cfg.ffn * cfg.hidden) * S
                    + cfg.n_layers * 2 * cfg.n_q_heads * cfg.head_dim * S * (S + 1) / 2 + cfg.vocab * cfg.hidden)
     peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    # whole decode step: every weight once, the lm_head table, the valid K/V slots at the mid-run length
+    E = 2 if cfg.dtype == "bf16" else 4
+    tok_bytes = E * (cfg.n_layers * (cfg.qkv_rows * cfg.hidden + cfg.hidden * cfg.n_q_heads * cfg.head_dim
+                                     + 3 * cfg.ffn * cfg.hidden + 2 * cfg.n_kv_heads * cfg.head_dim * t_mid)
+                     + cfg.vocab * cfg.hidden)
     out = {
         "metric": METRIC, "value": round((S + N) / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
@@ -290,6 +302,8 @@ def main():
         "prefill_tok_s": round(S / (pre_ms * 1e-3), 1), "decode_tok_s": round(N / (dec_ms * 1e-3), 1),
         "prefill_ms": round(pre_ms, 3), "decode_ms": round(dec_ms, 3),
         "prefill_mfma_frac": round(flops / (pre_ms * 1e-3) / (peak_mm * 1e12), 4),
+        "decode_bytes_per_token": tok_bytes,
+        "decode_hbm_frac": round(tok_bytes / (dec_ms * 1e-3 / max(N, 1)) / (PEAK_HBM_GBS * 1e9), 4),
         "decode_kernels_us": {k: round(v["us"], 2) for k, v in per.items()},
         "decode_kernels_gbs": {k: round(v["gbs"], 1) for k, v in per.items()},
         "roofline": roof,

@@ -15,6 +15,8 @@
 // weight panel) land on the same XCD and its L2.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -53,19 +55,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x16 (&acc)[T
                 }
         }
     } else if constexpr (EPI == Epi::SwiGLU) {
-        static_assert(TN == 2, "SwiGLU needs a 64-column wave tile (gate block, up block)");
-        const int ncol = (n0 + wn * WN) / 2 + l32;
+        static_assert(TN % 2 == 0, "SwiGLU needs whole 64-column (gate block, up block) pairs per wave tile");
         T* out = (T*)a.out;
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+        for (int jp = 0; jp < TN / 2; jp++) {
+            const int nb = n0 + wn * WN + jp * 64, ncol = nb / 2 + l32;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
-                if (m < M && n0 + wn * WN < N) {  // N = 2F is a multiple of 64: whole groups
-                    const float gt = acc[i][0][r], up = acc[i][1][r];
-                    Elt<T>::st(out, (size_t)m * a.ldo + ncol, silu_f(gt) * up);
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int m = m0 + wm * WM + i * 32 + (r / 4) * 8 + h * 4 + (r % 4);
+                    if (m < M && nb < N) {  // N = 2F is a multiple of 64: whole groups
+                        const float gt = acc[i][2 * jp][r], up = acc[i][2 * jp + 1][r];
+                        Elt<T>::st(out, (size_t)m * a.ldo + ncol, silu_f(gt) * up);
+                    }
                 }
-            }
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < TN; j++) {
@@ -237,10 +242,12 @@ __device__ __forceinline__ void wait_stages(int k) {
     }
 }
 
-template <int BM, int BN, int P, Epi EPI, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_lds_kernel(GemmArgs a) {
-    constexpr int BK = 64, WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
-    constexpr int AI = BM / 32, BI = BN / 32;  // load instructions per wave per stage (8 rows each, 4 waves)
+// WGM x WGN wavefronts per block, each owning a (BM/WGM) x (BN/WGN) sub-tile.
+template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
+    constexpr int NW = WGM * WGN, BK = 64, WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+    constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);  // load instructions per wave per stage (8 rows each)
+    static_assert(AI * 8 * NW == BM && BI * 8 * NW == BN && TM >= 1 && TN >= 1, "tile / wavefront grid");
     constexpr int LPS = AI + BI, STAGE = (BM + BN) * BK;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(GemmArgs a) {
     const int tile = xcd_remap(blockIdx.x, mt * nt);
     const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    const int wm = w / 2, wn = w % 2, h = lane / 32, l32 = lane % 32;
+    const int wm = w / WGN, wn = w % WGN, h = lane / 32, l32 = lane % 32;
     const bf16_t* A = (const bf16_t*)a.A;
     const bf16_t* B = (const bf16_t*)a.B;
 
@@ -388,18 +395,18 @@ static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int P, Epi EPI, bool SPLIT>
+template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT>
 static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
     const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
     const size_t smem = (size_t)P * (BM + BN) * 64 * sizeof(bf16_t);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, EPI, SPLIT>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_lds_kernel<BM, BN, P, EPI, SPLIT><<<dim3(mt * nt, SPLIT ? splits : 1), 256, smem, st>>>(a);
+    gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
     const size_t total = (size_t)a.M * (EPI == Epi::SwiGLU ? a.N / 2 : a.N);
@@ -421,7 +428,42 @@ static int target_blocks() {
     return v;
 }
 
-// Tile choice: the largest tile that still gives >= 256 blocks (one per CU),
+// Tile and K-split choice of the direct-to-LDS kernel from a per-CU feed model:
+// these GEMMs are bound by how fast one CU pulls its operand stages out of L2
+// (measured: ~48 GB/s per block with two 4-wavefront blocks per CU, ~40 GB/s
+// for one 8-wavefront block with its two-stage ring), so the estimated time is
+// rounds x (blocks per CU) x (stages per block) x (stage bytes) / feed, plus,
+// for a K split, ~4 us and the fp32 partials written and re-read by the reduce.
+struct LdsPlan { int bm, bn, sp; };
+static LdsPlan plan_lds(const GemmArgs& a, bool swiglu) {
+    // {BM, BN, blocks per CU that fit the LDS ring, per-block feed in bytes/us}
+    static const int cand[5][4] = {{256, 256, 1, 40000}, {128, 256, 1, 40000}, {128, 128, 2, 48000},
+                                   {64, 128, 2, 48000}, {64, 64, 2, 48000}};
+    static const int splits[6] = {1, 2, 3, 4, 6, 8};
+    const int nk = a.K / 64;
+    double best = 1e30;
+    LdsPlan bp{64, 128, 1};
+    for (const auto& c : cand) {
+        if (swiglu && c[1] < 128) continue;  // SwiGLU pairs a 32-column gate block with its up block
+        const long tiles = (long)((a.M + c[0] - 1) / c[0]) * ((a.N + c[1] - 1) / c[1]);
+        for (int sp : splits) {
+            if (sp > 1 && (!a.part || nk / sp < 4 || (size_t)sp * a.M * a.N > a.part_cap)) continue;
+            const long nb = tiles * sp;
+            const double rounds = (double)((nb + 256L * c[2] - 1) / (256L * c[2]));
+            const double per_cu = (double)std::min<long>(c[2], (nb + 255) / 256);  // blocks sharing a CU
+            const double stages = (double)((nk + sp - 1) / sp);
+            double t = rounds * per_cu * stages * (c[0] + c[1]) * 128.0 / c[3];  // us
+            if (sp > 1) t += 4.0 + (double)sp * a.M * a.N * 8.0 / 4.0e6;
+            if (t < best) {
+                best = t;
+                bp = {c[0], c[1], sp};
+            }
+        }
+    }
+    return bp;
+}
+
+// Tile choice of the register-staged kernel: the largest tile that still gives >= 256 blocks (one per CU),
 // else the smallest; then a K split (2-4 ways, >= 4 stages each) up to the
 // target block count when the caller provided split-K scratch.
 template <class T, Epi EPI>
@@ -437,21 +479,16 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
     };
     if constexpr (sizeof(T) == 2) {
         if (a.K % 64 == 0) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
-            if (tiles(128, 128) >= 256) {
-                const int sp = splits_for(tiles(128, 128));
-                return sp > 1 ? run_gemm_lds<128, 128, 2, EPI, true>(a, sp, st)
-                              : run_gemm_lds<128, 128, 2, EPI, false>(a, 1, st);
-            }
-            if (tiles(64, 128) >= 256 || EPI == Epi::SwiGLU) {
-                const int sp = splits_for(tiles(64, 128));
-                return sp > 1 ? run_gemm_lds<64, 128, 3, EPI, true>(a, sp, st)
-                              : run_gemm_lds<64, 128, 3, EPI, false>(a, 1, st);
-            }
-            if constexpr (EPI != Epi::SwiGLU) {
-                const int sp = splits_for(tiles(64, 64));
-                return sp > 1 ? run_gemm_lds<64, 64, 4, EPI, true>(a, sp, st)
-                              : run_gemm_lds<64, 64, 4, EPI, false>(a, 1, st);
-            }
+            const LdsPlan pl = plan_lds(a, EPI == Epi::SwiGLU);
+#define VLM_RUN_LDS(BM_, BN_, P_, GM_, GN_)                                                        \
+    return pl.sp > 1 ? run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, true>(a, pl.sp, st)             \
+                     : run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, false>(a, 1, st)
+            if (pl.bm == 256) VLM_RUN_LDS(256, 256, 2, 4, 2);
+            if (pl.bm == 128 && pl.bn == 256) VLM_RUN_LDS(128, 256, 2, 2, 4);
+            if (pl.bm == 128) VLM_RUN_LDS(128, 128, 2, 2, 2);
+            if (pl.bn == 128) VLM_RUN_LDS(64, 128, 3, 2, 2);
+            if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS(64, 64, 4, 2, 2);
+#undef VLM_RUN_LDS
         }
     }
     if (tiles(128, 128) >= 256) {
