@@ -34,25 +34,38 @@ namespace vlm {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ============================================================== prefill, bf16
+// A block covers 64 query rows of one head with 4 wavefronts: wavefronts
+// w and w+2 own the same 32 rows and take alternate 64-key tiles (a pair of
+// tiles is staged per iteration), which halves the sequential key chain of
+// the longest (last, causal) row block; their (m, l, O) merge through LDS at
+// the end.
 template <int D, int MASK>
 __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
-    constexpr int BQ = 128, BKEY = 64;
+    constexpr int BQ = 64, BKEY = 64;
     constexpr int DK = D / 16, NB = (D + 31) / 32, DP = NB * 32;
     constexpr int LDK = D + 8, LDV = BKEY + 8;
     constexpr int CH = D / 8;  // 16-byte chunks per key row
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[BKEY * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Vt[DP * LDV];
+    constexpr int KSZ = BKEY * LDK, VSZ = DP * LDV;                 // elements of one K / V^T tile
+    constexpr int MRG = NB * 16 + 2;                                // floats per lane in the final merge
+    constexpr int TILE_BYTES = 2 * (KSZ + VSZ) * 2, MRG_BYTES = 2 * 64 * MRG * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char sm[TILE_BYTES > MRG_BYTES ? TILE_BYTES : MRG_BYTES];
+    bf16_t* const Ks = reinterpret_cast<bf16_t*>(sm);   // [2][KSZ]
+    bf16_t* const Vt = Ks + 2 * KSZ;                     // [2][VSZ]
 
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, hh = lane / 32, l32 = lane % 32;
+    const int rg = w & 1, kpar = w >> 1;  // row group, key-tile parity
     const int hq = blockIdx.y, g = hq / (a.nq / a.nkv);
-    const int q0 = blockIdx.x * BQ + w * 32;
+    const int q0 = blockIdx.x * BQ + rg * 32;
     const int qrow = q0 + l32;
     const int S = a.S;
     const bf16_t* Q = (const bf16_t*)a.q + (size_t)hq * a.ldq * D;
     const bf16_t* Kg = (const bf16_t*)a.k + (size_t)g * a.ldkv * D;
     const bf16_t* Vg = (const bf16_t*)a.v + (size_t)g * a.ldkv * D;
 
-    for (int i = tid; i < (DP - D) * LDV; i += 256) Vt[D * LDV + i] = 0;
+    for (int i = tid; i < (DP - D) * LDV; i += 256) {
+        Vt[D * LDV + i] = 0;
+        Vt[VSZ + D * LDV + i] = 0;
+    }
 
     bf16x8 Qf[DK];
 #pragma unroll
@@ -104,16 +117,16 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
             }
         }
     };
-    u32x4 kreg[TCH], vreg[VP][2];
-    if (nkt > 0) request(0, kreg, vreg);
-    for (int kt = 0; kt < nkt; kt++) {
+    auto stage = [&](int kt, int buf, const u32x4 (&kreg)[TCH], const u32x4 (&vreg)[VP][2]) {
         const int key0 = kt * BKEY;
+        bf16_t* kd = Ks + buf * KSZ;
+        bf16_t* vd = Vt + buf * VSZ;
 #pragma unroll
         for (int i = 0; i < TCH; i++) {
             const int c = tid + 256 * i;
             if (c < BKEY * CH) {
                 const int r = c / CH, d0 = (c % CH) * 8;
-                *reinterpret_cast<u32x4*>(Ks + r * LDK + d0) = key0 + r < a.nkeys ? kreg[i] : u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4*>(kd + r * LDK + d0) = key0 + r < a.nkeys ? kreg[i] : u32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -124,16 +137,29 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
             const u32x4 v1 = key0 + 2 * kp + 1 < a.nkeys ? vreg[i][1] : u32x4{0, 0, 0, 0};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                uint32_t* row0 = reinterpret_cast<uint32_t*>(Vt + (d0 + 2 * e) * LDV + 2 * kp);
-                uint32_t* row1 = reinterpret_cast<uint32_t*>(Vt + (d0 + 2 * e + 1) * LDV + 2 * kp);
+                uint32_t* row0 = reinterpret_cast<uint32_t*>(vd + (d0 + 2 * e) * LDV + 2 * kp);
+                uint32_t* row1 = reinterpret_cast<uint32_t*>(vd + (d0 + 2 * e + 1) * LDV + 2 * kp);
                 *row0 = (v0[e] & 0xffffu) | (v1[e] << 16);
                 *row1 = (v0[e] >> 16) | (v1[e] & 0xffff0000u);
             }
         }
+    };
+    u32x4 kA[TCH], vA[VP][2], kB[TCH], vB[VP][2];
+    if (nkt > 0) request(0, kA, vA);
+    if (nkt > 1) request(1, kB, vB);
+    for (int kt2 = 0; kt2 < nkt; kt2 += 2) {
+        stage(kt2, 0, kA, vA);
+        if (kt2 + 1 < nkt) stage(kt2 + 1, 1, kB, vB);
         __syncthreads();
-        if (kt + 1 < nkt) request(kt + 1, kreg, vreg);  // in flight during this tile's MFMAs
-        bool active = true;
-        if (MASK == VLM_MASK_CAUSAL_ID) active = key0 <= a.pos0 + q0 + 31;
+        // the next pair is in flight during this pair's MFMAs
+        if (kt2 + 2 < nkt) request(kt2 + 2, kA, vA);
+        if (kt2 + 3 < nkt) request(kt2 + 3, kB, vB);
+        const int kt = kt2 + kpar;
+        const int key0 = kt * BKEY;
+        const bf16_t* const Kw = Ks + kpar * KSZ;
+        const bf16_t* const Vw = Vt + kpar * VSZ;
+        bool active = kt < nkt;
+        if (MASK == VLM_MASK_CAUSAL_ID) active = active && key0 <= a.pos0 + q0 + 31;
         if (active) {
             f32x16 sacc[2];
 #pragma unroll
@@ -142,7 +168,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                 for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
 #pragma unroll
                 for (int kk = 0; kk < DK; kk++) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + l32) * LDK + kk * 16 + hh * 8);
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kw + (kb * 32 + l32) * LDK + kk * 16 + hh * 8);
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, Qf[kk], sacc[kb], 0, 0, 0);
                 }
             }
@@ -217,7 +243,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                     const int kofs = kb * 32 + hs * 16 + hh * 4;
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
-                        const bf16_t* vp = Vt + (nb * 32 + l32) * LDV + kofs;
+                        const bf16_t* vp = Vw + (nb * 32 + l32) * LDV + kofs;
                         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
                         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
                         u32x4 raw = {lo.x, lo.y, hi.x, hi.y};
@@ -228,6 +254,29 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                 }
         }
         __syncthreads();
+    }
+    // merge the two key-parity halves of each row group: wavefronts 2, 3 hand (m, l, O) to 0, 1
+    float* mb = reinterpret_cast<float*>(sm) + (size_t)(rg * 64 + lane) * MRG;
+    if (kpar == 1) {
+        mb[0] = m;
+        mb[1] = l;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) mb[2 + nb * 16 + r] = oacc[nb][r];
+    }
+    __syncthreads();
+    if (kpar == 1) return;
+    {
+        const float m2 = mb[0], l2 = mb[1];
+        const float mn = fmaxf(m, m2);
+        const float fa = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float fb = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+        l = l * fa + l2 * fb;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) oacc[nb][r] = oacc[nb][r] * fa + mb[2 + nb * 16 + r] * fb;
     }
     if (qrow < S) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -384,7 +433,7 @@ static hipError_t run_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.S + 127) / 128, a.nq);
     if (dtype == 1) {
         if constexpr (D % 16 == 0) {
-            attn_prefill_bf16<D, MASK><<<grid, 256, 0, st>>>(a);
+            attn_prefill_bf16<D, MASK><<<dim3((a.S + 63) / 64, a.nq), 256, 0, st>>>(a);
         } else {
             return hipErrorInvalidValue;
         }
