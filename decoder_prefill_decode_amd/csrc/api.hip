@@ -69,7 +69,9 @@ vlm_status check_desc(const vlm_model_desc* d) {
         return fail(VLM_ERR_UNSUPPORTED, "bf16 attention needs head_dim %% 16 == 0 (got %d)", d->head_dim);
     if (d->rope_segments != 1 && d->rope_segments != 2) return fail(VLM_ERR_ARG, "rope_segments %d", d->rope_segments);
     if ((d->head_dim / d->rope_segments) % 2) return fail(VLM_ERR_SHAPE, "rope segment length must be even");
-    if (d->qk_norm != 0 && d->qk_norm != 1) return fail(VLM_ERR_UNSUPPORTED, "qk_norm %d", d->qk_norm);
+    if (d->qk_norm < 0 || d->qk_norm > 2) return fail(VLM_ERR_ARG, "qk_norm %d not in {0,1,2}", d->qk_norm);
+    if (d->rope_interleave != 0 && d->rope_interleave != 1)
+        return fail(VLM_ERR_ARG, "rope_interleave %d not in {0,1}", d->rope_interleave);
     if (d->ffn < 8 || d->ffn % 8) return fail(VLM_ERR_SHAPE, "ffn %d must be a positive multiple of 8", d->ffn);
     if (d->ffn > 16384) return fail(VLM_ERR_UNSUPPORTED, "ffn %d > 16384", d->ffn);
     if (d->block_kind == VLM_BLOCK_DECODER && d->ffn % 32)
@@ -304,6 +306,14 @@ vlm_status vlm_rope_table(const int32_t* d_pos, int32_t n_axes, int32_t n_rows, 
     return ok();
 }
 
+vlm_status vlm_rope_alpha_base(double theta, double alpha, int32_t head_dim, double* base) {
+    if (!base) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (!(theta > 0.0) || !(alpha > 0.0) || head_dim <= 2)
+        return fail(VLM_ERR_ARG, "need theta > 0, alpha > 0, head_dim > 2 (got %g, %g, %d)", theta, alpha, head_dim);
+    *base = theta * pow(alpha, (double)head_dim / (double)(head_dim - 2));
+    return ok();
+}
+
 // =============================================================================== embed / inject
 vlm_status vlm_embed(const vlm_model_desc* desc, const void* d_embed, const int32_t* d_ids, int32_t S, float* d_x,
                      hipStream_t stream) {
@@ -407,6 +417,7 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
         HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
         RopeArgs r{};
         r.qkv = qkv; r.S = S; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
+        r.interleave = desc->rope_interleave; r.norm_after = desc->qk_norm == 2;
         r.qn = desc->qk_norm ? y.q_norm : nullptr; r.kn = desc->qk_norm ? y.k_norm : nullptr; r.eps = desc->norm_eps;
         r.cos = d_cos; r.sin = d_sin; r.q = qb; r.ldq = S; r.kdst = kd; r.vdst = vd; r.ldkv = ldkv;
         r.pos0 = pos0; r.pos_dev = nullptr;
@@ -483,6 +494,7 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         DecAttnArgs at{};
         at.qkv = qkv; at.qn = desc->qk_norm ? y.q_norm : nullptr; at.kn = desc->qk_norm ? y.k_norm : nullptr;
         at.eps = desc->norm_eps; at.rope = rope; at.segments = desc->rope_segments;
+        at.interleave = desc->rope_interleave; at.norm_after = desc->qk_norm == 2;
         at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
         at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
         HIP_TRY(launch_attn_decode_fused(dt, at, st));
@@ -748,6 +760,7 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
                 at.qkv = (const float*)P(d_ws, w.qkvrow); at.qn = desc->qk_norm ? y.q_norm : nullptr;
                 at.kn = desc->qk_norm ? y.k_norm : nullptr; at.eps = desc->norm_eps; at.rope = rope;
                 at.segments = desc->rope_segments; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = kv->capacity;
+                at.interleave = desc->rope_interleave; at.norm_after = desc->qk_norm == 2;
                 at.nq = nq; at.nkv = desc->n_kv_heads; at.d = hd; at.len = kv->dlen();
                 at.nsplit = attn_decode_splits(kv->capacity); at.partial = (float*)P(d_ws, w.part);
                 HIP_TRY(launch_attn_decode_fused(dt, at, stream));

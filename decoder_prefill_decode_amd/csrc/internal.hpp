@@ -61,10 +61,12 @@ hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H,
 
 // qkv fp32 [S][(nq+2nkv)*d] -> q' [nq][ldq][d] (model type), K/V rows written to
 // kdst/vdst [nkv][ldkv][d] at slot base+s, base = pos_dev ? *pos_dev : pos0.
-// cos/sin rows base+s. Optional per-head RMSNorm (qn/kn gains) before RoPE.
+// cos/sin rows base+s. Optional per-head RMSNorm (qn/kn gains) before RoPE
+// (norm_after == 0) or after it (norm_after == 1). interleave: each segment's
+// adjacent pairs (2j, 2j+1) rotate together and land at j and j + segment/2.
 struct RopeArgs {
     const float* qkv;
-    int S, nq, nkv, d, segments;
+    int S, nq, nkv, d, segments, interleave, norm_after;
     const void* qn; const void* kn; float eps;
     const float* cos; const float* sin;
     void* q; int ldq;
@@ -97,6 +99,7 @@ struct DecAttnArgs {
     const float* qkv;  // [nq + 2*nkv][d] fp32 projections of the token
     const void* qn; const void* kn; float eps;
     const float* rope; int segments;  // cos[d] then sin[d] of position len (staged by the embed kernel)
+    int interleave, norm_after;       // as in RopeArgs
     void* kc; void* vc;  // layer K and V, [nkv][W][d]
     int W, nq, nkv, d;
     const int32_t* len;

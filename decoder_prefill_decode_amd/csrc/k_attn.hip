@@ -536,6 +536,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
     const bool on = lane < half;
     const int lp = on ? lane : 0;
     const int i0 = (lp / sh) * sd + lp % sh, i1 = i0 + sh;
+    // inputs of a rotated head: the adjacent pair for interleaved RoPE (V keeps i0, i1)
+    const int r0 = a.interleave ? (lp / sh) * sd + 2 * (lp % sh) : i0, r1 = a.interleave ? r0 + 1 : i1;
+    // gain index: input order if the norm runs before the rotation, output order after it
+    const int n0 = a.norm_after ? i0 : r0, n1 = a.norm_after ? i1 : r1;
     float x0[NI], x1[NI], g0[NI], g1[NI];
 #pragma unroll
     for (int ii = 0; ii < NI; ii++) {
@@ -545,10 +549,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
         const float* src = a.qkv + (size_t)row * D;
         const T* gn = (const T*)(isq ? a.qn : a.kn);
         const T* gp = (it <= G && gn) ? gn : (const T*)a.kc;  // any valid address when unused
-        x0[ii] = src[i0];
-        x1[ii] = src[i1];
-        g0[ii] = Elt<T>::ld(gp, i0);
-        g1[ii] = Elt<T>::ld(gp, i1);
+        x0[ii] = src[it <= G ? r0 : i0];
+        x1[ii] = src[it <= G ? r1 : i1];
+        g0[ii] = Elt<T>::ld(gp, n0);
+        g1[ii] = Elt<T>::ld(gp, n1);
     }
     const float c0 = a.rope[i0], c1 = a.rope[i1], s0 = a.rope[D + i0], s1 = a.rope[D + i1];
     __builtin_amdgcn_sched_barrier(0);
@@ -565,7 +569,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
             const bool isq = it < G, isk = it == G;
             const bool rot = isq || isk, norm = rot && (isq ? a.qn : a.kn) != nullptr;
             float y0 = on ? x0[ii] : 0.f, y1 = on ? x1[ii] : 0.f;
-            if (norm) {
+            if (norm && !a.norm_after) {
                 const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
                 y0 = y0 * r * g0[ii];
                 y1 = y1 * r * g1[ii];
@@ -575,6 +579,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
                 const float z1 = y1 * c1 + y0 * s1;
                 y0 = z0;
                 y1 = z1;
+            }
+            if (norm && a.norm_after) {
+                const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
+                y0 = y0 * r * g0[ii];
+                y1 = y1 * r * g1[ii];
             }
             if (!on) continue;
             if (isq) {

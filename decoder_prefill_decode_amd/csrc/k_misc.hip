@@ -118,8 +118,13 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict_
 
 // ---------------------------------------------------------------- QK-Norm + RoPE + cache write
 // One wavefront per (row, head); lane p < d/2 owns rotation pair p, i.e. the
-// elements i0 = g*sd + j and i1 = i0 + sd/2 of segment g (sd = d/segments).
-// rotate_half(a, b) = (-b, a): y[i0] = a cos - b sin, y[i1] = b cos + a sin.
+// output elements i0 = g*sd + j and i1 = i0 + sd/2 of segment g (sd =
+// d/segments). rotate_half(a, b) = (-b, a): y[i0] = a cos - b sin,
+// y[i1] = b cos + a sin, where (a, b) are the inputs at (i0, i1), or at
+// (g*sd + 2j, g*sd + 2j + 1) for interleaved RoPE (the adjacent pair,
+// de-interleaved into the rotate-half order; V is copied unpermuted). The
+// per-head RMSNorm gain is indexed by where the element sits when the norm
+// runs: input order before the rotation, output order after it.
 template <class T>
 __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
     const int wave = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -135,30 +140,36 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
     const int sd = d / a.segments, sh = sd / 2;
     const int g = on ? lane / sh : 0, j = on ? lane % sh : 0;
     const int i0 = g * sd + j, i1 = i0 + sh;
-    float x0 = on ? src[i0] : 0.f, x1 = on ? src[i1] : 0.f;
     if (h >= a.nq + a.nkv) {  // V head: plain copy (rounded to the cache type)
         if (on) {
             T* dst = (T*)a.vdst + ((size_t)(h - a.nq - a.nkv) * a.ldkv + pos) * d;
-            Elt<T>::st(dst, i0, x0);
-            Elt<T>::st(dst, i1, x1);
+            Elt<T>::st(dst, i0, src[i0]);
+            Elt<T>::st(dst, i1, src[i1]);
         }
         return;
     }
+    const int r0 = a.interleave ? g * sd + 2 * j : i0, r1 = a.interleave ? r0 + 1 : i1;
+    float x0 = on ? src[r0] : 0.f, x1 = on ? src[r1] : 0.f;
     const bool isq = h < a.nq;
     const T* gn = (const T*)(isq ? a.qn : a.kn);
-    if (gn) {
-        const float ms = wave_sum(x0 * x0 + x1 * x1) / (float)d;
-        const float r = rsqrtf(ms + a.eps);
+    if (gn && !a.norm_after) {
+        const float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)d + a.eps);
         if (on) {
-            x0 = x0 * r * Elt<T>::ld(gn, i0);
-            x1 = x1 * r * Elt<T>::ld(gn, i1);
+            x0 = x0 * r * Elt<T>::ld(gn, r0);
+            x1 = x1 * r * Elt<T>::ld(gn, r1);
+        }
+    }
+    const size_t ro = (size_t)pos * d;
+    float y0 = on ? x0 * a.cos[ro + i0] - x1 * a.sin[ro + i0] : 0.f;
+    float y1 = on ? x1 * a.cos[ro + i1] + x0 * a.sin[ro + i1] : 0.f;
+    if (gn && a.norm_after) {  // the rotation keeps the sum of squares; the norm sees the rotated values
+        const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)d + a.eps);
+        if (on) {
+            y0 = y0 * r * Elt<T>::ld(gn, i0);
+            y1 = y1 * r * Elt<T>::ld(gn, i1);
         }
     }
     if (!on) return;
-    const float* cr = a.cos + (size_t)pos * d;
-    const float* sr = a.sin + (size_t)pos * d;
-    const float y0 = x0 * cr[i0] - x1 * sr[i0];
-    const float y1 = x1 * cr[i1] + x0 * sr[i1];
     T* dst = isq ? (T*)a.q + ((size_t)h * a.ldq + s) * d : (T*)a.kdst + ((size_t)(h - a.nq) * a.ldkv + pos) * d;
     Elt<T>::st(dst, i0, y0);
     Elt<T>::st(dst, i1, y1);

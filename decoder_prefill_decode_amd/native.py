@@ -31,7 +31,7 @@ class ModelDesc(C.Structure):
     _fields_ = [("block_kind", C.c_int32), ("n_layers", C.c_int32), ("hidden", C.c_int32),
                 ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("vocab", C.c_int32), ("dtype", C.c_int32), ("qk_norm", C.c_int32),
-                ("rope_segments", C.c_int32), ("norm_eps", C.c_float)]
+                ("rope_segments", C.c_int32), ("norm_eps", C.c_float), ("rope_interleave", C.c_int32)]
 
 
 class Layer(C.Structure):
@@ -62,6 +62,7 @@ _SIG = {
     "vlm_pack_qkv": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "vlm_pack_gate_up": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "vlm_rope_table": (_I, [_P, _I, _I, C.POINTER(_I), _I, _I, C.c_double, _P, _P, _P]),
+    "vlm_rope_alpha_base": (_I, [C.c_double, C.c_double, _I, C.POINTER(C.c_double)]),
     "vlm_embed": (_I, [C.POINTER(ModelDesc), _P, _P, _I, _P, _P]),
     "vlm_inject_image_embeds": (_I, [C.POINTER(ModelDesc), _P, _I, C.POINTER(_I), _P, _I, _P, _I, _I, _P]),
     "vlm_prefill": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _I, _I, _P, _P, _I, C.POINTER(Mask), _I, _P,

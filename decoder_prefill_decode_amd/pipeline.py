@@ -23,8 +23,8 @@ class DecoderRun:
     def __init__(self, cfg, layer_weights, glob):
         self.cfg = cfg
         m = Model(n_layers=cfg.n_layers, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
-                  head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, dtype=cfg.dtype, qk_norm=cfg.qk_norm,
-                  eps=cfg.eps)
+                  head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, dtype=cfg.dtype, qk_norm=int(cfg.qk_norm),
+                  eps=cfg.eps, rope_interleave=getattr(cfg, "rope_interleave", False))
         for l in range(cfg.n_layers):
             m.set_decoder_layer(l, layer_weights(l))
         if cfg.vocab > 0:

@@ -34,10 +34,11 @@ class Model:
     """Model description + per-layer weights resident in HBM."""
 
     def __init__(self, *, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab=0, dtype="f32",
-                 qk_norm=False, rope_segments=1, eps=1e-6, block_kind=N.VLM_BLOCK_DECODER):
+                 qk_norm=0, rope_segments=1, eps=1e-6, block_kind=N.VLM_BLOCK_DECODER, rope_interleave=False):
+        """qk_norm: 0 none, 1 (or True) before RoPE, 2 after RoPE."""
         self.dtype = DTYPES[dtype] if isinstance(dtype, str) else dtype
         self.desc = N.ModelDesc(block_kind, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab,
-                                self.dtype, int(bool(qk_norm)), rope_segments, eps)
+                                self.dtype, int(qk_norm), rope_segments, eps, int(bool(rope_interleave)))
         self.layers = (N.Layer * n_layers)()
         self._keep = [dict() for _ in range(n_layers)]
         self.embed = None
@@ -185,6 +186,13 @@ def rope_table(positions: np.ndarray, axis_of_pair, segments: int, head_dim: int
            head_dim, float(theta), ptr(cos), ptr(sin), stream())
     torch.cuda.current_stream().synchronize()
     return cos, sin
+
+
+def rope_alpha_base(theta: float, alpha: float, head_dim: int) -> float:
+    """vlm_rope_alpha_base: the effective base of the alpha-scaled multi-axis RoPE."""
+    out = C.c_double()
+    N.call("vlm_rope_alpha_base", C.c_double(theta), C.c_double(alpha), head_dim, C.byref(out))
+    return out.value
 
 
 def text_rope(n_rows: int, head_dim: int, theta: float):

@@ -90,9 +90,16 @@ typedef struct {
     int32_t ffn;           /* F */
     int32_t vocab;         /* V rows of the embedding / lm_head table; 0 = none */
     int32_t dtype;         /* vlm_dtype of weights, gains, table, KV cache and GEMM operands */
-    int32_t qk_norm;       /* 1: per-head RMSNorm of q and k before RoPE (Qwen3 order, [Penguin] §5.4) */
+    int32_t qk_norm;       /* per-head RMSNorm of q and k with gains q_norm / k_norm: 0 none;
+                              1 before RoPE (Qwen3 order, [Penguin] §5.4); 2 after RoPE, so the
+                              cache holds the normalised k (HunyuanOCR order, [HyOCR10] 五.2) */
     int32_t rope_segments; /* 1: rotate-half over the whole head; 2: each half rotated on its own (2D vision RoPE, [Penguin] §2.3) */
     float norm_eps;        /* RMSNorm / LayerNorm epsilon (1e-6) */
+    int32_t rope_interleave; /* 0: rotate-half pairs (j, j + seg/2) of each RoPE segment; 1: adjacent
+                              pairs (2j, 2j+1) rotate (at the frequency of pair j) and are stored at
+                              j and j + seg/2, i.e. the head is de-interleaved before rotate-half
+                              ([Youtu] 实现难点 §2); q and the cached k keep that order, v does not
+                              move. The cos/sin tables are the same for both. */
 } vlm_model_desc;
 
 /* Per-layer weights (device pointers, element type desc->dtype).
@@ -175,6 +182,12 @@ vlm_status vlm_pack_gate_up(const void* d_wg, const void* d_wu, int32_t ffn, int
 vlm_status vlm_rope_table(const int32_t* d_pos, int32_t n_axes, int32_t n_rows, const int32_t* h_axis_of_pair,
                           int32_t rope_segments, int32_t head_dim, double theta, float* d_cos, float* d_sin,
                           hipStream_t stream);
+
+/* Effective base of the alpha-scaled multi-axis RoPE ([HyOCR10] 二 and 五.1):
+ * *base = theta * alpha^(head_dim / (head_dim - 2)), the value to pass as
+ * vlm_rope_table's theta. Host arithmetic in float64, no device work.
+ * VLM_ERR_ARG unless theta > 0, alpha > 0, head_dim > 2 and base != NULL. */
+vlm_status vlm_rope_alpha_base(double theta, double alpha, int32_t head_dim, double* base);
 
 /* ------------------------------------------------------------------------- */
 /* Embedding lookup ([Youtu] 实现流程 §5 and §6: tied [V][H] table, looked up

@@ -23,7 +23,11 @@ What the pages fix, in the order this file follows it:
     repeat_interleave, i.e. query head h reads KV head h // (nq / nkv)
     ([Penguin] §3).
   * RoPE is q*cos + rotate_half(q)*sin with cos/sin fed from outside
-    ([Youtu] 实现难点 §2, 实现流程 §6).
+    ([Youtu] 实现难点 §2, 实现流程 §6); the interleaved variant de-interleaves
+    the head first ([Youtu] 实现难点 §2). HunyuanOCR applies the per-head
+    q/k RMSNorm after RoPE instead of before, and the cache stores the
+    normalised k ([HyOCR10] 二, 五.2). Its multi-axis RoPE base is
+    theta * alpha^(d/(d-2)) ([HyOCR10] 五.1).
   * Softmax is written out as max, subtract, exp, sum, divide ([Youtu] 实现难点 §3).
   * The KV cache is a fixed window per layer; a finite additive mask holds 0
     for valid slots (position <= t) and -1e9 elsewhere; the runtime writes the
@@ -45,6 +49,8 @@ import time
 import numpy as np
 
 MASK_NEG = -1.0e9          # finite "minus infinity" of the fixed-window mask
+QK_NORM_BEFORE_ROPE = 1    # Qwen3 order ([Penguin] §5.4)
+QK_NORM_AFTER_ROPE = 2     # HunyuanOCR order: the cache holds the normalised k ([HyOCR10] 五.2)
 F64 = "f64"
 BF16 = "bf16"
 
@@ -141,12 +147,38 @@ def rope_tables(positions, axis_of_pair, n_seg, head_dim, theta):
     return cos, sin
 
 
-def rope_apply(u, cos, sin, n_seg):
-    """u*cos + rotate_half(u)*sin per segment; rotate_half(a, b) = (-b, a).
+def deinterleave(u, n_seg):
+    """Per segment, the even-indexed elements, then the odd-indexed ones.
 
-    u: [T, heads, d]; cos/sin: [T, d].
+    The interleaved RoPE of [Youtu] 实现难点 §2 views each head as d/2 adjacent
+    pairs and transposes that view before rotate-half: adjacent elements
+    (2i, 2i+1) become elements (i, i + d/2), the pair that rotate-half turns
+    together. Output stays in this de-interleaved order (it is what the cache
+    holds); q and k share it, so q.k is unchanged by the reordering itself.
     """
     u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    seg = d // n_seg
+    out = np.empty_like(u)
+    for s in range(n_seg):
+        part = u[..., s * seg:(s + 1) * seg]
+        out[..., s * seg:(s + 1) * seg] = np.concatenate([part[..., 0::2], part[..., 1::2]], axis=-1)
+    return out
+
+
+def alpha_scaled_base(theta, alpha, head_dim):
+    """Effective RoPE base theta * alpha^(d / (d - 2)) ([HyOCR10] 五.1)."""
+    d = float(head_dim)
+    return float(theta) * float(alpha) ** (d / (d - 2.0))
+
+
+def rope_apply(u, cos, sin, n_seg, interleave=False):
+    """u*cos + rotate_half(u)*sin per segment; rotate_half(a, b) = (-b, a).
+
+    u: [T, heads, d]; cos/sin: [T, d]. interleave: de-interleave u first
+    (deinterleave above), the interleaved form of [Youtu] 实现难点 §2.
+    """
+    u = deinterleave(u, n_seg) if interleave else np.asarray(u, dtype=np.float64)
     d = u.shape[-1]
     seg = d // n_seg
     half = seg // 2
@@ -224,12 +256,17 @@ def decoder_layer(x, w, cfg, k_cache, v_cache, pos0, cos, sin, prec):
     q = _lin(h, w["wq"], prec).reshape(S, nq, d)
     k = _lin(h, w["wk"], prec).reshape(S, nkv, d)
     v = _lin(h, w["wv"], prec).reshape(S, nkv, d)
-    if cfg.qk_norm:
+    qkn = int(cfg.qk_norm)
+    ilv = bool(getattr(cfg, "rope_interleave", False))
+    if qkn == QK_NORM_BEFORE_ROPE:
         q = rms_norm(q, w["q_norm"], cfg.eps)
         k = rms_norm(k, w["k_norm"], cfg.eps)
     c, s_ = cos[pos0:pos0 + S], sin[pos0:pos0 + S]
-    q = rope_apply(q, c, s_, 1)
-    k = rope_apply(k, c, s_, 1)
+    q = rope_apply(q, c, s_, 1, ilv)
+    k = rope_apply(k, c, s_, 1, ilv)
+    if qkn == QK_NORM_AFTER_ROPE:
+        q = rms_norm(q, w["q_norm"], cfg.eps)
+        k = rms_norm(k, w["k_norm"], cfg.eps)
     if prec == BF16:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     k_cache[:, pos0:pos0 + S] = k.transpose(1, 0, 2)

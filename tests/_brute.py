@@ -41,6 +41,19 @@ def rope_complex(u, angles):
     return out
 
 
+def rope_complex_adjacent(u, angles):
+    """Rotate adjacent pairs (u[2j], u[2j+1]) as the complex number
+    u[2j] + i u[2j+1] multiplied by exp(i angle_j); the real part goes to
+    element j, the imaginary part to element j + d/2."""
+    h = len(u) // 2
+    out = [0.0] * len(u)
+    for j in range(h):
+        z = complex(u[2 * j], u[2 * j + 1]) * complex(math.cos(angles[j]), math.sin(angles[j]))
+        out[j] = z.real
+        out[j + h] = z.imag
+    return out
+
+
 def text_angles(pos, d, theta):
     return [pos * theta ** (-2.0 * j / d) for j in range(d // 2)]
 
@@ -84,13 +97,15 @@ def expand_kv_rows(W, n_kv, head_dim, rep):
     return out
 
 
-def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v):
+def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v, interleave=False):
     """One decoder layer written as MHA over expanded K/V weights.
 
     xs: list of rows at positions pos0..; w: dict of nested lists with wk/wv
     already expanded to nq heads; cache_k/cache_v: lists (per position) of
-    [nq][d] rows, extended in place.
+    [nq][d] rows, extended in place. qk_norm: 0 none, 1 (or True) per-head
+    RMSNorm before the rotation, 2 after it. interleave: rotate adjacent pairs.
     """
+    rot = rope_complex_adjacent if interleave else rope_complex
     outs = []
     for s, x in enumerate(xs):
         pos = pos0 + s
@@ -102,12 +117,16 @@ def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v)
         for hd in range(nq):
             qq = q[hd * d:(hd + 1) * d]
             kk = k[hd * d:(hd + 1) * d]
-            if qk_norm:
+            if int(qk_norm) == 1:
                 qq = rmsnorm(qq, w["q_norm"], eps)
                 kk = rmsnorm(kk, w["k_norm"], eps)
             ang = text_angles(pos, d, theta)
-            qh.append(rope_complex(qq, ang))
-            kh.append(rope_complex(kk, ang))
+            qq, kk = rot(qq, ang), rot(kk, ang)
+            if int(qk_norm) == 2:
+                qq = rmsnorm(qq, w["q_norm"], eps)
+                kk = rmsnorm(kk, w["k_norm"], eps)
+            qh.append(qq)
+            kh.append(kk)
             vh.append(v[hd * d:(hd + 1) * d])
         cache_k.append(kh)
         cache_v.append(vh)

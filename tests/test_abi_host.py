@@ -59,6 +59,8 @@ def test_kv_and_workspace_sizes():
     (dict(n_q_heads=6, n_kv_heads=2), N.VLM_ERR_UNSUPPORTED),  # group of 3
     (dict(block_kind=1, n_kv_heads=2), N.VLM_ERR_UNSUPPORTED),
     (dict(rope_segments=3), N.VLM_ERR_ARG),
+    (dict(qk_norm=3), N.VLM_ERR_ARG),
+    (dict(rope_interleave=2), N.VLM_ERR_ARG),
 ])
 def test_desc_validation(bad, status):
     d = desc(**bad)
@@ -87,6 +89,18 @@ def test_rope_table_argument_checks():
     assert L.vlm_rope_table(fake, 2, 8, axes.ctypes.data_as(P), 1, 64, 1e6, fake, fake, None) == N.VLM_ERR_ARG
     axes[3] = 0
     assert L.vlm_rope_table(fake, 1, 8, axes.ctypes.data_as(P), 1, 64, -1.0, fake, fake, None) == N.VLM_ERR_ARG
+
+
+def test_rope_alpha_base_matches_oracle_and_checks_arguments():
+    from oracle import decoder as od
+    L = N.lib()
+    out = C.c_double()
+    for theta, alpha, d in [(1e4, 1e3, 128), (1e6, 1.0, 64), (5e5, 3.7, 80)]:
+        assert L.vlm_rope_alpha_base(theta, alpha, d, C.byref(out)) == N.VLM_OK
+        assert out.value == pytest.approx(od.alpha_scaled_base(theta, alpha, d), rel=1e-15)
+    for theta, alpha, d in [(0.0, 2.0, 64), (1e4, -1.0, 64), (1e4, 2.0, 2)]:
+        assert L.vlm_rope_alpha_base(theta, alpha, d, C.byref(out)) == N.VLM_ERR_ARG
+    assert L.vlm_rope_alpha_base(1e4, 2.0, 64, None) == N.VLM_ERR_ARG
 
 
 def test_window_index_matches_oracle():

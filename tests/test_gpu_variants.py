@@ -1,0 +1,88 @@
+"""GPU parity of the decoder layer variants against the oracle, through the C ABI.
+
+* QK-Norm after RoPE, with the cache holding the normalised k (HunyuanOCR
+  v1.0 ncnn port, 二 and 五.2): desc.qk_norm = 2.
+* Interleaved RoPE, adjacent pairs rotated and de-interleaved into the
+  rotate-half order (Youtu-VL-4B ncnn port, 实现难点 §2): desc.rope_interleave = 1.
+
+Both change the prefill RoPE kernel and the rotation inside the fused decode
+attention, so every case checks the prefill rows, the K/V cache after the
+prefill and after the decode steps, and the decode output. Gates as in the
+other parity tests: 1e-4 relative for fp32, 2e-2 for bf16, ids exact (fp32)
+or with near-tie attribution (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decoder as od
+import vlm_synth as vs
+from tests.test_gpu_decoder import TOL, check_ids, kv_host, make, rel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pipeline():
+    from decoder_prefill_decode_amd import pipeline
+    return pipeline
+
+
+def check_caches(run, ref, cfg, T, tol):
+    for l in range(cfg.n_layers):
+        k, v = kv_host(run, l)
+        assert rel(k[:, :T], ref["k_cache"][l][:, :T]) <= tol, f"layer {l} K"
+        assert rel(v[:, :T], ref["v_cache"][l][:, :T]) <= tol, f"layer {l} V"
+
+
+@pytest.mark.parametrize("qk_norm,interleave", [(2, False), (0, True), (2, True), (1, True)],
+                         ids=["norm_after", "interleave", "norm_after_interleave", "norm_before_interleave"])
+def test_f32_stack_variants(pipeline, qk_norm, interleave):
+    cfg = vs.scaled(vs.C1, qk_norm=qk_norm, rope_interleave=interleave)
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    x = run.prefill()
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    tok0 = int(run.first_token(logits)[0])
+    assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["f32"]
+    assert rel(logits.cpu().numpy(), ref["logits0"]) <= TOL["f32"]
+    check_caches(run, ref, cfg, cfg.seq, TOL["f32"])
+    ids = run.decode(cfg.decode_steps, loop=True)
+    assert [tok0] + list(ids) == list(ref["ids"])
+    check_caches(run, ref, cfg, cfg.seq + cfg.decode_steps, TOL["f32"])
+
+
+def test_bf16_layer_norm_after_interleave(pipeline):
+    cfg = vs.scaled(vs.C2_BF16, qk_norm=2, rope_interleave=True, seq=200, decode_steps=24, capacity=256)
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    x = run.prefill()
+    assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["bf16"]
+    check_caches(run, ref, cfg, cfg.seq, TOL["bf16"])
+    out = run.decode_hidden(run.dec_x).cpu().numpy()
+    assert rel(out, ref["decode_x"]) <= TOL["bf16"]
+    check_caches(run, ref, cfg, cfg.seq + cfg.decode_steps, TOL["bf16"])
+
+
+def test_bf16_head80_stack_interleave(pipeline):
+    """80-wide heads (40 rotation pairs, 4 query heads per KV head) with interleaved RoPE and QK-Norm after it."""
+    cfg = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=80, n_img=30, img_start=16, decode_steps=12, capacity=128,
+                    qk_norm=2, rope_interleave=True)
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    x = run.prefill()
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    tok0 = int(run.first_token(logits)[0])
+    lg = logits.cpu().numpy()
+    assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["bf16"]
+    assert rel(lg, ref["logits0"]) <= TOL["bf16"]
+    check_caches(run, ref, cfg, cfg.seq, TOL["bf16"])
+    free = [tok0] + list(run.decode(cfg.decode_steps))
+    run.kv.truncate(cfg.seq)
+    forced = [tok0] + list(run.decode_forced(ref["ids"][:-1]))
+    eps = 8 * float(np.abs(lg - ref["logits0"]).max())
+    flips, div = check_ids(free, forced, ref["ids"], ref["margins"], eps)
+    print(f"head80 variants: logit err {eps / 8:.2e}, first divergence {div}, tie flips {flips}")

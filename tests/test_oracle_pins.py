@@ -172,6 +172,76 @@ def test_rope_multi_axis_equal_axes_is_text_rope():
     assert np.array_equal(c, c1) and np.array_equal(s, s1)
 
 
+def test_interleaved_rope_matches_adjacent_pair_rotation():
+    """Youtu-VL ncnn port, 实现难点 §2: pairs of adjacent elements turn together
+    and land in the two halves of the head."""
+    d, T = 16, 9
+    cos, sin = _text_tables(T, d, 1e4)
+    u = np.random.default_rng(61).standard_normal((T, 2, d))
+    y = od.rope_apply(u, cos, sin, 1, interleave=True)
+    for t in range(T):
+        for h in range(2):
+            ref = bf.rope_complex_adjacent(list(u[t, h]), bf.text_angles(t, d, 1e4))
+            assert np.allclose(y[t, h], ref, rtol=1e-13, atol=1e-14)
+
+
+def test_interleaved_rope_is_a_permutation_then_rotation():
+    """The de-interleave is the fixed permutation P of the page (q @ P): a
+    permutation matrix, position 0 gives q @ P, and q.k is invariant under it."""
+    d = 64
+    P = np.zeros((d, d))
+    for j in range(d // 2):
+        P[2 * j, j] = 1.0
+        P[2 * j + 1, j + d // 2] = 1.0
+    cos, sin = _text_tables(40, d)
+    rng = np.random.default_rng(62)
+    q, k = rng.standard_normal((2, 1, 1, d))
+    assert np.array_equal(od.rope_apply(q, cos[:1], sin[:1], 1, interleave=True)[0, 0], q[0, 0] @ P)
+    rq = lambda m, v: od.rope_apply(v, cos[m:m + 1], sin[m:m + 1], 1, interleave=True)[0, 0]
+    for m, n in [(7, 3), (39, 0)]:
+        assert rq(m, q) @ rq(n, k) == pytest.approx(rq(m - n, q) @ (k[0, 0] @ P), rel=1e-10, abs=1e-10)
+
+
+def test_alpha_scaled_base_matches_page():
+    """HunyuanOCR v1.0 ncnn port, 二 and 五.1: base = theta * alpha^(d/(d-2)),
+    printed as ~1.11588e7 for its 128-wide heads (four 16-pair sections)."""
+    p = pages()["hunyuan_xdrope_base"]
+    d = p["head_dim"]
+    assert 4 * 16 * 2 == d
+    assert od.alpha_scaled_base(1e6, 1.0, d) == 1e6            # alpha 1: the plain base
+    b = od.alpha_scaled_base(p["rope_theta"], p["alpha"], d)
+    assert b == pytest.approx(p["value"], rel=5e-6)
+    assert math.log(b / p["rope_theta"]) == pytest.approx(math.log(p["alpha"]) * d / (d - 2), rel=1e-12)
+    # the page: frequencies of pairs j >= 32 (the last two axes) are near zero
+    inv = b ** (-2.0 * np.arange(d // 2) / d)
+    assert inv[32] < 3.1e-4 and inv[63] < 1.3e-7 and inv[0] == 1.0
+
+
+def test_qk_norm_orders():
+    """HunyuanOCR v1.0 ncnn port, 五.2: norm after the rotation, and the cache
+    holds the normalised k; with a unit gain both orders agree (a rotation
+    keeps each head's RMS), with a general gain they do not."""
+    cfg2 = vs.scaled(TINY, qk_norm=2, eps=0.0)   # eps 0: the normalised rows have RMS exactly 1
+    cfg1 = vs.scaled(TINY, qk_norm=1, eps=0.0)
+    w = {k: v.astype(np.float64) for k, v in vs.decoder_layer_weights(cfg2, 0).items()}
+    x = np.random.default_rng(63).standard_normal((cfg2.seq, cfg2.hidden))
+    cos, sin = _text_tables(cfg2.capacity, cfg2.head_dim, cfg2.theta)
+
+    def run(cfg, ww):
+        kc = np.zeros((cfg.n_kv_heads, cfg.capacity, cfg.head_dim)); vc = np.zeros_like(kc)
+        return od.decoder_layer(x, ww, cfg, kc, vc, 0, cos, sin, od.F64), kc
+
+    y2, k2 = run(cfg2, w)
+    y1, k1 = run(cfg1, w)
+    assert not np.allclose(y1, y2, rtol=1e-6)
+    ms = np.mean((k2[:, :cfg2.seq] / w["k_norm"]) ** 2, axis=-1)   # normalised after the rotation
+    assert np.allclose(ms, 1.0, rtol=0, atol=1e-12)
+    ms1 = np.mean((k1[:, :cfg1.seq] / w["k_norm"]) ** 2, axis=-1)
+    assert not np.allclose(ms1, 1.0, atol=1e-2)
+    u = dict(w, q_norm=np.ones(cfg2.head_dim), k_norm=np.ones(cfg2.head_dim))
+    assert np.allclose(run(cfg2, u)[0], run(cfg1, u)[0], rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- attention
 def test_attention_matches_brute_force_with_mask():
     rng = np.random.default_rng(10)
@@ -261,9 +331,9 @@ TINY = vs.DecoderConfig("tiny", 99, n_layers=2, hidden=8, n_q_heads=4, n_kv_head
                         qk_norm=True, theta=1e4)
 
 
-@pytest.mark.parametrize("qk_norm", [True, False])
-def test_decoder_layer_matches_brute_force_mha(qk_norm):
-    cfg = vs.scaled(TINY, qk_norm=qk_norm)
+@pytest.mark.parametrize("qk_norm,interleave", [(1, False), (0, False), (2, False), (0, True), (2, True)])
+def test_decoder_layer_matches_brute_force_mha(qk_norm, interleave):
+    cfg = vs.scaled(TINY, qk_norm=qk_norm, rope_interleave=interleave)
     w = {k: v.astype(np.float64) for k, v in vs.decoder_layer_weights(cfg, 0).items()}
     x = np.random.default_rng(15).standard_normal((cfg.seq, cfg.hidden))
     cos, sin = _text_tables(cfg.capacity, cfg.head_dim, cfg.theta)
@@ -274,7 +344,8 @@ def test_decoder_layer_matches_brute_force_mha(qk_norm):
     wl["wk"] = bf.expand_kv_rows(wl["wk"], cfg.n_kv_heads, cfg.head_dim, rep)
     wl["wv"] = bf.expand_kv_rows(wl["wv"], cfg.n_kv_heads, cfg.head_dim, rep)
     ck, cv = [], []
-    ref = bf.decoder_layer_mha(x.tolist(), wl, cfg.n_q_heads, cfg.head_dim, cfg.eps, cfg.theta, qk_norm, 0, ck, cv)
+    ref = bf.decoder_layer_mha(x.tolist(), wl, cfg.n_q_heads, cfg.head_dim, cfg.eps, cfg.theta, qk_norm, 0, ck, cv,
+                               interleave)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
     # the cache holds the roped, normed K of each KV head
     for s in range(cfg.seq):

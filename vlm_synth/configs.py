@@ -39,9 +39,10 @@ class DecoderConfig:
     decode_steps: int
     capacity: int           # KV window W (slots)
     dtype: str              # f32 or bf16 (weights, KV cache, GEMM operands)
-    qk_norm: bool
+    qk_norm: int            # 0 off, 1 per-head q/k RMSNorm before RoPE, 2 after RoPE
     theta: float = 1.0e6
     eps: float = 1.0e-6
+    rope_interleave: bool = False  # RoPE pairs adjacent elements (de-interleaved before rotate-half)
 
     @property
     def qkv_rows(self) -> int:
