@@ -217,16 +217,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 // stages are in flight. Here the operands go straight from global memory into
 // a ring of P LDS stages (global_load_lds_dwordx4: lane L's 16 bytes land at
 // the wave-uniform base + 16*L), P-1 stages ahead of the MFMAs, with no
-// register staging. One load instruction fills 8 tile rows of 64 bf16; lane L
-// fetches row L/8, chunk (L%8) ^ (L/8), so a row's eight 16-byte chunks are
-// XOR-swizzled by the row index and the MFMA operand reads (32 rows, one
-// chunk) spread over the LDS banks. Requires K % 64 == 0.
+// register staging. A stage holds BK (64 or 32) bf16 of each tile row; one
+// load instruction fills 1 KiB, i.e. 8 rows of 64 or 16 rows of 32. Chunk c
+// (16 bytes) of row r is stored at chunk position c ^ swz(r) of that row, so
+// the MFMA operand reads (32 rows, one chunk) spread over the LDS banks:
+// swz(r) = r & 7 for 128-byte rows, (r >> 1) & 3 for 64-byte rows (two rows
+// share one 128-byte bank window). Lane L therefore fetches row L / CPR and
+// chunk (L % CPR) ^ swz(L / CPR) (CPR = chunks per row). Requires K % BK == 0.
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int V>
 __device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(V), other counters untouched (gfx9 encoding)
     static_assert(V >= 0 && V < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() {  // s_waitcnt lgkmcnt(0), other counters untouched
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 // Waits until at most k * LPS of this wave's loads are outstanding, k in [0, KMAX] (wave-uniform).
 template <int LPS, int KMAX>
@@ -242,12 +248,17 @@ __device__ __forceinline__ void wait_stages(int k) {
     }
 }
 
+template <int BK>
+__device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
+
 // WGM x WGN wavefronts per block, each owning a (BM/WGM) x (BN/WGN) sub-tile.
-template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT>
+template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
-    constexpr int NW = WGM * WGN, BK = 64, WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
-    constexpr int AI = BM / (8 * NW), BI = BN / (8 * NW);  // load instructions per wave per stage (8 rows each)
-    static_assert(AI * 8 * NW == BM && BI * 8 * NW == BN && TM >= 1 && TN >= 1, "tile / wavefront grid");
+    static_assert(BK == 64 || BK == 32, "stage depth");
+    constexpr int NW = WGM * WGN, WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;  // 16-byte chunks per row, rows per load instruction
+    constexpr int AI = BM / (RPI * NW), BI = BN / (RPI * NW);  // load instructions per wave per stage
+    static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN && TM >= 1 && TN >= 1, "tile / wavefront grid");
     constexpr int LPS = AI + BI, STAGE = (BM + BN) * BK;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
@@ -263,13 +274,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
 
     // this lane's source row/chunk in each of the wave's load instructions (rows past M / N are clamped:
     // their products land in output rows / columns the epilogue never stores)
-    const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+    const int lr = lane / CPR, lc = (lane % CPR) ^ lds_swz<BK>(lr);  // RPI is a multiple of 8: swz(lr) = swz(row)
     const bf16_t* ga[AI];
     const bf16_t* gb[BI];
 #pragma unroll
-    for (int i = 0; i < AI; i++) ga[i] = A + (size_t)min(m0 + (w * AI + i) * 8 + lr, M - 1) * K + lc * 8;
+    for (int i = 0; i < AI; i++) ga[i] = A + (size_t)min(m0 + (w * AI + i) * RPI + lr, M - 1) * K + lc * 8;
 #pragma unroll
-    for (int i = 0; i < BI; i++) gb[i] = B + (size_t)min(n0 + (w * BI + i) * 8 + lr, N - 1) * K + lc * 8;
+    for (int i = 0; i < BI; i++) gb[i] = B + (size_t)min(n0 + (w * BI + i) * RPI + lr, N - 1) * K + lc * 8;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
         kt0 = blockIdx.y * per;
         nk = max(0, min(nk, kt0 + per) - kt0);
     }
-    // one K stage of both tiles into LDS stage ST: instruction i of wavefront w fills 8 rows (1 KiB).
+    // one K stage of both tiles into LDS stage ST: instruction i of wavefront w fills RPI rows (1 KiB).
     // (The source pointer is passed as const void*: the host pass silently drops the kernel otherwise.)
 #define VLM_LDS_STAGE(KOFF, ST)                                                                              \
     do {                                                                                                     \
@@ -297,41 +308,59 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < P - 1; s++)
         if (s < nk) VLM_LDS_STAGE((kt0 + s) * BK, smem + s * STAGE);
-    // operand rows of this lane inside a stage; chunk c of row r sits at r*64 + ((c ^ (r & 7)) * 8)
+    // operand rows of this lane inside a stage; chunk c of row r sits at r*BK + ((c ^ swz(r)) * 8)
     int ra[TM], rb[TN];
 #pragma unroll
     for (int i = 0; i < TM; i++) ra[i] = wm * WM + i * 32 + l32;
 #pragma unroll
     for (int j = 0; j < TN; j++) rb[j] = BM + wn * WN + j * 32 + l32;
-    for (int kt = 0; kt < nk; kt++) {
-        wait_stages<LPS, P - 2>(nk - 1 - kt);  // this lane's loads of stage kt have landed
-        // ... and every lane's; stage kt-1 is free (its reads fed MFMAs already). A plain s_barrier:
-        // __syncthreads() would add a fence that waits for every load in flight, later stages included.
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + P - 1 < nk) VLM_LDS_STAGE((kt0 + kt + P - 1) * BK, smem + ((kt + P - 1) % P) * STAGE);
-        const bf16_t* st = smem + (kt % P) * STAGE;
-        // every operand fragment of the stage is requested before the first MFMA, so the LDS
-        // latency is paid once per stage rather than once per 16-wide K step
-        bf16x8 fa[BK / 16][TM], fb[BK / 16][TN];
+    constexpr int KS = BK / 16;  // 16-wide MFMA steps per stage
+    auto read_frags = [&](const bf16_t* st, int kk, bf16x8* fa, bf16x8* fb) {
+        const int c = kk * 2 + h;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++) {
-            const int c = kk * 2 + h;
+        for (int i = 0; i < TM; i++)
+            fa[i] = *reinterpret_cast<const bf16x8*>(st + ra[i] * BK + ((c ^ lds_swz<BK>(ra[i])) * 8));
 #pragma unroll
-            for (int i = 0; i < TM; i++)
-                fa[kk][i] = *reinterpret_cast<const bf16x8*>(st + ra[i] * BK + ((c ^ (ra[i] & 7)) * 8));
+        for (int j = 0; j < TN; j++)
+            fb[j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ lds_swz<BK>(rb[j])) * 8));
+    };
+    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int j = 0; j < TN; j++)
-                fb[kk][j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ (rb[j] & 7)) * 8));
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // Software pipeline: the fragments of step kk+1 are read while the MFMAs of step kk run, and
+    // the first step of stage kt+1 is read (after its wait and barrier) before the last MFMAs of
+    // stage kt, so LDS reads overlap the matrix cores within each wavefront. (Reading a whole
+    // stage's fragments before its first MFMA measured 5-12% slower on the prefill shapes.)
+    {
+        bf16x8 fa[2][TM], fb[2][TN];
+        if (nk > 0) {
+            wait_stages<LPS, P - 2>(nk - 1);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (P - 1 < nk) VLM_LDS_STAGE((kt0 + P - 1) * BK, smem + (P - 1) * STAGE);
+            read_frags(smem, 0, fa[0], fb[0]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kt = 0; kt < nk; kt++) {
+            const bf16_t* st = smem + (kt % P) * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; kk++)
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+            for (int kk = 0; kk < KS - 1; kk++) {
+                read_frags(st, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                mfmas(fa[kk & 1], fb[kk & 1]);
+            }
+            if (kt + 1 < nk) {
+                wait_stages<LPS, P - 2>(nk - 2 - kt);  // stage kt+1 has landed (this lane)
+                wait_lgkm0();                          // this wave's reads of stage kt have returned
+                __builtin_amdgcn_s_barrier();          // ... every wave's; stage kt's slot may be refilled
+                __builtin_amdgcn_sched_barrier(0);
+                if (kt + P < nk) VLM_LDS_STAGE((kt0 + kt + P) * BK, smem + (kt % P) * STAGE);
+                read_frags(smem + ((kt + 1) % P) * STAGE, 0, fa[0], fb[0]);
+            }
+            mfmas(fa[(KS - 1) & 1], fb[(KS - 1) & 1]);
+        }
     }
 #undef VLM_LDS_STAGE
     gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32);
@@ -395,18 +424,18 @@ static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT>
+template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK>
 static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
     const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
-    const size_t smem = (size_t)P * (BM + BN) * 64 * sizeof(bf16_t);
+    const size_t smem = (size_t)P * (BM + BN) * BK * sizeof(bf16_t);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
+    gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
     const size_t total = (size_t)a.M * (EPI == Epi::SwiGLU ? a.N / 2 : a.N);
@@ -428,17 +457,21 @@ static int target_blocks() {
     return v;
 }
 
-// Tile and K-split choice of the direct-to-LDS kernel from a per-CU feed model:
-// these GEMMs are bound by how fast one CU pulls its operand stages out of L2
-// (measured: ~48 GB/s per block with two 4-wavefront blocks per CU, ~40 GB/s
-// for one 8-wavefront block with its two-stage ring), so the estimated time is
-// rounds x (blocks per CU) x (stages per block) x (stage bytes) / feed, plus,
-// for a K split, ~4 us and the fp32 partials written and re-read by the reduce.
+// Tile and K-split choice of the direct-to-LDS kernel from a per-CU feed model.
+// On these shapes a block's time is set by how fast its CU pulls operand
+// stages out of L2 rather than by the matrix cores: an estimate is
+//   3 us + q * stages * stage_bytes / feed,   q = ceil(blocks / 256),
+// with feed the measured per-CU rate of the tile shape (bytes/us, "one" for a
+// lone block per CU, "two" when two blocks share it), plus, for a K split,
+// 3 us and the fp32 partials written and re-read by the reduce (~4 GB/ms).
+// The constants come from timing every candidate on the decoder prefill
+// shapes (M 512-560; K 1024-9728); the model picks within ~6% of the fastest.
 struct LdsPlan { int bm, bn, sp; };
 static LdsPlan plan_lds(const GemmArgs& a, bool swiglu) {
-    // {BM, BN, blocks per CU that fit the LDS ring, per-block feed in bytes/us}
-    static const int cand[5][4] = {{256, 256, 1, 40000}, {128, 256, 1, 40000}, {128, 128, 2, 48000},
-                                   {64, 128, 2, 48000}, {64, 64, 2, 48000}};
+    // {BM, BN, blocks per CU that fit the LDS ring, feed with one block per CU, feed with two}
+    static const int cand[5][5] = {{256, 256, 1, 37000, 37000}, {128, 256, 1, 46500, 46500},
+                                   {128, 128, 2, 43000, 52000}, {64, 128, 2, 44000, 62000},
+                                   {64, 64, 2, 40000, 55000}};
     static const int splits[6] = {1, 2, 3, 4, 6, 8};
     const int nk = a.K / 64;
     double best = 1e30;
@@ -448,12 +481,11 @@ static LdsPlan plan_lds(const GemmArgs& a, bool swiglu) {
         const long tiles = (long)((a.M + c[0] - 1) / c[0]) * ((a.N + c[1] - 1) / c[1]);
         for (int sp : splits) {
             if (sp > 1 && (!a.part || nk / sp < 4 || (size_t)sp * a.M * a.N > a.part_cap)) continue;
-            const long nb = tiles * sp;
-            const double rounds = (double)((nb + 256L * c[2] - 1) / (256L * c[2]));
-            const double per_cu = (double)std::min<long>(c[2], (nb + 255) / 256);  // blocks sharing a CU
+            const long q = (tiles * sp + 255) / 256;  // blocks per CU
+            const double feed = (c[2] >= 2 && q >= 2) ? c[4] : c[3];
             const double stages = (double)((nk + sp - 1) / sp);
-            double t = rounds * per_cu * stages * (c[0] + c[1]) * 128.0 / c[3];  // us
-            if (sp > 1) t += 4.0 + (double)sp * a.M * a.N * 8.0 / 4.0e6;
+            double t = 3.0 + (double)q * stages * (c[0] + c[1]) * 128.0 / feed;  // us
+            if (sp > 1) t += 3.0 + (double)sp * a.M * a.N * 8.0 / 4.0e6;
             if (t < best) {
                 best = t;
                 bp = {c[0], c[1], sp};
@@ -480,14 +512,14 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
         if (a.K % 64 == 0) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
             const LdsPlan pl = plan_lds(a, EPI == Epi::SwiGLU);
-#define VLM_RUN_LDS(BM_, BN_, P_, GM_, GN_)                                                        \
-    return pl.sp > 1 ? run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, true>(a, pl.sp, st)             \
-                     : run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, false>(a, 1, st)
-            if (pl.bm == 256) VLM_RUN_LDS(256, 256, 2, 4, 2);
-            if (pl.bm == 128 && pl.bn == 256) VLM_RUN_LDS(128, 256, 2, 2, 4);
-            if (pl.bm == 128) VLM_RUN_LDS(128, 128, 2, 2, 2);
-            if (pl.bn == 128) VLM_RUN_LDS(64, 128, 3, 2, 2);
-            if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS(64, 64, 4, 2, 2);
+#define VLM_RUN_LDS(BM_, BN_, P_, GM_, GN_, BK_)                                                   \
+    return pl.sp > 1 ? run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, true, BK_>(a, pl.sp, st)         \
+                     : run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, false, BK_>(a, 1, st)
+            if (pl.bm == 256) VLM_RUN_LDS(256, 256, 2, 4, 2, 64);
+            if (pl.bm == 128 && pl.bn == 256) VLM_RUN_LDS(128, 256, 2, 2, 4, 64);
+            if (pl.bm == 128) VLM_RUN_LDS(128, 128, 2, 2, 2, 64);
+            if (pl.bn == 128) VLM_RUN_LDS(64, 128, 3, 2, 2, 64);
+            if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS(64, 64, 4, 2, 2, 64);
 #undef VLM_RUN_LDS
         }
     }
