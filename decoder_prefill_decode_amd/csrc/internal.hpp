@@ -33,7 +33,9 @@ struct GemmArgs {
 // dtype: 0 = f32, 1 = bf16 (vlm_dtype values)
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t st);
 
-enum class Pro : int { RmsNorm = 0, Plain = 1 };
+// Operand of a decode projection: RMSNorm of fp32 x, or a plain model-type vector (PlainLds: the
+// same operand, staged once per block in LDS; chosen inside launch_gemv for long rows).
+enum class Pro : int { RmsNorm = 0, Plain = 1, PlainLds = 2 };
 struct GemvArgs {
     const void* W;          // [N][K]
     const void* vec;        // Pro::RmsNorm: fp32 x [K]; Pro::Plain: model-type vector [K]

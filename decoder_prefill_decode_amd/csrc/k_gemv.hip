@@ -161,22 +161,32 @@ template <> struct Raw4<bf16_t> {
     }
 };
 
+//  * PlainLds operand: a plain vector staged once per block into LDS (raw
+//    16-byte chunks), so the four wavefronts of a block share one read of it;
+//    with long rows a per-lane copy would double the L2 traffic of the GEMV.
 template <class T, Pro PRO, Epi EPI, int NR, int KCH>
 __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
     constexpr int VEC = 16 / sizeof(T), STEP = kWave * VEC;
-    constexpr bool NORM = PRO == Pro::RmsNorm;
+    constexpr bool NORM = PRO == Pro::RmsNorm, SHARE = PRO == Pro::PlainLds, STAGED = NORM || SHARE;
     constexpr int VCH = NORM ? (KCH * STEP / 4 + 255) / 256 : 1;  // 4-float chunks of x per thread
-    extern __shared__ float vs[];
+    constexpr int SCH = SHARE ? (KCH * kWave + 255) / 256 : 1;     // 16-byte operand chunks per thread
+    extern __shared__ __attribute__((aligned(16))) float vs[];  // 16-byte aligned: PlainLds reads u32x4
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = blockIdx.x * 4 + tid / kWave;
     const int K = a.K;
     const T* W = (const T*)a.W;
 
-    // (1) operand: RMSNorm -> this thread's chunks of x and gain; Plain -> this lane's slice
-    u32x4 xr[NORM ? VCH : KCH];
+    // (1) operand: RMSNorm -> this thread's chunks of x and gain; Plain -> this lane's slice;
+    // PlainLds -> this thread's share of the vector
+    u32x4 xr[NORM ? VCH : (SHARE ? SCH : KCH)];
     Raw4<T> gr[VCH];
-    if constexpr (NORM) {
+    if constexpr (SHARE) {
+        const int nch = K / VEC;
+#pragma unroll
+        for (int i = 0; i < SCH; i++)
+            xr[i] = *reinterpret_cast<const u32x4*>((const T*)a.vec + VEC * min(tid + 256 * i, nch - 1));
+    } else if constexpr (NORM) {
         const int nx = K / 4;
 #pragma unroll
         for (int i = 0; i < VCH; i++) {
@@ -243,6 +253,13 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
                 for (int e = 0; e < 4; e++) vs[4 * c + e] = Elt<T>::rnd(__uint_as_float(xr[i][e]) * rs * gr[i].get(e));
         }
         __syncthreads();
+    } else if constexpr (SHARE) {
+        u32x4* vq = reinterpret_cast<u32x4*>(vs);
+        const int nch = K / VEC;
+#pragma unroll
+        for (int i = 0; i < SCH; i++)
+            if (tid + 256 * i < nch) vq[tid + 256 * i] = xr[i];
+        __syncthreads();
     }
     // (4) dot products
     float acc[NR];
@@ -256,6 +273,8 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
             if constexpr (NORM) {
 #pragma unroll
                 for (int e = 0; e < VEC; e++) h[e] = vs[k + e];
+            } else if constexpr (SHARE) {
+                unpack16(reinterpret_cast<const u32x4*>(vs)[k / VEC], (const T*)nullptr, h);
             } else {
                 unpack16(xr[c], (const T*)nullptr, h);
             }
@@ -319,13 +338,26 @@ static hipError_t run_gemv2(const GemvArgs& a, hipStream_t st) {
     const int nrows = a.N;  // SwiGLU: NR counts gate + up rows
     const int waves = (nrows + NR - 1) / NR;
     const int blocks = (waves + 3) / 4;
-    const size_t smem = PRO == Pro::RmsNorm ? (size_t)a.K * sizeof(float) : 0;
+    const size_t smem = PRO == Pro::RmsNorm ? (size_t)a.K * sizeof(float)
+                        : (PRO == Pro::PlainLds ? (size_t)a.K * sizeof(T) : 0);
     gemv2_kernel<T, PRO, EPI, NR, KCH><<<blocks, 256, smem, st>>>(a);
     return hipGetLastError();
 }
 
 // VLM_GEMV_ROWS (1, 2, 4 or 8) fixes the rows per wavefront of the decode
 // projections, for tuning; unset or 0 keeps the choice below.
+// Plain operands of at least this many 16-byte chunks per lane are staged in
+// LDS (Pro::PlainLds); VLM_GEMV_SHARE overrides it for tuning (0 = never).
+// Measured: the 36-layer stack's down projection (19 chunks) 11.7 -> 10.8 us,
+// the 28-layer stack's O projection (4 chunks) 3.2 -> 3.0 us.
+static int share_min_chunks() {
+    static int v = [] {
+        const char* e = getenv("VLM_GEMV_SHARE");
+        return e ? atoi(e) : 4;
+    }();
+    return v;
+}
+
 static int gemv_rows_override() {
     static int v = [] {
         const char* e = getenv("VLM_GEMV_ROWS");
@@ -342,6 +374,8 @@ static hipError_t pick_nr(const GemvArgs& a, hipStream_t st) {
     if constexpr (PRO == Pro::RmsNorm && KCH > 12) {
         return hipErrorNotSupported;
     } else {
+        if constexpr (PRO == Pro::Plain)
+            if (share_min_chunks() > 0 && KCH >= share_min_chunks()) return pick_nr<T, Pro::PlainLds, EPI, KCH>(a, st);
         constexpr int cap = 24 / KCH;
         const int n = a.N;
         switch (gemv_rows_override()) {  // tuning override: rows per wavefront, if the plan allows it
