@@ -274,9 +274,61 @@ def decoder_layer(x, w, cfg, k_cache, v_cache, pos0, cos, sin, prec):
     o = softmax_attention(q.transpose(1, 0, 2), k_cache, v_cache, window_mask(S, pos0, W), nq // nkv)
     o = o.transpose(1, 0, 2).reshape(S, nq * d)
     x = x + _lin(o, w["wo"], prec)
+    return _mlp(x, w, cfg, prec)
+
+
+def _mlp(x, w, cfg, prec):
+    """Post-attention RMSNorm, SwiGLU MLP and residual ([Penguin] §2.1, §4.2)."""
     h2 = rms_norm(x, w["mlp_norm"], cfg.eps)
     a = silu(_lin(h2, w["wg"], prec)) * _lin(h2, w["wu"], prec)
     return x + _lin(a, w["wd"], prec)
+
+
+def mla_layer(x, w, cfg, k_cache, v_cache, pos0, cos, sin, prec):
+    """One multi-head latent attention layer in the expanded form ([Youtu] 实现流程 §6).
+
+    The page's port does not absorb the latent: kv_b expands the 512-wide
+    compressed KV into full per-head keys and values, the cache holds those
+    (keys dn + dr wide, values dv wide), and every query head has its own KV
+    head; the q and kv paths each have a low-rank a/b projection pair. The
+    rotated part of the keys is the dr-wide tail of the kv_a output, shared by
+    all heads; RoPE is interleaved on the dr-wide parts ([Youtu] 实现难点 §2,
+    the 64x64 permutation). Order (the pages name the pieces, not the order;
+    this is the plainest arrangement of them):
+      h = RMSNorm(x)
+      q = RMSNorm(h Wq_a^T) Wq_b^T, per head [q_nope (dn) | q_rope (dr)]
+      [c (r) | k_rope (dr)] = h Wkv_a^T;  per head [k_nope (dn) | v (dv)] = RMSNorm(c) Wkv_b^T
+      q = [q_nope | RoPE(q_rope)], k = [k_nope | RoPE(k_rope)]   (the shared k_rope in every head)
+      attention with scale 1 / sqrt(dn + dr), o Wo^T added to x, then the SwiGLU MLP.
+    k_cache [nq, W, dn + dr], v_cache [nq, W, dv]; cos/sin: [>= pos0+S, dr] tables.
+    """
+    S = x.shape[0]
+    nq, d, dr, dv, r = cfg.n_q_heads, cfg.head_dim, cfg.qk_rope_dim, cfg.v_head_dim, cfg.kv_lora_rank
+    dn = d - dr
+    W = k_cache.shape[1]
+    if pos0 + S > W:
+        raise ValueError("sequence exceeds the KV window")
+    ilv = bool(cfg.rope_interleave)
+    h = rms_norm(x, w["attn_norm"], cfg.eps)
+    qa = rms_norm(_lin(h, w["wq_a"], prec), w["q_a_norm"], cfg.eps)
+    q = _lin(qa, w["wq_b"], prec).reshape(S, nq, d)
+    ckv = _lin(h, w["wkv_a"], prec)
+    c = rms_norm(ckv[:, :r], w["kv_a_norm"], cfg.eps)
+    kv = _lin(c, w["wkv_b"], prec).reshape(S, nq, dn + dv)
+    cr, sr = cos[pos0:pos0 + S], sin[pos0:pos0 + S]
+    q_rope = rope_apply(q[..., dn:], cr, sr, 1, ilv)
+    k_rope = rope_apply(ckv[:, None, r:], cr, sr, 1, ilv)
+    q = np.concatenate([q[..., :dn], q_rope], axis=-1)
+    k = np.concatenate([kv[..., :dn], np.broadcast_to(k_rope, (S, nq, dr))], axis=-1)
+    v = kv[..., dn:]
+    if prec == BF16:
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    k_cache[:, pos0:pos0 + S] = k.transpose(1, 0, 2)
+    v_cache[:, pos0:pos0 + S] = v.transpose(1, 0, 2)
+    o = softmax_attention(q.transpose(1, 0, 2), k_cache, v_cache, window_mask(S, pos0, W), 1)
+    o = o.transpose(1, 0, 2).reshape(S, nq * dv)
+    x = x + _lin(o, w["wo"], prec)
+    return _mlp(x, w, cfg, prec)
 
 
 # ----------------------------------------------------------------------------
@@ -326,10 +378,12 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
     L, W = cfg.n_layers, cfg.capacity
     ws = [_prep_weights(w, prec) for w in layers]
     assert len(ws) == L
-    cos, sin = rope_tables(np.arange(W)[None, :], np.zeros(cfg.head_dim // 2, np.int64), 1,
-                           cfg.head_dim, cfg.theta)
+    mla = getattr(cfg, "kv_lora_rank", 0) > 0
+    rd = cfg.qk_rope_dim if mla else cfg.head_dim   # width of the rotated part of a head
+    cos, sin = rope_tables(np.arange(W)[None, :], np.zeros(rd // 2, np.int64), 1, rd, cfg.theta)
     kc = np.zeros((L, cfg.n_kv_heads, W, cfg.head_dim))
-    vc = np.zeros_like(kc)
+    vc = np.zeros((L, cfg.n_kv_heads, W, cfg.v_head_dim if mla else cfg.head_dim))
+    layer_fn = mla_layer if mla else decoder_layer
     has_vocab = cfg.vocab > 0
     if has_vocab:
         table = np.asarray(glob["embed"], np.float32 if prec == BF16 else np.float64)
@@ -341,7 +395,7 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
 
     def stack(rows, pos0):
         for l in range(L):
-            rows = decoder_layer(rows, ws[l], cfg, kc[l], vc[l], pos0, cos, sin, prec)
+            rows = layer_fn(rows, ws[l], cfg, kc[l], vc[l], pos0, cos, sin, prec)
         return rows
 
     t_start = time.perf_counter()

@@ -242,6 +242,77 @@ def test_qk_norm_orders():
     assert np.allclose(run(cfg2, u)[0], run(cfg1, u)[0], rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- expanded MLA
+MLA_TINY = vs.scaled(vs.C_MLA, hidden=64, n_q_heads=3, n_kv_heads=3, head_dim=24, qk_rope_dim=8, v_head_dim=16,
+                     q_lora_rank=32, kv_lora_rank=40, ffn=96, vocab=0, seq=7, n_img=0, img_start=0, capacity=8)
+
+
+def test_mla_expanded_equals_absorbed_latent_form():
+    """Youtu-VL-4B ncnn port, 实现流程 §6: the port expands the latent with kv_b instead of absorbing
+    it. Absorbing (q_nope . W_uk c = (W_uk^T q_nope) . c, o = W_uv sum_j p_j c_j) is the same
+    function; computing it that way pins the per-head split of kv_b, the shared rotated key, the
+    head layout of the cache and the 1/sqrt(dn + dr) scale."""
+    cfg = MLA_TINY
+    w = {k: v.astype(np.float64) for k, v in vs.decoder_layer_weights(cfg, 0).items()}
+    rng = np.random.default_rng(71)
+    S, nq, d, dr, dv, r = cfg.seq, cfg.n_q_heads, cfg.head_dim, cfg.qk_rope_dim, cfg.v_head_dim, cfg.kv_lora_rank
+    dn = d - dr
+    x = rng.standard_normal((S, cfg.hidden))
+    cos, sin = _text_tables(cfg.capacity, dr, cfg.theta)
+    kc = np.zeros((nq, cfg.capacity, d)); vc = np.zeros((nq, cfg.capacity, dv))
+    got = od.mla_layer(x, w, cfg, kc, vc, 0, cos, sin, od.F64)
+    # absorbed form, written per head and per key
+    h = od.rms_norm(x, w["attn_norm"], cfg.eps)
+    q = od.rms_norm(h @ w["wq_a"].T, w["q_a_norm"], cfg.eps) @ w["wq_b"].T
+    ckv = h @ w["wkv_a"].T
+    c = od.rms_norm(ckv[:, :r], w["kv_a_norm"], cfg.eps)
+    att = np.zeros((S, nq * dv))
+    for i in range(nq):
+        wb = w["wkv_b"][i * (dn + dv):(i + 1) * (dn + dv)]
+        w_uk, w_uv = wb[:dn], wb[dn:]
+        for t in range(S):
+            qn = q[t, i * d:i * d + dn]
+            qr = od.rope_apply(q[t, None, None, i * d + dn:(i + 1) * d], cos[t:t + 1], sin[t:t + 1], 1, True)[0, 0]
+            sc = []
+            for j in range(t + 1):
+                kr = od.rope_apply(ckv[j, None, None, r:], cos[j:j + 1], sin[j:j + 1], 1, True)[0, 0]
+                sc.append(((w_uk.T @ qn) @ c[j] + qr @ kr) / math.sqrt(d))
+            sc = np.array(sc)
+            p = np.exp(sc - sc.max()); p /= p.sum()
+            att[t, i * dv:(i + 1) * dv] = w_uv @ (p @ c[:t + 1])
+    y = x + att @ w["wo"].T
+    h2 = od.rms_norm(y, w["mlp_norm"], cfg.eps)
+    g = h2 @ w["wg"].T
+    ref = y + ((g / (1 + np.exp(-g))) * (h2 @ w["wu"].T)) @ w["wd"].T
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-12)
+    # the cache holds the expanded per-head keys (192-style width) and values (128-style width)
+    assert kc.shape[-1] == dn + dr and vc.shape[-1] == dv
+    assert np.allclose(vc[0, :S], c @ w["wkv_b"][dn:dn + dv].T, rtol=1e-12)
+    assert np.allclose(kc[1, :S, :dn], c @ w["wkv_b"][(dn + dv):(dn + dv) + dn].T, rtol=1e-12)
+    kr = od.rope_apply(ckv[:, None, r:], cos[:S], sin[:S], 1, True)[:, 0]   # [nope | rope], rope shared
+    for i in range(nq):
+        assert np.allclose(kc[i, :S, dn:], kr, rtol=1e-12, atol=1e-14)
+
+
+def test_mla_cache_shapes_match_page():
+    """Youtu-VL-4B ncnn port, 实现流程 §6-§7: per-layer K [32, 512, 192], V [32, 512, 128], nkv = nq."""
+    p = pages()["youtu_kv_window"]
+    cfg = vs.scaled(vs.C_MLA, n_q_heads=32, n_kv_heads=32, capacity=p["window"])
+    assert [cfg.n_kv_heads, cfg.capacity, cfg.head_dim] == p["k_shape"]
+    assert [cfg.n_kv_heads, cfg.capacity, cfg.v_head_dim] == p["v_shape"]
+    assert cfg.head_dim - cfg.qk_rope_dim == 128 and cfg.kv_lora_rank == 512 and cfg.qk_rope_dim == 64
+
+
+def test_mla_prefill_equals_decode_replay():
+    cfg = vs.scaled(MLA_TINY, n_layers=2, seq=7, capacity=8)
+    glob = {"x": np.random.default_rng(72).standard_normal((cfg.seq, cfg.hidden))}
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(2)]
+    a = od.run_decoder(cfg, glob, layers, steps=0)
+    b = od.run_decoder(cfg, glob, layers, steps=0, prefill_split=3)
+    assert np.allclose(a["prefill_x"], b["prefill_x"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(a["k_cache"], b["k_cache"], rtol=1e-12, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- attention
 def test_attention_matches_brute_force_with_mask():
     rng = np.random.default_rng(10)

@@ -43,6 +43,24 @@ class DecoderConfig:
     theta: float = 1.0e6
     eps: float = 1.0e-6
     rope_interleave: bool = False  # RoPE pairs adjacent elements (de-interleaved before rotate-half)
+    # multi-head latent attention, expanded per head (kv_lora_rank > 0): head_dim is the q/k head width,
+    # qk_nope_dim + qk_rope_dim; v_head_dim the value width; only the qk_rope_dim part rotates
+    q_lora_rank: int = 0
+    kv_lora_rank: int = 0
+    qk_rope_dim: int = 0
+    v_head_dim: int = 0
+
+    @property
+    def is_mla(self) -> bool:
+        return self.kv_lora_rank > 0
+
+    @property
+    def v_dim(self) -> int:
+        return self.v_head_dim if self.is_mla else self.head_dim
+
+    @property
+    def rope_dim(self) -> int:
+        return self.qk_rope_dim if self.is_mla else self.head_dim
 
     @property
     def qkv_rows(self) -> int:
@@ -109,6 +127,13 @@ C4 = DecoderConfig("c4_llama_4b", 4, n_layers=36, hidden=2560, n_q_heads=32, n_k
 C5 = VitConfig("c5_vit_27l", 5, n_layers=27, hidden=1152, n_heads=16, head_dim=72, ffn=4304,
                grid_h=14, grid_w=92, merge=2, window=8, full_layers=(7, 15, 23, 26),
                merger_hidden=4608, out_dim=2560)
+
+# Youtu-LLM-style expanded MLA layer stack at reduced width (the pages: 32 heads, K 192 = 128 + 64
+# rotated, V 128, 512-wide latent, interleaved RoPE); q_lora_rank is a reading (the pages give none).
+C_MLA = DecoderConfig("c_mla_small", 6, n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=4, head_dim=192,
+                      ffn=1024, vocab=4096, seq=48, n_img=12, img_start=8, decode_steps=8, capacity=128,
+                      dtype=F32, qk_norm=0, rope_interleave=True, q_lora_rank=384, kv_lora_rank=512,
+                      qk_rope_dim=64, v_head_dim=128)
 
 DECODER_CONFIGS = {c.name: c for c in (C1, C2_F32, C2_BF16, C3, C4)}
 ALL_CONFIGS = dict(DECODER_CONFIGS, **{C5.name: C5})

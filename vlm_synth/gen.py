@@ -24,6 +24,7 @@ GLOBAL = 4096
 # per-layer slots
 S_ATTN_NORM, S_WQ, S_WK, S_WV, S_QNORM, S_KNORM, S_WO, S_MLP_NORM, S_WG, S_WU, S_WD = range(11)
 S_ATTN_NORM_B, S_BQ, S_BK, S_BV, S_BO, S_MLP_NORM_B, S_B1, S_B2, S_FC1, S_FC2 = range(11, 21)
+S_WQA, S_QANORM, S_WQB, S_WKVA, S_KVANORM, S_WKVB = range(21, 27)  # expanded MLA
 # global slots
 G_EMBED, G_FINAL_NORM, G_IDS, G_IMG, G_X, G_DECODE_X = range(6)
 G_VIT_X, G_POST_LN, G_POST_LN_B, G_M1, G_M1B, G_M2, G_M2B = range(6, 13)
@@ -96,6 +97,25 @@ def decoder_layer_weights(cfg: DecoderConfig, layer: int) -> dict:
     """
     base = layer * 32
     H, d, F = cfg.hidden, cfg.head_dim, cfg.ffn
+    if cfg.is_mla:
+        # expanded MLA: wq_a [qr, H], q_a_norm [qr], wq_b [nq*d, qr], wkv_a [r + dr, H] (latent rows,
+        # then the shared rotated-key rows), kv_a_norm [r], wkv_b [nq*(dn + dv), r] (per head: the dn
+        # key rows, then the dv value rows), wo [H, nq*dv]
+        nq, qr, r, dr, dv = cfg.n_q_heads, cfg.q_lora_rank, cfg.kv_lora_rank, cfg.qk_rope_dim, cfg.v_head_dim
+        return {
+            "attn_norm": _gain(cfg, base + S_ATTN_NORM, H),
+            "wq_a": _weight(cfg, base + S_WQA, (qr, H)),
+            "q_a_norm": _gain(cfg, base + S_QANORM, qr),
+            "wq_b": _weight(cfg, base + S_WQB, (nq * d, qr)),
+            "wkv_a": _weight(cfg, base + S_WKVA, (r + dr, H)),
+            "kv_a_norm": _gain(cfg, base + S_KVANORM, r),
+            "wkv_b": _weight(cfg, base + S_WKVB, (nq * (d - dr + dv), r)),
+            "wo": _weight(cfg, base + S_WO, (H, nq * dv)),
+            "mlp_norm": _gain(cfg, base + S_MLP_NORM, H),
+            "wg": _weight(cfg, base + S_WG, (F, H)),
+            "wu": _weight(cfg, base + S_WU, (F, H)),
+            "wd": _weight(cfg, base + S_WD, (H, F)),
+        }
     w = {
         "attn_norm": _gain(cfg, base + S_ATTN_NORM, H),
         "wq": _weight(cfg, base + S_WQ, (cfg.n_q_heads * d, H)),
