@@ -52,8 +52,19 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 vlm_status check_desc(const vlm_model_desc* d) {
     if (!d) return fail(VLM_ERR_ARG, "desc is NULL");
-    if (d->block_kind != VLM_BLOCK_DECODER && d->block_kind != VLM_BLOCK_VIT)
+    if (d->block_kind != VLM_BLOCK_DECODER && d->block_kind != VLM_BLOCK_VIT && d->block_kind != VLM_BLOCK_MLA)
         return fail(VLM_ERR_ARG, "block_kind %d invalid", d->block_kind);
+    if (d->block_kind == VLM_BLOCK_MLA) {
+        if (d->n_kv_heads != d->n_q_heads) return fail(VLM_ERR_SHAPE, "MLA needs n_kv_heads == n_q_heads");
+        if (d->head_dim != 192 || d->qk_rope_dim != 64 || d->v_head_dim != 128)
+            return fail(VLM_ERR_UNSUPPORTED, "MLA kernels exist for head_dim 192, qk_rope_dim 64, v_head_dim 128");
+        if (d->q_lora_rank < 8 || d->q_lora_rank % 8 || d->kv_lora_rank < 8 || d->kv_lora_rank % 8 ||
+            d->q_lora_rank > 16384 || d->kv_lora_rank > 16384)
+            return fail(VLM_ERR_SHAPE, "MLA ranks must be positive multiples of 8 up to 16384");
+        if (d->qk_norm || d->rope_segments != 1) return fail(VLM_ERR_UNSUPPORTED, "MLA takes no QK-Norm, one RoPE segment");
+    } else if (d->q_lora_rank || d->kv_lora_rank || d->qk_rope_dim || d->v_head_dim) {
+        return fail(VLM_ERR_ARG, "MLA fields must be 0 for block_kind %d", d->block_kind);
+    }
     if (d->dtype != VLM_F32 && d->dtype != VLM_BF16) return fail(VLM_ERR_DTYPE, "dtype %d invalid", d->dtype);
     if (d->n_layers < 1) return fail(VLM_ERR_SHAPE, "n_layers %d < 1", d->n_layers);
     if (d->hidden < 8 || d->hidden % 8) return fail(VLM_ERR_SHAPE, "hidden %d must be a positive multiple of 8", d->hidden);
@@ -63,7 +74,8 @@ vlm_status check_desc(const vlm_model_desc* d) {
     const int grp = d->n_q_heads / d->n_kv_heads;
     if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
         return fail(VLM_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}", grp);
-    if (d->head_dim != 64 && d->head_dim != 72 && d->head_dim != 80 && d->head_dim != 128)
+    if (d->block_kind != VLM_BLOCK_MLA && d->head_dim != 64 && d->head_dim != 72 && d->head_dim != 80 &&
+        d->head_dim != 128)
         return fail(VLM_ERR_UNSUPPORTED, "head_dim %d not in {64,72,80,128}", d->head_dim);
     if (d->dtype == VLM_BF16 && d->head_dim % 16)
         return fail(VLM_ERR_UNSUPPORTED, "bf16 attention needs head_dim %% 16 == 0 (got %d)", d->head_dim);
@@ -74,7 +86,7 @@ vlm_status check_desc(const vlm_model_desc* d) {
         return fail(VLM_ERR_ARG, "rope_interleave %d not in {0,1}", d->rope_interleave);
     if (d->ffn < 8 || d->ffn % 8) return fail(VLM_ERR_SHAPE, "ffn %d must be a positive multiple of 8", d->ffn);
     if (d->ffn > 16384) return fail(VLM_ERR_UNSUPPORTED, "ffn %d > 16384", d->ffn);
-    if (d->block_kind == VLM_BLOCK_DECODER && d->ffn % 32)
+    if (d->block_kind != VLM_BLOCK_VIT && d->ffn % 32)
         return fail(VLM_ERR_SHAPE, "decoder ffn %d must be a multiple of 32 (gate/up groups)", d->ffn);
     if (d->n_q_heads * d->head_dim > 16384) return fail(VLM_ERR_UNSUPPORTED, "n_q_heads*head_dim too large");
     if (d->vocab < 0) return fail(VLM_ERR_SHAPE, "vocab %d < 0", d->vocab);
@@ -84,10 +96,21 @@ vlm_status check_desc(const vlm_model_desc* d) {
     return VLM_OK;
 }
 
-int qkv_rows(const vlm_model_desc* d) { return (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim; }
+bool is_mla(const vlm_model_desc* d) { return d->block_kind == VLM_BLOCK_MLA; }
+int vdim(const vlm_model_desc* d) { return is_mla(d) ? d->v_head_dim : d->head_dim; }
+// Width of the projections' fp32 output per row: q, k, v of the fused QKV GEMM, or for MLA the
+// q_b output [nq*d] followed by the kv_b output [nq*(dn + dv)].
+int qkv_rows(const vlm_model_desc* d) {
+    if (is_mla(d)) return d->n_q_heads * (2 * d->head_dim - d->qk_rope_dim + d->v_head_dim);
+    return (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+}
+// MLA: columns of the shared down-projection output [q latent qr | kv latent r | rotated key dr].
+int mla_a_cols(const vlm_model_desc* d) { return is_mla(d) ? d->q_lora_rank + d->kv_lora_rank + d->qk_rope_dim : 0; }
 
 struct Ws {
-    size_t h, qkv, q, kv, o, a, gpart, gpart_floats, xrow, qkvrow, qrow, part, orow, arow, rope, lm, total;
+    size_t h, qkv, q, kv, o, a, gpart, gpart_floats, xrow, qkvrow, qrow, part, orow, arow, rope, lm;
+    size_t ma, mqa, mc, marow;  // MLA: down-projection output, normed q / kv latents (rows), its decode row
+    size_t total;
 };
 
 Ws ws_layout(const vlm_model_desc* d, int max_rows) {
@@ -106,8 +129,8 @@ Ws ws_layout(const vlm_model_desc* d, int max_rows) {
     w.kv = d->block_kind == VLM_BLOCK_VIT ? take(2 * nkv * R * hd * E) : off;
     w.o = take(R * nq * hd * E);
     w.a = take(R * F * E);
-    // split-K partials of the narrow prefill GEMMs: up to 4 splits of [R][max(QKV, H, F)] fp32
-    w.gpart_floats = 4 * R * std::max({(size_t)qkv_rows(d), H, F});
+    // split-K partials of the narrow prefill GEMMs: up to 4 splits of [R][max(N)] fp32
+    w.gpart_floats = 4 * R * std::max({(size_t)qkv_rows(d), H, 2 * F, (size_t)mla_a_cols(d)});
     w.gpart = take(w.gpart_floats * 4);
     w.xrow = take(H * 4);
     w.qkvrow = take(qkv_rows(d) * 4);
@@ -117,6 +140,10 @@ Ws ws_layout(const vlm_model_desc* d, int max_rows) {
     w.arow = take(F * E);
     w.rope = take(2 * hd * 4);  // cos/sin row of the decode position
     w.lm = take(d->vocab > 0 ? (size_t)lmhead_partials_max(d->vocab) * 8 : 8);
+    w.ma = take(R * mla_a_cols(d) * 4);
+    w.mqa = take(is_mla(d) ? R * d->q_lora_rank * E : 0);
+    w.mc = take(is_mla(d) ? R * d->kv_lora_rank * E : 0);
+    w.marow = take((size_t)mla_a_cols(d) * 4);
     w.total = off;
     return w;
 }
@@ -143,9 +170,16 @@ vlm_status check_layers(const vlm_model_desc* d, const vlm_layer* L) {
     for (int l = 0; l < d->n_layers; l++) {
         const vlm_layer& y = L[l];
         vlm_status s;
-        if ((s = need(y.attn_norm, "attn_norm", l)) || (s = need(y.wqkv, "wqkv", l)) || (s = need(y.wo, "wo", l)) ||
+        if ((s = need(y.attn_norm, "attn_norm", l)) || (s = need(y.wo, "wo", l)) ||
             (s = need(y.mlp_norm, "mlp_norm", l)) || (s = need(y.w1, "w1", l)) || (s = need(y.w2, "w2", l)))
             return s;
+        if (is_mla(d)) {
+            if ((s = need(y.w_a, "w_a", l)) || (s = need(y.q_a_norm, "q_a_norm", l)) || (s = need(y.q_b, "q_b", l)) ||
+                (s = need(y.kv_a_norm, "kv_a_norm", l)) || (s = need(y.kv_b, "kv_b", l)))
+                return s;
+            continue;
+        }
+        if ((s = need(y.wqkv, "wqkv", l))) return s;
         if (d->qk_norm && ((s = need(y.q_norm, "q_norm", l)) || (s = need(y.k_norm, "k_norm", l)))) return s;
         if (d->block_kind == VLM_BLOCK_VIT) {
             if ((s = need(y.attn_norm_b, "attn_norm_b", l)) || (s = need(y.bqkv, "bqkv", l)) ||
@@ -190,9 +224,10 @@ struct vlm_kv {
     bool has_key = false;
     GraphKey key;
     int32_t* dlen() const { return (int32_t*)buf; }
-    size_t layer_bytes() const { return 2 * (size_t)desc.n_kv_heads * capacity * desc.head_dim * esize(desc.dtype); }
+    size_t k_bytes() const { return (size_t)desc.n_kv_heads * capacity * desc.head_dim * esize(desc.dtype); }
+    size_t layer_bytes() const { return k_bytes() + (size_t)desc.n_kv_heads * capacity * vdim(&desc) * esize(desc.dtype); }
     char* kptr(int l) const { return (char*)buf + kHeader + (size_t)l * layer_bytes(); }
-    char* vptr(int l) const { return kptr(l) + layer_bytes() / 2; }
+    char* vptr(int l) const { return kptr(l) + k_bytes(); }
     void drop_graph() {
         if (exec) hipGraphExecDestroy(exec);
         if (graph) hipGraphDestroy(graph);
@@ -209,10 +244,11 @@ const char* vlm_last_error(void) { return g_err.c_str(); }
 vlm_status vlm_kv_bytes(const vlm_model_desc* desc, int32_t capacity, size_t* bytes) {
     vlm_status s = check_desc(desc);
     if (s) return s;
-    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "KV cache is for decoder stacks");
+    if (desc->block_kind == VLM_BLOCK_VIT) return fail(VLM_ERR_ARG, "KV cache is for decoder stacks");
     if (capacity < 1) return fail(VLM_ERR_SHAPE, "capacity %d < 1", capacity);
     if (!bytes) return fail(VLM_ERR_ARG, "bytes is NULL");
-    *bytes = kHeader + (size_t)desc->n_layers * 2 * desc->n_kv_heads * capacity * desc->head_dim * esize(desc->dtype);
+    *bytes = kHeader + (size_t)desc->n_layers * desc->n_kv_heads * capacity * (desc->head_dim + vdim(desc)) *
+                           esize(desc->dtype);
     return ok();
 }
 
@@ -376,6 +412,8 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
             return fail(VLM_ERR_ARG, "mask %d: additive mask NULL or ld_add %d < %d", i, m.ld_add, pos0 + S);
         if (m.kind == VLM_MASK_SEGMENT && (!m.seg || pos0 != 0))
             return fail(VLM_ERR_ARG, "mask %d: segment mask needs seg ids and pos0 == 0", i);
+        if (is_mla(desc) && m.kind != VLM_MASK_CAUSAL && m.kind != VLM_MASK_ADDITIVE)
+            return fail(VLM_ERR_UNSUPPORTED, "mask %d: MLA prefill takes CAUSAL or ADDITIVE masks", i);
     }
     Ws w;
     if ((s = check_ws(desc, S, d_ws, ws_bytes, &w))) return s;
@@ -388,7 +426,8 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
     }
 
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
-    const int hd = desc->head_dim, QKV = qkv_rows(desc);
+    const int hd = desc->head_dim, dv = vdim(desc), QKV = qkv_rows(desc);
+    const bool mla = is_mla(desc);
     const size_t E = esize(dt);
     void* hbuf = P(d_ws, w.h);
     float* qkv = (float*)P(d_ws, w.qkv);
@@ -412,23 +451,53 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
         HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.attn_norm, y.attn_norm_b, desc->norm_eps, hbuf, stream));
         float* gpart = (float*)P(d_ws, w.gpart);
         GemmArgs g{};
-        g.A = hbuf; g.B = y.wqkv; g.bias = vit ? y.bqkv : nullptr; g.out = qkv; g.M = S; g.N = QKV; g.K = H; g.ldo = QKV;
-        g.part = gpart; g.part_cap = w.gpart_floats;
-        HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
-        RopeArgs r{};
-        r.qkv = qkv; r.S = S; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
-        r.interleave = desc->rope_interleave; r.norm_after = desc->qk_norm == 2;
-        r.qn = desc->qk_norm ? y.q_norm : nullptr; r.kn = desc->qk_norm ? y.k_norm : nullptr; r.eps = desc->norm_eps;
-        r.cos = d_cos; r.sin = d_sin; r.q = qb; r.ldq = S; r.kdst = kd; r.vdst = vd; r.ldkv = ldkv;
-        r.pos0 = pos0; r.pos_dev = nullptr;
-        HIP_TRY(launch_rope_qkv(dt, r, stream));
+        if (mla) {
+            // down-projections of q and kv in one GEMM, their latents normed, then the per-head expansions
+            const int AC = mla_a_cols(desc), qr = desc->q_lora_rank, rk = desc->kv_lora_rank;
+            float* ma = (float*)P(d_ws, w.ma);
+            void* mqa = P(d_ws, w.mqa);
+            void* mc = P(d_ws, w.mc);
+            float* mkv = qkv + (size_t)S * nq * hd;
+            g.A = hbuf; g.B = y.w_a; g.out = ma; g.M = S; g.N = AC; g.K = H; g.ldo = AC;
+            g.part = gpart; g.part_cap = w.gpart_floats;
+            HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
+            HIP_TRY(launch_norm_rows(dt, false, ma, S, qr, y.q_a_norm, nullptr, desc->norm_eps, mqa, stream, AC));
+            HIP_TRY(launch_norm_rows(dt, false, ma + qr, S, rk, y.kv_a_norm, nullptr, desc->norm_eps, mc, stream, AC));
+            g = GemmArgs{};
+            g.A = mqa; g.B = y.q_b; g.out = qkv; g.M = S; g.N = nq * hd; g.K = qr; g.ldo = nq * hd;
+            g.part = gpart; g.part_cap = w.gpart_floats;
+            HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
+            const int KVC = nq * (hd - desc->qk_rope_dim + dv);
+            g = GemmArgs{};
+            g.A = mc; g.B = y.kv_b; g.out = mkv; g.M = S; g.N = KVC; g.K = rk; g.ldo = KVC;
+            g.part = gpart; g.part_cap = w.gpart_floats;
+            HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
+            MlaRopeArgs r{};
+            r.q = qkv; r.kv = mkv; r.ka = ma; r.lda = AC; r.kcol = qr + rk;
+            r.S = S; r.nq = nq; r.d = hd; r.dr = desc->qk_rope_dim; r.dv = dv; r.interleave = desc->rope_interleave;
+            r.cos = d_cos; r.sin = d_sin; r.qout = qb; r.ldq = S; r.kdst = kd; r.vdst = vd; r.ldkv = ldkv;
+            r.pos0 = pos0; r.pos_dev = nullptr;
+            HIP_TRY(launch_mla_rope(dt, r, stream));
+        } else {
+            g.A = hbuf; g.B = y.wqkv; g.bias = vit ? y.bqkv : nullptr; g.out = qkv; g.M = S; g.N = QKV; g.K = H;
+            g.ldo = QKV; g.part = gpart; g.part_cap = w.gpart_floats;
+            HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
+            RopeArgs r{};
+            r.qkv = qkv; r.S = S; r.nq = nq; r.nkv = nkv; r.d = hd; r.segments = desc->rope_segments;
+            r.interleave = desc->rope_interleave; r.norm_after = desc->qk_norm == 2;
+            r.qn = desc->qk_norm ? y.q_norm : nullptr; r.kn = desc->qk_norm ? y.k_norm : nullptr;
+            r.eps = desc->norm_eps;
+            r.cos = d_cos; r.sin = d_sin; r.q = qb; r.ldq = S; r.kdst = kd; r.vdst = vd; r.ldkv = ldkv;
+            r.pos0 = pos0; r.pos_dev = nullptr;
+            HIP_TRY(launch_rope_qkv(dt, r, stream));
+        }
         AttnArgs at{};
         at.q = qb; at.ldq = S; at.k = kd; at.v = vd; at.ldkv = ldkv; at.out = ob;
-        at.S = S; at.nq = nq; at.nkv = nkv; at.d = hd; at.pos0 = pos0; at.nkeys = pos0 + S;
+        at.S = S; at.nq = nq; at.nkv = nkv; at.d = hd; at.dv = dv; at.pos0 = pos0; at.nkeys = pos0 + S;
         at.mask_kind = mk.kind; at.add = mk.add; at.ld_add = mk.ld_add; at.seg = mk.seg;
         HIP_TRY(launch_attn_prefill(dt, at, stream));
         g = GemmArgs{};
-        g.A = ob; g.B = y.wo; g.bias = vit ? y.bo : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = nq * hd; g.ldo = H;
+        g.A = ob; g.B = y.wo; g.bias = vit ? y.bo : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = nq * dv; g.ldo = H;
         g.part = gpart; g.part_cap = w.gpart_floats;
         HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
         HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.mlp_norm, y.mlp_norm_b, desc->norm_eps, hbuf, stream));
@@ -477,18 +546,57 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
                                  const float* cosv, const float* sinv, int32_t* tok_out, float* x_out, int32_t* hist,
                                  void* ws, const Ws& w, hipStream_t st) {
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
-    const int hd = desc->head_dim, QKV = qkv_rows(desc), W = kv->capacity;
+    const int hd = desc->head_dim, dv = vdim(desc), QKV = qkv_rows(desc), W = kv->capacity;
+    const bool mla = is_mla(desc);
     float* x = (float*)P(ws, w.xrow);
+    void* qrow = P(ws, w.qrow);
     float* qkv = (float*)P(ws, w.qkvrow);
     float* part = (float*)P(ws, w.part);
     void* orow = P(ws, w.orow);
     void* arow = P(ws, w.arow);
     const int nsplit = attn_decode_splits(W);
     float* rope = (float*)P(ws, w.rope);
-    HIP_TRY(launch_embed_or_copy(dt, embed, desc->vocab, H, tok_in, x_in, x, kv->dlen(), cosv, sinv, hd, rope, st));
+    HIP_TRY(launch_embed_or_copy(dt, embed, desc->vocab, H, tok_in, x_in, x, kv->dlen(), cosv, sinv,
+                                 mla ? desc->qk_rope_dim : hd, rope, st));
     for (int l = 0; l < desc->n_layers; l++) {
         const vlm_layer& y = L[l];
         GemvArgs g{};
+        if (mla) {
+            // q / kv down-projections of the normed row, the latents' norms fused into the expansions
+            const int AC = mla_a_cols(desc), qr = desc->q_lora_rank, rk = desc->kv_lora_rank;
+            float* ma = (float*)P(ws, w.marow);
+            float* mkv = qkv + (size_t)nq * hd;
+            g.W = y.w_a; g.vec = x; g.gain = y.attn_norm; g.eps = desc->norm_eps; g.out = ma; g.N = AC; g.K = H;
+            HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
+            g = GemvArgs{};
+            g.W = y.q_b; g.vec = ma; g.gain = y.q_a_norm; g.eps = desc->norm_eps; g.out = qkv; g.N = nq * hd; g.K = qr;
+            HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
+            g = GemvArgs{};
+            g.W = y.kv_b; g.vec = ma + qr; g.gain = y.kv_a_norm; g.eps = desc->norm_eps; g.out = mkv;
+            g.N = nq * (hd - desc->qk_rope_dim + dv); g.K = rk;
+            HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
+            MlaRopeArgs r{};
+            r.q = qkv; r.kv = mkv; r.ka = ma; r.lda = AC; r.kcol = qr + rk;
+            r.S = 1; r.nq = nq; r.d = hd; r.dr = desc->qk_rope_dim; r.dv = dv; r.interleave = desc->rope_interleave;
+            r.cos = cosv; r.sin = sinv; r.qout = qrow; r.ldq = 1; r.kdst = kv->kptr(l); r.vdst = kv->vptr(l);
+            r.ldkv = W; r.pos0 = 0; r.pos_dev = kv->dlen();
+            HIP_TRY(launch_mla_rope(dt, r, st));
+            DecAttnArgs at{};
+            at.qrot = qrow; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
+            at.dv = dv; at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
+            HIP_TRY(launch_attn_decode_mla(dt, at, st));
+            HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, dv, orow, st));
+            g = GemvArgs{};
+            g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * dv;
+            HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
+            g = GemvArgs{};
+            g.W = y.w1; g.vec = x; g.gain = y.mlp_norm; g.eps = desc->norm_eps; g.out = arow; g.N = 2 * F; g.K = H;
+            HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::SwiGLU, g, st));
+            g = GemvArgs{};
+            g.W = y.w2; g.vec = arow; g.out = x; g.N = H; g.K = F;
+            HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
+            continue;
+        }
         g.W = y.wqkv; g.vec = x; g.gain = y.attn_norm; g.eps = desc->norm_eps; g.out = qkv; g.N = QKV; g.K = H;
         HIP_TRY(launch_gemv(dt, Pro::RmsNorm, Epi::StoreF32, g, st));
         DecAttnArgs at{};
@@ -526,7 +634,7 @@ static vlm_status check_decode(const vlm_model_desc* desc, const vlm_layer* L, c
                                void* ws, size_t ws_bytes, int steps, Ws* w) {
     vlm_status s = check_desc(desc);
     if (s) return s;
-    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decode needs a decoder stack");
+    if (desc->block_kind == VLM_BLOCK_VIT) return fail(VLM_ERR_ARG, "decode needs a decoder stack");
     if (!kv) return fail(VLM_ERR_ARG, "kv is NULL");
     if (memcmp(&kv->desc, desc, sizeof(*desc)) != 0) return fail(VLM_ERR_ARG, "KV cache bound to another model desc");
     if ((long)kv->len + steps > kv->capacity)
@@ -702,7 +810,7 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
                              hipStream_t stream) {
     vlm_status s = check_desc(desc);
     if (s) return s;
-    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decoder kernels only");
+    if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decoder (GQA) kernels only");
     if (which < VLM_KERNEL_LMHEAD || which > VLM_KERNEL_ATTN) return fail(VLM_ERR_ARG, "which %d", which);
     if (n_launches < 0) return fail(VLM_ERR_SHAPE, "n_launches < 0");
     if (!d_x_row) return fail(VLM_ERR_ARG, "d_x_row is NULL");

@@ -59,7 +59,7 @@ hipError_t launch_argmax_final(const unsigned long long* partials, int nblocks, 
 // Row norms producing the GEMM operand (model type): RMSNorm (shift == null, layer == false)
 // or LayerNorm (layer == true, shift may be null).
 hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H, const void* gain, const void* shift,
-                            float eps, void* out, hipStream_t st);
+                            float eps, void* out, hipStream_t st, int ldx = 0);  // ldx: row stride of x (0: H)
 
 // qkv fp32 [S][(nq+2nkv)*d] -> q' [nq][ldq][d] (model type), K/V rows written to
 // kdst/vdst [nkv][ldkv][d] at slot base+s, base = pos_dev ? *pos_dev : pos0.
@@ -77,14 +77,30 @@ struct RopeArgs {
 };
 hipError_t launch_rope_qkv(int dtype, const RopeArgs& a, hipStream_t st);
 
-// Prefill flash attention. q [nq][ldq][d], k/v [nkv][ldkv][d]; keys 0..nkeys-1;
-// query row s has position pos0+s; out [S][nq*d] (model type).
+// Expanded MLA heads: q [S][nq*d] and kv [S][nq*(dn + dv)] fp32 projections (per head
+// [q_nope | q_rope] and [k_nope | v]), the shared rotated key at column kcol of ka [S][lda];
+// writes q' [nq][ldq][d] (model type) and the K [nq][ldkv][d] / V [nq][ldkv][dv] cache rows of
+// slot base+s, k = [k_nope | RoPE(k_rope)]. cos/sin rows are dr wide.
+struct MlaRopeArgs {
+    const float* q; const float* kv; const float* ka;
+    int lda, kcol;
+    int S, nq, d, dr, dv, interleave;
+    const float* cos; const float* sin;
+    void* qout; int ldq;
+    void* kdst; void* vdst; int ldkv;
+    int pos0; const int32_t* pos_dev;
+};
+hipError_t launch_mla_rope(int dtype, const MlaRopeArgs& a, hipStream_t st);
+
+// Prefill flash attention. q [nq][ldq][d], k [nkv][ldkv][d], v [nkv][ldkv][dv]; keys
+// 0..nkeys-1; query row s has position pos0+s; out [S][nq*dv] (model type). dv = 0 means d.
 struct AttnArgs {
     const void* q; int ldq;
     const void* k; const void* v; int ldkv;
     void* out;
     int S, nq, nkv, d, pos0, nkeys;
     int mask_kind; const float* add; int ld_add; const int32_t* seg;
+    int dv = 0;
 };
 hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 
@@ -102,6 +118,8 @@ struct DecAttnArgs {
     const void* qn; const void* kn; float eps;
     const float* rope; int segments;  // cos[d] then sin[d] of position len (staged by the embed kernel)
     int interleave, norm_after;       // as in RopeArgs
+    const void* qrot = nullptr;       // expanded MLA: the rotated q [nq][d] (model type), k/v already in slot t
+    int dv = 0;                       // expanded MLA: value width (partial rows dv + 4)
     void* kc; void* vc;  // layer K and V, [nkv][W][d]
     int W, nq, nkv, d;
     const int32_t* len;
@@ -109,6 +127,8 @@ struct DecAttnArgs {
     float* partial;      // [nq][nsplit][d + 4]
 };
 hipError_t launch_attn_decode_fused(int dtype, const DecAttnArgs& a, hipStream_t st);
+// Expanded MLA decode attention (d 192, dv 128, nq == nkv): reads a.qrot and the cache only.
+hipError_t launch_attn_decode_mla(int dtype, const DecAttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
                                hipStream_t st);
 

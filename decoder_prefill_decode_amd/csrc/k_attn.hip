@@ -39,12 +39,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // tiles is staged per iteration), which halves the sequential key chain of
 // the longest (last, causal) row block; their (m, l, O) merge through LDS at
 // the end.
-template <int D, int MASK>
+// DQ: width of q and k rows, DV: width of v and output rows (equal except for expanded MLA).
+template <int DQ, int DV, int MASK>
 __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     constexpr int BQ = 64, BKEY = 64;
-    constexpr int DK = D / 16, NB = (D + 31) / 32, DP = NB * 32;
-    constexpr int LDK = D + 8, LDV = BKEY + 8;
-    constexpr int CH = D / 8;  // 16-byte chunks per key row
+    constexpr int DK = DQ / 16, NB = (DV + 31) / 32, DP = NB * 32;
+    constexpr int LDK = DQ + 8, LDV = BKEY + 8;
+    constexpr int CH = DQ / 8, CHV = DV / 8;  // 16-byte chunks per key / value row
     constexpr int KSZ = BKEY * LDK, VSZ = DP * LDV;                 // elements of one K / V^T tile
     constexpr int MRG = NB * 16 + 2;                                // floats per lane in the final merge
     constexpr int TILE_BYTES = 2 * (KSZ + VSZ) * 2, MRG_BYTES = 2 * 64 * MRG * 4;
@@ -58,20 +59,20 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     const int q0 = blockIdx.x * BQ + rg * 32;
     const int qrow = q0 + l32;
     const int S = a.S;
-    const bf16_t* Q = (const bf16_t*)a.q + (size_t)hq * a.ldq * D;
-    const bf16_t* Kg = (const bf16_t*)a.k + (size_t)g * a.ldkv * D;
-    const bf16_t* Vg = (const bf16_t*)a.v + (size_t)g * a.ldkv * D;
+    const bf16_t* Q = (const bf16_t*)a.q + (size_t)hq * a.ldq * DQ;
+    const bf16_t* Kg = (const bf16_t*)a.k + (size_t)g * a.ldkv * DQ;
+    const bf16_t* Vg = (const bf16_t*)a.v + (size_t)g * a.ldkv * DV;
 
-    for (int i = tid; i < (DP - D) * LDV; i += 256) {
-        Vt[D * LDV + i] = 0;
-        Vt[VSZ + D * LDV + i] = 0;
+    for (int i = tid; i < (DP - DV) * LDV; i += 256) {
+        Vt[DV * LDV + i] = 0;
+        Vt[VSZ + DV * LDV + i] = 0;
     }
 
     bf16x8 Qf[DK];
 #pragma unroll
     for (int kk = 0; kk < DK; kk++) {
         if (qrow < S) {
-            Qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * D + kk * 16 + hh * 8);
+            Qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * DQ + kk * 16 + hh * 8);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; i++) Qf[kk][i] = (__bf16)0.0f;
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[nb][r] = 0.f;
     float m = -INFINITY, l = 0.f;
-    const float scale = kLog2e / sqrtf((float)D);
+    const float scale = kLog2e / sqrtf((float)DQ);
 
     int kend = a.nkeys;
     if (MASK == VLM_MASK_CAUSAL_ID) {
@@ -99,13 +100,13 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     // each transposed LDS store writes two keys of one dimension as a dword, 32 lanes to 32
     // consecutive dwords.
     constexpr int TCH = (BKEY * CH + 255) / 256;        // 16-byte chunks of the K tile per thread
-    constexpr int NVP = (BKEY / 2) * CH, VP = (NVP + 255) / 256;  // (key pair, chunk) items of the V tile
+    constexpr int NVP = (BKEY / 2) * CHV, VP = (NVP + 255) / 256;  // (key pair, chunk) items of the V tile
     auto request = [&](int kt, u32x4 (&kreg)[TCH], u32x4 (&vreg)[VP][2]) {
 #pragma unroll
         for (int i = 0; i < TCH; i++) {
             const int c = min(tid + 256 * i, BKEY * CH - 1), r = c / CH, d0 = (c % CH) * 8;
             const int key = min(kt * BKEY + r, a.nkeys - 1);
-            kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + d0);
+            kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * DQ + d0);
         }
 #pragma unroll
         for (int i = 0; i < VP; i++) {
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 const int key = min(kt * BKEY + 2 * kp + u, a.nkeys - 1);
-                vreg[i][u] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + d0);
+                vreg[i][u] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * DV + d0);
             }
         }
     };
@@ -280,24 +281,24 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     }
     if (qrow < S) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
-        bf16_t* O = (bf16_t*)a.out + (size_t)qrow * a.nq * D + (size_t)hq * D;
+        bf16_t* O = (bf16_t*)a.out + (size_t)qrow * a.nq * DV + (size_t)hq * DV;
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int n = nb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
-                if (n < D) O[n] = f2bf(oacc[nb][r] * inv);
+                if (n < DV) O[n] = f2bf(oacc[nb][r] * inv);
             }
     }
 }
 
 // ============================================================== prefill, f32
-template <int D, int MASK>
+template <int DQ, int DV, int MASK>
 __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
-    constexpr int BQ = 128, KB = D >= 128 ? 1 : 2, BKEY = 32 * KB;
-    constexpr int NB = (D + 31) / 32, DP = NB * 32;
-    constexpr int LDK = D + 4, LDV = DP + 4;
-    constexpr int CH = D / 4;
+    constexpr int BQ = 128, KB = DQ >= 128 ? 1 : 2, BKEY = 32 * KB;
+    constexpr int NB = (DV + 31) / 32, DP = NB * 32;
+    constexpr int LDK = DQ + 4, LDV = DP + 4;
+    constexpr int CH = DQ / 4, CHV = DV / 4;
     __shared__ __attribute__((aligned(16))) float Ks[BKEY * LDK];
     __shared__ __attribute__((aligned(16))) float Vs[BKEY * LDV];
 
@@ -306,24 +307,24 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     const int q0 = blockIdx.x * BQ + w * 32;
     const int qrow = q0 + l32;
     const int S = a.S;
-    const float* Q = (const float*)a.q + (size_t)hq * a.ldq * D;
-    const float* Kg = (const float*)a.k + (size_t)g * a.ldkv * D;
-    const float* Vg = (const float*)a.v + (size_t)g * a.ldkv * D;
+    const float* Q = (const float*)a.q + (size_t)hq * a.ldq * DQ;
+    const float* Kg = (const float*)a.k + (size_t)g * a.ldkv * DQ;
+    const float* Vg = (const float*)a.v + (size_t)g * a.ldkv * DV;
 
-    if constexpr (DP > D) {
-        for (int i = tid; i < BKEY * (DP - D); i += 256) Vs[(i / (DP - D)) * LDV + D + i % (DP - D)] = 0.f;
+    if constexpr (DP > DV) {
+        for (int i = tid; i < BKEY * (DP - DV); i += 256) Vs[(i / (DP - DV)) * LDV + DV + i % (DP - DV)] = 0.f;
     }
 
-    float Qf[D / 2];
+    float Qf[DQ / 2];
 #pragma unroll
-    for (int kk = 0; kk < D / 2; kk++) Qf[kk] = qrow < S ? Q[(size_t)qrow * D + kk * 2 + hh] : 0.f;
+    for (int kk = 0; kk < DQ / 2; kk++) Qf[kk] = qrow < S ? Q[(size_t)qrow * DQ + kk * 2 + hh] : 0.f;
     f32x16 oacc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; nb++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[nb][r] = 0.f;
     float m = -INFINITY, l = 0.f;
-    const float scale = kLog2e / sqrtf((float)D);
+    const float scale = kLog2e / sqrtf((float)DQ);
 
     int kend = a.nkeys;
     if (MASK == VLM_MASK_CAUSAL_ID) {
@@ -338,12 +339,15 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
         for (int c = tid; c < BKEY * CH; c += 256) {
             const int r = c / CH, d0 = (c % CH) * 4;
             const int key = key0 + r;
-            f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (key < a.nkeys) {
-                kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)key * D + d0);
-                vv = *reinterpret_cast<const f32x4*>(Vg + (size_t)key * D + d0);
-            }
+            f32x4 kv = {0.f, 0.f, 0.f, 0.f};
+            if (key < a.nkeys) kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)key * DQ + d0);
             *reinterpret_cast<f32x4*>(Ks + r * LDK + d0) = kv;
+        }
+        for (int c = tid; c < BKEY * CHV; c += 256) {
+            const int r = c / CHV, d0 = (c % CHV) * 4;
+            const int key = key0 + r;
+            f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+            if (key < a.nkeys) vv = *reinterpret_cast<const f32x4*>(Vg + (size_t)key * DV + d0);
             *reinterpret_cast<f32x4*>(Vs + r * LDV + d0) = vv;
         }
         __syncthreads();
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                 for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
                 const float* kr = Ks + (kb * 32 + l32) * LDK + hh;
 #pragma unroll
-                for (int kk = 0; kk < D / 2; kk++)
+                for (int kk = 0; kk < DQ / 2; kk++)
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[kk * 2], Qf[kk], sacc[kb], 0, 0, 0);
             }
             float mt = -INFINITY;
@@ -417,50 +421,57 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     }
     if (qrow < S) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
-        float* O = (float*)a.out + (size_t)qrow * a.nq * D + (size_t)hq * D;
+        float* O = (float*)a.out + (size_t)qrow * a.nq * DV + (size_t)hq * DV;
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int n = nb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
-                if (n < D) O[n] = oacc[nb][r] * inv;
+                if (n < DV) O[n] = oacc[nb][r] * inv;
             }
     }
 }
 
-template <int D, int MASK>
+template <int DQ, int DV, int MASK>
 static hipError_t run_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.S + 127) / 128, a.nq);
     if (dtype == 1) {
-        if constexpr (D % 16 == 0) {
-            attn_prefill_bf16<D, MASK><<<dim3((a.S + 63) / 64, a.nq), 256, 0, st>>>(a);
+        if constexpr (DQ % 16 == 0 && DV % 16 == 0) {
+            attn_prefill_bf16<DQ, DV, MASK><<<dim3((a.S + 63) / 64, a.nq), 256, 0, st>>>(a);
         } else {
             return hipErrorInvalidValue;
         }
     } else {
-        attn_prefill_f32<D, MASK><<<grid, 256, 0, st>>>(a);
+        attn_prefill_f32<DQ, DV, MASK><<<grid, 256, 0, st>>>(a);
     }
     return hipGetLastError();
 }
 
-template <int D>
+template <int DQ, int DV>
 static hipError_t prefill_mask(int dtype, const AttnArgs& a, hipStream_t st) {
     switch (a.mask_kind) {
-        case VLM_MASK_CAUSAL_ID: return run_prefill<D, VLM_MASK_CAUSAL_ID>(dtype, a, st);
-        case VLM_MASK_NONE_ID: return run_prefill<D, VLM_MASK_NONE_ID>(dtype, a, st);
-        case VLM_MASK_ADDITIVE_ID: return run_prefill<D, VLM_MASK_ADDITIVE_ID>(dtype, a, st);
-        case VLM_MASK_SEGMENT_ID: return run_prefill<D, VLM_MASK_SEGMENT_ID>(dtype, a, st);
+        case VLM_MASK_CAUSAL_ID: return run_prefill<DQ, DV, VLM_MASK_CAUSAL_ID>(dtype, a, st);
+        case VLM_MASK_NONE_ID: return run_prefill<DQ, DV, VLM_MASK_NONE_ID>(dtype, a, st);
+        case VLM_MASK_ADDITIVE_ID: return run_prefill<DQ, DV, VLM_MASK_ADDITIVE_ID>(dtype, a, st);
+        case VLM_MASK_SEGMENT_ID: return run_prefill<DQ, DV, VLM_MASK_SEGMENT_ID>(dtype, a, st);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     if (a.S <= 0) return hipSuccess;
+    const int dv = a.dv > 0 ? a.dv : a.d;
+    if (dv != a.d) {  // expanded MLA heads: keys 192 wide (128 + 64 rotated), values 128
+        if (a.d == 192 && dv == 128 && (a.mask_kind == VLM_MASK_CAUSAL_ID || a.mask_kind == VLM_MASK_ADDITIVE_ID))
+            return a.mask_kind == VLM_MASK_CAUSAL_ID ? run_prefill<192, 128, VLM_MASK_CAUSAL_ID>(dtype, a, st)
+                                                     : run_prefill<192, 128, VLM_MASK_ADDITIVE_ID>(dtype, a, st);
+        return hipErrorInvalidValue;
+    }
     switch (a.d) {
-        case 64: return prefill_mask<64>(dtype, a, st);
-        case 72: return prefill_mask<72>(dtype, a, st);
-        case 80: return prefill_mask<80>(dtype, a, st);
-        case 128: return prefill_mask<128>(dtype, a, st);
+        case 64: return prefill_mask<64, 64>(dtype, a, st);
+        case 72: return prefill_mask<72, 72>(dtype, a, st);
+        case 80: return prefill_mask<80, 80>(dtype, a, st);
+        case 128: return prefill_mask<128, 128>(dtype, a, st);
     }
     return hipErrorInvalidValue;
 }
@@ -803,6 +814,179 @@ static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
         case 8: attn_decode_fused_kernel<T, D, 8, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// ============================================================== decode, expanded MLA
+// Keys DQ wide, values DV wide, one KV head per query head. The assembly
+// kernel (launch_mla_rope) has already written this token's rotated q into
+// a.qrot and its key and value into slot t, so this kernel only reads: one
+// block of NW wavefronts per (head, split) as in attn_decode_fused_kernel,
+// each 16-lane quarter scoring one key per step, partial rows of DV + 4
+// floats merged by attn_combine_fast_kernel.
+template <class T, int DQ, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_mla_kernel(DecAttnArgs a) {
+    constexpr int VEC = 16 / sizeof(T), CHK = DQ / VEC, CHV = DV / VEC;
+    constexpr int CPK = (CHK + 15) / 16, CPV = (CHV + 15) / 16, KSTEP = NW * 4, NB = kDecSteps;
+    constexpr int PS = DV + 4;
+    __shared__ float qs[DQ];
+    __shared__ float sm_m[NW], sm_l[NW];
+    __shared__ float sm_o[NW][DV];
+    const int g = blockIdx.x, sp = blockIdx.y;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
+    const int chunk = (a.W + a.nsplit - 1) / a.nsplit;
+    const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
+    const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;
+    const T* Kg = (const T*)a.kc + (size_t)g * a.W * DQ;
+    const T* Vg = (const T*)a.vc + (size_t)g * a.W * DV;
+    const int jl = max(kend - 1, 0);
+    u32x4 kr[NB][CPK], vr[NB][CPV];
+    const int jw = k0 + w * 4 + kq;
+    auto request = [&](int s0) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            if (s0 + b < nst) {  // uniform over the block
+                const int j = min(jw + (s0 + b) * KSTEP, jl);
+#pragma unroll
+                for (int c = 0; c < CPK; c++)
+                    kr[b][c] = *reinterpret_cast<const u32x4*>(Kg + (size_t)j * DQ + min(sub + 16 * c, CHK - 1) * VEC);
+#pragma unroll
+                for (int c = 0; c < CPV; c++)
+                    vr[b][c] = *reinterpret_cast<const u32x4*>(Vg + (size_t)j * DV + min(sub + 16 * c, CHV - 1) * VEC);
+            }
+        }
+    };
+    request(0);
+    const T* qh = (const T*)a.qrot + (size_t)g * DQ;
+    for (int e = tid; e < DQ; e += NW * kWave) qs[e] = Elt<T>::ld(qh, e);
+    const int t = a.len[0];
+    const int k1 = min(t + 1, kend);
+    __syncthreads();
+    float qf[CPK][VEC];
+#pragma unroll
+    for (int c = 0; c < CPK; c++) {
+        const int ch = min(sub + 16 * c, CHK - 1);
+#pragma unroll
+        for (int i = 0; i < VEC; i++) qf[c][i] = sub + 16 * c < CHK ? qs[ch * VEC + i] : 0.f;
+    }
+    const float scale = kLog2e / sqrtf((float)DQ);
+    float mrun = -INFINITY, lrun = 0.f, o[CPV][VEC];
+#pragma unroll
+    for (int c = 0; c < CPV; c++)
+#pragma unroll
+        for (int i = 0; i < VEC; i++) o[c][i] = 0.f;
+    for (int s0 = 0; s0 < nst; s0 += NB) {
+        if (s0 > 0) request(s0);
+        float sc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            const int j = jw + (s0 + b) * KSTEP;
+            const bool valid = s0 + b < nst && j < k1;
+            if (s0 + b >= nst) {  // uniform: a step past the slot range
+                sc[b] = -INFINITY;
+#pragma unroll
+                for (int c = 0; c < CPV; c++) vr[b][c] = u32x4{0, 0, 0, 0};
+                continue;
+            }
+            if (!valid) {  // clamped rows hold arbitrary bits: weight 0 must not meet NaN
+#pragma unroll
+                for (int c = 0; c < CPV; c++) vr[b][c] = u32x4{0, 0, 0, 0};
+            }
+            float sv = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPK; c++) {
+                float kf[VEC];
+                unpack16(kr[b][c], (const T*)nullptr, kf);
+#pragma unroll
+                for (int i = 0; i < VEC; i++) sv = fmaf(qf[c][i], kf[i], sv);
+            }
+            sv = row16_sum(sv);
+            sc[b] = valid ? sv * scale : -INFINITY;
+        }
+        float mb = sc[0];
+#pragma unroll
+        for (int b = 1; b < NB; b++)
+            if (s0 + b < nst) mb = fmaxf(mb, sc[b]);
+        if (mb == -INFINITY) continue;
+        const float mn = fmaxf(mrun, mb);
+        const float alpha = exp2f(mrun - mn);
+        lrun *= alpha;
+        mrun = mn;
+#pragma unroll
+        for (int c = 0; c < CPV; c++)
+#pragma unroll
+            for (int i = 0; i < VEC; i++) o[c][i] *= alpha;
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            if (s0 + b >= nst) break;  // uniform
+            const float pb = exp2f(sc[b] - mn);
+            lrun += pb;
+#pragma unroll
+            for (int c = 0; c < CPV; c++) {
+                float vf[VEC];
+                unpack16(vr[b][c], (const T*)nullptr, vf);
+#pragma unroll
+                for (int i = 0; i < VEC; i++) o[c][i] = fmaf(pb, vf[i], o[c][i]);
+            }
+        }
+    }
+    // merge the quarters (l, l^16 then l, l^32), then the wavefronts
+#pragma unroll
+    for (int lvl = 0; lvl < 2; lvl++) {
+        const LanePair m2 = lvl ? swap32(mrun) : swap16(mrun);
+        const LanePair l2 = lvl ? swap32(lrun) : swap16(lrun);
+        const float mn = fmaxf(m2.lo, m2.hi);
+        const float fa = mn == -INFINITY ? 0.f : exp2f(m2.lo - mn);
+        const float fb = mn == -INFINITY ? 0.f : exp2f(m2.hi - mn);
+        lrun = l2.lo * fa + l2.hi * fb;
+#pragma unroll
+        for (int c = 0; c < CPV; c++)
+#pragma unroll
+            for (int i = 0; i < VEC; i++) {
+                const LanePair o2 = lvl ? swap32(o[c][i]) : swap16(o[c][i]);
+                o[c][i] = o2.lo * fa + o2.hi * fb;
+            }
+        mrun = mn;
+    }
+    if (kq == 0) {
+#pragma unroll
+        for (int c = 0; c < CPV; c++) {
+            const int ch = sub + 16 * c;
+            if (ch < CHV)
+#pragma unroll
+                for (int i = 0; i < VEC; i++) sm_o[w][ch * VEC + i] = o[c][i];
+        }
+        if (sub == 0) {
+            sm_m[w] = mrun;
+            sm_l[w] = lrun;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < DV + 2; e += NW * kWave) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ww++) mx = fmaxf(mx, sm_m[ww]);
+        float v = 0.f;
+        if (e == DV) {
+            v = mx;
+        } else {
+#pragma unroll
+            for (int ww = 0; ww < NW; ww++) {
+                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[ww] - mx);
+                v += f * (e < DV ? sm_o[ww][e] : sm_l[ww]);
+            }
+        }
+        a.partial[((size_t)g * a.nsplit + sp) * PS + e] = v;
+    }
+}
+
+hipError_t launch_attn_decode_mla(int dtype, const DecAttnArgs& a, hipStream_t st) {
+    if (a.d != 192 || a.dv != 128 || a.nq != a.nkv || !a.qrot) return hipErrorInvalidValue;
+    const dim3 grid(a.nkv, a.nsplit);
+    if (dtype == 1)
+        attn_decode_mla_kernel<bf16_t, 192, 128, 4><<<grid, 4 * 64, 0, st>>>(a);
+    else
+        attn_decode_mla_kernel<float, 192, 128, 4><<<grid, 4 * 64, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -92,10 +92,11 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__
 // RMSNorm: y = x * rsqrt(mean(x^2) + eps) * g. LayerNorm: y = (x - mu) * rsqrt(var + eps) * g + b.
 // Output rounded to the operand type. One block per row.
 template <class T, bool LAYER>
-__global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict__ x, int H, const T* __restrict__ g,
-                                                        const T* __restrict__ b, float eps, T* __restrict__ out) {
+__global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict__ x, int H, int ldx,
+                                                        const T* __restrict__ g, const T* __restrict__ b, float eps,
+                                                        T* __restrict__ out) {
     __shared__ float red[4];
-    const float* row = x + (size_t)blockIdx.x * H;
+    const float* row = x + (size_t)blockIdx.x * ldx;
     float mu = 0.f;
     if (LAYER) {
         float s = 0.f;
@@ -173,6 +174,52 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
     T* dst = isq ? (T*)a.q + ((size_t)h * a.ldq + s) * d : (T*)a.kdst + ((size_t)(h - a.nq) * a.ldkv + pos) * d;
     Elt<T>::st(dst, i0, y0);
     Elt<T>::st(dst, i1, y1);
+}
+
+// ---------------------------------------------------------------- expanded MLA: assembly + RoPE + cache write
+// One wavefront per (row, head). The dn unrotated elements of q and k are
+// copied, v is copied, and rotation pair j (j < dr/2) of the rope parts turns
+// the inputs at (2j, 2j+1) (interleaved) or (j, j + dr/2) into the outputs at
+// dn + j and dn + j + dr/2 with the angle of table column j. The rotated key
+// is the shared one of the row, the same for every head.
+template <class T>
+__global__ __launch_bounds__(256) void mla_rope_kernel(MlaRopeArgs a) {
+    const int wave = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (wave >= a.S * a.nq) return;
+    const int s = wave / a.nq, h = wave % a.nq;
+    const int d = a.d, dr = a.dr, dn = d - dr, dv = a.dv, hr = dr / 2;
+    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + s;
+    const float* qi = a.q + (size_t)s * a.nq * d + (size_t)h * d;
+    const float* kvi = a.kv + (size_t)s * a.nq * (dn + dv) + (size_t)h * (dn + dv);
+    const float* kr = a.ka + (size_t)s * a.lda + a.kcol;
+    T* qo = (T*)a.qout + ((size_t)h * a.ldq + s) * d;
+    T* ko = (T*)a.kdst + ((size_t)h * a.ldkv + pos) * d;
+    T* vo = (T*)a.vdst + ((size_t)h * a.ldkv + pos) * dv;
+    for (int e = lane; e < dn; e += kWave) {
+        Elt<T>::st(qo, e, qi[e]);
+        Elt<T>::st(ko, e, kvi[e]);
+    }
+    for (int e = lane; e < dv; e += kWave) Elt<T>::st(vo, e, kvi[dn + e]);
+    for (int j = lane; j < hr; j += kWave) {
+        const int r0 = a.interleave ? 2 * j : j, r1 = a.interleave ? 2 * j + 1 : j + hr;
+        const float c = a.cos[(size_t)pos * dr + j], sn = a.sin[(size_t)pos * dr + j];
+        const float q0 = qi[dn + r0], q1 = qi[dn + r1], k0 = kr[r0], k1 = kr[r1];
+        Elt<T>::st(qo, dn + j, q0 * c - q1 * sn);
+        Elt<T>::st(qo, dn + j + hr, q1 * c + q0 * sn);
+        Elt<T>::st(ko, dn + j, k0 * c - k1 * sn);
+        Elt<T>::st(ko, dn + j + hr, k1 * c + k0 * sn);
+    }
+}
+
+hipError_t launch_mla_rope(int dtype, const MlaRopeArgs& a, hipStream_t st) {
+    const int waves = a.S * a.nq;
+    if (waves <= 0) return hipSuccess;
+    const int blocks = (waves + 3) / 4;
+    if (dtype == 1)
+        mla_rope_kernel<bf16_t><<<blocks, 256, 0, st>>>(a);
+    else
+        mla_rope_kernel<float><<<blocks, 256, 0, st>>>(a);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- RoPE tables
@@ -276,18 +323,19 @@ hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st) 
 }
 
 hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H, const void* gain, const void* shift,
-                            float eps, void* out, hipStream_t st) {
+                            float eps, void* out, hipStream_t st, int ldx) {
+    if (ldx <= 0) ldx = H;
     if (R <= 0) return hipSuccess;
     if (dtype == 1) {
         if (layer)
-            norm_rows_kernel<bf16_t, true><<<R, 256, 0, st>>>(x, H, (const bf16_t*)gain, (const bf16_t*)shift, eps, (bf16_t*)out);
+            norm_rows_kernel<bf16_t, true><<<R, 256, 0, st>>>(x, H, ldx, (const bf16_t*)gain, (const bf16_t*)shift, eps, (bf16_t*)out);
         else
-            norm_rows_kernel<bf16_t, false><<<R, 256, 0, st>>>(x, H, (const bf16_t*)gain, nullptr, eps, (bf16_t*)out);
+            norm_rows_kernel<bf16_t, false><<<R, 256, 0, st>>>(x, H, ldx, (const bf16_t*)gain, nullptr, eps, (bf16_t*)out);
     } else {
         if (layer)
-            norm_rows_kernel<float, true><<<R, 256, 0, st>>>(x, H, (const float*)gain, (const float*)shift, eps, (float*)out);
+            norm_rows_kernel<float, true><<<R, 256, 0, st>>>(x, H, ldx, (const float*)gain, (const float*)shift, eps, (float*)out);
         else
-            norm_rows_kernel<float, false><<<R, 256, 0, st>>>(x, H, (const float*)gain, nullptr, eps, (float*)out);
+            norm_rows_kernel<float, false><<<R, 256, 0, st>>>(x, H, ldx, (const float*)gain, nullptr, eps, (float*)out);
     }
     return hipGetLastError();
 }

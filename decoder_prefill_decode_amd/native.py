@@ -16,7 +16,7 @@ STATUS_NAMES = {0: "VLM_OK", -1: "VLM_ERR_ARG", -2: "VLM_ERR_SHAPE", -3: "VLM_ER
                 -4: "VLM_ERR_COUNT_MISMATCH", -5: "VLM_ERR_DTYPE", -6: "VLM_ERR_NONFINITE", -7: "VLM_ERR_HIP",
                 -8: "VLM_ERR_UNSUPPORTED", -9: "VLM_ERR_WORKSPACE"}
 VLM_F32, VLM_BF16 = 0, 1
-VLM_BLOCK_DECODER, VLM_BLOCK_VIT = 0, 1
+VLM_BLOCK_DECODER, VLM_BLOCK_VIT, VLM_BLOCK_MLA = 0, 1, 2
 VLM_MASK_CAUSAL, VLM_MASK_NONE, VLM_MASK_ADDITIVE, VLM_MASK_SEGMENT = 0, 1, 2, 3
 KV_HEADER_BYTES = 256
 
@@ -31,12 +31,15 @@ class ModelDesc(C.Structure):
     _fields_ = [("block_kind", C.c_int32), ("n_layers", C.c_int32), ("hidden", C.c_int32),
                 ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("vocab", C.c_int32), ("dtype", C.c_int32), ("qk_norm", C.c_int32),
-                ("rope_segments", C.c_int32), ("norm_eps", C.c_float), ("rope_interleave", C.c_int32)]
+                ("rope_segments", C.c_int32), ("norm_eps", C.c_float), ("rope_interleave", C.c_int32),
+                ("q_lora_rank", C.c_int32), ("kv_lora_rank", C.c_int32), ("qk_rope_dim", C.c_int32),
+                ("v_head_dim", C.c_int32)]
 
 
 class Layer(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "attn_norm_b", "wqkv", "bqkv", "q_norm", "k_norm", "wo",
-                                          "bo", "mlp_norm", "mlp_norm_b", "w1", "b1", "w2", "b2")]
+                                          "bo", "mlp_norm", "mlp_norm_b", "w1", "b1", "w2", "b2",
+                                          "w_a", "q_a_norm", "q_b", "kv_a_norm", "kv_b")]
 
 
 class Mask(C.Structure):

@@ -22,17 +22,21 @@ class DecoderRun:
 
     def __init__(self, cfg, layer_weights, glob):
         self.cfg = cfg
+        mla = getattr(cfg, "kv_lora_rank", 0) > 0
         m = Model(n_layers=cfg.n_layers, hidden=cfg.hidden, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
                   head_dim=cfg.head_dim, ffn=cfg.ffn, vocab=cfg.vocab, dtype=cfg.dtype, qk_norm=int(cfg.qk_norm),
-                  eps=cfg.eps, rope_interleave=getattr(cfg, "rope_interleave", False))
+                  eps=cfg.eps, rope_interleave=getattr(cfg, "rope_interleave", False),
+                  block_kind=N.VLM_BLOCK_MLA if mla else N.VLM_BLOCK_DECODER,
+                  q_lora_rank=cfg.q_lora_rank if mla else 0, kv_lora_rank=cfg.kv_lora_rank if mla else 0,
+                  qk_rope_dim=cfg.qk_rope_dim if mla else 0, v_head_dim=cfg.v_head_dim if mla else 0)
         for l in range(cfg.n_layers):
-            m.set_decoder_layer(l, layer_weights(l))
+            (m.set_mla_layer if mla else m.set_decoder_layer)(l, layer_weights(l))
         if cfg.vocab > 0:
             m.set_table(glob["embed"], glob["final_norm"])
         self.model = m
         self.kv = KVCache(m, cfg.capacity)
         self.ws = m.workspace(cfg.seq)
-        self.cos, self.sin = text_rope(cfg.capacity, cfg.head_dim, cfg.theta)
+        self.cos, self.sin = text_rope(cfg.capacity, cfg.qk_rope_dim if mla else cfg.head_dim, cfg.theta)
         self.glob = glob
         H = cfg.hidden
         self.x = torch.empty((cfg.seq, H), dtype=torch.float32, device="cuda")

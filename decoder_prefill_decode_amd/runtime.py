@@ -34,11 +34,14 @@ class Model:
     """Model description + per-layer weights resident in HBM."""
 
     def __init__(self, *, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab=0, dtype="f32",
-                 qk_norm=0, rope_segments=1, eps=1e-6, block_kind=N.VLM_BLOCK_DECODER, rope_interleave=False):
-        """qk_norm: 0 none, 1 (or True) before RoPE, 2 after RoPE."""
+                 qk_norm=0, rope_segments=1, eps=1e-6, block_kind=N.VLM_BLOCK_DECODER, rope_interleave=False,
+                 q_lora_rank=0, kv_lora_rank=0, qk_rope_dim=0, v_head_dim=0):
+        """qk_norm: 0 none, 1 (or True) before RoPE, 2 after RoPE. The last four sizes describe an
+        expanded MLA stack (block_kind VLM_BLOCK_MLA) and are 0 otherwise."""
         self.dtype = DTYPES[dtype] if isinstance(dtype, str) else dtype
         self.desc = N.ModelDesc(block_kind, n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab,
-                                self.dtype, int(qk_norm), rope_segments, eps, int(bool(rope_interleave)))
+                                self.dtype, int(qk_norm), rope_segments, eps, int(bool(rope_interleave)),
+                                q_lora_rank, kv_lora_rank, qk_rope_dim, v_head_dim)
         self.layers = (N.Layer * n_layers)()
         self._keep = [dict() for _ in range(n_layers)]
         self.embed = None
@@ -67,6 +70,21 @@ class Model:
         if d.qk_norm:
             keep["q_norm"] = self._dev(w["q_norm"])
             keep["k_norm"] = self._dev(w["k_norm"])
+        self._bind(l, keep)
+
+    def set_mla_layer(self, l, w):
+        """w: natural-form expanded-MLA weights (wq_a, q_a_norm, wq_b, wkv_a, kv_a_norm, wkv_b, wo, norms,
+        wg, wu, wd); the two down-projections are stacked into w_a as the header lays out."""
+        d = self.desc
+        st = stream()
+        wg, wu = self._dev(w["wg"]), self._dev(w["wu"])
+        w1 = torch.empty((2 * d.ffn, d.hidden), dtype=self.tdtype, device="cuda")
+        N.call("vlm_pack_gate_up", ptr(wg), ptr(wu), d.ffn, d.hidden, self.dtype, ptr(w1), st)
+        keep = {"w_a": self._dev(np.concatenate([w["wq_a"], w["wkv_a"]], axis=0)),
+                "q_a_norm": self._dev(w["q_a_norm"]), "q_b": self._dev(w["wq_b"]),
+                "kv_a_norm": self._dev(w["kv_a_norm"]), "kv_b": self._dev(w["wkv_b"]),
+                "w1": w1, "wo": self._dev(w["wo"]), "w2": self._dev(w["wd"]),
+                "attn_norm": self._dev(w["attn_norm"]), "mlp_norm": self._dev(w["mlp_norm"])}
         self._bind(l, keep)
 
     def set_vit_layer(self, l, w):
@@ -163,14 +181,14 @@ class KVCache:
         return self.buf[:4].view(torch.int32)
 
     def kv(self, layer: int):
-        """(K, V) views [nkv][W][d] of one layer."""
+        """(K, V) views [nkv][W][d] and [nkv][W][dv] of one layer (dv = v_head_dim for MLA, else d)."""
         d = self.model.desc
         e = 2 if d.dtype == N.VLM_BF16 else 4
-        per = d.n_kv_heads * self.capacity * d.head_dim
-        off = N.KV_HEADER_BYTES + layer * 2 * per * e
-        k = self.buf[off:off + per * e].view(self.model.tdtype).view(d.n_kv_heads, self.capacity, d.head_dim)
-        v = self.buf[off + per * e:off + 2 * per * e].view(self.model.tdtype).view(d.n_kv_heads, self.capacity,
-                                                                                   d.head_dim)
+        dv = d.v_head_dim if d.block_kind == N.VLM_BLOCK_MLA else d.head_dim
+        pk, pv = d.n_kv_heads * self.capacity * d.head_dim, d.n_kv_heads * self.capacity * dv
+        off = N.KV_HEADER_BYTES + layer * (pk + pv) * e
+        k = self.buf[off:off + pk * e].view(self.model.tdtype).view(d.n_kv_heads, self.capacity, d.head_dim)
+        v = self.buf[off + pk * e:off + (pk + pv) * e].view(self.model.tdtype).view(d.n_kv_heads, self.capacity, dv)
         return k, v
 
 

@@ -56,7 +56,11 @@ typedef enum {
 } vlm_status;
 
 typedef enum { VLM_F32 = 0, VLM_BF16 = 1 } vlm_dtype;
-typedef enum { VLM_BLOCK_DECODER = 0, VLM_BLOCK_VIT = 1 } vlm_block_kind;
+/* DECODER: Qwen3/Llama-style GQA layer. VIT: pre-LayerNorm vision layer.
+ * MLA: multi-head latent attention in the expanded form of [Youtu] 实现流程 §6
+ * (no latent absorption: kv_b expands the compressed KV into per-head keys and
+ * values, which the cache stores; n_kv_heads == n_q_heads). */
+typedef enum { VLM_BLOCK_DECODER = 0, VLM_BLOCK_VIT = 1, VLM_BLOCK_MLA = 2 } vlm_block_kind;
 
 /* Attention masks of the prefill ([Youtu] 实现流程 §3 and §7; [HyOCR10] 五.6).
  * CAUSAL:   query row s (position pos0+s) sees cache slots 0..pos0+s.
@@ -100,9 +104,28 @@ typedef struct {
                               j and j + seg/2, i.e. the head is de-interleaved before rotate-half
                               ([Youtu] 实现难点 §2); q and the cached k keep that order, v does not
                               move. The cos/sin tables are the same for both. */
+    /* VLM_BLOCK_MLA only (0 for the other kinds). head_dim is the q/k head width
+     * dn + dr, where the last dr = qk_rope_dim elements rotate; v_head_dim the
+     * value width; the RoPE tables are dr wide. Kernels exist for head_dim 192,
+     * qk_rope_dim 64, v_head_dim 128 (the pages' K 192 / V 128), q_lora_rank and
+     * kv_lora_rank multiples of 8; qk_norm 0, rope_segments 1. */
+    int32_t q_lora_rank;   /* qr: rank of the q down-projection */
+    int32_t kv_lora_rank;  /* r: width of the compressed KV (512 on the pages) */
+    int32_t qk_rope_dim;   /* dr */
+    int32_t v_head_dim;    /* dv */
 } vlm_model_desc;
 
 /* Per-layer weights (device pointers, element type desc->dtype).
+ * Expanded MLA (block_kind MLA; wqkv, q_norm, k_norm unused): attn_norm,
+ *   mlp_norm [H]; w_a [qr + r + dr][H] = the q down-projection rows, then the
+ *   kv down-projection rows (r latent rows, then dr rows of the shared rotated
+ *   key); q_a_norm [qr], kv_a_norm [r] RMSNorm gains; q_b [nq*(dn+dr)][qr]
+ *   (per head: dn rows, then dr rows to rotate); kv_b [nq*(dn+dv)][r] (per
+ *   head: dn key rows, then dv value rows); wo [H][nq*dv]; w1, w2 as for the
+ *   decoder. Order: h = RMSNorm(x); q = RMSNorm(h q_a^T) q_b^T;
+ *   [c | k_rope] = h kv_a^T; [k_nope | v] = RMSNorm(c) kv_b^T; q and k are
+ *   [nope | RoPE(rope part)], the rotated key shared by all heads; attention
+ *   scale 1/sqrt(dn + dr).
  * Decoder ([Penguin] §2.1, §4.2): RMSNorm gains attn_norm, mlp_norm [H];
  *   wqkv [(nq+2*nkv)*d][H] = rows of Wq, then Wk, then Wv (see vlm_pack_qkv);
  *   q_norm, k_norm [d] (qk_norm only); wo [H][nq*d];
@@ -127,6 +150,11 @@ typedef struct {
     const void* b1;
     const void* w2;
     const void* b2;
+    const void* w_a;        /* MLA only (see above); NULL otherwise */
+    const void* q_a_norm;
+    const void* q_b;
+    const void* kv_a_norm;
+    const void* kv_b;
 } vlm_layer;
 
 /* ------------------------------------------------------------------------- */
@@ -134,9 +162,10 @@ typedef struct {
  * [HyOCR15] §3.7: cache stays resident on the device).
  * The caller provides one device buffer of vlm_kv_bytes() bytes. Layout:
  *   bytes [0, 256): device header (int32 length at offset 0, rest reserved);
- *   then K/V elements of type desc->dtype as [L][2][nkv][W][d] (index 0 = K,
- *   1 = V; d contiguous), so one decode split reads a contiguous run of slots
- *   of one KV head.
+ *   then per layer the K elements [nkv][W][d], then the V elements
+ *   [nkv][W][dv] (type desc->dtype; dv = v_head_dim for MLA, else d; the
+ *   last index contiguous), so one decode split reads a contiguous run of
+ *   slots of one KV head.
  * The handle keeps a host mirror of the length; kernels use the device copy,
  * which lets a captured decode step replay unchanged. */
 typedef struct vlm_kv vlm_kv;
@@ -213,7 +242,8 @@ vlm_status vlm_inject_image_embeds(const vlm_model_desc* desc, float* d_x, int32
  * per layer (x, cos, sin, mask) -> hidden and K/V for the cache).
  * d_x [S][H] fp32: input rows on entry, hidden state after the last layer
  * (before the final norm) on return. Row s has position pos0+s and uses row
- * pos0+s of d_cos/d_sin ([table_rows][d] fp32).
+ * pos0+s of d_cos/d_sin ([table_rows][d] fp32; for MLA the rows are
+ * qk_rope_dim wide, and only CAUSAL and ADDITIVE masks are supported).
  * masks: n_masks == 1 (same mask for every layer) or n_layers.
  * Decoder: kv must be bound; requires pos0 <= current length and
  *   pos0+S <= capacity (else VLM_ERR_CAPACITY: an over-long sequence is

@@ -49,6 +49,17 @@ def test_kv_and_workspace_sizes():
     assert n.value > 512 * 256 * 2
 
 
+def test_mla_cache_layout_sizes():
+    """K rows 192 wide and V rows 128 wide per layer (the expanded MLA cache of the Youtu-VL port)."""
+    d = desc(block_kind=N.VLM_BLOCK_MLA, head_dim=192, n_kv_heads=4, q_lora_rank=384, kv_lora_rank=512,
+             qk_rope_dim=64, v_head_dim=128)
+    n = C.c_size_t()
+    N.call("vlm_kv_bytes", C.byref(d), 64, C.byref(n))
+    assert n.value == N.KV_HEADER_BYTES + 2 * 4 * 64 * (192 + 128) * 4
+    N.call("vlm_workspace_bytes", C.byref(d), 48, C.byref(n))
+    assert n.value > 48 * (384 + 512 + 64) * 4
+
+
 @pytest.mark.parametrize("bad,status", [
     (dict(n_q_heads=5), N.VLM_ERR_SHAPE),            # nq % nkv != 0
     (dict(head_dim=96), N.VLM_ERR_UNSUPPORTED),
@@ -61,6 +72,13 @@ def test_kv_and_workspace_sizes():
     (dict(rope_segments=3), N.VLM_ERR_ARG),
     (dict(qk_norm=3), N.VLM_ERR_ARG),
     (dict(rope_interleave=2), N.VLM_ERR_ARG),
+    (dict(v_head_dim=128), N.VLM_ERR_ARG),            # MLA sizes on a GQA decoder
+    (dict(block_kind=2, head_dim=192, n_kv_heads=4, q_lora_rank=384, kv_lora_rank=512, qk_rope_dim=64,
+          v_head_dim=96), N.VLM_ERR_UNSUPPORTED),      # no kernel for V 96
+    (dict(block_kind=2, head_dim=192, q_lora_rank=384, kv_lora_rank=512, qk_rope_dim=64,
+          v_head_dim=128), N.VLM_ERR_SHAPE),           # MLA needs nkv == nq
+    (dict(block_kind=2, head_dim=192, n_kv_heads=4, q_lora_rank=380, kv_lora_rank=512, qk_rope_dim=64,
+          v_head_dim=128), N.VLM_ERR_SHAPE),           # rank not a multiple of 8
 ])
 def test_desc_validation(bad, status):
     d = desc(**bad)
