@@ -313,6 +313,65 @@ def test_mla_prefill_equals_decode_replay():
     assert np.allclose(a["k_cache"], b["k_cache"], rtol=1e-12, atol=1e-13)
 
 
+# ----------------------------------------------------------------------------- sampling
+from oracle import sampling as osm
+
+
+def _softmax(z):
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def test_sampling_repetition_penalty_worked_example():
+    """HunyuanOCR v1.5 port §3.5/§6 name the penalty; reading: x/r for x > 0, x*r otherwise, once per id."""
+    got = osm.penalize([2.0, -1.0, 0.5, 3.0], [0, 1, 1], 2.0)
+    assert np.array_equal(got, [1.0, -2.0, 0.5, 3.0])
+
+
+def test_sampling_top_k_one_and_tiny_top_p_are_argmax():
+    c = vs.sampling_case(1, 500, 20, n_draws=50)
+    pen = osm.penalize(c["logits"], c["context"], 1.3)
+    best = int(np.argmax(pen))
+    for u in c["u"]:
+        assert osm.sample_token(c["logits"], c["context"], 0.7, 1, 1.0, 1.3, float(u))[0] == best
+        assert osm.sample_token(c["logits"], c["context"], 0.7, 0, 1e-9, 1.3, float(u))[0] == best
+
+
+def test_sampling_draws_follow_softmax_over_the_kept_set():
+    """Over an evenly spaced grid of u the draw counts are N p within 1 (inverse CDF), where p is
+    the softmax of the tempered, penalised logits over the top-k set, computed here on its own."""
+    c = vs.sampling_case(2, 60, 10)
+    N, T, k = 4000, 1.7, 25
+    x = osm.penalize(c["logits"], c["context"], 1.5) / T
+    top = np.argsort(-x, kind="stable")[:k]
+    p = np.zeros(60)
+    p[top] = _softmax(x[top])
+    counts = np.zeros(60)
+    for i in range(N):
+        counts[osm.sample_token(c["logits"], c["context"], T, k, 1.0, 1.5, (i + 0.5) / N)[0]] += 1
+    assert np.all(np.abs(counts - N * p) <= 1.0 + 1e-9)
+    assert counts[np.setdiff1d(np.arange(60), top)].sum() == 0
+
+
+def test_sampling_top_p_keeps_the_crossing_token():
+    """[MNN] §4.1: sorted by probability, tokens after the cumulative passes the threshold are cut."""
+    x = np.log([0.5, 0.3, 0.2])
+    kept = lambda p: osm.sample_token(x, [], 1.0, 0, p, 1.0, 0.0)[1]["kept"]
+    assert kept(0.6) == 2 and kept(0.49) == 1 and kept(0.81) == 3 and kept(0.79) == 2
+    # u just below the first token's share of the kept mass picks it, just above picks the next
+    assert osm.sample_token(x, [], 1.0, 0, 0.6, 1.0, 0.62)[0] == 0
+    assert osm.sample_token(x, [], 1.0, 0, 0.6, 1.0, 0.63)[0] == 1
+
+
+def test_sampling_temperature_scales_logits():
+    c = vs.sampling_case(3, 40, 0)
+    N, T = 3000, 2.5
+    p = _softmax(c["logits"].astype(np.float64) / T)
+    counts = np.bincount([osm.sample_token(c["logits"], [], T, 0, 1.0, 1.0, (i + 0.5) / N)[0] for i in range(N)],
+                         minlength=40)
+    assert np.all(np.abs(counts - N * p) <= 1.0 + 1e-9)
+
+
 # ----------------------------------------------------------------------------- attention
 def test_attention_matches_brute_force_with_mask():
     rng = np.random.default_rng(10)

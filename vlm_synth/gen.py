@@ -190,3 +190,14 @@ def vit_globals(cfg: VitConfig) -> dict:
         "m2": _weight(cfg, g + G_M2, (cfg.out_dim, cfg.merger_hidden)),
         "m2b": _shift(cfg, g + G_M2B, cfg.out_dim),
     }
+
+
+def sampling_case(case_id: int, vocab: int, n_context: int, sigma: float = 3.0, n_draws: int = 1) -> dict:
+    """Seeded sampler inputs: fp32 logits N(0, sigma^2) [vocab], context ids uniform on [0, vocab)
+    [n_context] (repeats allowed), uniform draws u in [0, 1) [n_draws] (float32 values)."""
+    rng = _rng(7000 + case_id, 0)
+    logits = (rng.standard_normal(vocab, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    ctx = rng.integers(0, vocab, size=n_context, dtype=np.int64).astype(np.int32)
+    u = rng.random(n_draws, dtype=np.float32)
+    return {"logits": logits, "context": ctx, "u": u}
+
