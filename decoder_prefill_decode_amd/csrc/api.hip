@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -537,6 +538,25 @@ vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_nor
     auto* part = (unsigned long long*)P(d_ws, w.lm);
     HIP_TRY(launch_lmhead_argmax(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab,
                                  desc->hidden, part, d_logits, d_token_out, nullptr, nullptr, stream));
+    return ok();
+}
+
+// =============================================================================== sampling
+vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sampling* h_params,
+                             const int32_t* d_context_ids, int32_t n_context, const float* d_uniform,
+                             int32_t* d_token_out, hipStream_t stream) {
+    if (!h_params || !d_logits || !d_uniform || !d_token_out) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (vocab < 1 || vocab > kSampleVocabMax) return fail(VLM_ERR_SHAPE, "vocab %d not in [1, %d]", vocab, kSampleVocabMax);
+    const vlm_sampling& p = *h_params;
+    if (!(p.temperature > 0.f) || !std::isfinite(p.temperature))
+        return fail(VLM_ERR_ARG, "temperature must be > 0 (greedy decoding is vlm_lmhead_argmax)");
+    if (p.top_k < 1 || p.top_k > kSampleMaxK) return fail(VLM_ERR_UNSUPPORTED, "top_k %d not in [1, %d]", p.top_k, kSampleMaxK);
+    if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(VLM_ERR_ARG, "top_p must be in (0, 1]");
+    if (!(p.repetition_penalty > 0.f) || !std::isfinite(p.repetition_penalty))
+        return fail(VLM_ERR_ARG, "repetition_penalty must be > 0");
+    if (n_context < 0 || (n_context > 0 && !d_context_ids)) return fail(VLM_ERR_ARG, "context ids");
+    SampleParams sp{p.temperature, p.top_k, p.top_p, p.repetition_penalty};
+    HIP_TRY(launch_sample_logits(d_logits, vocab, sp, d_context_ids, n_context, d_uniform, d_token_out, stream));
     return ok();
 }
 

@@ -132,6 +132,14 @@ hipError_t launch_attn_decode_mla(int dtype, const DecAttnArgs& a, hipStream_t s
 hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
                                hipStream_t st);
 
+// Next-token sampler over one logits row (one block): penalty on context ids,
+// temperature, top-k (1..kSampleMaxK), top-p, inverse-CDF draw with *u.
+constexpr int kSampleMaxK = 1024;
+constexpr int kSampleVocabMax = 1 << 19;
+struct SampleParams { float temperature; int top_k; float top_p; float penalty; };
+hipError_t launch_sample_logits(const float* logits, int V, const SampleParams& p, const int32_t* ctx, int nctx,
+                                const float* u, int32_t* out, hipStream_t st);
+
 // Final RMSNorm + lm_head GEMV + argmax. Writes per-block argmax keys to
 // `partials` (lmhead_partials_max(V) entries) and the logits when non-null.
 // token_out == null: partials only; otherwise a second kernel reduces the

@@ -1,0 +1,200 @@
+// Next-token sampling on the logits row: repetition penalty, temperature,
+// top-k, top-p, softmax and an inverse-CDF draw with a caller-supplied
+// uniform number (MNN llm_demo Omni article §4.1; HunyuanOCR v1.5 ncnn port
+// §3.5 for the generation options).
+//
+// One block of 1024 threads; the vocabulary streams from L2 a few times:
+//  1. the context ids become a bitmap in LDS (membership in one read);
+//  2. the k-th largest processed value is found by a 4-pass radix select on
+//     order-preserving 32-bit keys (LDS histograms of 256 bins);
+//  3. the values >= that one (ties kept) are gathered into LDS, sorted by
+//     (value descending, id ascending) with a bitonic sort;
+//  4. softmax over the sorted candidates, a block scan gives the cumulative
+//     sums: top-p keeps the prefix whose preceding mass is below top_p * Z,
+//     and the draw takes the first kept token whose cumulative sum exceeds
+//     u times the kept mass.
+// Processed value of id i: x = logits[i]; x = x > 0 ? x / r : x * r when i is
+// in the context; x /= temperature (fp32 throughout).
+#include <stdint.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace vlm {
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleCand = 2 * kSampleMaxK;  // candidate slots (ties at the k-th value included)
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const float* __restrict__ logits, int V,
+                                                                       SampleParams sp,
+                                                                       const int32_t* __restrict__ ctx, int nctx,
+                                                                       const float* __restrict__ uptr,
+                                                                       int32_t* __restrict__ out) {
+    __shared__ uint32_t bits[kSampleVocabMax / 32];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t ckey[kSampleCand];
+    __shared__ int32_t cidx[kSampleCand];
+    __shared__ float cval[kSampleCand];
+    __shared__ float red[kSampleThreads / kWave];
+    __shared__ uint32_t s_prefix, s_krem, s_count, s_bad;
+    const int tid = threadIdx.x;
+    const int nw = (V + 31) / 32;
+    for (int i = tid; i < nw; i += kSampleThreads) bits[i] = 0u;
+    if (tid == 0) {
+        s_prefix = 0u;
+        s_krem = (uint32_t)min(sp.top_k, V);
+        s_count = 0u;
+        s_bad = 0u;
+    }
+    __syncthreads();
+    for (int i = tid; i < nctx; i += kSampleThreads) {
+        const int id = ctx[i];
+        if (id >= 0 && id < V) atomicOr(&bits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    const float inv_t = 1.0f / sp.temperature, r = sp.penalty;
+    auto value = [&](int i) -> float {
+        float x = logits[i];
+        if ((bits[i >> 5] >> (i & 31)) & 1u) x = x > 0.f ? x / r : x * r;
+        return x * inv_t;
+    };
+
+    // (2) radix select of the k-th largest key, most significant byte first
+    uint32_t mask = 0u;
+    for (int pass = 0; pass < 4; pass++) {
+        const int shift = 24 - 8 * pass;
+        for (int b = tid; b < 256; b += kSampleThreads) hist[b] = 0u;
+        __syncthreads();
+        const uint32_t prefix = s_prefix;
+        for (int i = tid; i < V; i += kSampleThreads) {
+            const float x = value(i);
+            if (pass == 0 && !isfinite(x)) s_bad = 1u;
+            const uint32_t k = ordered_key(x);
+            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t need = s_krem, cum = 0u;
+            int b = 255;
+            for (; b > 0; b--) {
+                if (cum + hist[b] >= need) break;
+                cum += hist[b];
+            }
+            s_krem = need - cum;
+            s_prefix = prefix | ((uint32_t)b << shift);
+        }
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    if (s_bad) {  // a non-finite logit: no token (the argmax path reports it the same way)
+        if (tid == 0) out[0] = -1;
+        return;
+    }
+    const uint32_t kth = s_prefix;
+
+    // (3) gather the values >= the k-th one, then sort by (value desc, id asc)
+    for (int i = tid; i < V; i += kSampleThreads) {
+        const uint32_t k = ordered_key(value(i));
+        if (k >= kth) {
+            const uint32_t slot = atomicAdd(&s_count, 1u);
+            if (slot < (uint32_t)kSampleCand) {
+                ckey[slot] = k;
+                cidx[slot] = i;
+            }
+        }
+    }
+    __syncthreads();
+    const int n = (int)s_count;
+    if (n > kSampleCand) {  // more ties at the k-th value than slots
+        if (tid == 0) out[0] = -1;
+        return;
+    }
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    for (int i = n + tid; i < np2; i += kSampleThreads) {
+        ckey[i] = 0u;
+        cidx[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    // "a before b": larger key, or equal key and smaller id
+    for (int size = 2; size <= np2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < np2 / 2; t += kSampleThreads) {
+                const int lo = 2 * t - (t & (stride - 1)), hi = lo + stride;
+                const bool up = (lo & size) == 0;  // this run is sorted "before-first"
+                const uint32_t ka = ckey[lo], kb = ckey[hi];
+                const int ia = cidx[lo], ib = cidx[hi];
+                const bool b_first = kb > ka || (kb == ka && ib < ia);
+                if (b_first == up) {
+                    ckey[lo] = kb;
+                    ckey[hi] = ka;
+                    cidx[lo] = ib;
+                    cidx[hi] = ia;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // (4) softmax over the sorted candidates; inclusive scan of the weights
+    const float m = key_to_float(ckey[0]);
+    for (int i = tid; i < n; i += kSampleThreads) cval[i] = __expf(key_to_float(ckey[i]) - m);
+    __syncthreads();
+    // two elements per thread (n <= 2048): sequential pair, then a block scan of the pair sums
+    const int i0 = 2 * tid, i1 = 2 * tid + 1;
+    const float a0 = i0 < n ? cval[i0] : 0.f, a1 = i1 < n ? cval[i1] : 0.f;
+    const float pair = a0 + a1;
+    // inclusive scan of `pair` across the block: wavefront scan by shuffles, then the wave totals
+    const int lane = tid % kWave, w = tid / kWave;
+    float sc = pair;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(sc, off, kWave);
+        if (lane >= off) sc += o;
+    }
+    if (lane == kWave - 1) red[w] = sc;
+    __syncthreads();
+    float base = 0.f;
+    for (int j = 0; j < w; j++) base += red[j];
+    float Z = 0.f;
+    for (int j = 0; j < kSampleThreads / kWave; j++) Z += red[j];
+    const float incl1 = base + sc, incl0 = incl1 - a1, excl0 = incl0 - a0;
+    __syncthreads();
+    // cumulative sums back into cval: cval[i] = inclusive sum up to i
+    if (i0 < n) cval[i0] = incl0;
+    if (i1 < n) cval[i1] = incl1;
+    if (tid == 0) s_count = (uint32_t)n;  // kept count, reduced below
+    __syncthreads();
+    // top-p: candidate i is kept iff the mass before it is < top_p * Z; kept ones form a prefix
+    if (sp.top_p < 1.f) {
+        const float thr = sp.top_p * Z;
+        const float before0 = excl0, before1 = incl0;
+        if (i0 < n && before0 >= thr) atomicMin(&s_count, (uint32_t)i0);
+        if (i1 < n && before1 >= thr) atomicMin(&s_count, (uint32_t)i1);
+        __syncthreads();
+    }
+    const int nk = max((int)s_count, 1);
+    const float total = cval[nk - 1];
+    const float target = uptr[0] * total;
+    // the first kept candidate whose inclusive sum exceeds target (the last kept one if none does)
+    if (tid == 0) s_prefix = (uint32_t)(nk - 1);
+    __syncthreads();
+    for (int i = tid; i < nk; i += kSampleThreads) {
+        const float before = i == 0 ? 0.f : cval[i - 1];
+        if (cval[i] > target && before <= target) atomicMin(&s_prefix, (uint32_t)i);
+    }
+    __syncthreads();
+    if (tid == 0) out[0] = cidx[s_prefix];
+}
+
+hipError_t launch_sample_logits(const float* logits, int V, const SampleParams& p, const int32_t* ctx, int nctx,
+                                const float* u, int32_t* out, hipStream_t st) {
+    sample_logits_kernel<<<1, kSampleThreads, 0, st>>>(logits, V, p, ctx, nctx, u, out);
+    return hipGetLastError();
+}
+
+}  // namespace vlm

@@ -52,6 +52,11 @@ class Merger(C.Structure):
                [(n, C.c_void_p) for n in ("post_ln", "post_ln_b", "w1", "b1", "w2", "b2")]
 
 
+class Sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32), ("top_p", C.c_float),
+                ("repetition_penalty", C.c_float)]
+
+
 _P = C.c_void_p
 _I = C.c_int32
 _SIG = {
@@ -66,6 +71,7 @@ _SIG = {
     "vlm_pack_gate_up": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "vlm_rope_table": (_I, [_P, _I, _I, C.POINTER(_I), _I, _I, C.c_double, _P, _P, _P]),
     "vlm_rope_alpha_base": (_I, [C.c_double, C.c_double, _I, C.POINTER(C.c_double)]),
+    "vlm_sample_logits": (_I, [_P, _I, C.POINTER(Sampling), _P, _I, _P, _P, _P]),
     "vlm_embed": (_I, [C.POINTER(ModelDesc), _P, _P, _I, _P, _P]),
     "vlm_inject_image_embeds": (_I, [C.POINTER(ModelDesc), _P, _I, C.POINTER(_I), _P, _I, _P, _I, _I, _P]),
     "vlm_prefill": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _I, _I, _P, _P, _I, C.POINTER(Mask), _I, _P,

@@ -206,6 +206,15 @@ def rope_table(positions: np.ndarray, axis_of_pair, segments: int, head_dim: int
     return cos, sin
 
 
+def sample_logits(logits: torch.Tensor, temperature: float, top_k: int, top_p: float, penalty: float,
+                  context: torch.Tensor, u: torch.Tensor, out: torch.Tensor):
+    """vlm_sample_logits on a device fp32 logits row; context: device int32 ids (may be empty);
+    u: device float32 [1] uniform draw; out: device int32 [1]."""
+    prm = N.Sampling(temperature, top_k, top_p, penalty)
+    N.call("vlm_sample_logits", ptr(logits), logits.numel(), C.byref(prm), ptr(context) if context.numel() else None,
+           context.numel(), ptr(u), ptr(out), stream())
+
+
 def rope_alpha_base(theta: float, alpha: float, head_dim: int) -> float:
     """vlm_rope_alpha_base: the effective base of the alpha-scaled multi-axis RoPE."""
     out = C.c_double()

@@ -334,6 +334,34 @@ vlm_status vlm_vit_merger(const vlm_merger* m, const float* d_x, int32_t N, cons
 vlm_status vlm_vit_merger_workspace_bytes(const vlm_merger* m, int32_t N, size_t* bytes);
 
 /* ------------------------------------------------------------------------- */
+/* Sampling instead of the greedy argmax ([MNN] §4.1: temperature, top_k,
+ * top_p, softmax, draw; repeat penalty on tokens already in the context;
+ * [HyOCR15] §3.5 generation options). On one fp32 logits row d_logits [vocab]
+ * (e.g. the d_logits output of vlm_lmhead_argmax), in this order:
+ *   x_i = logits_i; for i in the context: x_i = x_i > 0 ? x_i / r : x_i * r;
+ *   x_i /= temperature; keep the x_i >= the top_k-th largest (ties kept);
+ *   order the kept ids by (x desc, id asc), p = softmax(x) over them;
+ *   top_p < 1 keeps the prefix whose preceding mass is < top_p * sum p;
+ *   the token is the first kept id whose cumulative p exceeds u * (kept mass),
+ *   u = d_uniform[0] in [0, 1) supplied by the caller (the random draw is an
+ *   input; a fixed u makes the call deterministic).
+ * fp32 throughout; d_token_out[0] = the id, or -1 for a non-finite logit or
+ * more than 2048 values tied at the top_k-th. d_context_ids [n_context]
+ * (repeats allowed, ids outside [0, vocab) ignored; NULL if n_context == 0).
+ * Greedy decoding (temperature 0) is vlm_lmhead_argmax.
+ * Errors (nothing enqueued): vocab not in [1, 524288], temperature not > 0,
+ * top_k not in [1, 1024], top_p not in (0, 1], repetition_penalty not > 0. */
+typedef struct {
+    float temperature;
+    int32_t top_k;
+    float top_p;
+    float repetition_penalty;
+} vlm_sampling;
+vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sampling* h_params,
+                             const int32_t* d_context_ids, int32_t n_context, const float* d_uniform,
+                             int32_t* d_token_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
 /* Measurement helper: enqueues n_launches back-to-back launches of one kernel
  * of the decode step, exactly as vlm_decode_step launches it, cycling over the
  * layers so that consecutive launches read different weights. Inputs come from

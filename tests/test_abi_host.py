@@ -121,6 +121,20 @@ def test_rope_alpha_base_matches_oracle_and_checks_arguments():
     assert L.vlm_rope_alpha_base(1e4, 2.0, 64, None) == N.VLM_ERR_ARG
 
 
+def test_sample_logits_argument_checks():
+    L = N.lib()
+    fake = C.c_void_p(0x1000)   # never dereferenced: every case fails its checks first
+    def st(V=1000, T=1.0, k=40, p=0.9, r=1.1, n=0, ctx=None):
+        prm = N.Sampling(T, k, p, r)
+        return L.vlm_sample_logits(fake, V, C.byref(prm), ctx, n, fake, fake, None)
+    assert st(V=0) == N.VLM_ERR_SHAPE and st(V=(1 << 19) + 1) == N.VLM_ERR_SHAPE
+    assert st(T=0.0) == N.VLM_ERR_ARG and st(T=float("nan")) == N.VLM_ERR_ARG
+    assert st(k=0) == N.VLM_ERR_UNSUPPORTED and st(k=1025) == N.VLM_ERR_UNSUPPORTED
+    assert st(p=0.0) == N.VLM_ERR_ARG and st(p=1.5) == N.VLM_ERR_ARG
+    assert st(r=0.0) == N.VLM_ERR_ARG
+    assert st(n=3, ctx=None) == N.VLM_ERR_ARG
+
+
 def test_window_index_matches_oracle():
     """Integer bookkeeping of the vision window permutation: bit-exact vs the oracle."""
     from decoder_prefill_decode_amd.pipeline import window_index
