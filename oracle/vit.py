@@ -25,10 +25,17 @@ Readings where the pages are silent (listed with the design notes):
     units are permuted window by window (windows in raster order, units in
     raster order inside each window); the merged output is returned in raster
     (unpermuted) unit order.
+  * bf16 storage (the Mixed policy of the HunyuanOCR v1.5 port, §3.6: the
+    vision tower keeps reduced-precision storage with fp32 accumulation; this
+    library's reduced storage type is bf16): weights, biases and norm
+    parameters hold bf16 values, the GEMM operands (normed rows, attention
+    output, GELU output, merger operands) and q, k, v are rounded to bf16, the
+    residual stream stays fp32 -- the same rounding points as the decoder.
 """
 import numpy as np
 
-from .decoder import MASK_NEG, _lin, gelu_tanh, layer_norm, rope_apply, rope_tables, softmax_attention, F64
+from .decoder import (BF16, MASK_NEG, _lin, bf16_round, gelu_tanh, layer_norm, rope_apply, rope_tables,
+                      softmax_attention, F64)
 
 
 def vit_window_order(cfg):
@@ -70,6 +77,8 @@ def vit_layer(x, w, mask_add, cos, sin, cfg, prec=F64):
     v = (_lin(h, w["wv"], prec) + w["bv"]).reshape(S, nh, d)
     q = rope_apply(q, cos, sin, 2)
     k = rope_apply(k, cos, sin, 2)
+    if prec == BF16:
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     o = softmax_attention(q.transpose(1, 0, 2), k.transpose(1, 0, 2), v.transpose(1, 0, 2), mask_add, 1)
     x = x + _lin(o.transpose(1, 0, 2).reshape(S, nh * d), w["wo"], prec) + w["bo"]
     h2 = layer_norm(x, w["mlp_norm"], w["mlp_norm_b"], cfg.eps)
@@ -91,13 +100,16 @@ def run_vit(cfg, glob, layers):
     cos, sin = rope_tables(pos, axes, 2, cfg.head_dim, cfg.theta)
     win_mask = np.where(seg_rows[:, None] == seg_rows[None, :], 0.0, MASK_NEG)
     full_mask = np.zeros_like(win_mask)
-    ws = [{k: np.asarray(v, np.float64) for k, v in w.items()} for w in layers]
+    prec = BF16 if getattr(cfg, "dtype", "f32") == "bf16" else F64
+    # bf16 mode: matrices as float32 arrays of bf16 values (fp32 products, as _lin expects)
+    mat = (lambda a: np.asarray(a, np.float32)) if prec == BF16 else (lambda a: np.asarray(a, np.float64))
+    ws = [{k: (mat(v) if v.ndim == 2 else np.asarray(v, np.float64)) for k, v in w.items()} for w in layers]
     for l, w in enumerate(ws):
-        x = vit_layer(x, w, full_mask if l in cfg.full_layers else win_mask, cos, sin, cfg)
-    g = {k: np.asarray(v, np.float64) for k, v in glob.items() if k != "x"}
+        x = vit_layer(x, w, full_mask if l in cfg.full_layers else win_mask, cos, sin, cfg, prec)
+    g = {k: (mat(v) if np.ndim(v) == 2 else np.asarray(v, np.float64)) for k, v in glob.items() if k != "x"}
     hpost = layer_norm(x, g["post_ln"], g["post_ln_b"], cfg.eps)
     z = hpost.reshape(cfg.n_merged, m2 * cfg.hidden)
-    y = gelu_tanh(z @ g["m1"].T + g["m1b"]) @ g["m2"].T + g["m2b"]
+    y = _lin(gelu_tanh(_lin(z, g["m1"], prec) + g["m1b"]), g["m2"], prec) + g["m2b"]
     out = np.empty_like(y)
     out[perm_u] = y
     return {"out": out, "x_final": x, "perm_units": perm_u, "seg_units": seg_u, "row_perm": row_perm}

@@ -538,6 +538,19 @@ def test_bf16_mode_stays_close_to_f64():
     assert 1e-5 < err < 2e-2
 
 
+def test_vit_bf16_mode_stays_close_to_f64():
+    """The vision tower's bf16-storage mode (HunyuanOCR v1.5 port §3.6 Mixed policy) moves the
+    merged rows by bf16 rounding only: same bf16-valued weights, the two rounding modes differ by
+    more than float noise and by less than the bf16 gate."""
+    cfgb = vs.scaled_vit(vs.C5, n_layers=2, full_layers=(1,), grid_h=4, grid_w=8, window=2, dtype="bf16")
+    glob = vs.vit_globals(cfgb)
+    layers = [vs.vit_layer_weights(cfgb, l) for l in range(cfgb.n_layers)]
+    rb = ov.run_vit(cfgb, glob, layers)["out"]
+    rf = ov.run_vit(vs.scaled_vit(cfgb, dtype="f32"), glob, layers)["out"]
+    err = np.abs(rb - rf).max() / np.abs(rf).max()
+    assert 1e-5 < err < 2e-2
+
+
 # ----------------------------------------------------------------------------- whole decoder
 def _tiny_run(cfg, **kw):
     glob = vs.decoder_globals(cfg)
