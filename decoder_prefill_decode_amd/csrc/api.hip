@@ -78,8 +78,6 @@ vlm_status check_desc(const vlm_model_desc* d) {
     if (d->block_kind != VLM_BLOCK_MLA && d->head_dim != 64 && d->head_dim != 72 && d->head_dim != 80 &&
         d->head_dim != 128)
         return fail(VLM_ERR_UNSUPPORTED, "head_dim %d not in {64,72,80,128}", d->head_dim);
-    if (d->dtype == VLM_BF16 && d->head_dim % 16)
-        return fail(VLM_ERR_UNSUPPORTED, "bf16 attention needs head_dim %% 16 == 0 (got %d)", d->head_dim);
     if (d->rope_segments != 1 && d->rope_segments != 2) return fail(VLM_ERR_ARG, "rope_segments %d", d->rope_segments);
     if ((d->head_dim / d->rope_segments) % 2) return fail(VLM_ERR_SHAPE, "rope segment length must be even");
     if (d->qk_norm < 0 || d->qk_norm > 2) return fail(VLM_ERR_ARG, "qk_norm %d not in {0,1,2}", d->qk_norm);

@@ -43,8 +43,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int DQ, int DV, int MASK>
 __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     constexpr int BQ = 64, BKEY = 64;
-    constexpr int DK = DQ / 16, NB = (DV + 31) / 32, DP = NB * 32;
-    constexpr int LDK = DQ + 8, LDV = BKEY + 8;
+    // a q/k width that is not a multiple of 16 (72) is zero-padded to DK * 16 in the K tile and
+    // the q fragments, which leaves every dot product unchanged
+    constexpr int DK = (DQ + 15) / 16, NB = (DV + 31) / 32, DP = NB * 32, DQP = DK * 16;
+    constexpr int LDK = DQP + 8, LDV = BKEY + 8;
     constexpr int CH = DQ / 8, CHV = DV / 8;  // 16-byte chunks per key / value row
     constexpr int KSZ = BKEY * LDK, VSZ = DP * LDV;                 // elements of one K / V^T tile
     constexpr int MRG = NB * 16 + 2;                                // floats per lane in the final merge
@@ -67,11 +69,18 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
         Vt[DV * LDV + i] = 0;
         Vt[VSZ + DV * LDV + i] = 0;
     }
+    if constexpr (DQP > DQ) {  // pad columns of both K tiles (the stages write columns < DQ only)
+        for (int i = tid; i < BKEY * (DQP - DQ); i += 256) {
+            const int r = i / (DQP - DQ), c = DQ + i % (DQP - DQ);
+            Ks[r * LDK + c] = 0;
+            Ks[KSZ + r * LDK + c] = 0;
+        }
+    }
 
     bf16x8 Qf[DK];
 #pragma unroll
     for (int kk = 0; kk < DK; kk++) {
-        if (qrow < S) {
+        if (qrow < S && kk * 16 + hh * 8 < DQ) {
             Qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * DQ + kk * 16 + hh * 8);
         } else {
 #pragma unroll
@@ -436,7 +445,7 @@ template <int DQ, int DV, int MASK>
 static hipError_t run_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.S + 127) / 128, a.nq);
     if (dtype == 1) {
-        if constexpr (DQ % 16 == 0 && DV % 16 == 0) {
+        if constexpr (DQ % 8 == 0 && DV % 8 == 0) {
             attn_prefill_bf16<DQ, DV, MASK><<<dim3((a.S + 63) / 64, a.nq), 256, 0, st>>>(a);
         } else {
             return hipErrorInvalidValue;

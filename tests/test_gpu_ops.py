@@ -186,6 +186,21 @@ def test_truncate_then_redecode_is_deterministic(mods):
 
 
 # ---------------------------------------------------------------- vision tower
+def test_vit_tower_and_merger_scaled_bf16(mods):
+    """bf16 storage, fp32 accumulation (the Mixed policy of the HunyuanOCR v1.5 port, §3.6), with the
+    72-wide heads zero-padded to the 16-wide MFMA steps inside the attention kernel."""
+    _, pipeline, _ = mods
+    cfg = vs.scaled_vit(vs.C5, n_layers=3, full_layers=(1,), dtype="bf16")
+    glob = vs.vit_globals(cfg)
+    layers = [vs.vit_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    ref = ov.run_vit(cfg, glob, layers)
+    run = pipeline.VitRun(cfg, lambda l: layers[l], glob)
+    out = run.run().cpu().numpy()
+    ex, eo = rel(run.x.cpu().numpy(), ref["x_final"]), rel(out, ref["out"])
+    print(f"bf16 tower: final rows {ex:.2e}, merged rows {eo:.2e}")
+    assert ex <= 2e-2 and eo <= 2e-2
+
+
 def test_vit_tower_and_merger_scaled(mods):
     _, pipeline, _ = mods
     cfg = vs.scaled_vit(vs.C5, n_layers=3, full_layers=(1,))
