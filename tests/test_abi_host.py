@@ -49,6 +49,14 @@ def test_kv_and_workspace_sizes():
     assert n.value > 512 * 256 * 2
 
 
+def test_bf16_head72_is_accepted():
+    """The bf16 attention zero-pads 72-wide heads to 80, so a bf16 vision stack of 72-wide heads is valid."""
+    d = desc(block_kind=N.VLM_BLOCK_VIT, dtype=N.VLM_BF16, head_dim=72, n_kv_heads=4)
+    n = C.c_size_t()
+    N.call("vlm_workspace_bytes", C.byref(d), 16, C.byref(n))
+    assert n.value > 0
+
+
 def test_mla_cache_layout_sizes():
     """K rows 192 wide and V rows 128 wide per layer (the expanded MLA cache of the Youtu-VL port)."""
     d = desc(block_kind=N.VLM_BLOCK_MLA, head_dim=192, n_kv_heads=4, q_lora_rank=384, kv_lora_rank=512,
@@ -66,7 +74,8 @@ def test_mla_cache_layout_sizes():
     (dict(dtype=7), N.VLM_ERR_DTYPE),
     (dict(ffn=770), N.VLM_ERR_SHAPE),
     (dict(ffn=776), N.VLM_ERR_SHAPE),                 # decoder ffn not a multiple of 32
-    (dict(dtype=N.VLM_BF16, head_dim=72), N.VLM_ERR_UNSUPPORTED),
+    (dict(block_kind=2, head_dim=128, n_kv_heads=4, q_lora_rank=384, kv_lora_rank=512, qk_rope_dim=64,
+          v_head_dim=128), N.VLM_ERR_UNSUPPORTED),   # no MLA kernel for 128-wide keys
     (dict(n_q_heads=6, n_kv_heads=2), N.VLM_ERR_UNSUPPORTED),  # group of 3
     (dict(block_kind=1, n_kv_heads=2), N.VLM_ERR_UNSUPPORTED),
     (dict(rope_segments=3), N.VLM_ERR_ARG),
