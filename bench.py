@@ -7,9 +7,10 @@ cache, lm_head + argmax of the last prompt row, then the workload's greedy
 decode steps (one HIP-graph launch per token), starting from an empty cache.
 Inputs and weights are resident in HBM before the timed region.
 
-Default workload: the 28-layer Qwen3-style bf16 stack (hidden 1024, 16/8
-heads, head_dim 128, FFN 3072, tied vocabulary 151936), 560-token prompt
-with a 495-row image span, 128 decode steps.
+Default workload: the 36-layer 4B-class bf16 stack (hidden 2560, 32/8 heads
+of 80, FFN 9728, tied vocabulary 128256, 2048-slot window), 512-token prompt
+with a 322-row image span, 256 decode steps. --config c3_qwen3_28l runs the
+28-layer Qwen3-style stack (vocabulary 151936) the same way.
 
 Prints one JSON line: value = (prompt + generated tokens) / step time, with
 the prefill and decode rates beside it, the roofline of the dominant kernel
@@ -38,8 +39,8 @@ KERNEL_SOURCES = {k: os.path.join(ROOT, "decoder_prefill_decode_amd", "csrc", f)
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4_llama_4b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-decode-steps", type=int, default=128)
@@ -47,6 +48,12 @@ def parse():
                     help="launch one decode kernel (lmhead, qkv, o, gate_up, down, attn) --launches times, then "
                          "one plain copy of --copy-mib MiB (reference for HBM counters), and exit")
     ap.add_argument("--launches", type=int, default=200)
+    ap.add_argument("--mfma", default=None, metavar="CSV",
+                    help="summarise a rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 counter CSV of a --prefill-only run "
+                         "(per prefill kernel: MFMA busy %% and counted vs algorithmic FLOPs) and exit")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="N",
+                    help="run N prefills (embed, inject, all layers, first-token head) and exit; the run the "
+                         "MFMA counters are collected on")
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --kernel-only run "
@@ -168,17 +175,99 @@ def time_kernel(run, name, launches):
     return e0.elapsed_time(e1) * 1e3 / launches  # us per launch (includes the one-row copy, < 1 us)
 
 
+def mfma_summary(cfg_name, csv_path):
+    """Markdown table of the prefill kernels' MFMA counters: MfmaUtil (busy cycles of the matrix cores over
+    all SIMDs and the kernel's active cycles) and MfmaFlopsBF16 (512 x bf16 MFMA MOPs) per dispatch, next
+    to the algorithmic FLOPs of the launch for the gate/up, down, O, QKV GEMMs and the causal attention."""
+    import csv
+    from collections import defaultdict
+
+    import vlm_synth as vs
+    cfg = vs.ALL_CONFIGS[cfg_name]
+    S, H, F = cfg.seq, cfg.hidden, cfg.ffn
+    qd = cfg.n_q_heads * cfg.head_dim
+    algo = {"Epi)2": 2.0 * S * 2 * F * H, "Epi)0": 2.0 * S * cfg.qkv_rows * H,
+            "attn_prefill": 4.0 * cfg.n_q_heads * cfg.head_dim * S * (S + 1) / 2}
+    util, flops = defaultdict(list), defaultdict(list)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "gemm_lds_kernel" not in name and "attn_prefill" not in name:
+                continue
+            key = name.split("(vlm::GemmArgs)")[0].split("(vlm::AttnArgs)")[0].replace("vlm::", "").replace("void ", "")
+            (util if r["Counter_Name"] == "MfmaUtil" else flops)[key].append(float(r["Counter_Value"]))
+    print("| kernel | dispatches | MFMA busy % (mean) | counted GFLOP / launch | algorithmic GFLOP / launch |")
+    print("|---|---:|---:|---:|---:|")
+    for key in sorted(util, key=lambda k: -sum(util[k])):
+        a = next((v for frag, v in algo.items() if frag in key), None)
+        if a is None and "Epi)1" in key:   # O (K = nq*d) or down (K = F): told apart by the counted work
+            c = sum(flops[key]) / max(len(flops[key]), 1)
+            a = min((2.0 * S * H * qd, 2.0 * S * H * F), key=lambda v: abs(v - c))
+        cf = sum(flops[key]) / max(len(flops[key]), 1) / 1e9
+        print(f"| `{key}` | {len(util[key])} | {sum(util[key]) / len(util[key]):.1f} | {cf:.2f} | "
+              f"{'' if a is None else f'{a / 1e9:.2f}'} |")
+
+
+def measured_peaks():
+    """Peaks measured on this device: HBM from a stream copy of 1 GiB (torch's vectorised copy kernel;
+    read + write bytes / time, best of 6), bf16 MFMA from rocminfo's compute units x max clock x 1024 FLOP
+    per clock per SIMD x 4 SIMDs per CU (the dense 32x32x16 bf16 rate)."""
+    import subprocess
+
+    import torch
+
+    n = 1 << 28                                         # 2^28 floats = 1 GiB read, 1 GiB written
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = 1e30
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    hbm = 2.0 * n * 4 / (best * 1e-3) / 1e9
+    cus = clk = None
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        for blk in txt.split("Agent ")[1:]:
+            if "gfx9" in blk and "Compute Unit" in blk:
+                for line in blk.splitlines():
+                    if "Max Clock Freq" in line:
+                        clk = float(line.split(":")[1].split("(")[0])
+                    if "Compute Unit" in line:
+                        cus = int(line.split(":")[1])
+                break
+    except Exception:
+        pass
+    mfma = cus * clk * 1e6 * 4 * 1024 / 1e12 if cus and clk else None
+    return {"hbm_copy_gbs": round(hbm, 1), "bf16_mfma_tflops": round(mfma, 1) if mfma else None,
+            "compute_units": cus, "max_clock_mhz": clk}
+
+
 def cpu_baseline(cfg, glob, layers, n_dec):
     """The oracle, untuned, on this host: prefill of the whole prompt plus n_dec
     decode steps; scaled to a full step (prompt + all decode steps)."""
     import numpy as np
 
     from oracle import decoder as od
+    blas = None
     try:
         import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+        info = threadpoolctl.threadpool_info()
+        threads = max(i.get("num_threads", 1) for i in info) or 1
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} x{i.get('num_threads')}" for i in info)
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     r = od.run_decoder(cfg, glob, layers, steps=n_dec)
     t_pre = r["t_prefill_s"]
     t_dec = r["t_decode_s"] / max(n_dec, 1)
@@ -186,13 +275,17 @@ def cpu_baseline(cfg, glob, layers, n_dec):
     return {"value": (cfg.seq + cfg.decode_steps) / t_step, "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"{cfg.name}: oracle prefill of {cfg.seq} tokens ({t_pre:.1f} s) and {n_dec} decode steps "
                       f"({t_dec:.2f} s each), scaled to {cfg.seq} + {cfg.decode_steps} tokens",
-            "prefill_tok_s": cfg.seq / t_pre, "decode_tok_s": 1.0 / t_dec, "ids_head": [int(i) for i in r["ids"][:4]]}
+            "prefill_tok_s": cfg.seq / t_pre, "decode_tok_s": 1.0 / t_dec, "ids_head": [int(i) for i in r["ids"][:4]],
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu, "blas": blas}
 
 
 def main():
     args = parse()
     if args.traffic:
         traffic_from_csv(args.config, args.traffic[0], args.traffic[1], args.traffic[2], args.copy_mib)
+        return
+    if args.mfma:
+        mfma_summary(args.config, args.mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
@@ -236,6 +329,15 @@ def main():
         print(f"# {args.kernel_only}: {t:.2f} us per launch over {args.launches} launches", file=sys.stderr)
         return
 
+    if args.prefill_only:
+        for _ in range(args.prefill_only):
+            run.reset()
+            run.prefill()
+            run.first_token()
+        torch.cuda.synchronize()
+        print(f"# {args.prefill_only} prefills of {cfg.seq} rows done", file=sys.stderr)
+        return
+
     S, N = cfg.seq, cfg.decode_steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
@@ -262,6 +364,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     pre_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
     dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
     ids = run.hist[S + 1:S + 1 + N].cpu().numpy()
     print(f"# step {ms_step:.2f} ms: prefill {pre_ms:.3f} ms, decode {dec_ms:.2f} ms ({dec_ms / N * 1e3:.1f} us/token); "
           f"first ids {[int(run.tok[0])] if N == 0 else list(map(int, ids[:6]))}", file=sys.stderr, flush=True)
@@ -307,7 +410,13 @@ def main():
         "decode_kernels_us": {k: round(v["us"], 2) for k, v in per.items()},
         "decode_kernels_gbs": {k: round(v["gbs"], 1) for k, v in per.items()},
         "roofline": roof,
+        "step_ms_median": round(float(np.median(step_ms)), 3), "step_ms_min": round(float(np.min(step_ms)), 3),
     }
+    mp = measured_peaks()
+    out["measured_peaks"] = mp
+    out["decode_hbm_frac_of_measured"] = round(tok_bytes / (dec_ms * 1e-3 / max(N, 1)) / (mp["hbm_copy_gbs"] * 1e9), 4)
+    out["prefill_mfma_frac_of_rocminfo"] = (round(flops / (pre_ms * 1e-3) / (mp["bf16_mfma_tflops"] * 1e12), 4)
+                                            if mp["bf16_mfma_tflops"] and cfg.dtype == "bf16" else None)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, glob, layers, args.cpu_decode_steps)
     else:
