@@ -90,6 +90,31 @@ class DecoderRun:
         torch.cuda.current_stream().synchronize()
         return self.hist[t0 + 1:t0 + 1 + n].cpu().numpy().astype(np.int64)
 
+    def generate_sampled(self, n, temperature, top_k, top_p, penalty, u):
+        """Sampled generation after prefill(): the first token from the last prompt row, then n
+        decode steps, each token drawn by vlm_sample_logits from the lm_head logits with the prompt
+        and the tokens so far as the penalty context; u: host float32 [n + 1] uniform draws (inputs).
+        Everything stays on the device (the sampled id is written straight into the context
+        buffer that the next step reads). Returns the n + 1 ids (host)."""
+        from .runtime import sample_logits
+        cfg = self.cfg
+        S, V = cfg.seq, cfg.vocab
+        ctx = torch.empty(S + n + 1, dtype=torch.int32, device="cuda")
+        ctx[:S].copy_(self.ids_dev)
+        ud = torch.from_numpy(np.ascontiguousarray(u, np.float32)).to("cuda")
+        logits = torch.empty(V, dtype=torch.float32, device="cuda")
+        scratch = torch.empty(1, dtype=torch.int32, device="cuda")
+        self.model.lmhead_argmax(self.x[S - 1], scratch, self.ws, logits)
+        sample_logits(logits, temperature, top_k, top_p, penalty, ctx[:S], ud[0:1], ctx[S:S + 1])
+        for i in range(n):
+            self.model.decode_step(self.kv, self.cos, self.sin, self.ws, x_out=self.x_row, with_head=False,
+                                   token_in=ctx[S + i:S + i + 1])
+            self.model.lmhead_argmax(self.x_row, scratch, self.ws, logits)
+            sample_logits(logits, temperature, top_k, top_p, penalty, ctx[:S + i + 1], ud[i + 1:i + 2],
+                          ctx[S + i + 1:S + i + 2])
+        torch.cuda.current_stream().synchronize()
+        return ctx[S:].cpu().numpy().astype(np.int64)
+
     def decode_forced(self, ids):
         """Teacher-forced greedy steps: step i feeds ids[i] (host ints) and records
         the token the GPU picks next; returns those picks (host)."""

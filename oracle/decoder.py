@@ -362,12 +362,15 @@ def _prep_weights(w, prec):
     return {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
 
 
-def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=False):
+def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=False, sampler=None):
     """Prefill the prompt, then greedy-decode `steps` tokens (default cfg.decode_steps).
 
     glob: vlm_synth.decoder_globals(cfg); layers: list of decoder_layer_weights.
     prefill_split: optional t0 < S; prefill only rows [0, t0) in parallel and
       feed rows t0..S-1 one at a time through the decode path (replay).
+    sampler: optional f(logits, context_ids, i) -> id replacing the greedy argmax
+      of the i-th generated token; context_ids are the prompt ids and the ids
+      generated so far (oracle/sampling.py provides the sampler itself).
     Returns a dict with x_in [S,H], prefill_x [S,H] (hidden after the stack),
     k_cache/v_cache [L,nkv,W,d], logits0 (head of the last prompt row, vocab>0),
     ids [steps+1], margins [steps+1], decode_x [steps,H] (hidden after the
@@ -408,10 +411,17 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
         out = np.concatenate(rows, axis=0)
     res = {"x_in": x_in, "prefill_x": out, "k_cache": kc, "v_cache": vc}
     ids, margins, dec_x, all_logits = [], [], [], []
+    prompt_ids = [int(i) for i in np.asarray(glob["ids"])] if has_vocab else []
+
+    def pick(lg):
+        if sampler is None:
+            return greedy_argmax(lg)
+        return int(sampler(lg, prompt_ids + ids, len(ids)))
+
     if has_vocab:
         lg = lm_head_logits(out[-1], glob["final_norm"], table, cfg.eps, prec)
         res["logits0"] = lg
-        ids.append(greedy_argmax(lg))
+        ids.append(pick(lg))
         margins.append(_top2_margin(lg))
     res["t_prefill_s"] = time.perf_counter() - t_start
     t_start = time.perf_counter()
@@ -425,7 +435,7 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
         dec_x.append(hx[0])
         if has_vocab:
             lg = lm_head_logits(hx[0], glob["final_norm"], table, cfg.eps, prec)
-            ids.append(greedy_argmax(lg))
+            ids.append(pick(lg))
             margins.append(_top2_margin(lg))
             if keep_logits:
                 all_logits.append(lg)

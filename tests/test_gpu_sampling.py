@@ -63,3 +63,37 @@ def test_sampler_top_k_one_is_argmax_and_nonfinite_is_rejected():
     bad[123] = float("nan")
     rt.sample_logits(bad, 0.9, 10, 1.0, 1.0, ctx, torch.tensor([0.5], device="cuda"), out)
     assert int(out.cpu()[0]) == -1
+
+
+@pytest.mark.parametrize("cfg_name", ["c1", "c_mla"])
+def test_sampled_generation_matches_oracle(cfg_name):
+    """Prefill, then sampled generation with the prompt and the generated ids as the penalty context,
+    entirely on the device; the oracle runs the same stack with oracle/sampling.py as its sampler and
+    the same uniform draws. fp32 stacks: ids must match step by step; a mismatch is accepted only at a
+    decision within 1e-4 of a boundary, and the comparison stops there (the sequences diverge)."""
+    from decoder_prefill_decode_amd import pipeline
+    from oracle import decoder as od
+    cfg = vs.scaled(vs.C1 if cfg_name == "c1" else vs.C_MLA, decode_steps=10)
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    T, k, p, r = 1.6, 64, 0.95, 1.3
+    u = vs.sampling_case(20, 2, 0, n_draws=cfg.decode_steps + 1)["u"]
+    infos = []
+
+    def sampler(lg, ctx, i):
+        tok, info = osm.sample_token(lg, ctx, T, k, p, r, float(u[i]))
+        infos.append(info)
+        return tok
+
+    ref = od.run_decoder(cfg, glob, layers, sampler=sampler)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.prefill()
+    got = run.generate_sampled(cfg.decode_steps, T, k, p, r, u)
+    assert len(set(ref["ids"].tolist())) > 1, "the draws never left the top token: the test would be vacuous"
+    for i, (g, e) in enumerate(zip(got, ref["ids"])):
+        if g != e:
+            near = min(infos[i].get("topk_gap", np.inf), infos[i].get("topp_margin", np.inf), infos[i]["cdf_margin"])
+            assert near < 1e-4, f"step {i}: GPU {g} != oracle {e}, nearest boundary {near}"
+            print(f"{cfg_name}: sampled ids agree up to step {i} (boundary case {near:.1e})")
+            return
+    print(f"{cfg_name}: sampled ids {[int(i) for i in got]} agree with the oracle")
