@@ -91,6 +91,46 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__
 // ---------------------------------------------------------------- row norms
 // RMSNorm: y = x * rsqrt(mean(x^2) + eps) * g. LayerNorm: y = (x - mu) * rsqrt(var + eps) * g + b.
 // Output rounded to the operand type. One block per row.
+// Rows of up to NPT * 256 elements: every load of the row and its gain/shift is issued before
+// the first arithmetic (indices clamped, lanes past H masked), and the row stays in registers
+// between the reduction and the output.
+template <class T, bool LAYER, int NPT>
+__global__ __launch_bounds__(256) void norm_rows_reg_kernel(const float* __restrict__ x, int H, int ldx,
+                                                            const T* __restrict__ g, const T* __restrict__ b,
+                                                            float eps, T* __restrict__ out) {
+    __shared__ float red[4];
+    const float* row = x + (size_t)blockIdx.x * ldx;
+    const int tid = threadIdx.x;
+    float v[NPT], gv[NPT], bv[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        const int j = min(tid + 256 * i, H - 1);
+        v[i] = row[j];
+        gv[i] = Elt<T>::ld(g, j);
+        bv[i] = (LAYER && b) ? Elt<T>::ld(b, j) : 0.f;
+    }
+    float mu = 0.f;
+    if (LAYER) {
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < NPT; i++) sm += tid + 256 * i < H ? v[i] : 0.f;
+        mu = block_sum<256>(sm, red) / (float)H;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        const float c = v[i] - mu;
+        ss += tid + 256 * i < H ? c * c : 0.f;
+    }
+    const float r = rsqrtf(block_sum<256>(ss, red) / (float)H + eps);
+    T* o = out + (size_t)blockIdx.x * H;
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        const int j = tid + 256 * i;
+        if (j < H) Elt<T>::st(o, j, (v[i] - mu) * r * gv[i] + bv[i]);
+    }
+}
+
 template <class T, bool LAYER>
 __global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict__ x, int H, int ldx,
                                                         const T* __restrict__ g, const T* __restrict__ b, float eps,
@@ -322,20 +362,32 @@ hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t st) 
     return hipGetLastError();
 }
 
+template <class T, bool LAYER>
+static void norm_rows_dispatch(const float* x, int R, int H, int ldx, const void* gain, const void* shift, float eps,
+                               void* out, hipStream_t st) {
+    const T* g = (const T*)gain;
+    const T* b = (const T*)shift;
+    const int npt = (H + 255) / 256;
+#define VLM_NORM_REG(N) norm_rows_reg_kernel<T, LAYER, N><<<R, 256, 0, st>>>(x, H, ldx, g, b, eps, (T*)out)
+    if (npt <= 2) VLM_NORM_REG(2);
+    else if (npt <= 4) VLM_NORM_REG(4);
+    else if (npt <= 8) VLM_NORM_REG(8);
+    else if (npt <= 12) VLM_NORM_REG(12);
+    else if (npt <= 16) VLM_NORM_REG(16);
+    else norm_rows_kernel<T, LAYER><<<R, 256, 0, st>>>(x, H, ldx, g, b, eps, (T*)out);
+#undef VLM_NORM_REG
+}
+
 hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H, const void* gain, const void* shift,
                             float eps, void* out, hipStream_t st, int ldx) {
     if (ldx <= 0) ldx = H;
-    if (R <= 0) return hipSuccess;
+    if (R <= 0 || H <= 0) return hipSuccess;
     if (dtype == 1) {
-        if (layer)
-            norm_rows_kernel<bf16_t, true><<<R, 256, 0, st>>>(x, H, ldx, (const bf16_t*)gain, (const bf16_t*)shift, eps, (bf16_t*)out);
-        else
-            norm_rows_kernel<bf16_t, false><<<R, 256, 0, st>>>(x, H, ldx, (const bf16_t*)gain, nullptr, eps, (bf16_t*)out);
+        if (layer) norm_rows_dispatch<bf16_t, true>(x, R, H, ldx, gain, shift, eps, out, st);
+        else norm_rows_dispatch<bf16_t, false>(x, R, H, ldx, gain, nullptr, eps, out, st);
     } else {
-        if (layer)
-            norm_rows_kernel<float, true><<<R, 256, 0, st>>>(x, H, ldx, (const float*)gain, (const float*)shift, eps, (float*)out);
-        else
-            norm_rows_kernel<float, false><<<R, 256, 0, st>>>(x, H, ldx, (const float*)gain, nullptr, eps, (float*)out);
+        if (layer) norm_rows_dispatch<float, true>(x, R, H, ldx, gain, shift, eps, out, st);
+        else norm_rows_dispatch<float, false>(x, R, H, ldx, gain, nullptr, eps, out, st);
     }
     return hipGetLastError();
 }
