@@ -176,3 +176,30 @@ def test_generic_gemv_fallback_shapes(rt):
     assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["bf16"]
     out = run.decode_hidden(run.dec_x).cpu().numpy()
     assert rel(out, ref["decode_x"]) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ decode attention forms
+def test_decode_past_a_thousand_slots(rt):
+    """A prompt of 1016 rows and 16 decode steps in a 1152-slot window: the
+    decode attention splits the window into 32 ranges of 36 slots, so every
+    split holds valid keys and the merge combines 32 live partial rows. The
+    graph loop and the eager steps must give the oracle's ids and cache rows
+    (fp32: 1e-4)."""
+    pipeline, _ = rt
+    cfg = vs.scaled(vs.C1, seq=1016, decode_steps=16, capacity=1152, name="c1_long")
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    T = cfg.seq + cfg.decode_steps
+    runs = []
+    for loop in (True, False):
+        run = gpu_run(pipeline, cfg, glob, layers)
+        run.prefill()
+        tok0 = int(run.first_token()[0])
+        ids = [tok0] + list(run.decode(cfg.decode_steps, loop=loop))
+        assert ids == list(ref["ids"]), f"loop={loop}"
+        for l in range(cfg.n_layers):
+            k, v = kv_host(run, l)
+            assert rel(k[:, :T], ref["k_cache"][l][:, :T]) <= TOL["f32"]
+            assert rel(v[:, :T], ref["v_cache"][l][:, :T]) <= TOL["f32"]
+        runs.append(ids)
+    assert runs[0] == runs[1]
