@@ -433,6 +433,7 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
     void* qb = P(d_ws, w.q);
     void* ob = P(d_ws, w.o);
     void* ab = P(d_ws, w.a);
+    bool normed = false;  // hbuf already holds this layer's input norm (written by the previous reduction)
     for (int l = 0; l < desc->n_layers; l++) {
         const vlm_layer& y = h_layers[l];
         const vlm_mask& mk = h_masks[n_masks == 1 ? 0 : l];
@@ -447,7 +448,8 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
             vd = kv->vptr(l);
             ldkv = kv->capacity;
         }
-        HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.attn_norm, y.attn_norm_b, desc->norm_eps, hbuf, stream));
+        if (!normed)
+            HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.attn_norm, y.attn_norm_b, desc->norm_eps, hbuf, stream));
         float* gpart = (float*)P(d_ws, w.gpart);
         GemmArgs g{};
         if (mla) {
@@ -495,11 +497,16 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
         at.S = S; at.nq = nq; at.nkv = nkv; at.d = hd; at.dv = dv; at.pos0 = pos0; at.nkeys = pos0 + S;
         at.mask_kind = mk.kind; at.add = mk.add; at.ld_add = mk.ld_add; at.seg = mk.seg;
         HIP_TRY(launch_attn_prefill(dt, at, stream));
+        // O projection + residual; a split-K reduction also writes the post-attention norm of the rows
+        int fused = 0;
         g = GemmArgs{};
         g.A = ob; g.B = y.wo; g.bias = vit ? y.bo : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = nq * dv; g.ldo = H;
         g.part = gpart; g.part_cap = w.gpart_floats;
+        g.norm_gain = y.mlp_norm; g.norm_shift = vit ? y.mlp_norm_b : nullptr; g.norm_eps = desc->norm_eps;
+        g.norm_layer = vit; g.norm_out = hbuf; g.fused_norm = &fused;
         HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
-        HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.mlp_norm, y.mlp_norm_b, desc->norm_eps, hbuf, stream));
+        if (!fused)
+            HIP_TRY(launch_norm_rows(dt, vit, d_x, S, H, y.mlp_norm, y.mlp_norm_b, desc->norm_eps, hbuf, stream));
         g = GemmArgs{};
         g.A = hbuf; g.B = y.w1; g.out = ab; g.M = S; g.K = H; g.ldo = F;
         g.part = gpart; g.part_cap = w.gpart_floats;
@@ -510,10 +517,18 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
             g.N = 2 * F;
             HIP_TRY(launch_gemm(dt, Epi::SwiGLU, g, stream));
         }
+        // down projection + residual; a split-K reduction also writes the next layer's input norm
+        fused = 0;
         g = GemmArgs{};
         g.A = ab; g.B = y.w2; g.bias = vit ? y.b2 : nullptr; g.out = d_x; g.M = S; g.N = H; g.K = F; g.ldo = H;
         g.part = gpart; g.part_cap = w.gpart_floats;
+        if (l + 1 < desc->n_layers) {
+            const vlm_layer& yn = h_layers[l + 1];
+            g.norm_gain = yn.attn_norm; g.norm_shift = vit ? yn.attn_norm_b : nullptr; g.norm_eps = desc->norm_eps;
+            g.norm_layer = vit; g.norm_out = hbuf; g.fused_norm = &fused;
+        }
         HIP_TRY(launch_gemm(dt, Epi::Resid, g, stream));
+        normed = fused != 0;
     }
     if (!vit) {
         HIP_TRY(launch_set_len(kv->dlen(), pos0 + S, stream));

@@ -28,6 +28,16 @@ struct GemmArgs {
     int ldo;           // row stride of `out` in elements
     float* part = nullptr;  // split-K scratch (fp32 [splits][M][N]); null: no split-K
     size_t part_cap = 0;    // floats available at `part`
+    // Epi::Resid with norm_out set: when the GEMM splits K (and N <= 4096), the reduction that adds
+    // the partials into the residual rows also writes their RMSNorm (LayerNorm when norm_layer)
+    // with norm_gain / norm_shift to norm_out ([M][N], model type) and sets *fused_norm = 1.
+    // Bitwise the same rows as a separate launch_norm_rows over the updated x.
+    const void* norm_gain = nullptr;
+    const void* norm_shift = nullptr;
+    float norm_eps = 0.f;
+    bool norm_layer = false;
+    void* norm_out = nullptr;
+    int* fused_norm = nullptr;  // host flag
 };
 
 // dtype: 0 = f32, 1 = bf16 (vlm_dtype values)

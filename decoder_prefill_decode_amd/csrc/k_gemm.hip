@@ -402,6 +402,102 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int spli
     }
 }
 
+// Split-K reduction of a residual GEMM fused with the row norm that follows it:
+// one block per row, thread t owns columns t + 256 i (the column split and the
+// summation order of norm_rows_reg_kernel, so the normalised row is bitwise the
+// one a separate norm launch would write). x[m] += sum of the partials (split
+// order) + bias, then norm_out[m] = norm(x[m]).
+constexpr int kReduceNormMaxSplits = 8;
+template <class T, bool LAYER, int NPT>
+__global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs a, int splits) {
+    constexpr int SM = kReduceNormMaxSplits;
+    __shared__ float red[4];
+    const int m = blockIdx.x, N = a.N, tid = threadIdx.x;
+    const size_t MN = (size_t)a.M * N;
+    const T* bias = (const T*)a.bias;
+    const T* gn = (const T*)a.norm_gain;
+    const T* sh = (const T*)a.norm_shift;
+    float* x = (float*)a.out + (size_t)m * a.ldo;
+    const float* pr = a.part + (size_t)m * N;
+    // every load of the row is requested before the first sum (split and column indices clamped)
+    float pv[SM][NPT], xv[NPT], gv[NPT], bv[NPT], cb[NPT];
+#pragma unroll
+    for (int sp = 0; sp < SM; sp++)
+#pragma unroll
+        for (int i = 0; i < NPT; i++) pv[sp][i] = pr[(size_t)min(sp, splits - 1) * MN + min(tid + 256 * i, N - 1)];
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        const int j = min(tid + 256 * i, N - 1);
+        xv[i] = x[j];
+        cb[i] = bias ? Elt<T>::ld(bias, j) : 0.f;
+        gv[i] = Elt<T>::ld(gn, j);
+        bv[i] = (LAYER && sh) ? Elt<T>::ld(sh, j) : 0.f;
+    }
+    float v[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        float acc = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < SM; sp++)
+            if (sp < splits) acc += pv[sp][i];
+        if (bias) acc += cb[i];
+        v[i] = xv[i] + acc;
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; i++)
+        if (tid + 256 * i < N) x[tid + 256 * i] = v[i];
+    float mu = 0.f;
+    if (LAYER) {
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < NPT; i++) sm += tid + 256 * i < N ? v[i] : 0.f;
+        mu = block_sum<256>(sm, red) / (float)N;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        const float c = v[i] - mu;
+        ss += tid + 256 * i < N ? c * c : 0.f;
+    }
+    const float r = rsqrtf(block_sum<256>(ss, red) / (float)N + a.norm_eps);
+    T* o = (T*)a.norm_out + (size_t)m * N;
+#pragma unroll
+    for (int i = 0; i < NPT; i++) {
+        const int j = tid + 256 * i;
+        if (j < N) Elt<T>::st(o, j, (v[i] - mu) * r * gv[i] + bv[i]);
+    }
+}
+
+// The reduction of a split residual GEMM: fused with the following row norm when the caller asked
+// for it and the row fits the register form (N <= 4096), else the plain reduction.
+template <class T, Epi EPI>
+static hipError_t run_reduce(const GemmArgs& a, int splits, hipStream_t st) {
+    if constexpr (EPI == Epi::Resid) {
+        if (a.norm_out && a.norm_gain && a.N <= 4096 && splits <= kReduceNormMaxSplits) {
+            const int npt = (a.N + 255) / 256;
+#define VLM_RED_NORM(NPT_)                                                                                \
+    do {                                                                                                  \
+        if (a.norm_layer) splitk_reduce_norm_kernel<T, true, NPT_><<<a.M, 256, 0, st>>>(a, splits);       \
+        else splitk_reduce_norm_kernel<T, false, NPT_><<<a.M, 256, 0, st>>>(a, splits);                   \
+    } while (0)
+            if (npt <= 2) VLM_RED_NORM(2);
+            else if (npt <= 4) VLM_RED_NORM(4);
+            else if (npt <= 8) VLM_RED_NORM(8);
+            else if (npt <= 12) VLM_RED_NORM(12);
+            else VLM_RED_NORM(16);
+#undef VLM_RED_NORM
+            const hipError_t e = hipGetLastError();
+            if (e == hipSuccess && a.fused_norm) *a.fused_norm = 1;
+            return e;
+        }
+    }
+    const size_t total = (size_t)a.M * (EPI == Epi::SwiGLU ? a.N / 2 : a.N);
+    int blocks = (int)((total + 255) / 256);
+    blocks = blocks > 4096 ? 4096 : blocks;
+    splitk_reduce_kernel<T, EPI><<<blocks, 256, 0, st>>>(a, splits);
+    return hipGetLastError();
+}
+
 template <class T, int BM, int BN, Epi EPI, bool SPLIT>
 static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     using Tr = GemmTraits<T>;
@@ -417,11 +513,7 @@ static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     gemm_kernel<T, BM, BN, EPI, SPLIT><<<dim3(mt * nt, SPLIT ? splits : 1), 256, smem, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
-    const size_t total = (size_t)a.M * (EPI == Epi::SwiGLU ? a.N / 2 : a.N);
-    int blocks = (int)((total + 255) / 256);
-    blocks = blocks > 4096 ? 4096 : blocks;
-    splitk_reduce_kernel<T, EPI><<<blocks, 256, 0, st>>>(a, splits);
-    return hipGetLastError();
+    return run_reduce<T, EPI>(a, splits, st);
 }
 
 template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK>
@@ -438,11 +530,7 @@ static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
     gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
-    const size_t total = (size_t)a.M * (EPI == Epi::SwiGLU ? a.N / 2 : a.N);
-    int blocks = (int)((total + 255) / 256);
-    blocks = blocks > 4096 ? 4096 : blocks;
-    splitk_reduce_kernel<bf16_t, EPI><<<blocks, 256, 0, st>>>(a, splits);
-    return hipGetLastError();
+    return run_reduce<bf16_t, EPI>(a, splits, st);
 }
 
 // Blocks a prefill GEMM aims for before it splits K (several blocks per CU

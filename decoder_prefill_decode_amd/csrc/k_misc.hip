@@ -158,62 +158,81 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- QK-Norm + RoPE + cache write
-// One wavefront per (row, head); lane p < d/2 owns rotation pair p, i.e. the
-// output elements i0 = g*sd + j and i1 = i0 + sd/2 of segment g (sd =
-// d/segments). rotate_half(a, b) = (-b, a): y[i0] = a cos - b sin,
-// y[i1] = b cos + a sin, where (a, b) are the inputs at (i0, i1), or at
+// A wavefront takes IT consecutive (row, head) items; lane p < d/2 owns
+// rotation pair p, i.e. the output elements i0 = g*sd + j and i1 = i0 + sd/2
+// of segment g (sd = d/segments). rotate_half(a, b) = (-b, a): y[i0] = a cos -
+// b sin, y[i1] = b cos + a sin, where (a, b) are the inputs at (i0, i1), or at
 // (g*sd + 2j, g*sd + 2j + 1) for interleaved RoPE (the adjacent pair,
 // de-interleaved into the rotate-half order; V is copied unpermuted). The
 // per-head RMSNorm gain is indexed by where the element sits when the norm
-// runs: input order before the rotation, output order after it.
+// runs: input order before the rotation, output order after it. Every item's
+// inputs and table entries are requested before the first item is computed,
+// so a wavefront has IT items' loads in flight instead of one.
+constexpr int kRopeItems = 4;
 template <class T>
 __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
-    const int wave = blockIdx.x * 4 + threadIdx.x / kWave;
+    constexpr int IT = kRopeItems;
     const int lane = threadIdx.x % kWave;
-    const int nh = a.nq + 2 * a.nkv;
-    if (wave >= a.S * nh) return;
-    const int s = wave / nh, h = wave % nh;
+    const int nh = a.nq + 2 * a.nkv, total = a.S * nh;
+    const int w0 = (blockIdx.x * 4 + threadIdx.x / kWave) * IT;
+    if (w0 >= total) return;
     const int d = a.d, half = d / 2;
     const int base = a.pos_dev ? a.pos_dev[0] : a.pos0;
-    const int pos = base + s;
-    const float* src = a.qkv + (size_t)s * nh * d + (size_t)h * d;
     const bool on = lane < half;
     const int sd = d / a.segments, sh = sd / 2;
     const int g = on ? lane / sh : 0, j = on ? lane % sh : 0;
     const int i0 = g * sd + j, i1 = i0 + sh;
-    if (h >= a.nq + a.nkv) {  // V head: plain copy (rounded to the cache type)
-        if (on) {
-            T* dst = (T*)a.vdst + ((size_t)(h - a.nq - a.nkv) * a.ldkv + pos) * d;
-            Elt<T>::st(dst, i0, src[i0]);
-            Elt<T>::st(dst, i1, src[i1]);
-        }
-        return;
-    }
     const int r0 = a.interleave ? g * sd + 2 * j : i0, r1 = a.interleave ? r0 + 1 : i1;
-    float x0 = on ? src[r0] : 0.f, x1 = on ? src[r1] : 0.f;
-    const bool isq = h < a.nq;
-    const T* gn = (const T*)(isq ? a.qn : a.kn);
-    if (gn && !a.norm_after) {
-        const float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) / (float)d + a.eps);
-        if (on) {
-            x0 = x0 * r * Elt<T>::ld(gn, r0);
-            x1 = x1 * r * Elt<T>::ld(gn, r1);
-        }
+    float x0[IT], x1[IT], c0[IT], c1[IT], s0[IT], s1[IT];
+#pragma unroll
+    for (int it = 0; it < IT; it++) {  // items past the end re-read the last one and are not stored
+        const int item = min(w0 + it, total - 1), s = item / nh, h = item % nh;
+        const float* src = a.qkv + (size_t)s * nh * d + (size_t)h * d;
+        const bool isv = h >= a.nq + a.nkv;
+        const size_t ro = (size_t)(base + s) * d;
+        x0[it] = on ? src[isv ? i0 : r0] : 0.f;
+        x1[it] = on ? src[isv ? i1 : r1] : 0.f;
+        c0[it] = on ? a.cos[ro + i0] : 0.f;
+        c1[it] = on ? a.cos[ro + i1] : 0.f;
+        s0[it] = on ? a.sin[ro + i0] : 0.f;
+        s1[it] = on ? a.sin[ro + i1] : 0.f;
     }
-    const size_t ro = (size_t)pos * d;
-    float y0 = on ? x0 * a.cos[ro + i0] - x1 * a.sin[ro + i0] : 0.f;
-    float y1 = on ? x1 * a.cos[ro + i1] + x0 * a.sin[ro + i1] : 0.f;
-    if (gn && a.norm_after) {  // the rotation keeps the sum of squares; the norm sees the rotated values
-        const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)d + a.eps);
-        if (on) {
-            y0 = y0 * r * Elt<T>::ld(gn, i0);
-            y1 = y1 * r * Elt<T>::ld(gn, i1);
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        if (w0 + it >= total) break;  // uniform
+        const int item = w0 + it, s = item / nh, h = item % nh, pos = base + s;
+        if (h >= a.nq + a.nkv) {  // V head: plain copy (rounded to the cache type)
+            if (on) {
+                T* dst = (T*)a.vdst + ((size_t)(h - a.nq - a.nkv) * a.ldkv + pos) * d;
+                Elt<T>::st(dst, i0, x0[it]);
+                Elt<T>::st(dst, i1, x1[it]);
+            }
+            continue;
         }
+        float u0 = x0[it], u1 = x1[it];
+        const bool isq = h < a.nq;
+        const T* gn = (const T*)(isq ? a.qn : a.kn);
+        if (gn && !a.norm_after) {
+            const float r = rsqrtf(wave_sum(u0 * u0 + u1 * u1) / (float)d + a.eps);
+            if (on) {
+                u0 = u0 * r * Elt<T>::ld(gn, r0);
+                u1 = u1 * r * Elt<T>::ld(gn, r1);
+            }
+        }
+        float y0 = on ? u0 * c0[it] - u1 * s0[it] : 0.f;
+        float y1 = on ? u1 * c1[it] + u0 * s1[it] : 0.f;
+        if (gn && a.norm_after) {  // the rotation keeps the sum of squares; the norm sees the rotated values
+            const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)d + a.eps);
+            if (on) {
+                y0 = y0 * r * Elt<T>::ld(gn, i0);
+                y1 = y1 * r * Elt<T>::ld(gn, i1);
+            }
+        }
+        if (!on) continue;
+        T* dst = isq ? (T*)a.q + ((size_t)h * a.ldq + s) * d : (T*)a.kdst + ((size_t)(h - a.nq) * a.ldkv + pos) * d;
+        Elt<T>::st(dst, i0, y0);
+        Elt<T>::st(dst, i1, y1);
     }
-    if (!on) return;
-    T* dst = isq ? (T*)a.q + ((size_t)h * a.ldq + s) * d : (T*)a.kdst + ((size_t)(h - a.nq) * a.ldkv + pos) * d;
-    Elt<T>::st(dst, i0, y0);
-    Elt<T>::st(dst, i1, y1);
 }
 
 // ---------------------------------------------------------------- expanded MLA: assembly + RoPE + cache write
@@ -393,8 +412,9 @@ hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H,
 }
 
 hipError_t launch_rope_qkv(int dtype, const RopeArgs& a, hipStream_t st) {
-    const int waves = a.S * (a.nq + 2 * a.nkv);
-    if (waves <= 0) return hipSuccess;
+    const int items = a.S * (a.nq + 2 * a.nkv);
+    if (items <= 0) return hipSuccess;
+    const int waves = (items + kRopeItems - 1) / kRopeItems;
     const int blocks = (waves + 3) / 4;
     if (dtype == 1)
         rope_qkv_kernel<bf16_t><<<blocks, 256, 0, st>>>(a);

@@ -203,3 +203,54 @@ def test_decode_past_a_thousand_slots(rt):
             assert rel(v[:, :T], ref["v_cache"][l][:, :T]) <= TOL["f32"]
         runs.append(ids)
     assert runs[0] == runs[1]
+
+
+# ------------------------------------------------------------------ degenerate and ragged prompts
+EDGE = [
+    # one-token prompt, no image rows
+    vs.scaled(vs.C1, seq=1, n_img=0, img_start=0, decode_steps=5, capacity=8, name="c1_s1"),
+    # ragged prompt (not a multiple of any tile), image span ending one row before the last
+    vs.scaled(vs.C1, seq=37, n_img=5, img_start=31, decode_steps=6, capacity=48, name="c1_s37"),
+    # every prompt row is an image row; the window is filled exactly by the last decode step
+    vs.scaled(vs.C1, seq=16, n_img=16, img_start=0, decode_steps=8, capacity=24, name="c1_all_img"),
+    # bf16 4B-class layer shape, ragged prompt with no image rows
+    vs.scaled(vs.C4, n_layers=2, vocab=4096, seq=77, n_img=0, img_start=0, decode_steps=6, capacity=96,
+              name="c4_s77"),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
+def test_degenerate_and_ragged_prompts(rt, cfg):
+    """Prompt lengths 1, 37 and 77 (ragged against every tile), a prompt made
+    only of image rows, no image rows, and a window filled to its last slot:
+    prefill rows, first-token logits, KV rows and greedy ids against the
+    oracle (fp32 1e-4, bf16 2e-2; bf16 ids with near-ties attributed)."""
+    pipeline, _ = rt
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    run = gpu_run(pipeline, cfg, glob, layers)
+    x = run.prefill()
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    tok0 = int(run.first_token(logits)[0])
+    tol = TOL[cfg.dtype]
+    lg = logits.cpu().numpy()
+    assert rel(x.cpu().numpy(), ref["prefill_x"]) <= tol
+    assert rel(lg, ref["logits0"]) <= tol
+    free = [tok0] + list(run.decode(cfg.decode_steps))
+    assert run.kv.len() == cfg.seq + cfg.decode_steps <= cfg.capacity
+    T = cfg.seq + cfg.decode_steps
+    for l in range(cfg.n_layers):
+        k, v = kv_host(run, l)
+        if cfg.dtype == "f32":
+            assert rel(k[:, :T], ref["k_cache"][l][:, :T]) <= tol
+            assert rel(v[:, :T], ref["v_cache"][l][:, :T]) <= tol
+        else:  # free-running bf16 ids may leave the oracle's path at a near-tie: compare the prompt slots
+            assert rel(k[:, :cfg.seq], ref["k_cache"][l][:, :cfg.seq]) <= tol
+            assert rel(v[:, :cfg.seq], ref["v_cache"][l][:, :cfg.seq]) <= tol
+    if cfg.dtype == "f32":
+        assert free == list(ref["ids"])
+    else:
+        run.kv.truncate(cfg.seq)
+        forced = [tok0] + list(run.decode_forced(ref["ids"][:-1]))
+        eps = 8 * float(np.abs(lg - ref["logits0"]).max())
+        check_ids(free, forced, ref["ids"], ref["margins"], eps)
