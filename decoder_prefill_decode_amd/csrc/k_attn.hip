@@ -523,8 +523,12 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
     __shared__ float qs[G][D];
     __shared__ __attribute__((aligned(16))) T knew[D];
     __shared__ __attribute__((aligned(16))) T vnew[D];
-    __shared__ float sm_m[NW][G], sm_l[NW][G];
-    __shared__ float sm_o[NW][G][D];
+    // LDS merge: one (m, l, o) partial per 16-lane quarter (NQ = NW * 4 of them) when they fit;
+    // otherwise the quarters merge in registers first and one partial per wavefront is stored
+    constexpr bool QMERGE = NW * 4 * G * D * 4 <= 48 * 1024;
+    constexpr int NQ = QMERGE ? NW * 4 : NW;
+    __shared__ float sm_m[NQ][G], sm_l[NQ][G];
+    __shared__ float sm_o[NQ][G][D];
     const int g = blockIdx.x, sp = blockIdx.y;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
     const int chunk = (a.W + a.nsplit - 1) / a.nsplit;
@@ -713,6 +717,24 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
             }
         }
     }
+    if constexpr (QMERGE) {
+        // every quarter stores its partial; the block merges the NQ partials of each head below
+        const int slot = w * 4 + kq;
+#pragma unroll
+        for (int gg = 0; gg < G; gg++) {
+#pragma unroll
+            for (int c = 0; c < CPL; c++) {
+                const int ch = sub + 16 * c;
+                if (ch < CH)
+#pragma unroll
+                    for (int i = 0; i < VEC; i++) sm_o[slot][gg][ch * VEC + i] = o[gg][c][i];
+            }
+            if (sub == 0) {
+                sm_m[slot][gg] = mrun[gg];
+                sm_l[slot][gg] = lrun[gg];
+            }
+        }
+    } else {
     // merge the four 16-lane quarters of the wavefront (lane pairs l, l^16 then
     // l, l^32; each pair computes the same symmetric merge), then the wavefronts
 #pragma unroll
@@ -748,20 +770,21 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
             }
         }
     }
+    }
     __syncthreads();
     for (int idx = tid; idx < G * (D + 2); idx += NW * kWave) {
         const int gg = idx / (D + 2), e = idx % (D + 2);
         float mx = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < NW; ww++) mx = fmaxf(mx, sm_m[ww][gg]);
+        for (int q = 0; q < NQ; q++) mx = fmaxf(mx, sm_m[q][gg]);
         float v = 0.f;
         if (e == D) {
             v = mx;
         } else {
 #pragma unroll
-            for (int ww = 0; ww < NW; ww++) {
-                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[ww][gg] - mx);
-                v += f * (e < D ? sm_o[ww][gg][e] : sm_l[ww][gg]);
+            for (int q = 0; q < NQ; q++) {
+                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[q][gg] - mx);
+                v += f * (e < D ? sm_o[q][gg][e] : sm_l[q][gg]);
             }
         }
         a.partial[((size_t)(g * G + gg) * a.nsplit + sp) * PS + e] = v;
