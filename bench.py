@@ -10,7 +10,11 @@ Inputs and weights are resident in HBM before the timed region.
 Default workload: the 36-layer 4B-class bf16 stack (hidden 2560, 32/8 heads
 of 80, FFN 9728, tied vocabulary 128256, 2048-slot window), 512-token prompt
 with a 322-row image span, 256 decode steps. --config c3_qwen3_28l runs the
-28-layer Qwen3-style stack (vocabulary 151936) the same way.
+28-layer Qwen3-style stack (vocabulary 151936) the same way. --config
+c5_vit_27l times the 27-layer window/full-attention vision tower with its 2x2
+merger instead (one step = one tower pass over the 1288 patch rows; fp32, or
+bf16 storage with fp32 accumulation with --vit-dtype bf16), with the roofline of
+the whole pass against the matrix-core peak of its type.
 
 Prints one JSON line: value = (prompt + generated tokens) / step time, with
 the prefill and decode rates beside it, the roofline of the dominant kernel
@@ -55,6 +59,8 @@ def parse():
                     help="run N prefills (embed, inject, all layers, first-token head) and exit; the run the "
                          "MFMA counters are collected on")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--vit-dtype", default="f32", choices=("f32", "bf16"),
+                    help="storage type of the vision tower (c5_vit_27l only)")
     ap.add_argument("--traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --kernel-only run "
                          "into profiles/traffic.json and exit")
@@ -279,6 +285,83 @@ def cpu_baseline(cfg, glob, layers, n_dec):
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu, "blas": blas}
 
 
+def vit_flops(cfg, row_seg):
+    """Algorithmic FLOPs of one tower pass: linear layers, attention over the visible pairs of each
+    layer's mask (windows or full), the merger MLP."""
+    import numpy as np
+    N, H, F, hd = cfg.n_patches, cfg.hidden, cfg.ffn, cfg.n_heads * cfg.head_dim
+    lin = 2.0 * N * (3 * H * hd + hd * H + 2 * F * H)
+    _, counts = np.unique(row_seg, return_counts=True)
+    pairs_win = float(np.sum(counts.astype(np.float64) ** 2))
+    attn = [4.0 * hd * (N * N if l in cfg.full_layers else pairs_win) for l in range(cfg.n_layers)]
+    m2 = cfg.merge * cfg.merge
+    merger = 2.0 * (N // m2) * (m2 * H * cfg.merger_hidden + cfg.merger_hidden * cfg.out_dim)
+    return cfg.n_layers * lin + sum(attn) + merger
+
+
+def vit_main(args, cfg):
+    """One tower pass per step; the oracle tower on this host beside it."""
+    import numpy as np
+    import torch
+
+    import vlm_synth as vs
+    from decoder_prefill_decode_amd.pipeline import VitRun
+    if args.vit_dtype != cfg.dtype:
+        cfg = vs.scaled_vit(cfg, dtype=args.vit_dtype)
+    t_gen = time.perf_counter()
+    glob = vs.vit_globals(cfg)
+    layers = [vs.vit_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    run = VitRun(cfg, lambda l: layers[l], glob)
+    torch.cuda.synchronize()
+    print(f"# {cfg.name} ({cfg.dtype}): weights generated and resident in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        run.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        run.run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    pass_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    t_ms = float(np.median(pass_ms))
+    flops = vit_flops(cfg, run.row_seg)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops / (t_ms * 1e-3) / 1e12
+    N = cfg.n_patches
+    print(f"# tower pass {t_ms:.3f} ms ({flops / 1e9:.1f} GFLOP, {achieved:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+    out = {
+        "metric": METRIC, "value": round(N / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.n_layers}-layer vision tower, hidden {cfg.hidden}, "
+                               f"{cfg.n_heads} heads x {cfg.head_dim}, FFN {cfg.ffn}, {N} patches on a "
+                               f"{cfg.grid_h}x{cfg.grid_w} grid, window {cfg.window}x{cfg.window} merged cells, "
+                               f"full attention on layers {list(cfg.full_layers)}, 2x2 merge -> {cfg.out_dim}",
+                   "prefill_tokens": N, "global_batch": 1, "seq_len": N, "parallelism": "single GPU"},
+        "prefill_tok_s": round(N / (t_ms * 1e-3), 1), "prefill_ms": round(t_ms, 3),
+        "prefill_mfma_frac": round(achieved / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "whole tower pass",
+                     "flops_per_pass": flops, "avg_pass_ms": round(t_ms, 3)},
+        "step_ms_median": round(t_ms, 3), "step_ms_min": round(float(np.min(pass_ms)), 3),
+    }
+    if not args.no_cpu:
+        from oracle import vit as ov
+        t0 = time.perf_counter()
+        ov.run_vit(cfg, glob, layers)
+        t_cpu = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": N / t_cpu, "unit": "tok/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"{cfg.name}: one whole oracle tower pass ({t_cpu:.1f} s)"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.traffic:
@@ -298,6 +381,9 @@ def main():
     from decoder_prefill_decode_amd.pipeline import DecoderRun
 
     cfg = vs.ALL_CONFIGS[args.config]
+    if isinstance(cfg, vs.VitConfig):
+        vit_main(args, cfg)
+        return
     t_gen = time.perf_counter()
     glob = vs.decoder_globals(cfg)
     keep_layers = not args.no_cpu and args.kernel_only is None

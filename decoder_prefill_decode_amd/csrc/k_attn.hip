@@ -523,9 +523,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
     __shared__ float qs[G][D];
     __shared__ __attribute__((aligned(16))) T knew[D];
     __shared__ __attribute__((aligned(16))) T vnew[D];
-    // LDS merge: one (m, l, o) partial per 16-lane quarter (NQ = NW * 4 of them) when they fit;
-    // otherwise the quarters merge in registers first and one partial per wavefront is stored
-    constexpr bool QMERGE = NW * 4 * G * D * 4 <= 48 * 1024;
+    // LDS merge: one (m, l, o) partial per 16-lane quarter (NQ = NW * 4 of them) for groups of 4+
+    // query heads whose partials fit (the register merge there costs 2 * G * 8 permlane swaps per
+    // lane); otherwise the quarters merge in registers first and one partial per wavefront is stored
+    constexpr bool QMERGE = G >= 4 && NW * 4 * G * D * 4 <= 48 * 1024;
     constexpr int NQ = QMERGE ? NW * 4 : NW;
     __shared__ float sm_m[NQ][G], sm_l[NQ][G];
     __shared__ float sm_o[NQ][G][D];
