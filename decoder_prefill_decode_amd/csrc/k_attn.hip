@@ -33,6 +33,59 @@ namespace vlm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Key tiles a query block has to visit under a segment (window) mask: a tile
+// can hold a visible key only if some key in it has a segment id within
+// [min, max] of the block's query segments, so every other tile is skipped
+// (exact for any id assignment; with windows laid out contiguously, as the
+// vision tower does, a block visits only the tiles of its own windows instead
+// of the whole sequence). Writes the visited tiles in order to list and
+// returns their count; all threads of the block take part.
+// Under a segment mask: true when every query row of this wavefront (lane % 32 -> row q0 + lane % 32)
+// and every key of the tile [key0, key0 + BKEY) lie in one and the same segment, so the tile needs no
+// per-element test. Wavefront-uniform.
+template <int BKEY>
+__device__ __forceinline__ bool segment_tile_full(const int32_t* seg, int seg_q, bool row_ok, int key0, int nkeys) {
+    const int s0 = __builtin_amdgcn_readfirstlane(seg_q);
+    const int lane = threadIdx.x % kWave;
+    const int key = key0 + lane % BKEY;
+    const bool key_ok = key < nkeys && seg[min(key, nkeys - 1)] == s0;
+    return __all(row_ok && seg_q == s0 && key_ok);
+}
+
+constexpr int kSegMaxTiles = 512;
+template <int NT, int BKEY>
+__device__ int segment_tiles(const int32_t* seg, int row0, int nrows, int S, int nkeys, int nkt, short* list,
+                             unsigned char* flag, int* lohi) {
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        lohi[0] = 0x7fffffff;
+        lohi[1] = (int)0x80000000;
+    }
+    for (int t = tid; t < nkt; t += NT) flag[t] = 0;
+    __syncthreads();
+    for (int r = tid; r < nrows; r += NT)
+        if (row0 + r < S) {
+            const int sv = seg[row0 + r];
+            atomicMin(lohi, sv);
+            atomicMax(lohi + 1, sv);
+        }
+    __syncthreads();
+    const int lo = lohi[0], hi = lohi[1];
+    for (int k = tid; k < nkeys; k += NT) {
+        const int sv = seg[k];
+        if (sv >= lo && sv <= hi) flag[k / BKEY] = 1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int n = 0;
+        for (int t = 0; t < nkt; t++)
+            if (flag[t]) list[n++] = (short)t;
+        lohi[2] = n;
+    }
+    __syncthreads();
+    return lohi[2];
+}
+
 // ============================================================== prefill, bf16
 // A block covers 64 query rows of one head with 4 wavefronts: wavefronts
 // w and w+2 own the same 32 rows and take alternate 64-key tiles (a pair of
@@ -102,6 +155,15 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
     }
     const int seg_q = (MASK == VLM_MASK_SEGMENT_ID && qrow < S) ? a.seg[qrow] : 0;
     const int nkt = (kend + BKEY - 1) / BKEY;
+    // tiles visited, in order: all of them, or under a segment mask those that can hold a visible key
+    int nvis = nkt;
+    __shared__ short tlist[MASK == VLM_MASK_SEGMENT_ID ? kSegMaxTiles : 1];
+    __shared__ unsigned char tflag[MASK == VLM_MASK_SEGMENT_ID ? kSegMaxTiles : 1];
+    __shared__ int tlohi[3];
+    const bool listed = MASK == VLM_MASK_SEGMENT_ID && nkt <= kSegMaxTiles;
+    if constexpr (MASK == VLM_MASK_SEGMENT_ID)
+        if (listed) nvis = segment_tiles<256, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
+    auto tile_at = [&](int i) { return listed ? (int)tlist[i] : i; };
 
     // K/V tile kt+1 is requested into registers (unconditional, key index clamped; keys past nkeys
     // are zeroed when stored) while tile kt runs on the matrix cores. K chunks are spread along rows
@@ -155,20 +217,20 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
         }
     };
     u32x4 kA[TCH], vA[VP][2], kB[TCH], vB[VP][2];
-    if (nkt > 0) request(0, kA, vA);
-    if (nkt > 1) request(1, kB, vB);
-    for (int kt2 = 0; kt2 < nkt; kt2 += 2) {
-        stage(kt2, 0, kA, vA);
-        if (kt2 + 1 < nkt) stage(kt2 + 1, 1, kB, vB);
+    if (nvis > 0) request(tile_at(0), kA, vA);
+    if (nvis > 1) request(tile_at(1), kB, vB);
+    for (int kt2 = 0; kt2 < nvis; kt2 += 2) {
+        stage(tile_at(kt2), 0, kA, vA);
+        if (kt2 + 1 < nvis) stage(tile_at(kt2 + 1), 1, kB, vB);
         __syncthreads();
         // the next pair is in flight during this pair's MFMAs
-        if (kt2 + 2 < nkt) request(kt2 + 2, kA, vA);
-        if (kt2 + 3 < nkt) request(kt2 + 3, kB, vB);
-        const int kt = kt2 + kpar;
-        const int key0 = kt * BKEY;
+        if (kt2 + 2 < nvis) request(tile_at(kt2 + 2), kA, vA);
+        if (kt2 + 3 < nvis) request(tile_at(kt2 + 3), kB, vB);
+        const int kv = kt2 + kpar;  // position in the visit order
+        const int key0 = (kv < nvis ? tile_at(kv) : 0) * BKEY;
         const bf16_t* const Kw = Ks + kpar * KSZ;
         const bf16_t* const Vw = Vt + kpar * VSZ;
-        bool active = kt < nkt;
+        bool active = kv < nvis;
         if (MASK == VLM_MASK_CAUSAL_ID) active = active && key0 <= a.pos0 + q0 + 31;
         if (active) {
             f32x16 sacc[2];
@@ -183,9 +245,11 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
                 }
             }
             // a tile every key of which is visible to every query row of this wavefront skips the mask
-            const bool full = (MASK == VLM_MASK_NONE_ID ||
-                               (MASK == VLM_MASK_CAUSAL_ID && key0 + BKEY - 1 <= a.pos0 + q0)) &&
-                              key0 + BKEY <= a.nkeys;
+            bool full = (MASK == VLM_MASK_NONE_ID ||
+                         (MASK == VLM_MASK_CAUSAL_ID && key0 + BKEY - 1 <= a.pos0 + q0)) &&
+                        key0 + BKEY <= a.nkeys;
+            if constexpr (MASK == VLM_MASK_SEGMENT_ID)
+                full = segment_tile_full<BKEY>(a.seg, seg_q, qrow < S, key0, a.nkeys);
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
@@ -342,8 +406,17 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     }
     const int seg_q = (MASK == VLM_MASK_SEGMENT_ID && qrow < S) ? a.seg[qrow] : 0;
     const int nkt = (kend + BKEY - 1) / BKEY;
+    // tiles visited, in order: all of them, or under a segment mask those that can hold a visible key
+    int nvis = nkt;
+    __shared__ short tlist[MASK == VLM_MASK_SEGMENT_ID ? kSegMaxTiles : 1];
+    __shared__ unsigned char tflag[MASK == VLM_MASK_SEGMENT_ID ? kSegMaxTiles : 1];
+    __shared__ int tlohi[3];
+    const bool listed = MASK == VLM_MASK_SEGMENT_ID && nkt <= kSegMaxTiles;
+    if constexpr (MASK == VLM_MASK_SEGMENT_ID)
+        if (listed) nvis = segment_tiles<256, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
 
-    for (int kt = 0; kt < nkt; kt++) {
+    for (int kv = 0; kv < nvis; kv++) {
+        const int kt = listed ? (int)tlist[kv] : kv;
         const int key0 = kt * BKEY;
         for (int c = tid; c < BKEY * CH; c += 256) {
             const int r = c / CH, d0 = (c % CH) * 4;
@@ -373,6 +446,9 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                 for (int kk = 0; kk < DQ / 2; kk++)
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[kk * 2], Qf[kk], sacc[kb], 0, 0, 0);
             }
+            bool full = false;  // segment mask: the whole tile lies in this wavefront's one segment
+            if constexpr (MASK == VLM_MASK_SEGMENT_ID)
+                full = segment_tile_full<BKEY>(a.seg, seg_q, qrow < S, key0, a.nkeys);
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
@@ -382,7 +458,7 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                     float s = sacc[kb][r] * scale;
                     bool vis = key < a.nkeys;
                     if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
-                    if (MASK == VLM_MASK_SEGMENT_ID) vis = vis && qrow < S && a.seg[key] == seg_q;
+                    if (MASK == VLM_MASK_SEGMENT_ID) vis = full || (vis && qrow < S && a.seg[key] == seg_q);
                     if (MASK == VLM_MASK_ADDITIVE_ID && vis && qrow < S)
                         s += a.add[(size_t)qrow * a.ld_add + key] * kLog2e;
                     s = vis ? s : -INFINITY;

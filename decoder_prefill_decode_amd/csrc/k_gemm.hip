@@ -533,18 +533,6 @@ static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
     return run_reduce<bf16_t, EPI>(a, splits, st);
 }
 
-// Blocks a prefill GEMM aims for before it splits K (several blocks per CU
-// keep more loads in flight; the GEMMs here are latency-bound, not MFMA-bound).
-// VLM_GEMM_TARGET_BLOCKS overrides it for tuning.
-static int target_blocks() {
-    static int v = [] {
-        const char* e = getenv("VLM_GEMM_TARGET_BLOCKS");
-        const int t = e ? atoi(e) : 0;
-        return t > 0 ? t : 512;
-    }();
-    return v;
-}
-
 // Tile and K-split choice of the direct-to-LDS kernel from a per-CU feed model.
 // On these shapes a block's time is set by how fast its CU pulls operand
 // stages out of L2 rather than by the matrix cores: an estimate is
@@ -583,20 +571,12 @@ static LdsPlan plan_lds(const GemmArgs& a, bool swiglu) {
     return bp;
 }
 
-// Tile choice of the register-staged kernel: the largest tile that still gives >= 256 blocks (one per CU),
-// else the smallest; then a K split (2-4 ways, >= 4 stages each) up to the
-// target block count when the caller provided split-K scratch.
+// Tile and K split: the direct-to-LDS kernel for bf16 with K % 64 == 0 (plan_lds), else the
+// register-staged kernel planned by the work model below.
 template <class T, Epi EPI>
 static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
     auto tiles = [&](int bm, int bn) { return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
     const int nk = (a.K + GemmTraits<T>::BK - 1) / GemmTraits<T>::BK;
-    auto splits_for = [&](long t) {
-        if (!a.part) return 1;
-        int sp = (int)(target_blocks() / t);
-        sp = sp > 4 ? 4 : sp;
-        while (sp > 1 && (nk / sp < 4 || (size_t)sp * a.M * a.N > a.part_cap)) sp--;
-        return sp < 1 ? 1 : sp;
-    };
     if constexpr (sizeof(T) == 2) {
         if (a.K % 64 == 0) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
             const LdsPlan pl = plan_lds(a, EPI == Epi::SwiGLU);
@@ -611,18 +591,39 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
 #undef VLM_RUN_LDS
         }
     }
-    if (tiles(128, 128) >= 256) {
-        const int sp = splits_for(tiles(128, 128));
-        return sp > 1 ? run_gemm<T, 128, 128, EPI, true>(a, sp, st) : run_gemm<T, 128, 128, EPI, false>(a, 1, st);
+    // register-staged kernel (f32, or bf16 with K % 64 != 0): tile and K split from a per-CU work
+    // model fitted on the vision tower's shapes (M 322-1288, N 1152-4608, K 1152-4608, f32):
+    // a CU runs ceil(blocks / 256) blocks one after another at a rate set by the tile shape, and a
+    // split adds its reduction (the fp32 partials written and read back, ~4 GB/ms, plus 3 us); a
+    // 128x128 tile does 6.7 ns of work per 1000 MACs-columns unit, smaller tiles 0.8x / 0.74x that
+    // rate. The model reproduces the measured times within ~10% and picks within ~5% of the fastest.
+    struct Cand { int bm, bn; double eff; };
+    static const Cand cand[3] = {{128, 128, 1.0}, {64, 128, 0.8}, {64, 64, 0.74}};
+    static const int splits[4] = {1, 2, 3, 4};
+    double best = 1e30;
+    int bbm = 64, bbn = 128, bsp = 1;
+    for (const auto& c : cand) {
+        if (EPI == Epi::SwiGLU && c.bn < 128) continue;  // a wave tile holds whole (gate, up) 64-column pairs
+        const long t = tiles(c.bm, c.bn);
+        for (int sp : splits) {
+            if (sp > 1 && (!a.part || nk / sp < 4 || (size_t)sp * a.M * a.N > a.part_cap)) continue;
+            const double per = (double)c.bm * c.bn * ((nk + sp - 1) / sp) * GemmTraits<T>::BK;
+            double us = (double)((t * sp + 255) / 256) * per * 6.7e-6 / c.eff;
+            if (sp > 1) us += 3.0 + (double)(sp + 1) * a.M * a.N * 4.0 / 4.0e6;
+            if (us < best) {
+                best = us;
+                bbm = c.bm;
+                bbn = c.bn;
+                bsp = sp;
+            }
+        }
     }
-    if (tiles(64, 128) >= 256 || EPI == Epi::SwiGLU) {
-        const int sp = splits_for(tiles(64, 128));
-        return sp > 1 ? run_gemm<T, 64, 128, EPI, true>(a, sp, st) : run_gemm<T, 64, 128, EPI, false>(a, 1, st);
-    }
-    if constexpr (EPI != Epi::SwiGLU) {
-        const int sp = splits_for(tiles(64, 64));
-        return sp > 1 ? run_gemm<T, 64, 64, EPI, true>(a, sp, st) : run_gemm<T, 64, 64, EPI, false>(a, 1, st);
-    }
+#define VLM_RUN_REG(BM_, BN_)                                                                  \
+    return bsp > 1 ? run_gemm<T, BM_, BN_, EPI, true>(a, bsp, st) : run_gemm<T, BM_, BN_, EPI, false>(a, 1, st)
+    if (bbm == 128) VLM_RUN_REG(128, 128);
+    if (bbn == 128) VLM_RUN_REG(64, 128);
+    if constexpr (EPI != Epi::SwiGLU) VLM_RUN_REG(64, 64);
+#undef VLM_RUN_REG
     return hipErrorInvalidValue;
 }
 
