@@ -868,49 +868,40 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
     }
 }
 
-// Merge of the split partials: one wavefront per query head. Lane s holds the
-// statistics (m, l) of split s; every lane requests its elements of all
-// splits' o rows up front (indices clamped, unconditional), then the split
-// weights f_s = exp2(m_s - max m) are broadcast with readlane.
+// Merge of the split partials: one wavefront per 64 columns of a query head's
+// output row (a block per head). Lane s holds the statistics (m, l) of split
+// s; every lane requests its column of all splits' o rows up front (indices
+// clamped, unconditional: 32 + 2 loads, within the 63 a wavefront keeps in
+// flight, so the merge is one memory round trip), then the split weights
+// f_s = exp2(m_s - max m) are broadcast with readlane.
 template <class T, int D>
-__global__ __launch_bounds__(64) void attn_combine_fast_kernel(const float* __restrict__ partial, int nsplit,
-                                                               T* __restrict__ out) {
-    constexpr int NS = kDecMaxSplits, PS = D + 4, EPL = (D + 63) / 64;
+__global__ __launch_bounds__(64 * ((D + 63) / 64)) void attn_combine_fast_kernel(const float* __restrict__ partial,
+                                                                                  int nsplit, T* __restrict__ out) {
+    constexpr int NS = kDecMaxSplits, PS = D + 4;
     static_assert(NS <= 64, "one lane per split");
-    const int h = blockIdx.x, lane = threadIdx.x;
+    const int h = blockIdx.x, lane = threadIdx.x % kWave, e = threadIdx.x;
     const float* p = partial + (size_t)h * nsplit * PS;
     const int sl = min(lane, nsplit - 1);
     const float ms = p[sl * PS + D], ls = p[sl * PS + D + 1];
-    float ov[NS][EPL];
+    const int ec = min(e, D - 1);
+    float ov[NS];
 #pragma unroll
-    for (int s = 0; s < NS; s++)
-#pragma unroll
-        for (int q = 0; q < EPL; q++) ov[s][q] = p[min(s, nsplit - 1) * PS + min(lane + 64 * q, D - 1)];
+    for (int s = 0; s < NS; s++) ov[s] = p[min(s, nsplit - 1) * PS + ec];
     __builtin_amdgcn_sched_barrier(0);
     const float m = lane < nsplit ? ms : -INFINITY;
     const float mx = wave_max(m);
     const float f = (lane < nsplit && m != -INFINITY) ? exp2f(m - mx) : 0.f;
     const float lsum = wave_sum(f * (lane < nsplit ? ls : 0.f));
-    float v[EPL];
-#pragma unroll
-    for (int q = 0; q < EPL; q++) v[q] = 0.f;
+    float v = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
         const float fsv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), s));
-#pragma unroll
-        for (int q = 0; q < EPL; q++) v[q] = fmaf(fsv, ov[s][q], v[q]);
+        v = fmaf(fsv, ov[s], v);
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-    for (int q = 0; q < EPL; q++) {
-        v[q] *= inv;
-        asm volatile("" ::"v"(v[q]));  // computed here: keeps the loads from sinking into the store branch
-    }
-#pragma unroll
-    for (int q = 0; q < EPL; q++) {
-        const int e = lane + 64 * q;
-        if (e < D) Elt<T>::st(out, (size_t)h * D + e, v[q]);
-    }
+    v *= inv;
+    asm volatile("" ::"v"(v));  // computed here: keeps the loads from sinking into the store branch
+    if (e < D) Elt<T>::st(out, (size_t)h * D + e, v);
 }
 
 template <class T, int D>
@@ -1103,9 +1094,9 @@ template <class T>
 static hipError_t combine_dim(const float* partial, int nq, int nsplit, int d, void* out, hipStream_t st) {
     switch (d) {
         case 64: attn_combine_fast_kernel<T, 64><<<nq, 64, 0, st>>>(partial, nsplit, (T*)out); break;
-        case 72: attn_combine_fast_kernel<T, 72><<<nq, 64, 0, st>>>(partial, nsplit, (T*)out); break;
-        case 80: attn_combine_fast_kernel<T, 80><<<nq, 64, 0, st>>>(partial, nsplit, (T*)out); break;
-        case 128: attn_combine_fast_kernel<T, 128><<<nq, 64, 0, st>>>(partial, nsplit, (T*)out); break;
+        case 72: attn_combine_fast_kernel<T, 72><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
+        case 80: attn_combine_fast_kernel<T, 80><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
+        case 128: attn_combine_fast_kernel<T, 128><<<nq, 128, 0, st>>>(partial, nsplit, (T*)out); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
