@@ -94,7 +94,7 @@ __device__ int segment_tiles(const int32_t* seg, int row0, int nrows, int S, int
 // the end.
 // DQ: width of q and k rows, DV: width of v and output rows (equal except for expanded MLA).
 template <int DQ, int DV, int MASK>
-__global__ __launch_bounds__(256) void attn_prefill_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnArgs a) {
     constexpr int BQ = 64, BKEY = 64;
     // a q/k width that is not a multiple of 16 (72) is zero-padded to DK * 16 in the K tile and
     // the q fragments, which leaves every dot product unchanged
