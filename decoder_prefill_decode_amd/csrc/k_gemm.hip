@@ -223,7 +223,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 // the MFMA operand reads (32 rows, one chunk) spread over the LDS banks:
 // swz(r) = r & 7 for 128-byte rows, (r >> 1) & 3 for 64-byte rows (two rows
 // share one 128-byte bank window). Lane L therefore fetches row L / CPR and
-// chunk (L % CPR) ^ swz(L / CPR) (CPR = chunks per row). Requires K % BK == 0.
+// chunk (L % CPR) ^ swz(L / CPR) (CPR = chunks per row). Requires K % 8 == 0:
+// when K is not a multiple of BK, the last stage's loads past K are clamped to
+// the row's last chunk and those columns are zeroed in LDS (A and B rows)
+// before any wavefront reads the stage.
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int V>
@@ -252,7 +255,7 @@ template <int BK>
 __device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 
 // WGM x WGN wavefronts per block, each owning a (BM/WGM) x (BN/WGN) sub-tile.
-template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK>
+template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     static_assert(BK == 64 || BK == 32, "stage depth");
     constexpr int NW = WGM * WGN, WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
@@ -278,9 +281,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     const bf16_t* ga[AI];
     const bf16_t* gb[BI];
 #pragma unroll
-    for (int i = 0; i < AI; i++) ga[i] = A + (size_t)min(m0 + (w * AI + i) * RPI + lr, M - 1) * K + lc * 8;
+    for (int i = 0; i < AI; i++) ga[i] = A + (size_t)min(m0 + (w * AI + i) * RPI + lr, M - 1) * K;
 #pragma unroll
-    for (int i = 0; i < BI; i++) gb[i] = B + (size_t)min(n0 + (w * BI + i) * RPI + lr, N - 1) * K + lc * 8;
+    for (int i = 0; i < BI; i++) gb[i] = B + (size_t)min(n0 + (w * BI + i) * RPI + lr, N - 1) * K;
+    const int kmax = K - 8;  // last 16-byte chunk of a row: loads of the tail stage are clamped to it
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -290,7 +294,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    int kt0 = 0, nk = K / BK;
+    const int nk_all = (K + BK - 1) / BK, ktail = K - (nk_all - 1) * BK;  // columns of the last stage
+    int kt0 = 0, nk = nk_all;
     if constexpr (SPLIT) {
         const int per = (nk + gridDim.y - 1) / gridDim.y;
         kt0 = blockIdx.y * per;
@@ -300,11 +305,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     // (The source pointer is passed as const void*: the host pass silently drops the kernel otherwise.)
 #define VLM_LDS_STAGE(KOFF, ST)                                                                              \
     do {                                                                                                     \
+        const int kc_ = TAIL ? min((KOFF) + lc * 8, kmax) : (KOFF) + lc * 8;                                 \
         _Pragma("unroll") for (int i = 0; i < AI; i++) __builtin_amdgcn_global_load_lds(                     \
-            (const void*)(ga[i] + (KOFF)), (lds_void*)((ST) + (w * AI + i) * 512), 16, 0, 0);                \
+            (const void*)(ga[i] + kc_), (lds_void*)((ST) + (w * AI + i) * 512), 16, 0, 0);                   \
         _Pragma("unroll") for (int i = 0; i < BI; i++) __builtin_amdgcn_global_load_lds(                     \
-            (const void*)(gb[i] + (KOFF)), (lds_void*)((ST) + BM * BK + (w * BI + i) * 512), 16, 0, 0);      \
+            (const void*)(gb[i] + kc_), (lds_void*)((ST) + BM * BK + (w * BI + i) * 512), 16, 0, 0);         \
     } while (0)
+    // the last stage (global index nk_all - 1) of a K that is not a multiple of BK: zero its columns
+    // ktail..BK-1 in every A and B row once they have landed (callers hold a barrier on both sides)
+    auto zero_tail = [&](int kt_local, bf16_t* st) {
+        if (!TAIL || ktail == BK || kt0 + kt_local != nk_all - 1) return;  // uniform
+        const int c0 = ktail / 8;
+        for (int idx = tid; idx < (BM + BN) * CPR; idx += NW * kWave) {
+            const int r = idx / CPR, c = idx % CPR;
+            if (c >= c0) *reinterpret_cast<u32x4*>(st + r * BK + ((c ^ lds_swz<BK>(r)) * 8)) = u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
+    };
 #pragma unroll
     for (int s = 0; s < P - 1; s++)
         if (s < nk) VLM_LDS_STAGE((kt0 + s) * BK, smem + s * STAGE);
@@ -341,6 +358,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
             wait_stages<LPS, P - 2>(nk - 1);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (TAIL) zero_tail(0, smem);
             if (P - 1 < nk) VLM_LDS_STAGE((kt0 + P - 1) * BK, smem + (P - 1) * STAGE);
             read_frags(smem, 0, fa[0], fb[0]);
         }
@@ -356,6 +374,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
                 wait_lgkm0();                          // this wave's reads of stage kt have returned
                 __builtin_amdgcn_s_barrier();          // ... every wave's; stage kt's slot may be refilled
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (TAIL) zero_tail(kt + 1, smem + ((kt + 1) % P) * STAGE);
                 if (kt + P < nk) VLM_LDS_STAGE((kt0 + kt + P) * BK, smem + (kt % P) * STAGE);
                 read_frags(smem + ((kt + 1) % P) * STAGE, 0, fa[0], fb[0]);
             }
@@ -516,18 +535,18 @@ static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     return run_reduce<T, EPI>(a, splits, st);
 }
 
-template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK>
+template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
 static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
     const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
     const size_t smem = (size_t)P * (BM + BN) * BK * sizeof(bf16_t);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK, TAIL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
+    gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK, TAIL><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
     return run_reduce<bf16_t, EPI>(a, splits, st);
@@ -549,7 +568,7 @@ static LdsPlan plan_lds(const GemmArgs& a, bool swiglu) {
                                    {128, 128, 2, 43000, 52000}, {64, 128, 2, 44000, 62000},
                                    {64, 64, 2, 40000, 55000}};
     static const int splits[6] = {1, 2, 3, 4, 6, 8};
-    const int nk = a.K / 64;
+    const int nk = (a.K + 63) / 64;
     double best = 1e30;
     LdsPlan bp{64, 128, 1};
     for (const auto& c : cand) {
@@ -571,27 +590,33 @@ static LdsPlan plan_lds(const GemmArgs& a, bool swiglu) {
     return bp;
 }
 
-// Tile and K split: the direct-to-LDS kernel for bf16 with K % 64 == 0 (plan_lds), else the
+// Tile and K split: the direct-to-LDS kernel for bf16 with K % 8 == 0 (plan_lds), else the
 // register-staged kernel planned by the work model below.
 template <class T, Epi EPI>
 static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
     auto tiles = [&](int bm, int bn) { return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
     const int nk = (a.K + GemmTraits<T>::BK - 1) / GemmTraits<T>::BK;
     if constexpr (sizeof(T) == 2) {
-        if (a.K % 64 == 0) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
+        if (a.K % 8 == 0 && a.K >= 64) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
             const LdsPlan pl = plan_lds(a, EPI == Epi::SwiGLU);
+#define VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, T_)                                            \
+    return pl.sp > 1 ? run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, true, BK_, T_>(a, pl.sp, st)     \
+                     : run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, false, BK_, T_>(a, 1, st)
 #define VLM_RUN_LDS(BM_, BN_, P_, GM_, GN_, BK_)                                                   \
-    return pl.sp > 1 ? run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, true, BK_>(a, pl.sp, st)         \
-                     : run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, false, BK_>(a, 1, st)
+    do {                                                                                          \
+        if (a.K % BK_ != 0) VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, true);                     \
+        VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, false);                                        \
+    } while (0)
             if (pl.bm == 256) VLM_RUN_LDS(256, 256, 2, 4, 2, 64);
             if (pl.bm == 128 && pl.bn == 256) VLM_RUN_LDS(128, 256, 2, 2, 4, 64);
             if (pl.bm == 128) VLM_RUN_LDS(128, 128, 2, 2, 2, 64);
             if (pl.bn == 128) VLM_RUN_LDS(64, 128, 3, 2, 2, 64);
             if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS(64, 64, 4, 2, 2, 64);
 #undef VLM_RUN_LDS
+#undef VLM_RUN_LDS_T
         }
     }
-    // register-staged kernel (f32, or bf16 with K % 64 != 0): tile and K split from a per-CU work
+    // register-staged kernel (f32, or bf16 with K % 8 != 0): tile and K split from a per-CU work
     // model fitted on the vision tower's shapes (M 322-1288, N 1152-4608, K 1152-4608, f32):
     // a CU runs ceil(blocks / 256) blocks one after another at a rate set by the tile shape, and a
     // split adds its reduction (the fp32 partials written and read back, ~4 GB/ms, plus 3 us); a

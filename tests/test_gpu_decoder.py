@@ -144,7 +144,12 @@ SMALL_C3 = vs.scaled(vs.C3, n_layers=2, vocab=8192, seq=96, n_img=40, img_start=
 SMALL_C4 = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=80, n_img=30, img_start=16, decode_steps=12, capacity=128)
 
 
-@pytest.mark.parametrize("cfg", [SMALL_C3, SMALL_C4], ids=["c3_2layer", "c4_2layer"])
+# FFN 1056: the down projection's K is not a multiple of the 64-column GEMM stage (tail of 32 columns)
+SMALL_C4_FFN_TAIL = vs.scaled(SMALL_C4, ffn=1056, name="c4_2layer_ffn1056")
+
+
+@pytest.mark.parametrize("cfg", [SMALL_C3, SMALL_C4, SMALL_C4_FFN_TAIL],
+                         ids=["c3_2layer", "c4_2layer", "c4_2layer_ffn1056"])
 def test_scaled_bf16_stacks(rt, cfg):
     pipeline, _ = rt
     glob, layers = make(cfg)
