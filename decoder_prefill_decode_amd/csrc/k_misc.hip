@@ -158,58 +158,52 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- QK-Norm + RoPE + cache write
-// A wavefront takes IT consecutive (row, head) items; lane p < d/2 owns
-// rotation pair p, i.e. the output elements i0 = g*sd + j and i1 = i0 + sd/2
-// of segment g (sd = d/segments). rotate_half(a, b) = (-b, a): y[i0] = a cos -
+// One block per row s: the row's q, k, v projections (fp32, nh * d) and the
+// cos / sin row of its position are read once into LDS with 16-byte loads;
+// then wavefront w takes heads w, w + 16, ..., and lane p < d/2 owns rotation
+// pair p, i.e. the output elements i0 = g*sd + j and i1 = i0 + sd/2 of
+// segment g (sd = d/segments). rotate_half(a, b) = (-b, a): y[i0] = a cos -
 // b sin, y[i1] = b cos + a sin, where (a, b) are the inputs at (i0, i1), or at
 // (g*sd + 2j, g*sd + 2j + 1) for interleaved RoPE (the adjacent pair,
 // de-interleaved into the rotate-half order; V is copied unpermuted). The
 // per-head RMSNorm gain is indexed by where the element sits when the norm
-// runs: input order before the rotation, output order after it. Every item's
-// inputs and table entries are requested before the first item is computed,
-// so a wavefront has IT items' loads in flight instead of one.
-constexpr int kRopeItems = 4;
+// runs: input order before the rotation, output order after it.
+constexpr int kRopeThreads = 1024;  // 16 wavefronts: a 48-head row is 3 heads per wavefront
 template <class T>
-__global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
-    constexpr int IT = kRopeItems;
-    const int lane = threadIdx.x % kWave;
-    const int nh = a.nq + 2 * a.nkv, total = a.S * nh;
-    const int w0 = (blockIdx.x * 4 + threadIdx.x / kWave) * IT;
-    if (w0 >= total) return;
-    const int d = a.d, half = d / 2;
-    const int base = a.pos_dev ? a.pos_dev[0] : a.pos0;
+__global__ __launch_bounds__(kRopeThreads) void rope_qkv_kernel(RopeArgs a) {
+    constexpr int NT = kRopeThreads, NWV = NT / kWave;
+    extern __shared__ __attribute__((aligned(16))) float rs[];  // [nh * d] projections, [d] cos, [d] sin
+    const int s = blockIdx.x, tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+    const int nh = a.nq + 2 * a.nkv, d = a.d, half = d / 2, nrow = nh * d;
+    const int pos = (a.pos_dev ? a.pos_dev[0] : a.pos0) + s;
+    float* cs = rs + nrow;
+    float* sn = cs + d;
+    {
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.qkv + (size_t)s * nrow);
+        for (int i = tid; i < nrow / 4; i += NT) reinterpret_cast<f32x4*>(rs)[i] = src[i];
+        for (int i = tid; i < d; i += NT) {
+            cs[i] = a.cos[(size_t)pos * d + i];
+            sn[i] = a.sin[(size_t)pos * d + i];
+        }
+    }
+    __syncthreads();
     const bool on = lane < half;
     const int sd = d / a.segments, sh = sd / 2;
     const int g = on ? lane / sh : 0, j = on ? lane % sh : 0;
     const int i0 = g * sd + j, i1 = i0 + sh;
     const int r0 = a.interleave ? g * sd + 2 * j : i0, r1 = a.interleave ? r0 + 1 : i1;
-    float x0[IT], x1[IT], c0[IT], c1[IT], s0[IT], s1[IT];
-#pragma unroll
-    for (int it = 0; it < IT; it++) {  // items past the end re-read the last one and are not stored
-        const int item = min(w0 + it, total - 1), s = item / nh, h = item % nh;
-        const float* src = a.qkv + (size_t)s * nh * d + (size_t)h * d;
-        const bool isv = h >= a.nq + a.nkv;
-        const size_t ro = (size_t)(base + s) * d;
-        x0[it] = on ? src[isv ? i0 : r0] : 0.f;
-        x1[it] = on ? src[isv ? i1 : r1] : 0.f;
-        c0[it] = on ? a.cos[ro + i0] : 0.f;
-        c1[it] = on ? a.cos[ro + i1] : 0.f;
-        s0[it] = on ? a.sin[ro + i0] : 0.f;
-        s1[it] = on ? a.sin[ro + i1] : 0.f;
-    }
-#pragma unroll
-    for (int it = 0; it < IT; it++) {
-        if (w0 + it >= total) break;  // uniform
-        const int item = w0 + it, s = item / nh, h = item % nh, pos = base + s;
+    const float c0 = cs[i0], c1 = cs[i1], s0 = sn[i0], s1 = sn[i1];
+    for (int h = w; h < nh; h += NWV) {  // uniform per wavefront
+        const float* x = rs + h * d;
         if (h >= a.nq + a.nkv) {  // V head: plain copy (rounded to the cache type)
             if (on) {
                 T* dst = (T*)a.vdst + ((size_t)(h - a.nq - a.nkv) * a.ldkv + pos) * d;
-                Elt<T>::st(dst, i0, x0[it]);
-                Elt<T>::st(dst, i1, x1[it]);
+                Elt<T>::st(dst, i0, x[i0]);
+                Elt<T>::st(dst, i1, x[i1]);
             }
             continue;
         }
-        float u0 = x0[it], u1 = x1[it];
+        float u0 = on ? x[r0] : 0.f, u1 = on ? x[r1] : 0.f;
         const bool isq = h < a.nq;
         const T* gn = (const T*)(isq ? a.qn : a.kn);
         if (gn && !a.norm_after) {
@@ -219,8 +213,8 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(RopeArgs a) {
                 u1 = u1 * r * Elt<T>::ld(gn, r1);
             }
         }
-        float y0 = on ? u0 * c0[it] - u1 * s0[it] : 0.f;
-        float y1 = on ? u1 * c1[it] + u0 * s1[it] : 0.f;
+        float y0 = on ? u0 * c0 - u1 * s0 : 0.f;
+        float y1 = on ? u1 * c1 + u0 * s1 : 0.f;
         if (gn && a.norm_after) {  // the rotation keeps the sum of squares; the norm sees the rotated values
             const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)d + a.eps);
             if (on) {
@@ -412,14 +406,13 @@ hipError_t launch_norm_rows(int dtype, bool layer, const float* x, int R, int H,
 }
 
 hipError_t launch_rope_qkv(int dtype, const RopeArgs& a, hipStream_t st) {
-    const int items = a.S * (a.nq + 2 * a.nkv);
-    if (items <= 0) return hipSuccess;
-    const int waves = (items + kRopeItems - 1) / kRopeItems;
-    const int blocks = (waves + 3) / 4;
+    if (a.S <= 0) return hipSuccess;
+    const size_t smem = ((size_t)(a.nq + 2 * a.nkv) * a.d + 2 * a.d) * sizeof(float);
+    if (a.d % 4 != 0 || a.d > 128 || smem > 64 * 1024) return hipErrorInvalidValue;
     if (dtype == 1)
-        rope_qkv_kernel<bf16_t><<<blocks, 256, 0, st>>>(a);
+        rope_qkv_kernel<bf16_t><<<a.S, kRopeThreads, smem, st>>>(a);
     else
-        rope_qkv_kernel<float><<<blocks, 256, 0, st>>>(a);
+        rope_qkv_kernel<float><<<a.S, kRopeThreads, smem, st>>>(a);
     return hipGetLastError();
 }
 
