@@ -251,13 +251,24 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
             if constexpr (MASK == VLM_MASK_SEGMENT_ID)
                 full = segment_tile_full<BKEY>(a.seg, seg_q, qrow < S, key0, a.nkeys);
             float mt = -INFINITY;
+            // wavefront-uniform: one scalar branch per tile (the segment mask keeps the test per
+            // element: its two loop bodies together would spill)
+            if (MASK != VLM_MASK_SEGMENT_ID && __builtin_amdgcn_readfirstlane((int)full)) {
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        sacc[kb][r] *= scale;
+                        mt = fmaxf(mt, sacc[kb][r]);
+                    }
+            } else {
 #pragma unroll
             for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int key = key0 + kb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
                     float s = sacc[kb][r] * scale;
-                    if (full) {
+                    if (MASK == VLM_MASK_SEGMENT_ID && full) {
                         sacc[kb][r] = s;
                         mt = fmaxf(mt, s);
                         continue;
@@ -271,6 +282,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
                     sacc[kb][r] = s;
                     mt = fmaxf(mt, s);
                 }
+            }
             {
                 const LanePair h2 = swap32(mt);
                 mt = fmaxf(h2.lo, h2.hi);
