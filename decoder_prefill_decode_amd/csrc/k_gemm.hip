@@ -190,18 +190,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             }
         } else {
+            // K is taken in quads of 8 columns: in MFMA step e of quad q the lanes of half h
+            // contribute column 8q + 4h + e, so one 16-byte LDS read per operand and half feeds
+            // four steps (the same permutation on A and B leaves the contraction unchanged)
 #pragma unroll
-            for (int kk = 0; kk < BK / 2; kk++) {
-                float fa[TM], fb[TN];
+            for (int kq = 0; kq < BK / 8; kq++) {
+                f32x4 fa[TM], fb[TN];
 #pragma unroll
-                for (int i = 0; i < TM; i++) fa[i] = as[i * 32 * LDK + kk * 2 + h];
+                for (int i = 0; i < TM; i++) fa[i] = *reinterpret_cast<const f32x4*>(as + i * 32 * LDK + kq * 8 + h * 4);
 #pragma unroll
-                for (int j = 0; j < TN; j++) fb[j] = bs[j * 32 * LDK + kk * 2 + h];
+                for (int j = 0; j < TN; j++) fb[j] = *reinterpret_cast<const f32x4*>(bs + j * 32 * LDK + kq * 8 + h * 4);
 #pragma unroll
-                for (int i = 0; i < TM; i++)
+                for (int e = 0; e < 4; e++)
 #pragma unroll
-                    for (int j = 0; j < TN; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int j = 0; j < TN; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e], acc[i][j], 0, 0, 0);
             }
         }
         if (kt + 1 < nk) sstore(cur ^ 1);
