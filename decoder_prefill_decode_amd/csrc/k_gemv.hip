@@ -164,16 +164,18 @@ template <> struct Raw4<bf16_t> {
 //  * PlainLds operand: a plain vector staged once per block into LDS (raw
 //    16-byte chunks), so the four wavefronts of a block share one read of it;
 //    with long rows a per-lane copy would double the L2 traffic of the GEMV.
-template <class T, Pro PRO, Epi EPI, int NR, int KCH>
-__global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
-    constexpr int VEC = 16 / sizeof(T), STEP = kWave * VEC;
+//  * NW wavefronts per block (4, or 5 where that gives every CU the same
+//    number of blocks).
+template <class T, Pro PRO, Epi EPI, int NR, int KCH, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv2_kernel(GemvArgs a) {
+    constexpr int VEC = 16 / sizeof(T), STEP = kWave * VEC, BT = NW * kWave;
     constexpr bool NORM = PRO == Pro::RmsNorm, SHARE = PRO == Pro::PlainLds, STAGED = NORM || SHARE;
-    constexpr int VCH = NORM ? (KCH * STEP / 4 + 255) / 256 : 1;  // 4-float chunks of x per thread
-    constexpr int SCH = SHARE ? (KCH * kWave + 255) / 256 : 1;     // 16-byte operand chunks per thread
+    constexpr int VCH = NORM ? (KCH * STEP / 4 + BT - 1) / BT : 1;  // 4-float chunks of x per thread
+    constexpr int SCH = SHARE ? (KCH * kWave + BT - 1) / BT : 1;     // 16-byte operand chunks per thread
     extern __shared__ __attribute__((aligned(16))) float vs[];  // 16-byte aligned: PlainLds reads u32x4
-    __shared__ float red[4];
+    __shared__ float red[NW];
     const int tid = threadIdx.x, lane = tid % kWave;
-    const int wave = blockIdx.x * 4 + tid / kWave;
+    const int wave = blockIdx.x * NW + tid / kWave;
     const int K = a.K;
     const T* W = (const T*)a.W;
 
@@ -185,12 +187,12 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
         const int nch = K / VEC;
 #pragma unroll
         for (int i = 0; i < SCH; i++)
-            xr[i] = *reinterpret_cast<const u32x4*>((const T*)a.vec + VEC * min(tid + 256 * i, nch - 1));
+            xr[i] = *reinterpret_cast<const u32x4*>((const T*)a.vec + VEC * min(tid + BT * i, nch - 1));
     } else if constexpr (NORM) {
         const int nx = K / 4;
 #pragma unroll
         for (int i = 0; i < VCH; i++) {
-            const int c = min(tid + 256 * i, nx - 1);
+            const int c = min(tid + BT * i, nx - 1);
             xr[i] = *reinterpret_cast<const u32x4*>((const float*)a.vec + 4 * c);
             gr[i].load((const T*)a.gain + 4 * c);
         }
@@ -241,13 +243,13 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < VCH; i++)
-            if (tid + 256 * i < nx)
+            if (tid + BT * i < nx)
 #pragma unroll
                 for (int e = 0; e < 4; e++) ss += __uint_as_float(xr[i][e]) * __uint_as_float(xr[i][e]);
-        const float rs = rsqrtf(block_sum<256>(ss, red) / (float)K + a.eps);
+        const float rs = rsqrtf(block_sum<BT>(ss, red) / (float)K + a.eps);
 #pragma unroll
         for (int i = 0; i < VCH; i++) {
-            const int c = tid + 256 * i;
+            const int c = tid + BT * i;
             if (c < nx)
 #pragma unroll
                 for (int e = 0; e < 4; e++) vs[4 * c + e] = Elt<T>::rnd(__uint_as_float(xr[i][e]) * rs * gr[i].get(e));
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
         const int nch = K / VEC;
 #pragma unroll
         for (int i = 0; i < SCH; i++)
-            if (tid + 256 * i < nch) vq[tid + 256 * i] = xr[i];
+            if (tid + BT * i < nch) vq[tid + BT * i] = xr[i];
         __syncthreads();
     }
     // (4) dot products
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
     for (int r = 0; r < NR; r++) acc[r] = wave_sum(acc[r]);
     // (5) epilogue: lane r stores row r
     if constexpr (EPI == Epi::Argmax) {
-        __shared__ unsigned long long bk[4];
+        __shared__ unsigned long long bk[NW];
         unsigned long long best = 0ull;
 #pragma unroll
         for (int r = 0; r < NR; r++) {
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
         __syncthreads();
         if (tid == 0) {
             unsigned long long b = bk[0];
-            for (int i = 1; i < 4; i++) b = bk[i] > b ? bk[i] : b;
+            for (int i = 1; i < NW; i++) b = bk[i] > b ? bk[i] : b;
             a.partials[blockIdx.x] = b;
         }
     } else if constexpr (EPI == Epi::SwiGLU) {
@@ -333,15 +335,57 @@ __global__ __launch_bounds__(256) void gemv2_kernel(GemvArgs a) {
     }
 }
 
+static int device_cus() {
+    static int v = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 256;
+        return n > 0 ? n : 256;
+    }();
+    return v;
+}
+
+// Share of the CU slots the busiest CU's blocks fill: blocks / (cus * ceil(blocks / cus)).
+static double cu_balance(int blocks, int cus) {
+    const int rounds = (blocks + cus - 1) / cus;
+    return rounds > 0 ? (double)blocks / ((double)rounds * cus) : 0.0;
+}
+
+// VLM_GEMV_WAVES (4 or 5) fixes the wavefronts per block of the plain-operand
+// projections, for tuning; unset or 0 lets the balance decide.
+static int gemv_waves_override() {
+    static int v = [] {
+        const char* e = getenv("VLM_GEMV_WAVES");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
+template <class T, Pro PRO, Epi EPI, int NR, int KCH, int NW>
+static hipError_t launch_gemv2(const GemvArgs& a, int waves, hipStream_t st) {
+    const int blocks = (waves + NW - 1) / NW;
+    const size_t smem = PRO == Pro::RmsNorm ? (size_t)a.K * sizeof(float)
+                        : (PRO == Pro::PlainLds ? (size_t)a.K * sizeof(T) : 0);
+    gemv2_kernel<T, PRO, EPI, NR, KCH, NW><<<blocks, NW * kWave, smem, st>>>(a);
+    return hipGetLastError();
+}
+
+// Blocks of 4 wavefronts, or of 5 for the plain-operand row projections when
+// that spreads the blocks evenly over the CUs (a CU holding one block more
+// than the others streams that block's rows after the rest have finished).
+// The argmax head keeps 4 (its block partials are counted in 4-wavefront
+// blocks) and the RMSNorm prologues keep 4 (the block sum's order).
 template <class T, Pro PRO, Epi EPI, int NR, int KCH>
 static hipError_t run_gemv2(const GemvArgs& a, hipStream_t st) {
     const int nrows = a.N;  // SwiGLU: NR counts gate + up rows
     const int waves = (nrows + NR - 1) / NR;
-    const int blocks = (waves + 3) / 4;
-    const size_t smem = PRO == Pro::RmsNorm ? (size_t)a.K * sizeof(float)
-                        : (PRO == Pro::PlainLds ? (size_t)a.K * sizeof(T) : 0);
-    gemv2_kernel<T, PRO, EPI, NR, KCH><<<blocks, 256, smem, st>>>(a);
-    return hipGetLastError();
+    if constexpr (PRO != Pro::RmsNorm && (EPI == Epi::Resid || EPI == Epi::StoreF32)) {
+        const int cus = device_cus(), ov = gemv_waves_override();
+        const bool five = ov ? ov == 5
+                             : cu_balance((waves + 4) / 5, cus) > cu_balance((waves + 3) / 4, cus) + 0.05;
+        if (five) return launch_gemv2<T, PRO, EPI, NR, KCH, 5>(a, waves, st);
+    }
+    return launch_gemv2<T, PRO, EPI, NR, KCH, 4>(a, waves, st);
 }
 
 // VLM_GEMV_ROWS (1, 2, 4 or 8) fixes the rows per wavefront of the decode
