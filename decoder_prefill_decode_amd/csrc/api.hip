@@ -218,8 +218,9 @@ struct vlm_kv {
     size_t bytes;
     int len;  // host mirror
     hipStream_t cap_stream = nullptr;
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
+    // one decode-step graph per count of launched attention splits (index nact)
+    hipGraph_t graph[kDecMaxSplits + 1] = {};
+    hipGraphExec_t exec[kDecMaxSplits + 1] = {};
     bool has_key = false;
     GraphKey key;
     int32_t* dlen() const { return (int32_t*)buf; }
@@ -228,10 +229,12 @@ struct vlm_kv {
     char* kptr(int l) const { return (char*)buf + kHeader + (size_t)l * layer_bytes(); }
     char* vptr(int l) const { return kptr(l) + k_bytes(); }
     void drop_graph() {
-        if (exec) hipGraphExecDestroy(exec);
-        if (graph) hipGraphDestroy(graph);
-        exec = nullptr;
-        graph = nullptr;
+        for (int i = 0; i <= kDecMaxSplits; i++) {
+            if (exec[i]) hipGraphExecDestroy(exec[i]);
+            if (graph[i]) hipGraphDestroy(graph[i]);
+            exec[i] = nullptr;
+            graph[i] = nullptr;
+        }
         has_key = false;
     }
 };
@@ -577,7 +580,7 @@ vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sam
 static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L, const void* embed, const void* fnorm,
                                  const void* table, vlm_kv* kv, const int32_t* tok_in, const float* x_in,
                                  const float* cosv, const float* sinv, int32_t* tok_out, float* x_out, int32_t* hist,
-                                 void* ws, const Ws& w, hipStream_t st) {
+                                 void* ws, const Ws& w, int nact, hipStream_t st) {
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
     const int hd = desc->head_dim, dv = vdim(desc), QKV = qkv_rows(desc), W = kv->capacity;
     const bool mla = is_mla(desc);
@@ -616,9 +619,9 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
             HIP_TRY(launch_mla_rope(dt, r, st));
             DecAttnArgs at{};
             at.qrot = qrow; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
-            at.dv = dv; at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
+            at.dv = dv; at.len = kv->dlen(); at.nsplit = nsplit; at.nact = nact; at.partial = part;
             HIP_TRY(launch_attn_decode_mla(dt, at, st));
-            HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, dv, orow, st));
+            HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, nact, dv, orow, st));
             g = GemvArgs{};
             g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * dv;
             HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
@@ -637,9 +640,9 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         at.eps = desc->norm_eps; at.rope = rope; at.segments = desc->rope_segments;
         at.interleave = desc->rope_interleave; at.norm_after = desc->qk_norm == 2;
         at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
-        at.len = kv->dlen(); at.nsplit = nsplit; at.partial = part;
+        at.len = kv->dlen(); at.nsplit = nsplit; at.nact = nact; at.partial = part;
         HIP_TRY(launch_attn_decode_fused(dt, at, st));
-        HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, hd, orow, st));
+        HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, nact, hd, orow, st));
         g = GemvArgs{};
         g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * hd;
         HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
@@ -697,7 +700,8 @@ vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers
                                 table_rows, d_token_out, d_ws, ws_bytes, 1, &w);
     if (s) return s;
     if ((s = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_in, d_x_in, d_cos, d_sin,
-                            d_token_out, d_x_out, d_token_hist, d_ws, w, stream)))
+                            d_token_out, d_x_out, d_token_hist, d_ws, w, attn_decode_active(kv->capacity, kv->len),
+                            stream)))
         return s;
     kv->len += 1;
     return ok();
@@ -722,10 +726,18 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
     key.ws = d_ws; key.ws_bytes = ws_bytes;
     if (!kv->has_key || !(kv->key == key)) {
         kv->drop_graph();
+        kv->key = key;
+        kv->has_key = true;
+    }
+    // the graphs the steps need (the launched split count only grows with the position), captured before any launch
+    const int na0 = attn_decode_active(kv->capacity, kv->len);
+    const int na1 = attn_decode_active(kv->capacity, kv->len + n_steps - 1);
+    for (int na = na0; na <= na1; na++) {
+        if (kv->exec[na]) continue;
         if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
         HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
         vlm_status es = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos,
-                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, kv->cap_stream);
+                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, na, kv->cap_stream);
         hipGraph_t graph = nullptr;
         hipError_t ee = hipStreamEndCapture(kv->cap_stream, &graph);
         if (es) {
@@ -739,13 +751,14 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
             hipGraphDestroy(graph);
             return fail(VLM_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ie));
         }
-        kv->graph = graph;
-        kv->exec = exec;
-        kv->key = key;
-        kv->has_key = true;
+        kv->graph[na] = graph;
+        kv->exec[na] = exec;
     }
-    for (int i = 0; i < n_steps; i++) HIP_TRY(hipGraphLaunch(kv->exec, stream));
-    kv->len += n_steps;
+    for (int i = 0; i < n_steps; i++) {
+        const hipError_t le = hipGraphLaunch(kv->exec[attn_decode_active(kv->capacity, kv->len)], stream);
+        if (le != hipSuccess) return fail(VLM_ERR_HIP, "graph launch at position %d: %s", kv->len, hipGetErrorString(le));
+        kv->len += 1;  // the launched step advances the device length
+    }
     return ok();
 }
 
@@ -903,7 +916,8 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
                 at.segments = desc->rope_segments; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = kv->capacity;
                 at.interleave = desc->rope_interleave; at.norm_after = desc->qk_norm == 2;
                 at.nq = nq; at.nkv = desc->n_kv_heads; at.d = hd; at.len = kv->dlen();
-                at.nsplit = attn_decode_splits(kv->capacity); at.partial = (float*)P(d_ws, w.part);
+                at.nsplit = attn_decode_splits(kv->capacity); at.nact = attn_decode_active(kv->capacity, kv->len);
+                at.partial = (float*)P(d_ws, w.part);
                 HIP_TRY(launch_attn_decode_fused(dt, at, stream));
                 break;
             }
