@@ -218,9 +218,9 @@ struct vlm_kv {
     size_t bytes;
     int len;  // host mirror
     hipStream_t cap_stream = nullptr;
-    // one decode-step graph per count of launched attention splits (index nact)
-    hipGraph_t graph[kDecMaxSplits + 1] = {};
-    hipGraphExec_t exec[kDecMaxSplits + 1] = {};
+    // one decode-step graph per band of positions (the attention split plan changes from band to band)
+    std::vector<hipGraph_t> graph;
+    std::vector<hipGraphExec_t> exec;
     bool has_key = false;
     GraphKey key;
     int32_t* dlen() const { return (int32_t*)buf; }
@@ -229,12 +229,12 @@ struct vlm_kv {
     char* kptr(int l) const { return (char*)buf + kHeader + (size_t)l * layer_bytes(); }
     char* vptr(int l) const { return kptr(l) + k_bytes(); }
     void drop_graph() {
-        for (int i = 0; i <= kDecMaxSplits; i++) {
-            if (exec[i]) hipGraphExecDestroy(exec[i]);
-            if (graph[i]) hipGraphDestroy(graph[i]);
-            exec[i] = nullptr;
-            graph[i] = nullptr;
-        }
+        for (hipGraphExec_t e : exec)
+            if (e) hipGraphExecDestroy(e);
+        for (hipGraph_t g : graph)
+            if (g) hipGraphDestroy(g);
+        exec.clear();
+        graph.clear();
         has_key = false;
     }
 };
@@ -580,7 +580,7 @@ vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sam
 static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L, const void* embed, const void* fnorm,
                                  const void* table, vlm_kv* kv, const int32_t* tok_in, const float* x_in,
                                  const float* cosv, const float* sinv, int32_t* tok_out, float* x_out, int32_t* hist,
-                                 void* ws, const Ws& w, int nact, hipStream_t st) {
+                                 void* ws, const Ws& w, const DecSplitPlan& plan, hipStream_t st) {
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
     const int hd = desc->head_dim, dv = vdim(desc), QKV = qkv_rows(desc), W = kv->capacity;
     const bool mla = is_mla(desc);
@@ -590,7 +590,7 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
     float* part = (float*)P(ws, w.part);
     void* orow = P(ws, w.orow);
     void* arow = P(ws, w.arow);
-    const int nsplit = attn_decode_splits(W);
+    const int nsplit = plan.nsplit;
     float* rope = (float*)P(ws, w.rope);
     HIP_TRY(launch_embed_or_copy(dt, embed, desc->vocab, H, tok_in, x_in, x, kv->dlen(), cosv, sinv,
                                  mla ? desc->qk_rope_dim : hd, rope, st));
@@ -619,9 +619,9 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
             HIP_TRY(launch_mla_rope(dt, r, st));
             DecAttnArgs at{};
             at.qrot = qrow; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
-            at.dv = dv; at.len = kv->dlen(); at.nsplit = nsplit; at.nact = nact; at.partial = part;
+            at.dv = dv; at.len = kv->dlen(); at.nsplit = nsplit; at.chunk = plan.chunk; at.partial = part;
             HIP_TRY(launch_attn_decode_mla(dt, at, st));
-            HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, nact, dv, orow, st));
+            HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, dv, orow, st));
             g = GemvArgs{};
             g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * dv;
             HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
@@ -640,9 +640,9 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         at.eps = desc->norm_eps; at.rope = rope; at.segments = desc->rope_segments;
         at.interleave = desc->rope_interleave; at.norm_after = desc->qk_norm == 2;
         at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = W; at.nq = nq; at.nkv = nkv; at.d = hd;
-        at.len = kv->dlen(); at.nsplit = nsplit; at.nact = nact; at.partial = part;
+        at.len = kv->dlen(); at.nsplit = nsplit; at.chunk = plan.chunk; at.partial = part;
         HIP_TRY(launch_attn_decode_fused(dt, at, st));
-        HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, nact, hd, orow, st));
+        HIP_TRY(launch_attn_combine(dt, part, nq, nsplit, hd, orow, st));
         g = GemvArgs{};
         g.W = y.wo; g.vec = orow; g.out = x; g.N = H; g.K = nq * hd;
         HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
@@ -700,7 +700,7 @@ vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers
                                 table_rows, d_token_out, d_ws, ws_bytes, 1, &w);
     if (s) return s;
     if ((s = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_in, d_x_in, d_cos, d_sin,
-                            d_token_out, d_x_out, d_token_hist, d_ws, w, attn_decode_active(kv->capacity, kv->len),
+                            d_token_out, d_x_out, d_token_hist, d_ws, w, attn_decode_plan(kv->capacity, kv->len),
                             stream)))
         return s;
     kv->len += 1;
@@ -729,15 +729,20 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
         kv->key = key;
         kv->has_key = true;
     }
-    // the graphs the steps need (the launched split count only grows with the position), captured before any launch
-    const int na0 = attn_decode_active(kv->capacity, kv->len);
-    const int na1 = attn_decode_active(kv->capacity, kv->len + n_steps - 1);
-    for (int na = na0; na <= na1; na++) {
-        if (kv->exec[na]) continue;
+    // the graphs of the bands the steps pass through, captured before any launch
+    const int b0 = attn_decode_plan(kv->capacity, kv->len).band;
+    const int b1 = attn_decode_plan(kv->capacity, kv->len + n_steps - 1).band;
+    if ((int)kv->exec.size() <= b1) {
+        kv->exec.resize(b1 + 1, nullptr);
+        kv->graph.resize(b1 + 1, nullptr);
+    }
+    for (int b = b0; b <= b1; b++) {
+        if (kv->exec[b]) continue;
+        const DecSplitPlan plan = attn_decode_plan(kv->capacity, b * kDecBand);
         if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
         HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
         vlm_status es = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos,
-                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, na, kv->cap_stream);
+                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, plan, kv->cap_stream);
         hipGraph_t graph = nullptr;
         hipError_t ee = hipStreamEndCapture(kv->cap_stream, &graph);
         if (es) {
@@ -751,11 +756,11 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
             hipGraphDestroy(graph);
             return fail(VLM_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ie));
         }
-        kv->graph[na] = graph;
-        kv->exec[na] = exec;
+        kv->graph[b] = graph;
+        kv->exec[b] = exec;
     }
     for (int i = 0; i < n_steps; i++) {
-        const hipError_t le = hipGraphLaunch(kv->exec[attn_decode_active(kv->capacity, kv->len)], stream);
+        const hipError_t le = hipGraphLaunch(kv->exec[attn_decode_plan(kv->capacity, kv->len).band], stream);
         if (le != hipSuccess) return fail(VLM_ERR_HIP, "graph launch at position %d: %s", kv->len, hipGetErrorString(le));
         kv->len += 1;  // the launched step advances the device length
     }
@@ -916,7 +921,8 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
                 at.segments = desc->rope_segments; at.kc = kv->kptr(l); at.vc = kv->vptr(l); at.W = kv->capacity;
                 at.interleave = desc->rope_interleave; at.norm_after = desc->qk_norm == 2;
                 at.nq = nq; at.nkv = desc->n_kv_heads; at.d = hd; at.len = kv->dlen();
-                at.nsplit = attn_decode_splits(kv->capacity); at.nact = attn_decode_active(kv->capacity, kv->len);
+                const DecSplitPlan plan = attn_decode_plan(kv->capacity, kv->len);
+                at.nsplit = plan.nsplit; at.chunk = plan.chunk;
                 at.partial = (float*)P(d_ws, w.part);
                 HIP_TRY(launch_attn_decode_fused(dt, at, stream));
                 break;

@@ -118,11 +118,17 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 // Decode attention splits the valid slots over at most this many blocks per KV
 // head; each writes one partial row of d + 4 floats (o[d], m, l, pad) per query head.
 constexpr int kDecMaxSplits = 32;
-int attn_decode_splits(int capacity);
-// Splits that hold a valid slot when the token at position t (0-based) is
-// decoded: those whose slot range starts at or below t. The launches cover
-// only these; the rest of the window holds nothing yet.
-int attn_decode_active(int capacity, int t);
+// Split plan of the decode attention at position t (0-based): the positions
+// come in bands of kDecBand; a band's launches cover slots [0, tb), tb the
+// band's end (at most the capacity), with nsplit <= kDecMaxSplits splits of
+// `chunk` slots (a multiple of the 16 keys a block scores per step). The
+// split layout lives only between one attention launch and its merge, so it
+// may change from band to band; the decode graphs are kept per band.
+constexpr int kDecBand = 64;
+struct DecSplitPlan {
+    int nsplit, chunk, band;
+};
+DecSplitPlan attn_decode_plan(int capacity, int t);
 
 // Decode attention of one layer: QK-Norm + RoPE of the new token's q and k
 // (position t = *len), K/V written into slot t, split-K attention over slots
@@ -137,15 +143,13 @@ struct DecAttnArgs {
     void* kc; void* vc;  // layer K and V, [nkv][W][d]
     int W, nq, nkv, d;
     const int32_t* len;
-    int nsplit;          // splits of the window (slot range of split sp: [sp*chunk, (sp+1)*chunk))
-    int nact = 0;        // splits launched (attn_decode_active); 0 = all nsplit
-    float* partial;      // [nq][nsplit][d + 4], splits 0..nact-1 written
+    int nsplit, chunk;   // launched splits; split sp scores slots [sp*chunk, (sp+1)*chunk) below t + 1
+    float* partial;      // [nq][nsplit][d + 4]
 };
 hipError_t launch_attn_decode_fused(int dtype, const DecAttnArgs& a, hipStream_t st);
 // Expanded MLA decode attention (d 192, dv 128, nq == nkv): reads a.qrot and the cache only.
 hipError_t launch_attn_decode_mla(int dtype, const DecAttnArgs& a, hipStream_t st);
-// Merges splits 0..nact-1 of each query head's partial rows (row stride nsplit).
-hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int nact, int d, void* out,
+hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
                                hipStream_t st);
 
 // Next-token sampler over one logits row (one block): penalty on context ids,

@@ -575,10 +575,10 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
 
 // ============================================================== decode, fused
 // One block of kDecWaves wavefronts per (KV head g, split sp); split sp owns the
-// window slots [sp*chunk, (sp+1)*chunk), chunk = ceil(W / nsplit), of which
-// those below T = t+1 are valid. Only the splits starting at or below t are
-// launched (grid y = nact: the host knows the position it decodes; the device
-// length stays the one the kernel reads). Each 16-lane quarter of a wavefront scores
+// slots [sp*chunk, (sp+1)*chunk) of the window, of which those below T = t+1
+// are valid. The host sizes the splits for the band of positions it decodes
+// (attn_decode_plan); the device length t is read by the kernel. Each 16-lane
+// quarter of a wavefront scores
 // one key per step (a step covers 4 keys per wavefront). Phases:
 //  1. the block's K/V rows, the projections it rotates (q heads of g, the
 //     new k and v), their norm gains and the RoPE row of position t (staged
@@ -594,20 +594,20 @@ hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
 constexpr int kDecWaves = 4;  // wavefronts per block
 constexpr int kDecSteps = 8;  // key steps requested in one batch (fewer for 4 or 8 heads per KV head)
 
-// Splits: one per 32 window slots (up to kDecMaxSplits). A block streams at
-// most ~50 GB/s, so the KV read needs >= ~128 blocks in flight; the combine
-// then reads the launched splits' partials per query head. (Measured on the 28-layer
+// Splits: slots [0, tb) of a band in up to kDecMaxSplits splits of a
+// multiple of 16 slots (the keys a block scores per step). A block streams at
+// most ~50 GB/s, so the KV read wants >= ~128 blocks in flight; fewer, longer
+// splits lengthen each block's serial scoring chain. (Measured on the 28-layer
 // stack's shape at 624 valid slots: 4 wavefronts x 32 splits 5.1 us,
 // 8 x 16 5.6 us, 2 x 64 5.8 us.)
-int attn_decode_splits(int capacity) {
-    const int n = (capacity + 31) / 32;
-    return n < 1 ? 1 : (n > kDecMaxSplits ? kDecMaxSplits : n);
-}
-
-int attn_decode_active(int capacity, int t) {
-    const int ns = attn_decode_splits(capacity), chunk = (capacity + ns - 1) / ns;
-    const int n = (t < 0 ? 0 : t) / chunk + 1;
-    return n > ns ? ns : n;
+DecSplitPlan attn_decode_plan(int capacity, int t) {
+    constexpr int unit = kDecWaves * 4;
+    DecSplitPlan p;
+    p.band = (t < 0 ? 0 : t) / kDecBand;
+    const int tb = std::max(1, std::min(capacity, (p.band + 1) * kDecBand));
+    p.chunk = unit * ((tb + unit * kDecMaxSplits - 1) / (unit * kDecMaxSplits));
+    p.nsplit = (tb + p.chunk - 1) / p.chunk;
+    return p;
 }
 
 template <class T, int D, int G, int NW>
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
     __shared__ float sm_o[NQ][G][D];
     const int g = blockIdx.x, sp = blockIdx.y;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
-    const int chunk = (a.W + a.nsplit - 1) / a.nsplit;
+    const int chunk = a.chunk;
     const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
     const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;  // key steps of the slot range
     const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
@@ -890,29 +890,28 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
 
 // Merge of the split partials: one wavefront per 64 columns of a query head's
 // output row (a block per head). Lane s holds the statistics (m, l) of split
-// s; every lane requests its column of the NS >= nact launched splits' o rows
+// s; every lane requests its column of the NS >= nsplit launched splits' o rows
 // up front (indices clamped, unconditional: at most 32 + 2 loads, within the
 // 63 a wavefront keeps in flight, so the merge is one memory round trip),
 // then the split weights f_s = exp2(m_s - max m) are broadcast with readlane.
 template <class T, int D, int NS>
 __global__ __launch_bounds__(64 * ((D + 63) / 64)) void attn_combine_fast_kernel(const float* __restrict__ partial,
-                                                                                  int nsplit, int nact,
-                                                                                  T* __restrict__ out) {
+                                                                                  int nsplit, T* __restrict__ out) {
     constexpr int PS = D + 4;
     static_assert(NS <= 64, "one lane per split");
     const int h = blockIdx.x, lane = threadIdx.x % kWave, e = threadIdx.x;
     const float* p = partial + (size_t)h * nsplit * PS;
-    const int sl = min(lane, nact - 1);
+    const int sl = min(lane, nsplit - 1);
     const float ms = p[sl * PS + D], ls = p[sl * PS + D + 1];
     const int ec = min(e, D - 1);
     float ov[NS];
 #pragma unroll
-    for (int s = 0; s < NS; s++) ov[s] = p[min(s, nact - 1) * PS + ec];
+    for (int s = 0; s < NS; s++) ov[s] = p[min(s, nsplit - 1) * PS + ec];
     __builtin_amdgcn_sched_barrier(0);
-    const float m = lane < nact ? ms : -INFINITY;
+    const float m = lane < nsplit ? ms : -INFINITY;
     const float mx = wave_max(m);
-    const float f = (lane < nact && m != -INFINITY) ? exp2f(m - mx) : 0.f;
-    const float lsum = wave_sum(f * (lane < nact ? ls : 0.f));
+    const float f = (lane < nsplit && m != -INFINITY) ? exp2f(m - mx) : 0.f;
+    const float lsum = wave_sum(f * (lane < nsplit ? ls : 0.f));
     float v = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
@@ -927,7 +926,7 @@ __global__ __launch_bounds__(64 * ((D + 63) / 64)) void attn_combine_fast_kernel
 
 template <class T, int D>
 static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
-    const dim3 grid(a.nkv, a.nact > 0 ? a.nact : a.nsplit);
+    const dim3 grid(a.nkv, a.nsplit);
     switch (a.nq / a.nkv) {
         case 1: attn_decode_fused_kernel<T, D, 1, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
         case 2: attn_decode_fused_kernel<T, D, 2, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
@@ -955,7 +954,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mla_kernel(DecAttnArgs a)
     __shared__ float sm_o[NW][DV];
     const int g = blockIdx.x, sp = blockIdx.y;
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
-    const int chunk = (a.W + a.nsplit - 1) / a.nsplit;
+    const int chunk = a.chunk;
     const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
     const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;
     const T* Kg = (const T*)a.kc + (size_t)g * a.W * DQ;
@@ -1103,7 +1102,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mla_kernel(DecAttnArgs a)
 
 hipError_t launch_attn_decode_mla(int dtype, const DecAttnArgs& a, hipStream_t st) {
     if (a.d != 192 || a.dv != 128 || a.nq != a.nkv || !a.qrot) return hipErrorInvalidValue;
-    const dim3 grid(a.nkv, a.nact > 0 ? a.nact : a.nsplit);
+    const dim3 grid(a.nkv, a.nsplit);
     if (dtype == 1)
         attn_decode_mla_kernel<bf16_t, 192, 128, 4><<<grid, 4 * 64, 0, st>>>(a);
     else
@@ -1113,33 +1112,33 @@ hipError_t launch_attn_decode_mla(int dtype, const DecAttnArgs& a, hipStream_t s
 
 // Loads per lane follow the launched splits: 8, 16 or 32 rows requested.
 template <class T, int D>
-static void combine_ns(const float* partial, int nq, int nsplit, int nact, void* out, hipStream_t st) {
+static void combine_ns(const float* partial, int nq, int nsplit, void* out, hipStream_t st) {
     constexpr int threads = 64 * ((D + 63) / 64);
-    if (nact <= 8)
-        attn_combine_fast_kernel<T, D, 8><<<nq, threads, 0, st>>>(partial, nsplit, nact, (T*)out);
-    else if (nact <= 16)
-        attn_combine_fast_kernel<T, D, 16><<<nq, threads, 0, st>>>(partial, nsplit, nact, (T*)out);
+    if (nsplit <= 8)
+        attn_combine_fast_kernel<T, D, 8><<<nq, threads, 0, st>>>(partial, nsplit, (T*)out);
+    else if (nsplit <= 16)
+        attn_combine_fast_kernel<T, D, 16><<<nq, threads, 0, st>>>(partial, nsplit, (T*)out);
     else
-        attn_combine_fast_kernel<T, D, kDecMaxSplits><<<nq, threads, 0, st>>>(partial, nsplit, nact, (T*)out);
+        attn_combine_fast_kernel<T, D, kDecMaxSplits><<<nq, threads, 0, st>>>(partial, nsplit, (T*)out);
 }
 
 template <class T>
-static hipError_t combine_dim(const float* partial, int nq, int nsplit, int nact, int d, void* out, hipStream_t st) {
+static hipError_t combine_dim(const float* partial, int nq, int nsplit, int d, void* out, hipStream_t st) {
     switch (d) {
-        case 64: combine_ns<T, 64>(partial, nq, nsplit, nact, out, st); break;
-        case 72: combine_ns<T, 72>(partial, nq, nsplit, nact, out, st); break;
-        case 80: combine_ns<T, 80>(partial, nq, nsplit, nact, out, st); break;
-        case 128: combine_ns<T, 128>(partial, nq, nsplit, nact, out, st); break;
+        case 64: combine_ns<T, 64>(partial, nq, nsplit, out, st); break;
+        case 72: combine_ns<T, 72>(partial, nq, nsplit, out, st); break;
+        case 80: combine_ns<T, 80>(partial, nq, nsplit, out, st); break;
+        case 128: combine_ns<T, 128>(partial, nq, nsplit, out, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int nact, int d, void* out,
+hipError_t launch_attn_combine(int dtype, const float* partial, int nq, int nsplit, int d, void* out,
                                hipStream_t st) {
-    if (nsplit < 1 || nsplit > kDecMaxSplits || nact < 1 || nact > nsplit) return hipErrorInvalidValue;
-    return dtype == 1 ? combine_dim<bf16_t>(partial, nq, nsplit, nact, d, out, st)
-                      : combine_dim<float>(partial, nq, nsplit, nact, d, out, st);
+    if (nsplit < 1 || nsplit > kDecMaxSplits) return hipErrorInvalidValue;
+    return dtype == 1 ? combine_dim<bf16_t>(partial, nq, nsplit, d, out, st)
+                      : combine_dim<float>(partial, nq, nsplit, d, out, st);
 }
 
 template <class T>
