@@ -600,12 +600,25 @@ constexpr int kDecSteps = 8;  // key steps requested in one batch (fewer for 4 o
 // splits lengthen each block's serial scoring chain. (Measured on the 28-layer
 // stack's shape at 624 valid slots: 4 wavefronts x 32 splits 5.1 us,
 // 8 x 16 5.6 us, 2 x 64 5.8 us.)
+// VLM_DEC_SPLITS (1..kDecMaxSplits) caps the splits, for tuning. Measured on
+// the 36-layer stack (positions 512..767): a cap of 32 gives 465.8 ms per
+// 256-token decode, 16 467.1 ms, 48 and 64 (with a 64-split maximum) 473.5 ms.
+static int dec_split_cap() {
+    static int v = [] {
+        const char* e = getenv("VLM_DEC_SPLITS");
+        const int n = e ? atoi(e) : 32;
+        return n < 1 ? 1 : (n > kDecMaxSplits ? kDecMaxSplits : n);
+    }();
+    return v;
+}
+
 DecSplitPlan attn_decode_plan(int capacity, int t) {
     constexpr int unit = kDecWaves * 4;
+    const int cap = dec_split_cap();
     DecSplitPlan p;
     p.band = (t < 0 ? 0 : t) / kDecBand;
     const int tb = std::max(1, std::min(capacity, (p.band + 1) * kDecBand));
-    p.chunk = unit * ((tb + unit * kDecMaxSplits - 1) / (unit * kDecMaxSplits));
+    p.chunk = unit * ((tb + unit * cap - 1) / (unit * cap));
     p.nsplit = (tb + p.chunk - 1) / p.chunk;
     return p;
 }
