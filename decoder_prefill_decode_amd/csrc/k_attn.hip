@@ -25,6 +25,9 @@
 // loads), softmax statistics merge across lanes, wavefronts and blocks by
 // log-sum-exp.
 #include <math.h>
+#include <stdlib.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "internal.hpp"

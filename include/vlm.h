@@ -176,7 +176,7 @@ vlm_status vlm_kv_bytes(const vlm_model_desc* desc, int32_t capacity, size_t* by
  * handle and enqueues a kernel that sets the device length to 0. */
 vlm_status vlm_kv_alloc(const vlm_model_desc* desc, int32_t capacity, void* d_buf, size_t bytes,
                         hipStream_t stream, vlm_kv** out);
-/* Frees the host handle (and its cached decode graph), not the device memory. */
+/* Frees the host handle (and its cached decode graphs), not the device memory. */
 vlm_status vlm_kv_free(vlm_kv* kv);
 /* Host mirror of the number of valid slots. */
 vlm_status vlm_kv_len(const vlm_kv* kv, int32_t* len);
@@ -282,11 +282,13 @@ vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers
                            size_t ws_bytes, hipStream_t stream);
 
 /* n_steps greedy decode steps with each step's token feeding the next
- * (d_token_io is read and written by every step). The first call captures one
- * step into a HIP graph, cached on the kv handle and re-captured when any
- * argument changes; each step is then one graph launch on `stream`, and the
- * host never synchronises inside the loop. Requires vocab > 0 and
- * length + n_steps <= min(capacity, table_rows). */
+ * (d_token_io is read and written by every step). One step is captured into a
+ * HIP graph per band of 64 positions (the decode attention's split layout
+ * follows the band), before the first launch of the call; the graphs are
+ * cached on the kv handle and dropped when any argument changes. Each step is
+ * then one graph launch on `stream`, and the host never synchronises inside
+ * the loop. Requires vocab > 0 and length + n_steps <= min(capacity,
+ * table_rows). */
 vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
                            const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
                            const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
