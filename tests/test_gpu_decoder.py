@@ -185,11 +185,12 @@ def test_generic_gemv_fallback_shapes(rt):
 
 # ------------------------------------------------------------------ decode attention forms
 def test_decode_past_a_thousand_slots(rt):
-    """A prompt of 1016 rows and 16 decode steps in a 1152-slot window: the
-    decode attention splits the window into 32 ranges of 36 slots, so every
-    split holds valid keys and the merge combines 32 live partial rows. The
-    graph loop and the eager steps must give the oracle's ids and cache rows
-    (fp32: 1e-4)."""
+    """A prompt of 1016 rows and 16 decode steps in a 1152-slot window. The
+    steps cross the band boundary at position 1024: positions 1016..1023
+    take 32 splits of 32 slots (every split holds valid keys, the merge
+    combines 32 live partial rows), 1024..1031 take 23 splits of 48 slots,
+    so the graph loop switches graphs mid-loop. The graph loop and the eager
+    steps must give the oracle's ids and cache rows (fp32: 1e-4)."""
     pipeline, _ = rt
     cfg = vs.scaled(vs.C1, seq=1016, decode_steps=16, capacity=1152, name="c1_long")
     glob, layers = make(cfg)
