@@ -620,6 +620,13 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
     } while (0)
             if constexpr (EPI == Epi::SwiGLU)
                 if (pl.bm == 256 && pl.bn == 192) VLM_RUN_LDS(256, 192, 2, 8, 1, 64);
+            // an unsplit 128x256 plan whose blocks fit one round as 128x192 tiles takes those (eight
+            // 32x96 wavefront tiles; three 32-column blocks per wavefront, so not for SwiGLU): the
+            // vision tower's fc1 (N 4304: 187 -> 253 blocks) and QKV (N 3456: 154 -> 198), bf16 tower
+            // 5.05 -> 4.83 ms per pass (a four-wavefront 64x96 form: 5.07 ms)
+            if constexpr (EPI != Epi::SwiGLU)
+                if (pl.bm == 128 && pl.bn == 256 && pl.sp == 1 && tiles(128, 192) <= 256)
+                    VLM_RUN_LDS(128, 192, 2, 4, 2, 64);
             if (pl.bm == 256) VLM_RUN_LDS(256, 256, 2, 4, 2, 64);
             if (pl.bm == 128 && pl.bn == 256) VLM_RUN_LDS(128, 256, 2, 2, 4, 64);
             if (pl.bm == 128) VLM_RUN_LDS(128, 128, 2, 2, 2, 64);
