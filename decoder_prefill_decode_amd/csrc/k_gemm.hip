@@ -4,15 +4,18 @@
 // matmuls that dominate prefill (MNN llm_demo Omni article §5.3; HunyuanOCR
 // v1.5 ncnn port §5).
 //
-// gfx950 tiling: 256 threads = 4 wavefronts in a 2x2 grid, each owning a
-// (BM/2) x (BN/2) sub-tile built from 32x32 MFMA blocks:
+// Register-staged kernel (fp32, and bf16 rows with K % 8 != 0): 256 threads =
+// 4 wavefronts in a 2x2 grid, each owning a (BM/2) x (BN/2) sub-tile built
+// from 32x32 MFMA blocks:
 //   bf16: v_mfma_f32_32x32x16_bf16, 64-element K stage;
 //   f32:  v_mfma_f32_32x32x2f32,   32-element K stage.
 // Both operands are K-contiguous, so every lane feeds the MFMA from one
-// 16-byte LDS read (bf16) or one 4-byte read (f32). LDS is double-buffered
-// and the next stage's global loads are in flight during the current stage's
-// MFMAs. Blocks are remapped so that consecutive output tiles (which share a
-// weight panel) land on the same XCD and its L2.
+// 16-byte LDS read (bf16: one 16-wide step; f32: four 2-wide steps of a quad
+// of 8 columns). LDS is double-buffered and the next stage's global loads are
+// in flight during the current stage's MFMAs. The bf16 prefill shapes use the
+// direct-to-LDS kernel further down (its own wavefront grids and tile plan).
+// Blocks are remapped so that consecutive output tiles (which share a weight
+// panel) land on the same XCD and its L2.
 #include <stdlib.h>
 
 #include <algorithm>
