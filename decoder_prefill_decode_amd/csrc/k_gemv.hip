@@ -162,7 +162,7 @@ template <> struct Raw4<bf16_t> {
 };
 
 //  * PlainLds operand: a plain vector staged once per block into LDS (raw
-//    16-byte chunks), so the wavefronts of a block share one read of it;
+//    16-byte chunks), so the four wavefronts of a block share one read of it;
 //    with long rows a per-lane copy would double the L2 traffic of the GEMV.
 //  * NW wavefronts per block (4, or 5 where that gives every CU the same
 //    number of blocks).
