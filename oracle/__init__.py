@@ -12,8 +12,8 @@ holds the seeded input generators and no arithmetic of the method.
 
 Precision: fp32 workloads are evaluated in float64. bf16 workloads keep the
 same bf16 values as the GPU path, round GEMM operands to bf16 at the points
-the GPU does, contract them in float32 BLAS (a product of two bf16 values is
-exact in float32) and do norm statistics, softmax and argmax in float64.
+the GPU does, and add the exact products of bf16 values in float64 (so no
+summation order is built in); norm statistics, softmax and argmax are float64.
 
 Parity status of each function is listed in the module docstrings; every
 function here is pinned by a -m "not gpu" test in tests/test_oracle_pins.py.

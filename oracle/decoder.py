@@ -43,6 +43,13 @@ Readings where the pages are silent (listed with the design notes):
   is 1e6; RMSNorm eps 1e-6; in bf16 mode the GEMM A-operands (normed rows,
   attention output, SwiGLU product, final-norm row), q and the cached k/v are
   rounded to bf16 (ties to even), the softmax P stays unrounded.
+  bf16 storage with fp32 accumulation (the Mixed policy of [HyOCR15] §3.7)
+  is read as: the products of bf16 values are exact, and the oracle adds them
+  exactly (float64 sums of the float64 products), so its result does not
+  depend on a summation order. BF16_F32SUM keeps every operand and rounding
+  point but sums in float32 BLAS order; it exists only to measure how far a
+  valid float32 summation order moves the results (the noise floor that
+  decides which greedy steps are near-ties).
 """
 import time
 
@@ -52,7 +59,9 @@ MASK_NEG = -1.0e9          # finite "minus infinity" of the fixed-window mask
 QK_NORM_BEFORE_ROPE = 1    # Qwen3 order ([Penguin] §5.4)
 QK_NORM_AFTER_ROPE = 2     # HunyuanOCR order: the cache holds the normalised k ([HyOCR10] 五.2)
 F64 = "f64"
-BF16 = "bf16"
+BF16 = "bf16"                # bf16 operands and rounding points, exact (float64) sums
+BF16_F32SUM = "bf16_f32sum"  # the same, summed in float32 BLAS order (noise-floor measurement only)
+BF16_MODES = (BF16, BF16_F32SUM)
 
 
 # ----------------------------------------------------------------------------
@@ -104,10 +113,16 @@ def gelu_tanh(z):
 
 
 def _lin(a, w, prec):
-    """a @ w.T. f64: in float64. bf16: a rounded to bf16, fp32 BLAS, result float64."""
+    """a @ w.T.
+
+    F64: float64. BF16: a rounded to bf16; w holds bf16 values as float64, so
+    every product is exact and the float64 sums are exact to ~1e-16 relative.
+    BF16_F32SUM: the same operands summed by float32 BLAS (w float32)."""
     if prec == BF16:
+        return bf16_round(a) @ np.asarray(w, np.float64).T
+    if prec == BF16_F32SUM:
         ar = bf16_round(a).astype(np.float32)
-        return (ar @ w.T).astype(np.float64)
+        return (ar @ np.asarray(w, np.float32).T).astype(np.float64)
     return np.asarray(a, np.float64) @ w.T
 
 
@@ -267,7 +282,7 @@ def decoder_layer(x, w, cfg, k_cache, v_cache, pos0, cos, sin, prec):
     if qkn == QK_NORM_AFTER_ROPE:
         q = rms_norm(q, w["q_norm"], cfg.eps)
         k = rms_norm(k, w["k_norm"], cfg.eps)
-    if prec == BF16:
+    if prec in BF16_MODES:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     k_cache[:, pos0:pos0 + S] = k.transpose(1, 0, 2)
     v_cache[:, pos0:pos0 + S] = v.transpose(1, 0, 2)
@@ -321,7 +336,7 @@ def mla_layer(x, w, cfg, k_cache, v_cache, pos0, cos, sin, prec):
     q = np.concatenate([q[..., :dn], q_rope], axis=-1)
     k = np.concatenate([kv[..., :dn], np.broadcast_to(k_rope, (S, nq, dr))], axis=-1)
     v = kv[..., dn:]
-    if prec == BF16:
+    if prec in BF16_MODES:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     k_cache[:, pos0:pos0 + S] = k.transpose(1, 0, 2)
     v_cache[:, pos0:pos0 + S] = v.transpose(1, 0, 2)
@@ -357,12 +372,13 @@ def _top2_margin(logits):
 # whole run
 # ----------------------------------------------------------------------------
 def _prep_weights(w, prec):
-    if prec == BF16:
+    if prec == BF16_F32SUM:
         return {k: np.asarray(v, dtype=np.float32) for k, v in w.items()}
     return {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
 
 
-def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=False, sampler=None):
+def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=False, sampler=None,
+                prec=None, forced_ids=None):
     """Prefill the prompt, then greedy-decode `steps` tokens (default cfg.decode_steps).
 
     glob: vlm_synth.decoder_globals(cfg); layers: list of decoder_layer_weights.
@@ -371,12 +387,19 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
     sampler: optional f(logits, context_ids, i) -> id replacing the greedy argmax
       of the i-th generated token; context_ids are the prompt ids and the ids
       generated so far (oracle/sampling.py provides the sampler itself).
+    prec: override of the arithmetic mode (default F64 for f32 workloads, BF16
+      for bf16 ones; BF16_F32SUM only to measure the noise floor).
+    forced_ids: teacher forcing; decode step i embeds forced_ids[i] instead of
+      the previous pick (ids, margins and logits are still the stack's own).
+    layers may be any sequence; each element is read once, so a lazy sequence
+      keeps only one layer's input arrays alive at a time.
     Returns a dict with x_in [S,H], prefill_x [S,H] (hidden after the stack),
     k_cache/v_cache [L,nkv,W,d], logits0 (head of the last prompt row, vocab>0),
     ids [steps+1], margins [steps+1], decode_x [steps,H] (hidden after the
     stack for each decode step).
     """
-    prec = BF16 if cfg.dtype == "bf16" else F64
+    if prec is None:
+        prec = BF16 if cfg.dtype == "bf16" else F64
     steps = cfg.decode_steps if steps is None else steps
     L, W = cfg.n_layers, cfg.capacity
     ws = [_prep_weights(w, prec) for w in layers]
@@ -389,7 +412,7 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
     layer_fn = mla_layer if mla else decoder_layer
     has_vocab = cfg.vocab > 0
     if has_vocab:
-        table = np.asarray(glob["embed"], np.float32 if prec == BF16 else np.float64)
+        table = np.asarray(glob["embed"], np.float32 if prec == BF16_F32SUM else np.float64)
         x = embed_inject(glob["embed"], glob["ids"], cfg.placeholder_id, glob.get("img"))
     else:
         x = np.asarray(glob["x"], np.float64)
@@ -429,8 +452,11 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
         pos = S + i
         if pos >= W:
             raise ValueError("decode position exceeds the KV window")
-        row = table[ids[-1]][None, :].astype(np.float64) if has_vocab else \
-            np.asarray(glob["decode_x"][i], np.float64)[None, :]
+        if has_vocab:
+            feed = ids[-1] if forced_ids is None else int(forced_ids[i])
+            row = table[feed][None, :].astype(np.float64)
+        else:
+            row = np.asarray(glob["decode_x"][i], np.float64)[None, :]
         hx = stack(row, pos)
         dec_x.append(hx[0])
         if has_vocab:
@@ -446,3 +472,30 @@ def run_decoder(cfg, glob, layers, steps=None, prefill_split=None, keep_logits=F
     if keep_logits:
         res["step_logits"] = all_logits
     return res
+
+
+def block_logits(cfg, glob, layers, block_ids, prec=None):
+    """Logits of every row of a token block appended to the prompt, by definition:
+    one causal forward over prompt + block (embedding, image injection, every
+    layer over the whole sequence), final RMSNorm and lm_head on each block row.
+
+    This is what a multi-token verify of a drafted block computes ([HyOCR15]
+    §3.8: the target checks the drafted tokens in one causal forward): row i's
+    logits pick the token that follows prompt + block[0..i].
+    Returns [len(block_ids), V] float64.
+    """
+    if prec is None:
+        prec = BF16 if cfg.dtype == "bf16" else F64
+    block_ids = [int(i) for i in block_ids]
+    S, k = len(glob["ids"]), len(block_ids)
+    W = S + k
+    ws = [_prep_weights(w, prec) for w in layers]
+    table = np.asarray(glob["embed"], np.float32 if prec == BF16_F32SUM else np.float64)
+    x = embed_inject(glob["embed"], glob["ids"], cfg.placeholder_id, glob.get("img"))
+    x = np.concatenate([x, table[block_ids].astype(np.float64)], axis=0)
+    cos, sin = rope_tables(np.arange(W)[None, :], np.zeros(cfg.head_dim // 2, np.int64), 1, cfg.head_dim, cfg.theta)
+    for l in range(cfg.n_layers):
+        kc = np.zeros((cfg.n_kv_heads, W, cfg.head_dim))
+        vc = np.zeros_like(kc)
+        x = decoder_layer(x, ws[l], cfg, kc, vc, 0, cos, sin, prec)
+    return np.stack([lm_head_logits(x[S + i], glob["final_norm"], table, cfg.eps, prec) for i in range(k)])

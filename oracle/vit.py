@@ -25,17 +25,18 @@ Readings where the pages are silent (listed with the design notes):
     units are permuted window by window (windows in raster order, units in
     raster order inside each window); the merged output is returned in raster
     (unpermuted) unit order.
-  * bf16 storage (the Mixed policy of the HunyuanOCR v1.5 port, §3.6: the
+  * bf16 storage (the Mixed policy of the HunyuanOCR v1.5 port, §3.7: the
     vision tower keeps reduced-precision storage with fp32 accumulation; this
     library's reduced storage type is bf16): weights, biases and norm
     parameters hold bf16 values, the GEMM operands (normed rows, attention
     output, GELU output, merger operands) and q, k, v are rounded to bf16, the
-    residual stream stays fp32 -- the same rounding points as the decoder.
+    residual stream stays fp32 -- the same rounding points as the decoder,
+    and the same exact (float64) sums of the exact bf16 products.
 """
 import numpy as np
 
-from .decoder import (BF16, MASK_NEG, _lin, bf16_round, gelu_tanh, layer_norm, rope_apply, rope_tables,
-                      softmax_attention, F64)
+from .decoder import (BF16, BF16_F32SUM, BF16_MODES, MASK_NEG, _lin, bf16_round, gelu_tanh, layer_norm,
+                      rope_apply, rope_tables, softmax_attention, F64)
 
 
 def vit_window_order(cfg):
@@ -77,7 +78,7 @@ def vit_layer(x, w, mask_add, cos, sin, cfg, prec=F64):
     v = (_lin(h, w["wv"], prec) + w["bv"]).reshape(S, nh, d)
     q = rope_apply(q, cos, sin, 2)
     k = rope_apply(k, cos, sin, 2)
-    if prec == BF16:
+    if prec in BF16_MODES:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     o = softmax_attention(q.transpose(1, 0, 2), k.transpose(1, 0, 2), v.transpose(1, 0, 2), mask_add, 1)
     x = x + _lin(o.transpose(1, 0, 2).reshape(S, nh * d), w["wo"], prec) + w["bo"]
@@ -86,9 +87,10 @@ def vit_layer(x, w, mask_add, cos, sin, cfg, prec=F64):
     return x + _lin(f, w["w2"], prec) + w["b2"]
 
 
-def run_vit(cfg, glob, layers):
+def run_vit(cfg, glob, layers, prec=None):
     """Vision tower + merger. Returns out [n_merged, out_dim] in raster unit order,
-    plus the permuted final hidden rows and the permutation."""
+    plus the permuted final hidden rows and the permutation. prec overrides the
+    arithmetic mode (BF16_F32SUM only to measure the bf16 tower's noise floor)."""
     m2 = cfg.merge * cfg.merge
     perm_u, seg_u = vit_window_order(cfg)
     row_perm = (perm_u[:, None] * m2 + np.arange(m2)[None, :]).reshape(-1)
@@ -100,9 +102,10 @@ def run_vit(cfg, glob, layers):
     cos, sin = rope_tables(pos, axes, 2, cfg.head_dim, cfg.theta)
     win_mask = np.where(seg_rows[:, None] == seg_rows[None, :], 0.0, MASK_NEG)
     full_mask = np.zeros_like(win_mask)
-    prec = BF16 if getattr(cfg, "dtype", "f32") == "bf16" else F64
-    # bf16 mode: matrices as float32 arrays of bf16 values (fp32 products, as _lin expects)
-    mat = (lambda a: np.asarray(a, np.float32)) if prec == BF16 else (lambda a: np.asarray(a, np.float64))
+    if prec is None:
+        prec = BF16 if getattr(cfg, "dtype", "f32") == "bf16" else F64
+    # matrices in the element type _lin contracts them in (bf16 values are exact in float64)
+    mat = (lambda a: np.asarray(a, np.float32)) if prec == BF16_F32SUM else (lambda a: np.asarray(a, np.float64))
     ws = [{k: (mat(v) if v.ndim == 2 else np.asarray(v, np.float64)) for k, v in w.items()} for w in layers]
     for l, w in enumerate(ws):
         x = vit_layer(x, w, full_mask if l in cfg.full_layers else win_mask, cos, sin, cfg, prec)

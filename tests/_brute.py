@@ -5,8 +5,39 @@ that the vectorised oracle can be checked against them. Every formula below is
 restated from the pages: RMSNorm / LayerNorm, the textbook rotation form of
 RoPE (complex multiplication), written-out softmax, GQA head mapping through
 repeat_interleave expansion, SwiGLU, pre-LN ViT block.
+
+bf16 forms: `bf16` rounds a Python float to the nearest bfloat16 from its
+IEEE-754 double bits (8 significant bits, ties to even); the layer functions
+take an optional rounding op applied at the points where the bf16 policy
+stores a value (operands of every projection, q and the cached k/v), and
+their dot products then use math.fsum (correctly rounded sums).
 """
 import math
+import struct
+
+
+def bf16(v):
+    """Nearest bfloat16 value of a finite double (round half to even), as a float.
+
+    A double holds 52 explicit mantissa bits, a bfloat16 7: the low 45 bits are
+    dropped, rounding the kept part up when they exceed half an ulp, or equal
+    it with an odd kept part (a carry into the exponent is the correct result).
+    Values in the bf16 normal range only (the workloads produce no others)."""
+    if v == 0.0:
+        return v
+    b = struct.unpack("<Q", struct.pack("<d", v))[0]
+    drop = 45
+    low = b & ((1 << drop) - 1)
+    b >>= drop
+    half = 1 << (drop - 1)
+    if low > half or (low == half and (b & 1)):
+        b += 1
+    return struct.unpack("<d", struct.pack("<Q", b << drop))[0]
+
+
+def matvec_exact(W, x):
+    """W [n][k] times x [k] with correctly rounded sums (math.fsum)."""
+    return [math.fsum(W[i][j] * x[j] for j in range(len(x))) for i in range(len(W))]
 
 
 def matvec(W, x):
@@ -97,22 +128,28 @@ def expand_kv_rows(W, n_kv, head_dim, rep):
     return out
 
 
-def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v, interleave=False):
+def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v, interleave=False, rnd=None):
     """One decoder layer written as MHA over expanded K/V weights.
 
     xs: list of rows at positions pos0..; w: dict of nested lists with wk/wv
     already expanded to nq heads; cache_k/cache_v: lists (per position) of
     [nq][d] rows, extended in place. qk_norm: 0 none, 1 (or True) per-head
     RMSNorm before the rotation, 2 after it. interleave: rotate adjacent pairs.
+    rnd: None (plain float64), or f(vec, tag) -> vec, the storage rounding
+    applied at each point tagged "h" (normed row), "q", "k", "v" (after the
+    rotation), "o" (attention output), "h2" (post-attention normed row) and
+    "a" (SwiGLU product); projections then use correctly rounded sums.
     """
     rot = rope_complex_adjacent if interleave else rope_complex
+    mv = matvec if rnd is None else matvec_exact
+    r = (lambda vec, tag: vec) if rnd is None else rnd
     outs = []
     for s, x in enumerate(xs):
         pos = pos0 + s
-        h = rmsnorm(x, w["attn_norm"], eps)
-        q = matvec(w["wq"], h)
-        k = matvec(w["wk"], h)
-        v = matvec(w["wv"], h)
+        h = r(rmsnorm(x, w["attn_norm"], eps), "h")
+        q = mv(w["wq"], h)
+        k = mv(w["wk"], h)
+        v = mv(w["wv"], h)
         qh, kh, vh = [], [], []
         for hd in range(nq):
             qq = q[hd * d:(hd + 1) * d]
@@ -125,9 +162,9 @@ def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v,
             if int(qk_norm) == 2:
                 qq = rmsnorm(qq, w["q_norm"], eps)
                 kk = rmsnorm(kk, w["k_norm"], eps)
-            qh.append(qq)
-            kh.append(kk)
-            vh.append(v[hd * d:(hd + 1) * d])
+            qh.append(r(qq, "q"))
+            kh.append(r(kk, "k"))
+            vh.append(r(v[hd * d:(hd + 1) * d], "v"))
         cache_k.append(kh)
         cache_v.append(vh)
         o = []
@@ -135,47 +172,51 @@ def decoder_layer_mha(xs, w, nq, d, eps, theta, qk_norm, pos0, cache_k, cache_v,
             ks = [cache_k[j][hd] for j in range(pos + 1)]
             vs = [cache_v[j][hd] for j in range(pos + 1)]
             o.extend(attention_rows([qh[hd]], ks, vs, lambda i, j: True)[0])
-        att = matvec(w["wo"], o)
+        att = mv(w["wo"], r(o, "o"))
         x = [x[i] + att[i] for i in range(len(x))]
-        h2 = rmsnorm(x, w["mlp_norm"], eps)
-        g = matvec(w["wg"], h2)
-        u = matvec(w["wu"], h2)
-        a = [silu(g[i]) * u[i] for i in range(len(g))]
-        dn = matvec(w["wd"], a)
+        h2 = r(rmsnorm(x, w["mlp_norm"], eps), "h2")
+        g = mv(w["wg"], h2)
+        u = mv(w["wu"], h2)
+        a = r([silu(g[i]) * u[i] for i in range(len(g))], "a")
+        dn = mv(w["wd"], a)
         outs.append([x[i] + dn[i] for i in range(len(x))])
     return outs
 
 
-def vit_layer(xs, w, nh, d, eps, pos_hw, theta, visible):
-    """Pre-LN ViT block; 2D RoPE: first half of each head by h, second by w."""
+def vit_layer(xs, w, nh, d, eps, pos_hw, theta, visible, rnd=None):
+    """Pre-LN ViT block; 2D RoPE: first half of each head by h, second by w.
+    rnd: as in decoder_layer_mha, with tags "h", "q", "k", "v", "o", "h2" and
+    "f" (GELU output); correctly rounded projection sums."""
+    mv = matvec if rnd is None else matvec_exact
+    r = (lambda vec, tag: vec) if rnd is None else rnd
     S = len(xs)
     q_all, k_all, v_all = [], [], []
     for s in range(S):
-        h = layernorm(xs[s], w["attn_norm"], w["attn_norm_b"], eps)
-        q = [a + b for a, b in zip(matvec(w["wq"], h), w["bq"])]
-        k = [a + b for a, b in zip(matvec(w["wk"], h), w["bk"])]
-        v = [a + b for a, b in zip(matvec(w["wv"], h), w["bv"])]
+        h = r(layernorm(xs[s], w["attn_norm"], w["attn_norm_b"], eps), "h")
+        q = [a + b for a, b in zip(mv(w["wq"], h), w["bq"])]
+        k = [a + b for a, b in zip(mv(w["wk"], h), w["bk"])]
+        v = [a + b for a, b in zip(mv(w["wv"], h), w["bv"])]
         qr, kr = [], []
         for hd in range(nh):
             qq, kk = q[hd * d:(hd + 1) * d], k[hd * d:(hd + 1) * d]
             half = d // 2
             ah = text_angles(pos_hw[0][s], half, theta)
             aw = text_angles(pos_hw[1][s], half, theta)
-            qr.append(rope_complex(qq[:half], ah) + rope_complex(qq[half:], aw))
-            kr.append(rope_complex(kk[:half], ah) + rope_complex(kk[half:], aw))
+            qr.append(r(rope_complex(qq[:half], ah) + rope_complex(qq[half:], aw), "q"))
+            kr.append(r(rope_complex(kk[:half], ah) + rope_complex(kk[half:], aw), "k"))
         q_all.append(qr)
         k_all.append(kr)
-        v_all.append([v[hd * d:(hd + 1) * d] for hd in range(nh)])
+        v_all.append([r(v[hd * d:(hd + 1) * d], "v") for hd in range(nh)])
     outs = []
     for s in range(S):
         o = []
         for hd in range(nh):
             o.extend(attention_rows([q_all[s][hd]], [k_all[j][hd] for j in range(S)],
                                     [v_all[j][hd] for j in range(S)], lambda i, j: visible(s, j))[0])
-        att = [a + b for a, b in zip(matvec(w["wo"], o), w["bo"])]
+        att = [a + b for a, b in zip(mv(w["wo"], r(o, "o")), w["bo"])]
         x = [xs[s][i] + att[i] for i in range(len(att))]
-        h2 = layernorm(x, w["mlp_norm"], w["mlp_norm_b"], eps)
-        f = [gelu_tanh(a + b) for a, b in zip(matvec(w["w1"], h2), w["b1"])]
-        dn = [a + b for a, b in zip(matvec(w["w2"], f), w["b2"])]
+        h2 = r(layernorm(x, w["mlp_norm"], w["mlp_norm_b"], eps), "h2")
+        f = r([gelu_tanh(a + b) for a, b in zip(mv(w["w1"], h2), w["b1"])], "f")
+        dn = [a + b for a, b in zip(mv(w["w2"], f), w["b2"])]
         outs.append([x[i] + dn[i] for i in range(len(x))])
     return outs

@@ -538,8 +538,122 @@ def test_bf16_mode_stays_close_to_f64():
     assert 1e-5 < err < 2e-2
 
 
+def _sharpened(w):
+    """bf16 layer weights with every matrix scaled by 16 (still bf16 values): at
+    the workloads' 0.02 scale a tiny layer's attention is nearly uniform, so a
+    rounding of q can vanish under the later rounding of the attention output;
+    larger weights make each rounding point visible."""
+    return {k: v.astype(np.float64) * (16.0 if v.ndim == 2 else 1.0) for k, v in w.items()}
+
+
+def _bf16_rounder(skip=None):
+    """Storage rounding for the brute-force layers, optionally left out at one point."""
+    return lambda vec, tag: list(vec) if tag == skip else [bf.bf16(t) for t in vec]
+
+
+def test_bf16_round_agrees_with_bit_level_rounding():
+    """Two independent roundings to bfloat16 (the oracle's frexp form and the
+    brute-force bit-level form) agree on random values, exact ties and carries."""
+    rng = np.random.default_rng(31)
+    vals = np.r_[rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 6, 4000),
+                 1.0 + (2 * np.arange(64) + 1) * 2.0 ** -9, 1.9999999, -3.99609375, 255.5]
+    ref = od.bf16_round(vals)
+    assert all(bf.bf16(float(v)) == float(r) for v, r in zip(vals, ref))
+
+
+BF16_TAGS = ("h", "q", "k", "v", "o", "h2", "a")
+
+
+@pytest.mark.parametrize("qk_norm", [1, 0])
+def test_bf16_decoder_layer_rounding_points_match_brute_force(qk_norm):
+    """Reading of the bf16 policy: the operands of every projection (normed
+    rows, attention output, SwiGLU product), q and the cached k/v are stored
+    as bf16; products are exact and summed exactly. The oracle's bf16 layer
+    equals a pure-Python layer that rounds at exactly those points (fsum
+    sums); leaving any one of the seven rounding points out of the brute
+    force breaks the agreement of the layer output or of the cached K/V, so
+    each point is pinned."""
+    cfg = vs.scaled(TINY, dtype="bf16", hidden=16, head_dim=8, ffn=24, qk_norm=qk_norm)
+    w = _sharpened(vs.decoder_layer_weights(cfg, 0))
+    x = np.random.default_rng(32).standard_normal((cfg.seq, cfg.hidden))
+    cos, sin = _text_tables(cfg.capacity, cfg.head_dim, cfg.theta)
+    kc = np.zeros((cfg.n_kv_heads, cfg.capacity, cfg.head_dim)); vc = np.zeros_like(kc)
+    got = od.decoder_layer(x, w, cfg, kc, vc, 0, cos, sin, od.BF16)
+    rep = cfg.n_q_heads // cfg.n_kv_heads
+    wl = {k: v.tolist() for k, v in w.items()}
+    wl["wk"] = bf.expand_kv_rows(wl["wk"], cfg.n_kv_heads, cfg.head_dim, rep)
+    wl["wv"] = bf.expand_kv_rows(wl["wv"], cfg.n_kv_heads, cfg.head_dim, rep)
+
+    def brute(skip):
+        ck, cv = [], []
+        out = bf.decoder_layer_mha(x.tolist(), wl, cfg.n_q_heads, cfg.head_dim, cfg.eps, cfg.theta, qk_norm, 0,
+                                   ck, cv, rnd=_bf16_rounder(skip))
+        return np.asarray(out), ck, cv
+    ref, ck, cv = brute(None)
+    delta = np.abs(got - x).max()          # what the layer adds to the residual rows
+    assert np.abs(got - ref).max() <= 1e-12 * delta
+    for s in range(cfg.seq):
+        for g in range(cfg.n_kv_heads):
+            assert np.array_equal(kc[g, s], ck[s][g * rep]) and np.array_equal(vc[g, s], cv[s][g * rep])
+    for tag in BF16_TAGS:   # observable in the layer output or in the cached K/V
+        other, ok_, ov_ = brute(tag)
+        moved = np.abs(other - got).max() > 1e-6 * delta
+        moved |= any(not np.array_equal(kc[g, s], ok_[s][g * rep]) or not np.array_equal(vc[g, s], ov_[s][g * rep])
+                     for s in range(cfg.seq) for g in range(cfg.n_kv_heads))
+        assert moved, tag
+
+
+def test_bf16_lm_head_rounds_the_final_row():
+    rng = np.random.default_rng(33)
+    E = np.asarray(vs.to_bf16_values(rng.standard_normal((9, 6)).astype(np.float32)), np.float64)
+    x, g = rng.standard_normal(6), np.asarray(vs.to_bf16_values(rng.standard_normal(6).astype(np.float32)), np.float64)
+    lg = od.lm_head_logits(x, g, E, 1e-6, od.BF16)
+    row = [bf.bf16(t) for t in bf.rmsnorm(list(x), list(g), 1e-6)]
+    assert np.allclose(lg, bf.matvec_exact(E.tolist(), row), rtol=1e-13, atol=1e-15)
+    assert not np.allclose(lg, bf.matvec(E.tolist(), bf.rmsnorm(list(x), list(g), 1e-6)), rtol=1e-6)
+
+
+def test_bf16_sum_modes_differ_only_by_summation_order():
+    """BF16_F32SUM (float32 BLAS sums, the noise-floor probe) moves a layer by
+    float32 rounding only; the exact mode equals the brute force above."""
+    cfg = vs.scaled(TINY, dtype="bf16", hidden=64, head_dim=16, ffn=96)
+    w = vs.decoder_layer_weights(cfg, 0)
+    x = np.random.default_rng(34).standard_normal((cfg.seq, cfg.hidden))
+    cos, sin = _text_tables(cfg.capacity, cfg.head_dim, cfg.theta)
+    outs = []
+    for prec in (od.BF16, od.BF16_F32SUM):
+        kc = np.zeros((2, cfg.capacity, 16)); vc = np.zeros_like(kc)
+        outs.append(od.decoder_layer(x, w, cfg, kc, vc, 0, cos, sin, prec))
+    err = np.abs(outs[0] - outs[1]).max() / np.abs(outs[0]).max()
+    assert err < 2e-2
+
+
+def test_bf16_vit_layer_rounding_points_match_brute_force():
+    """The bf16-storage vision layer (HunyuanOCR v1.5 port §3.7, Mixed policy)
+    rounds at the same kinds of points as the decoder (tags h, q, k, v, o, h2 and
+    the GELU output f); each point pinned as in the decoder test."""
+    cfg = vs.scaled_vit(TINY_VIT, dtype="bf16")
+    w = _sharpened(vs.vit_layer_weights(cfg, 0))
+    x = np.random.default_rng(35).standard_normal((cfg.n_patches, cfg.hidden))
+    pos = ov.vit_positions(cfg)
+    axes = np.r_[np.zeros(1, np.int64), np.ones(1, np.int64)]
+    cos, sin = od.rope_tables(pos, axes, 2, cfg.head_dim, cfg.theta)
+    seg = (pos[0] // 4) * 10 + pos[1] // 4
+    mask = np.where(seg[:, None] == seg[None, :], 0.0, od.MASK_NEG)
+    got = ov.vit_layer(x, w, mask, cos, sin, cfg, od.BF16)
+    wl = {k: v.tolist() for k, v in w.items()}
+
+    def brute(skip):
+        return np.asarray(bf.vit_layer(x.tolist(), wl, cfg.n_heads, cfg.head_dim, cfg.eps, pos.tolist(), cfg.theta,
+                                       lambda i, j: seg[i] == seg[j], rnd=_bf16_rounder(skip)))
+    delta = np.abs(got - x).max()
+    assert np.abs(got - brute(None)).max() <= 1e-12 * delta
+    for tag in ("h", "q", "k", "v", "o", "h2", "f"):
+        assert np.abs(brute(tag) - got).max() > 1e-6 * delta, tag
+
+
 def test_vit_bf16_mode_stays_close_to_f64():
-    """The vision tower's bf16-storage mode (HunyuanOCR v1.5 port §3.6 Mixed policy) moves the
+    """The vision tower's bf16-storage mode (HunyuanOCR v1.5 port §3.7 Mixed policy) moves the
     merged rows by bf16 rounding only: same bf16-valued weights, the two rounding modes differ by
     more than float noise and by less than the bf16 gate."""
     cfgb = vs.scaled_vit(vs.C5, n_layers=2, full_layers=(1,), grid_h=4, grid_w=8, window=2, dtype="bf16")
@@ -571,6 +685,32 @@ def test_prefill_equals_decode_replay():
     assert list(a["ids"]) == list(b["ids"])
     T = cfg.seq + cfg.decode_steps
     assert np.allclose(a["k_cache"][:, :, :T], b["k_cache"][:, :, :T], rtol=1e-11, atol=1e-13)
+
+
+def test_block_logits_equal_decode_steps():
+    """The verify head's definition (one causal forward over prompt + block, a head on every
+    block row) gives the logits of one-token decode steps fed the same tokens (the pages'
+    prefill = decode replay, HunyuanOCR v1.5 port §3.8 for the verify use)."""
+    cfg = vs.scaled(vs.C1, seq=12, n_img=4, img_start=3, decode_steps=5, capacity=20, n_layers=2)
+    a, glob, layers = _tiny_run(cfg, keep_logits=True)
+    block = [int(i) for i in a["ids"][:5]]
+    got = od.block_logits(cfg, glob, layers, block)
+    want = np.stack(a["step_logits"])
+    assert np.allclose(got, want, rtol=1e-11, atol=1e-12)
+    assert [int(np.argmax(r)) for r in got] == [int(i) for i in a["ids"][1:6]]
+
+
+def test_hidden_state_decode_equals_longer_prefill():
+    """A stack without vocabulary decodes given rows: the hidden output of decode step i equals
+    the prefill output of the same row appended to the prompt (prefill = decode replay)."""
+    cfg = vs.scaled(vs.C2_F32, hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, ffn=64, seq=6, decode_steps=3,
+                    capacity=12)
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    a = od.run_decoder(cfg, glob, layers)
+    cfg9 = vs.scaled(cfg, seq=9, decode_steps=0)
+    b = od.run_decoder(cfg9, dict(glob, x=np.concatenate([glob["x"], glob["decode_x"]])), layers)
+    assert np.allclose(a["decode_x"], b["prefill_x"][6:], rtol=1e-11, atol=1e-12)
 
 
 def test_cache_after_short_prefill_is_prefix_of_long_prefill():
