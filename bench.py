@@ -379,6 +379,7 @@ def main():
 
     import vlm_synth as vs
     from decoder_prefill_decode_amd.pipeline import DecoderRun
+    from decoder_prefill_decode_amd.runtime import causal_mask as pipeline_causal
 
     cfg = vs.ALL_CONFIGS[args.config]
     if isinstance(cfg, vs.VitConfig):
@@ -395,10 +396,16 @@ def main():
           flush=True)
 
     if args.kernel_only:
-        if args.kernel_only == "attn":   # a filled cache for the attention kernel to read (eager steps:
-            run.prefill()                 # counter collection does not handle graph launches)
-            run.first_token()
-            run.decode(cfg.decode_steps, loop=False)
+        if args.kernel_only == "attn":
+            # A cache filled to the mid-run length for the attention kernel to read: the prompt's prefill,
+            # then one chunked prefill of the next decode_steps/2 rows (copies of prompt rows). Two prefills
+            # are a few hundred dispatches; filling it with eager decode steps instead issued ~55k
+            # dispatches before the measured launches, and a counter-collection run over that many
+            # dispatches ended in a host-side fault inside the profiled launch path.
+            run.prefill()
+            extra = cfg.decode_steps // 2
+            xr = run.x[:extra].clone()
+            run.model.prefill(xr, cfg.seq, run.cos, run.sin, pipeline_causal(), run.kv, run.ws)
         t = time_kernel(run, args.kernel_only, args.launches)
         # the counters' reference: a plain row copy (the library's gather kernel with the identity
         # index) reading and writing exactly copy_mib MiB
@@ -419,7 +426,7 @@ def main():
         for _ in range(args.prefill_only):
             run.reset()
             run.prefill()
-            run.first_token()
+            run.first_token(check=False)
         torch.cuda.synchronize()
         print(f"# {args.prefill_only} prefills of {cfg.seq} rows done", file=sys.stderr)
         return
@@ -432,7 +439,7 @@ def main():
         if e:
             e[0].record()
         run.prefill()
-        run.first_token()
+        run.first_token(check=False)
         if e:
             e[1].record()
         run.model.decode_loop(run.kv, run.cos, run.sin, run.ws, run.tok, N, hist=run.hist)

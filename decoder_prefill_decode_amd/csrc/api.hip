@@ -42,8 +42,9 @@ vlm_status ok() {
         if (e_ != hipSuccess) return fail(VLM_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
 
-// KV buffer header (int32 words): [0] length; the rest is zeroed at bind time
-// and reserved.
+// KV buffer header (int32 words): [0] length; [1] set when a decode step's
+// argmax saw a non-finite logit, [2] that step's position; the rest is zeroed
+// at bind time and reserved.
 constexpr size_t kHeader = 256;
 constexpr int kHdrWords = 64;
 
@@ -293,6 +294,30 @@ vlm_status vlm_kv_truncate(vlm_kv* kv, int32_t new_len, hipStream_t stream) {
         return fail(VLM_ERR_CAPACITY, "new length %d outside [0, %d]", new_len, kv->len);
     HIP_TRY(launch_set_len(kv->dlen(), new_len, stream));
     kv->len = new_len;
+    return ok();
+}
+
+vlm_status vlm_kv_status(vlm_kv* kv, hipStream_t stream, int32_t* h_pos) {
+    if (!kv) return fail(VLM_ERR_ARG, "kv is NULL");
+    int32_t hdr[3] = {0, 0, 0};
+    HIP_TRY(hipStreamSynchronize(stream));
+    HIP_TRY(hipMemcpy(hdr, kv->buf, sizeof(hdr), hipMemcpyDeviceToHost));
+    if (h_pos) *h_pos = hdr[1] ? hdr[2] : -1;
+    if (!hdr[1]) return ok();
+    kv->len = hdr[0];  // the failed steps did not advance the device length
+    HIP_TRY(launch_zero_i32((int32_t*)kv->buf + 1, 2, stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+    return fail(VLM_ERR_NONFINITE, "non-finite logits at decode position %d; the cache length stays %d", hdr[2],
+                hdr[0]);
+}
+
+vlm_status vlm_token_status(const int32_t* d_token, hipStream_t stream, int32_t* h_token) {
+    if (!d_token) return fail(VLM_ERR_ARG, "d_token is NULL");
+    int32_t tok = 0;
+    HIP_TRY(hipStreamSynchronize(stream));
+    HIP_TRY(hipMemcpy(&tok, d_token, sizeof(tok), hipMemcpyDeviceToHost));
+    if (h_token) *h_token = tok;
+    if (tok == -1) return fail(VLM_ERR_NONFINITE, "the token was taken over non-finite logits");
     return ok();
 }
 
@@ -554,6 +579,56 @@ vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_nor
     auto* part = (unsigned long long*)P(d_ws, w.lm);
     HIP_TRY(launch_lmhead_argmax(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab,
                                  desc->hidden, part, d_logits, d_token_out, nullptr, nullptr, stream));
+    return ok();
+}
+
+vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
+                                  const float* d_x, int32_t S, int32_t* d_tokens_out, float* d_logits, void* d_ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->vocab < 1) return fail(VLM_ERR_SHAPE, "model has no lm_head table (vocab 0)");
+    if (S < 0) return fail(VLM_ERR_SHAPE, "S %d < 0", S);
+    if (!d_final_norm || !d_table || !aligned16(d_table) || !d_x || !aligned16(d_x) || !d_tokens_out)
+        return fail(VLM_ERR_ARG, "NULL or misaligned pointer");
+    Ws w;
+    if ((s = check_ws(desc, S, d_ws, ws_bytes, &w))) return s;
+    float* logits = d_logits;
+    if (!logits) {
+        if ((size_t)S * desc->vocab > w.gpart_floats)
+            return fail(VLM_ERR_WORKSPACE, "%d rows x vocab %d logits exceed the workspace scratch; pass d_logits",
+                        S, desc->vocab);
+        logits = (float*)P(d_ws, w.gpart);
+    }
+    if (S == 0) return ok();
+    const int dt = desc->dtype, H = desc->hidden;
+    void* hbuf = P(d_ws, w.h);
+    HIP_TRY(launch_norm_rows(dt, false, d_x, S, H, d_final_norm, nullptr, desc->norm_eps, hbuf, stream));
+    GemmArgs g{};
+    g.A = hbuf; g.B = d_table; g.out = logits; g.M = S; g.N = desc->vocab; g.K = H; g.ldo = desc->vocab;
+    HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
+    HIP_TRY(launch_argmax_rows(logits, S, desc->vocab, desc->vocab, d_tokens_out, stream));
+    return ok();
+}
+
+vlm_status vlm_verify_commit(vlm_kv* kv, int32_t pos0, const int32_t* h_draft, int32_t k, const int32_t* d_pred,
+                             hipStream_t stream, int32_t* h_n_accept, int32_t* h_next) {
+    if (!kv || !h_draft || !d_pred || !h_n_accept || !h_next) return fail(VLM_ERR_ARG, "NULL argument");
+    if (k < 1 || k > 4096) return fail(VLM_ERR_SHAPE, "block length %d not in [1, 4096]", k);
+    if (pos0 < 0 || (long)pos0 + k != kv->len)
+        return fail(VLM_ERR_CAPACITY, "the verified block [%d, %d) must end at the cache length %d", pos0, pos0 + k,
+                    kv->len);
+    std::vector<int32_t> pred(k);
+    HIP_TRY(hipStreamSynchronize(stream));
+    HIP_TRY(hipMemcpy(pred.data(), d_pred, k * sizeof(int32_t), hipMemcpyDeviceToHost));
+    for (int i = 0; i < k; i++)
+        if (pred[i] < 0) return fail(VLM_ERR_NONFINITE, "non-finite logits at verified row %d", i);
+    int a = 0;
+    while (a + 1 < k && h_draft[a + 1] == pred[a]) a++;
+    HIP_TRY(launch_set_len(kv->dlen(), pos0 + a + 1, stream));
+    kv->len = pos0 + a + 1;
+    *h_n_accept = a;
+    *h_next = pred[a];
     return ok();
 }
 

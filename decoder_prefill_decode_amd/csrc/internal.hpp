@@ -62,9 +62,13 @@ hipError_t launch_gemv(int dtype, Pro pro, Epi epi, const GemvArgs& a, hipStream
 int lmhead_blocks(int V);
 hipError_t launch_lmhead(int dtype, const void* table, const float* x, const void* gain, float eps, int V, int K,
                          unsigned long long* partials, float* logits, hipStream_t st);
-// token_out[0] = argmax (or -1); when kv_len != null: hist[len+1] = token (if hist), *kv_len += 1.
+// token_out[0] = argmax (or -1); when kv_len != null (the cache header): hist[len+1] = token (if hist),
+// *kv_len += 1; for -1 instead the length stays and header words 1, 2 record the first such position.
 hipError_t launch_argmax_final(const unsigned long long* partials, int nblocks, int32_t* token_out, int32_t* hist,
                                int32_t* kv_len, hipStream_t st);
+
+// out[r] = argmax of logits row r (r < S, row stride ld; lowest index on ties, -1 for a non-finite row).
+hipError_t launch_argmax_rows(const float* logits, int S, int V, int ld, int32_t* out, hipStream_t st);
 
 // Row norms producing the GEMM operand (model type): RMSNorm (shift == null, layer == false)
 // or LayerNorm (layer == true, shift may be null).
@@ -163,7 +167,8 @@ hipError_t launch_sample_logits(const float* logits, int V, const SampleParams& 
 // Final RMSNorm + lm_head GEMV + argmax. Writes per-block argmax keys to
 // `partials` (lmhead_partials_max(V) entries) and the logits when non-null.
 // token_out == null: partials only; otherwise a second kernel reduces the
-// token, then hist[len+1] = token (if hist) and *kv_len += 1 (if kv_len).
+// token, then hist[len+1] = token (if hist) and *kv_len += 1 (if kv_len; a non-finite step is not
+// committed: the length stays and header words 1, 2 flag it, see launch_argmax_final).
 int lmhead_partials_max(int V);
 hipError_t launch_lmhead_argmax(int dtype, const void* table, const float* x, const void* gain, float eps, int V,
                                 int K, unsigned long long* partials, float* logits, int32_t* token_out, int32_t* hist,

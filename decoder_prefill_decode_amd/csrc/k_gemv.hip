@@ -559,12 +559,51 @@ __global__ __launch_bounds__(1024) void argmax_final_kernel(const unsigned long 
         const unsigned long long best = sm[0];
         const int32_t tok = best == ~0ull ? -1 : (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
         token_out[0] = tok;
-        if (kv_len) {
+        if (kv_len) {  // kv_len: the cache header (word 0 length, 1 non-finite flag, 2 its first position)
             const int t = kv_len[0];
-            if (hist) hist[t + 1] = tok;
-            kv_len[0] = t + 1;
+            if (tok >= 0) {
+                if (hist) hist[t + 1] = tok;
+                kv_len[0] = t + 1;
+            } else if (kv_len[1] == 0) {  // not committed: the length stays at t
+                kv_len[1] = 1;
+                kv_len[2] = t;
+            }
         }
     }
+}
+
+// Row-wise argmax of a logits matrix (the multi-token verify head): block r
+// scans row r with the same u64 keys (largest logit, lowest index; -1 when the
+// row holds a non-finite value).
+__global__ __launch_bounds__(1024) void argmax_rows_kernel(const float* __restrict__ logits, int V, int ld,
+                                                           int32_t* __restrict__ out) {
+    __shared__ unsigned long long sm[1024 / kWave];
+    const float* row = logits + (size_t)blockIdx.x * ld;
+    unsigned long long best = 0ull;
+    for (int n = threadIdx.x; n < V; n += 1024) {
+        const float v = row[n];
+        const unsigned long long key = isfinite(v)
+            ? (((unsigned long long)ordered_key(v)) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n)
+            : ~0ull;
+        best = key > best ? key : best;
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off);
+        best = o > best ? o : best;
+    }
+    if (threadIdx.x % kWave == 0) sm[threadIdx.x / kWave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long b = sm[0];
+        for (int i = 1; i < 1024 / kWave; i++) b = sm[i] > b ? sm[i] : b;
+        out[blockIdx.x] = b == ~0ull ? -1 : (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+    }
+}
+
+hipError_t launch_argmax_rows(const float* logits, int S, int V, int ld, int32_t* out, hipStream_t st) {
+    if (S <= 0) return hipSuccess;
+    argmax_rows_kernel<<<S, 1024, 0, st>>>(logits, V, ld, out);
+    return hipGetLastError();
 }
 
 int lmhead_blocks(int V) { return (V + 4 * kLmRows - 1) / (4 * kLmRows); }

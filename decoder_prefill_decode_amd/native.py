@@ -66,6 +66,8 @@ _SIG = {
     "vlm_kv_free": (_I, [_P]),
     "vlm_kv_len": (_I, [_P, C.POINTER(_I)]),
     "vlm_kv_truncate": (_I, [_P, _I, _P]),
+    "vlm_kv_status": (_I, [_P, _P, C.POINTER(_I)]),
+    "vlm_token_status": (_I, [_P, _P, C.POINTER(_I)]),
     "vlm_workspace_bytes": (_I, [C.POINTER(ModelDesc), _I, C.POINTER(C.c_size_t)]),
     "vlm_pack_qkv": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "vlm_pack_gate_up": (_I, [_P, _P, _I, _I, _I, _P, _P]),
@@ -77,6 +79,8 @@ _SIG = {
     "vlm_prefill": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _I, _I, _P, _P, _I, C.POINTER(Mask), _I, _P,
                          _P, C.c_size_t, _P]),
     "vlm_lmhead_argmax": (_I, [C.POINTER(ModelDesc), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "vlm_lmhead_argmax_rows": (_I, [C.POINTER(ModelDesc), _P, _P, _P, _I, _P, _P, _P, C.c_size_t, _P]),
+    "vlm_verify_commit": (_I, [_P, _I, C.POINTER(_I), _I, _P, _P, C.POINTER(_I), C.POINTER(_I)]),
     "vlm_decode_step": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                              _P, C.c_size_t, _P]),
     "vlm_decode_loop": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P,

@@ -9,7 +9,8 @@ import numpy as np
 import torch
 
 from . import native as N
-from .runtime import KVCache, Model, causal_mask, rope_table, segment_mask, none_mask, ptr, stream, text_rope, to_device
+from .runtime import (KVCache, Model, causal_mask, none_mask, ptr, rope_table, segment_mask, stream, text_rope,
+                      to_device, token_status)
 
 
 class DecoderRun:
@@ -71,9 +72,12 @@ class DecoderRun:
         self.model.prefill(x, pos0, self.cos, self.sin, mask or causal_mask(), self.kv, self.ws)
         return x
 
-    def first_token(self, logits=None):
-        """lm_head + argmax of the last prompt row (writes self.tok)."""
+    def first_token(self, logits=None, check=True):
+        """lm_head + argmax of the last prompt row (writes self.tok). check: synchronize and raise
+        VlmError (VLM_ERR_NONFINITE) on a non-finite row; check=False keeps the call asynchronous."""
         self.model.lmhead_argmax(self.x[self.cfg.seq - 1], self.tok, self.ws, logits)
+        if check:
+            token_status(self.tok)
         return self.tok
 
     def decode(self, n, loop=True):
@@ -87,7 +91,7 @@ class DecoderRun:
             for _ in range(n):
                 self.model.decode_step(self.kv, self.cos, self.sin, self.ws, token_in=self.tok, token_out=self.tok,
                                        hist=self.hist)
-        torch.cuda.current_stream().synchronize()
+        self.kv.status()   # synchronizes; raises on a non-finite step
         return self.hist[t0 + 1:t0 + 1 + n].cpu().numpy().astype(np.int64)
 
     def generate_sampled(self, n, temperature, top_k, top_p, penalty, u):
@@ -124,8 +128,24 @@ class DecoderRun:
         for i in range(n):
             self.model.decode_step(self.kv, self.cos, self.sin, self.ws, token_in=fin[i:i + 1],
                                    token_out=out[i:i + 1])
-        torch.cuda.current_stream().synchronize()
+        self.kv.status()
         return out.cpu().numpy().astype(np.int64)
+
+    def verify_block(self, draft, logits=None):
+        """Multi-token verify of a drafted block: draft[0] is the last committed token (not yet in the
+        cache), draft[1:] the drafted ones. Embeds the block, prefills it as a causal chunk at the cache
+        length, takes every row's argmax in one lm_head pass and commits the accepted prefix.
+        Returns (accepted drafted tokens + the correction, the next token to feed)."""
+        k = len(draft)
+        pos0 = self.kv.len()
+        ids = torch.from_numpy(np.ascontiguousarray(draft, np.int32)).to("cuda")
+        xb = torch.empty((k, self.cfg.hidden), dtype=torch.float32, device="cuda")
+        self.model.embed_ids(ids, xb)
+        self.model.prefill(xb, pos0, self.cos, self.sin, causal_mask(), self.kv, self.ws)
+        pred = torch.empty(k, dtype=torch.int32, device="cuda")
+        self.model.lmhead_argmax_rows(xb, pred, self.ws, logits)
+        a, nxt = self.kv.verify_commit(pos0, draft, pred)
+        return [int(t) for t in draft[1:a + 1]] + [nxt], nxt
 
     def decode_hidden(self, rows: torch.Tensor):
         """Hidden-state decode (no vocabulary): one step per input row; returns [n][H]."""

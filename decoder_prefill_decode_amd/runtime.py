@@ -134,6 +134,10 @@ class Model:
         N.call("vlm_lmhead_argmax", C.byref(self.desc), ptr(self.final_norm), ptr(self.embed), ptr(x_row),
                ptr(token_out), ptr(logits), ptr(ws), ws.numel(), stream())
 
+    def lmhead_argmax_rows(self, x_rows, tokens_out, ws, logits=None):
+        N.call("vlm_lmhead_argmax_rows", C.byref(self.desc), ptr(self.final_norm), ptr(self.embed), ptr(x_rows),
+               x_rows.shape[0], ptr(tokens_out), ptr(logits), ptr(ws), ws.numel(), stream())
+
     def decode_step(self, kv, cos, sin, ws, token_in=None, x_in=None, token_out=None, x_out=None, hist=None,
                     with_head=True):
         table = self.embed if (with_head and self.desc.vocab > 0) else None
@@ -177,6 +181,21 @@ class KVCache:
     def truncate(self, new_len: int):
         N.call("vlm_kv_truncate", self.handle, new_len, stream())
 
+    def verify_commit(self, pos0: int, draft, pred: torch.Tensor):
+        """vlm_verify_commit: (drafted tokens accepted, next token); the cache keeps the accepted rows."""
+        d = np.ascontiguousarray(draft, dtype=np.int32)
+        na, nx = C.c_int32(), C.c_int32()
+        N.call("vlm_verify_commit", self.handle, pos0, d.ctypes.data_as(C.POINTER(C.c_int32)), len(d), ptr(pred),
+               stream(), C.byref(na), C.byref(nx))
+        return na.value, nx.value
+
+    def status(self) -> int:
+        """vlm_kv_status: synchronizes the stream; raises VlmError (VLM_ERR_NONFINITE) when a decode
+        step's argmax saw a non-finite logit (the cache then stays at that step's position)."""
+        pos = C.c_int32()
+        N.call("vlm_kv_status", self.handle, stream(), C.byref(pos))
+        return pos.value
+
     def device_len(self) -> torch.Tensor:
         return self.buf[:4].view(torch.int32)
 
@@ -190,6 +209,14 @@ class KVCache:
         k = self.buf[off:off + pk * e].view(self.model.tdtype).view(d.n_kv_heads, self.capacity, d.head_dim)
         v = self.buf[off + pk * e:off + (pk + pv) * e].view(self.model.tdtype).view(d.n_kv_heads, self.capacity, dv)
         return k, v
+
+
+def token_status(token: torch.Tensor) -> int:
+    """vlm_token_status: synchronizes the stream and returns the device token; raises VlmError
+    (VLM_ERR_NONFINITE) when it is -1 (the argmax or sampler saw a non-finite logit)."""
+    tok = C.c_int32()
+    N.call("vlm_token_status", ptr(token), stream(), C.byref(tok))
+    return tok.value
 
 
 def rope_table(positions: np.ndarray, axis_of_pair, segments: int, head_dim: int, theta: float):

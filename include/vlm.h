@@ -49,7 +49,7 @@ typedef enum {
     VLM_ERR_CAPACITY = -3,       /* sequence would exceed the KV window or the RoPE table */
     VLM_ERR_COUNT_MISMATCH = -4, /* placeholder count != image rows */
     VLM_ERR_DTYPE = -5,          /* dtype not valid for this call */
-    VLM_ERR_NONFINITE = -6,      /* reserved for host wrappers: argmax over non-finite logits */
+    VLM_ERR_NONFINITE = -6,      /* an argmax saw a non-finite logit (vlm_kv_status, vlm_token_status) */
     VLM_ERR_HIP = -7,            /* a HIP runtime call failed */
     VLM_ERR_UNSUPPORTED = -8,    /* valid request that this build has no kernel for */
     VLM_ERR_WORKSPACE = -9       /* workspace too small */
@@ -186,6 +186,23 @@ vlm_status vlm_kv_len(const vlm_kv* kv, int32_t* len);
  * multi-token verify ([HyOCR15] §3.8). */
 vlm_status vlm_kv_truncate(vlm_kv* kv, int32_t new_len, hipStream_t stream);
 
+/* Non-finite results ([Penguin] §4.1: a mismatch that silently produced token 0
+ * is the failure to avoid; an explicit error instead). A decode step whose
+ * argmax sees a NaN or infinite logit writes -1 as its token, does not advance
+ * the device length (the step is not committed: slots 0..t-1 and the length
+ * stay as they were) and sets a flag in the cache header with its position t;
+ * later steps of a loop then read token -1, whose embedding row is NaN, and
+ * fail the same way, so the cache stays at t.
+ * vlm_kv_status synchronizes `stream`, reads the header and returns
+ * VLM_ERR_NONFINITE with *h_pos = t (the first failed position) when the flag
+ * is set; it then sets the host length mirror to the device length and clears
+ * the flag. Otherwise VLM_OK and *h_pos = -1 (h_pos may be NULL).
+ * vlm_token_status synchronizes `stream` and reads d_token[0] (the output of
+ * vlm_lmhead_argmax or vlm_sample_logits): VLM_ERR_NONFINITE when it is -1,
+ * else VLM_OK; *h_token receives the value (h_token may be NULL). */
+vlm_status vlm_kv_status(vlm_kv* kv, hipStream_t stream, int32_t* h_pos);
+vlm_status vlm_token_status(const int32_t* d_token, hipStream_t stream, int32_t* h_token);
+
 /* Bytes of scratch needed by vlm_prefill (S <= max_rows), vlm_decode_step,
  * vlm_decode_loop and vlm_lmhead_argmax for this model. */
 vlm_status vlm_workspace_bytes(const vlm_model_desc* desc, int32_t max_rows, size_t* bytes);
@@ -259,11 +276,40 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
 /* Final RMSNorm + lm_head + greedy argmax of one row ([Youtu] 实现流程 §6 and
  * 解码与采样说明; [HyOCR15] §3.4: a single [V][H] table, one weight copy).
  * d_token_out[0] = index of the largest logit (lowest index on ties); -1 if any
- * logit is NaN or infinite. d_logits ([V] fp32) receives the logits when
+ * logit is NaN or infinite (vlm_token_status reports it). d_logits ([V] fp32) receives the logits when
  * non-NULL. The table may alias the embedding (tied weights). */
 vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
                              const float* d_x_row, int32_t* d_token_out, float* d_logits, void* d_ws,
                              size_t ws_bytes, hipStream_t stream);
+
+/* Multi-token verify head ([HyOCR15] §3.8: the target model checks a drafted
+ * block in one causal forward). Rows d_x [S][H] fp32 (hidden rows after the
+ * last layer, e.g. of a vlm_prefill over the block at pos0 = cache length):
+ * final RMSNorm of each row, logits against the [V][H] table in one pass over
+ * the table (an MFMA GEMM), then d_tokens_out[r] = argmax of row r (lowest
+ * index on ties; -1 for a non-finite row). d_logits [S][V] fp32 receives the
+ * logits when non-NULL; with NULL they live in the workspace, which must then
+ * hold S * V floats of split scratch (else VLM_ERR_WORKSPACE; the workspace of
+ * vlm_workspace_bytes(desc, max_rows >= S) is also required for the rows). */
+vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
+                                  const float* d_x, int32_t S, int32_t* d_tokens_out, float* d_logits, void* d_ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/* Accept and commit a verified block ([HyOCR15] §3.8: keep the longest prefix
+ * of drafted tokens the target agrees with, plus the target's first
+ * correction, then trim the cache). The block h_draft[0..k) (host; h_draft[0]
+ * is the last committed token, h_draft[1..k) the drafted ones) occupies cache
+ * slots [pos0, pos0 + k), which must end at the current length, and d_pred
+ * [k] holds the verify head's picks (d_pred[i] = the target's token after
+ * h_draft[0..i]). Synchronizes `stream`, finds the largest a < k with
+ * h_draft[i + 1] == d_pred[i] for all i < a, sets the cache length to
+ * pos0 + a + 1 (slots of the accepted rows stay, the rest are dropped) and
+ * returns *h_n_accept = a (drafted tokens accepted) and *h_next = d_pred[a]
+ * (the correction, or the next token when every draft matched): the a + 1
+ * tokens h_draft[1..a], *h_next are what greedy one-token decoding gives.
+ * VLM_ERR_NONFINITE (nothing changed) if a verified row was non-finite. */
+vlm_status vlm_verify_commit(vlm_kv* kv, int32_t pos0, const int32_t* h_draft, int32_t k, const int32_t* d_pred,
+                             hipStream_t stream, int32_t* h_n_accept, int32_t* h_next);
 
 /* One-token decode step ([Youtu] 实现流程 §8; [HyOCR10] 四.4: q/k/v of the new
  * token, K/V written into slot t, attention over the window with slots > t

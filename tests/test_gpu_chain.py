@@ -7,7 +7,8 @@ The GPU runs the ViT, keeps its output on the device and hands it to the
 decoder's injection; the oracle runs oracle/vit.py and feeds its output to
 oracle/decoder.py. Gates: the merged rows within 1e-4 (fp32 tower) or 2e-2 (bf16 tower), decoder
 prefill rows and first-token logits within the bf16 gate 2e-2, greedy ids
-free-running and teacher-forced with near-tie attribution (check_ids).
+free-running and teacher-forced, exempt only below the oracle's own noise
+floor (tests/_parity.py).
 Stacks are cut to 2 layers each (decoder vocabulary 8192) so the oracle
 finishes in seconds; the shapes at the seam are the full ones.
 """
@@ -18,7 +19,7 @@ import torch
 import vlm_synth as vs
 from oracle import decoder as od
 from oracle import vit as ov
-from tests.test_gpu_decoder import check_ids
+from tests._parity import check_ids, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,7 @@ def test_vit_output_feeds_decoder(vit_dtype):
     assert vref.shape == (dcfg.n_img, dcfg.hidden)
     oglob = dict(dglob)
     oglob["img"] = vref
-    ref = od.run_decoder(dcfg, oglob, dlayers)
+    ref = oracle_run(dcfg, oglob, dlayers)
 
     vrun = pipeline.VitRun(vcfg, lambda l: vlayers[l], vglob)
     img = vrun.run()  # device fp32 [322, 2560], raster order
@@ -59,7 +60,6 @@ def test_vit_output_feeds_decoder(vit_dtype):
     free = [tok0] + list(drun.decode(dcfg.decode_steps))
     drun.kv.truncate(dcfg.seq)
     forced = [tok0] + list(drun.decode_forced(ref["ids"][:-1]))
-    eps = 8 * float(np.abs(lg - ref["logits0"]).max())
-    flips, div = check_ids(free, forced, ref["ids"], ref["margins"], eps)
-    print(f"chain ({vit_dtype} tower): vit err {rel(img.cpu().numpy(), vref):.2e}, logit err {eps / 8:.2e}, "
-          f"first divergence {div}, tie flips {flips}")
+    print(f"chain ({vit_dtype} tower): vit err {rel(img.cpu().numpy(), vref):.2e}, "
+          f"first-token logit err {np.abs(lg - ref['logits0']).max():.2e}")
+    check_ids(f"chain ({vit_dtype} tower)", free, forced, ref["ids"], ref["margins"], ref["floor"])

@@ -2,7 +2,8 @@
 
 Tolerances: max relative error = max|gpu - oracle| / max|oracle| per tensor,
 <= 1e-4 for fp32 workloads and <= 2e-2 for bf16 ones; token ids and
-embedding/injection rows bit-exact.
+embedding/injection rows bit-exact (bf16 ids: exact except at steps below the
+oracle's own noise floor, tests/_parity.py).
 """
 import numpy as np
 import pytest
@@ -11,6 +12,7 @@ import torch
 import oracle
 from oracle import decoder as od
 import vlm_synth as vs
+from tests._parity import check_ids, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -33,23 +35,6 @@ def make(cfg):
     glob = vs.decoder_globals(cfg)
     layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
     return glob, layers
-
-
-def check_ids(free, forced, ref_ids, margins, eps):
-    """Greedy-id parity with near-ties attributed.
-
-    free: GPU free-running ids; forced: GPU picks when fed the oracle's ids
-    (forced[0] is the prefill's pick). A step whose oracle top-2 margin is
-    below eps (the measured logit noise) is tie-ambiguous: a flip there is
-    counted and reported, anywhere else it fails. Returns the tie-ambiguous
-    steps where the GPU differs."""
-    ref_ids = list(ref_ids)
-    ties = [i for i, m in enumerate(margins) if m < eps]
-    bad = [i for i in range(len(ref_ids)) if forced[i] != ref_ids[i] and i not in ties]
-    assert not bad, f"teacher-forced mismatch at decisive steps {bad} (margins {[margins[i] for i in bad]})"
-    div = next((i for i in range(len(ref_ids)) if free[i] != ref_ids[i]), None)
-    assert div is None or div in ties, f"free-running divergence at step {div}, margin {margins[div]} >= {eps}"
-    return [i for i in ties if forced[i] != ref_ids[i]], div
 
 
 def gpu_run(pipeline, cfg, glob, layers):
@@ -139,6 +124,41 @@ def test_c2_layer_prefill_and_decode(rt, cfg):
     assert rel(v[:, :T], ref["v_cache"][0][:, :T]) <= tol
 
 
+# ------------------------------------------------------------------ fp32, ids that vary
+# The 4B-class layer shape (hidden 2560, 32/8 heads of 80, FFN 9728) in fp32, 2 layers, vocab 8192,
+# seeds of the 36-layer stack: its greedy sequence changes token at almost every step (the tiny
+# stack's tied table repeats its first token), so exact id equality checks a real sequence.
+C4_F32_2L = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=80, n_img=30, img_start=16, decode_steps=40,
+                      capacity=128, dtype="f32", name="c4_2layer_f32")
+
+
+def test_fp32_stack_varied_ids_exact(rt):
+    """fp32 gates: ids identical to the oracle at every one of 41 steps (graph loop and eager
+    steps), prefill rows, first-token logits and every valid KV slot within 1e-4."""
+    pipeline, _ = rt
+    cfg = C4_F32_2L
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    ids_ref = [int(i) for i in ref["ids"]]
+    assert len(set(ids_ref)) >= 8 and len(ids_ref) >= 33, ids_ref
+    T = cfg.seq + cfg.decode_steps
+    for loop in (True, False):
+        run = gpu_run(pipeline, cfg, glob, layers)
+        x = run.prefill()
+        logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+        tok0 = int(run.first_token(logits)[0])
+        assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["f32"]
+        assert rel(logits.cpu().numpy(), ref["logits0"]) <= TOL["f32"]
+        ids = [tok0] + [int(i) for i in run.decode(cfg.decode_steps, loop=loop)]
+        assert ids == ids_ref, f"loop={loop}: {ids} != {ids_ref}"
+        for l in range(cfg.n_layers):
+            k, v = kv_host(run, l)
+            assert rel(k[:, :T], ref["k_cache"][l][:, :T]) <= TOL["f32"]
+            assert rel(v[:, :T], ref["v_cache"][l][:, :T]) <= TOL["f32"]
+    print(f"{cfg.name}: {len(ids_ref)} ids ({len(set(ids_ref))} distinct) identical; min oracle margin "
+          f"{ref['margins'].min():.3e}")
+
+
 # ------------------------------------------------------------------ scaled C3 / C4 (live oracle)
 SMALL_C3 = vs.scaled(vs.C3, n_layers=2, vocab=8192, seq=96, n_img=40, img_start=20, decode_steps=12, capacity=128)
 SMALL_C4 = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=80, n_img=30, img_start=16, decode_steps=12, capacity=128)
@@ -153,7 +173,7 @@ SMALL_C4_FFN_TAIL = vs.scaled(SMALL_C4, ffn=1056, name="c4_2layer_ffn1056")
 def test_scaled_bf16_stacks(rt, cfg):
     pipeline, _ = rt
     glob, layers = make(cfg)
-    ref = od.run_decoder(cfg, glob, layers)
+    ref = oracle_run(cfg, glob, layers)
     run = gpu_run(pipeline, cfg, glob, layers)
     x = run.prefill()
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
@@ -164,9 +184,8 @@ def test_scaled_bf16_stacks(rt, cfg):
     free = [tok0] + list(run.decode(cfg.decode_steps))
     run.kv.truncate(cfg.seq)
     forced = [tok0] + list(run.decode_forced(ref["ids"][:-1]))
-    eps = 8 * float(np.abs(lg - ref["logits0"]).max())
-    flips, div = check_ids(free, forced, ref["ids"], ref["margins"], eps)
-    print(f"{cfg.name}: logit err {eps / 8:.2e}, tie eps {eps:.2e}, first divergence {div}, tie flips {flips}")
+    print(f"{cfg.name}: first-token logit err {np.abs(lg - ref['logits0']).max():.2e}")
+    check_ids(cfg.name, free, forced, ref["ids"], ref["margins"], ref["floor"])
 
 
 def test_generic_gemv_fallback_shapes(rt):
@@ -233,7 +252,7 @@ def test_degenerate_and_ragged_prompts(rt, cfg):
     oracle (fp32 1e-4, bf16 2e-2; bf16 ids with near-ties attributed)."""
     pipeline, _ = rt
     glob, layers = make(cfg)
-    ref = od.run_decoder(cfg, glob, layers)
+    ref = oracle_run(cfg, glob, layers)
     run = gpu_run(pipeline, cfg, glob, layers)
     x = run.prefill()
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
@@ -258,5 +277,4 @@ def test_degenerate_and_ragged_prompts(rt, cfg):
     else:
         run.kv.truncate(cfg.seq)
         forced = [tok0] + list(run.decode_forced(ref["ids"][:-1]))
-        eps = 8 * float(np.abs(lg - ref["logits0"]).max())
-        check_ids(free, forced, ref["ids"], ref["margins"], eps)
+        check_ids(cfg.name, free, forced, ref["ids"], ref["margins"], ref["floor"])

@@ -1,0 +1,90 @@
+"""Multi-token verify and commit (HunyuanOCR v1.5 ncnn port §3.8: the target model
+verifies a drafted block in one causal forward, keeps the longest matching
+prefix plus its first correction, and trims the caches).
+
+fp32 4B-class layer shape (2 layers, vocab 8192), whose greedy sequence varies:
+  * the verify head's logits of a block equal the oracle's by definition (one
+    causal forward over prompt + block) within 1e-4, its picks are the
+    oracle's greedy ids;
+  * drafting from the greedy sequence with wrong tokens injected at chosen
+    positions, verify + commit reproduces the one-token decode's ids exactly
+    and leaves the same cache (1e-4) and length.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decoder as od
+import vlm_synth as vs
+from tests._parity import rel
+
+pytestmark = pytest.mark.gpu
+
+CFG = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=80, n_img=30, img_start=16, decode_steps=40, capacity=128,
+                dtype="f32", name="c4_2layer_f32_verify")
+
+
+@pytest.fixture(scope="module")
+def env():
+    from decoder_prefill_decode_amd import pipeline
+    glob = vs.decoder_globals(CFG)
+    layers = [vs.decoder_layer_weights(CFG, l) for l in range(CFG.n_layers)]
+    ref = od.run_decoder(CFG, glob, layers, steps=CFG.decode_steps + 8)   # ids past the last step for drafts
+    return pipeline, glob, layers, [int(i) for i in ref["ids"]]
+
+
+def test_verify_head_matches_causal_forward(env):
+    pipeline, glob, layers, ids = env
+    k = 8
+    block = ids[:k]
+    want = od.block_logits(CFG, glob, layers, block)
+    run = pipeline.DecoderRun(CFG, lambda l: layers[l], glob)
+    run.prefill()
+    assert int(run.first_token()[0]) == ids[0]
+    logits = torch.empty((k, CFG.vocab), dtype=torch.float32, device="cuda")
+    toks, nxt = run.verify_block(block, logits)
+    assert rel(logits.cpu().numpy(), want) <= 1e-4
+    assert [int(np.argmax(r)) for r in want] == ids[1:k + 1]
+    assert toks == ids[1:k + 1] and nxt == ids[k]          # every draft accepted, plus the next token
+    assert run.kv.len() == CFG.seq + k
+
+
+@pytest.mark.parametrize("k,wrong", [(6, {1: [3], 2: [1], 4: [5], 5: [1, 2]}), (4, {0: [1], 3: [2]})],
+                         ids=["block6", "block4"])
+def test_draft_accept_commit_reproduces_greedy_decode(env, k, wrong):
+    """wrong: {block number: block offsets whose drafted token is replaced by another id}."""
+    pipeline, glob, layers, ids = env
+    N = CFG.decode_steps
+    ar = pipeline.DecoderRun(CFG, lambda l: layers[l], glob)
+    ar.prefill()
+    t0 = int(ar.first_token()[0])
+    ar_ids = [t0] + [int(t) for t in ar.decode(N)]
+    assert ar_ids == ids[:N + 1]
+    T = CFG.seq + N
+
+    sp = pipeline.DecoderRun(CFG, lambda l: layers[l], glob)
+    sp.prefill()
+    gen = [int(sp.first_token()[0])]
+    blocks = 0
+    while len(gen) < N + 1:
+        i0 = len(gen) - 1                                   # gen[-1] == ids[i0], not yet in the cache
+        draft = [gen[-1]] + ids[i0 + 1:i0 + k]
+        for off in wrong.get(blocks, []):
+            if off < k:
+                draft[off] = (draft[off] + 1) % (CFG.vocab - 1)
+        pos0 = sp.kv.len()
+        assert pos0 == CFG.seq + i0
+        toks, _ = sp.verify_block(draft)
+        bad = [off for off in range(1, k) if draft[off] != ids[i0 + off]]
+        expect_acc = (bad[0] - 1) if bad else k - 1         # drafted tokens before the first wrong one
+        assert len(toks) == expect_acc + 1 and sp.kv.len() == pos0 + expect_acc + 1
+        gen += toks
+        blocks += 1
+    assert gen[:N + 1] == ids[:N + 1]
+    assert blocks < N                                       # fewer target passes than one-token decode
+    assert sp.kv.len() >= T
+    for l in range(CFG.n_layers):
+        ka, va = (t[:, :T].cpu().numpy() for t in ar.kv.kv(l))
+        kb, vb = (t[:, :T].cpu().numpy() for t in sp.kv.kv(l))
+        assert rel(kb, ka) <= 1e-4 and rel(vb, va) <= 1e-4
+    print(f"block {k}: {N + 1} greedy ids reproduced in {blocks} verify passes")
