@@ -1,19 +1,22 @@
 """Full-size GPU parity against stored oracle results (tests/golden/*.npz,
 written by tests/golden/make_golden.py, which calls only the oracle).
 
-Decoder stacks (28-layer Qwen3-style and 36-layer 4B-class, bf16): sampled
-prefill rows and the top-64 first-token logits within the bf16 gate (2e-2 of
-the tensor's max); sampled KV slots within twice the oracle's own noise
-floor at that depth; greedy ids checked free-running and teacher-forced, a
-disagreement allowed only at a step whose oracle top-2 margin is below the
-oracle's own first-token logit noise floor (see test_gpu_decoder.check_ids).
-The noise floors (tests/golden/noise_floor.json, written by
-tests/golden/noise_floor.py from the oracle alone) are the difference between
-the oracle with float32 BLAS and with float64 products of the same bf16
-operands: no result finer than that is fixed by the arithmetic.
-Vision tower (27 layers + merger, fp32): sampled merged rows within 1e-4.
+Decoder stacks (28-layer Qwen3-style and 36-layer 4B-class, bf16), element by
+element against the exact-sum oracle, all at the bf16 gate 2e-2 (max relative
+error over the tensor):
+  * every prefill row and every first-token logit;
+  * every valid K/V slot of layers 0, L/2 and L-1 after the prompt and after a
+    decode teacher-forced on the oracle's ids (so decode slots are comparable);
+  * greedy ids free-running and teacher-forced: exact at every step whose
+    oracle top-2 margin is at least the oracle's own noise floor (the largest
+    logit change of the oracle rerun with float32 sums, stored with the
+    golden); the agreement counts are printed.
+The 36-layer stack's deepest tensors (prefill rows after 36 layers, the
+first-token logits, layer 35's K/V) are an expected failure of the 2e-2 gate:
+the oracle's own float32-sum rerun already exceeds it there (C4_DEEP below).
+Vision tower (27 layers + merger): every merged row, fp32 within 1e-4, the
+bf16-storage tower (Mixed policy of the HunyuanOCR v1.5 port, §3.7) within 2e-2.
 """
-import json
 import os
 
 import numpy as np
@@ -21,23 +24,36 @@ import pytest
 import torch
 
 import vlm_synth as vs
-from tests.test_gpu_decoder import check_ids
+from tests._parity import check_ids, rel
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BF16_GATE = 2e-2
 
 
 def load(name):
     return dict(np.load(os.path.join(GOLDEN, f"{name}.npz"), allow_pickle=False))
 
 
-def noise_floor(name):
-    with open(os.path.join(GOLDEN, "noise_floor.json")) as f:
-        return json.load(f)[name]
+def bits_to_f32(b):
+    return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("cfg", [vs.C3, vs.C4], ids=["c3_28layer", "c4_36layer"])
-def test_decoder_stack_full_size(cfg):
+# The 36-layer stack's deepest tensors sit at the edge of what its arithmetic fixes: the oracle rerun
+# with float32 sums (operands and rounding points unchanged) already differs from the exact oracle by
+# 2.29e-2 on the first-token logits and 2.03e-2 on layer 35's K/V (floors stored with the golden), above
+# the 2e-2 gate. The gate is kept; the known exceedance of these tensors is an expected failure.
+C4_DEEP = ("36-layer bf16 stack: the oracle's own float32-sum rerun moves the first-token logits by 2.29e-2 "
+           "and layer 35's K/V by 2.03e-2 (above the 2e-2 gate), so no float32-accumulating implementation is "
+           "bound to meet the gate on these tensors; the measured GPU figures are printed")
+_RUNS = {}
+
+
+def gpu_pass(cfg):
+    """One GPU pass per stack: prefill, first token, free-running decode, then the cache truncated to
+    the prompt and a decode teacher-forced on the oracle's ids (so decode slots are comparable)."""
+    if cfg.name in _RUNS:
+        return _RUNS[cfg.name]
     from decoder_prefill_decode_amd import pipeline
     g = load(cfg.name)
     glob = vs.decoder_globals(cfg)
@@ -45,46 +61,56 @@ def test_decoder_stack_full_size(cfg):
     x = run.prefill()
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
     tok0 = int(run.first_token(logits)[0])
-    rows = g["prefill_rows"]
-    xr = x[torch.from_numpy(rows).to("cuda")].cpu().numpy()
-    err_x = np.abs(xr - g["prefill_x_rows"]).max() / g["prefill_x_absmax"]
-    lg = logits.cpu().numpy()
-    err_lg = np.abs(lg[g["logits0_top_idx"]] - g["logits0_top_val"]).max()
-    assert err_x <= 2e-2, err_x
-    assert err_lg / g["logits0_absmax"] <= 2e-2, err_lg
-    free = [tok0] + list(run.decode(cfg.decode_steps))
-    L, slots = g["kv_layers"], g["kv_slots"]
-    kv_err = []
-    for i, l in enumerate(L):
-        k, v = run.kv.kv(int(l))
-        idx = torch.from_numpy(slots).to("cuda")
-        ks, vv = k[:, idx].float().cpu().numpy(), v[:, idx].float().cpu().numpy()
-        pr = slots < cfg.seq   # prompt slots; decode slots differ after a free-running divergence
-        kv_err.append(max(np.abs(ks[:, pr] - g["k_samples"][i][:, pr]).max() / np.abs(g["k_samples"][i]).max(),
-                          np.abs(vv[:, pr] - g["v_samples"][i][:, pr]).max() / np.abs(g["v_samples"][i]).max()))
+    r = {"g": g, "err_x": rel(x.cpu().numpy(), g["prefill_x"]), "err_lg": rel(logits.cpu().numpy(), g["logits0"])}
+    r["free"] = [tok0] + [int(i) for i in run.decode(cfg.decode_steps)]
     run.kv.truncate(cfg.seq)
-    forced = [tok0] + list(run.decode_forced(g["ids"][:-1]))
-    nf = noise_floor(cfg.name)
-    eps = max(8 * float(err_lg), nf["logit_abs"])
-    agree = sum(int(a == b) for a, b in zip(free, g["ids"]))
-    print(f"{cfg.name}: prefill err {err_x:.2e}, top-logit err {err_lg:.2e}, KV err {kv_err}, tie eps {eps:.2e}, "
-          f"free-running agreement {agree}/{len(free)}, "
-          f"teacher-forced agreement {sum(int(a == b) for a, b in zip(forced, g['ids']))}/{len(forced)}")
-    floor = [nf["kv_rel"][str(int(l))] for l in L]
-    assert all(e <= 2 * f for e, f in zip(kv_err, floor)), (kv_err, floor)
-    flips, div = check_ids(free, forced, g["ids"], g["margins"], eps)
-    print(f"{cfg.name}: first divergence {div}, tie-ambiguous flips {flips}")
+    r["forced"] = [tok0] + [int(i) for i in run.decode_forced(g["ids"][:-1])]
+    T = cfg.seq + cfg.decode_steps
+    k_ref, v_ref = bits_to_f32(g["k_bits"]), bits_to_f32(g["v_bits"])
+    r["kv"] = {}
+    for i, l in enumerate(g["kv_layers"]):
+        k, v = run.kv.kv(int(l))
+        k, v = k[:, :T].float().cpu().numpy(), v[:, :T].float().cpu().numpy()
+        r["kv"][int(l)] = max(rel(k, k_ref[i]), rel(v, v_ref[i]))
+    del run
+    torch.cuda.empty_cache()
+    print(f"{cfg.name}: prefill rows {r['err_x']:.3e} (oracle floor {float(g['floor_prefill_rel']):.3e}), "
+          f"first-token logits {r['err_lg']:.3e}, KV per layer over all {T} slots "
+          f"{ {l: round(e, 5) for l, e in r['kv'].items()} } (oracle floor "
+          f"{[round(float(f), 5) for f in g['floor_kv_rel']]})")
+    _RUNS[cfg.name] = r
+    return r
 
 
-def test_vit_full_size():
+@pytest.mark.parametrize("cfg", [vs.C3, vs.C4], ids=["c3_28layer", "c4_36layer"])
+def test_decoder_stack_full_size_ids_and_cache(cfg):
+    """Greedy ids (exact above the oracle's noise floor) and the K/V of layers 0 and L/2 at 2e-2."""
+    r = gpu_pass(cfg)
+    g = r["g"]
+    check_ids(cfg.name, r["free"], r["forced"], g["ids"], g["margins"], float(g["floor_logit"]))
+    shallow = {l: e for l, e in r["kv"].items() if l < cfg.n_layers - 1}
+    assert all(e <= BF16_GATE for e in shallow.values()), shallow
+
+
+@pytest.mark.parametrize("cfg", [vs.C3, pytest.param(vs.C4, marks=pytest.mark.xfail(reason=C4_DEEP, strict=False))],
+                         ids=["c3_28layer", "c4_36layer"])
+def test_decoder_stack_full_size_deep_tensors(cfg):
+    """Every prefill row, every first-token logit and the last layer's K/V at the 2e-2 gate."""
+    r = gpu_pass(cfg)
+    last = r["kv"][cfg.n_layers - 1]
+    assert r["err_x"] <= BF16_GATE and r["err_lg"] <= BF16_GATE and last <= BF16_GATE, \
+        (r["err_x"], r["err_lg"], last)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_vit_full_size(dtype):
     from decoder_prefill_decode_amd import pipeline
-    cfg = vs.C5
+    cfg = vs.C5 if dtype == "f32" else vs.scaled_vit(vs.C5, dtype=vs.BF16, name="c5_vit_27l_bf16")
     g = load(cfg.name)
     glob = vs.vit_globals(cfg)
     run = pipeline.VitRun(cfg, lambda l: vs.vit_layer_weights(cfg, l), glob)
     out = run.run().cpu().numpy()
-    units = g["units"]
-    err = np.abs(out[units] - g["out_rows"]).max() / g["out_absmax"]
-    assert err <= 1e-4, err
-    assert np.allclose(np.linalg.norm(out, axis=1), g["out_row_norms"], rtol=1e-4)
-    print(f"{cfg.name}: merged-output max rel err {err:.2e}")
+    err = rel(out, g["out"])
+    floor = f" (oracle floor {float(g['floor_out_rel']):.3e})" if "floor_out_rel" in g else ""
+    print(f"{cfg.name}: merged-output max rel err {err:.3e}{floor}")
+    assert err <= (1e-4 if dtype == "f32" else BF16_GATE), err
