@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -577,6 +578,50 @@ vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_nor
     Ws w;
     if ((s = check_ws(desc, 0, d_ws, ws_bytes, &w))) return s;
     auto* part = (unsigned long long*)P(d_ws, w.lm);
+    HIP_TRY(launch_lmhead_argmax(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab,
+                                 desc->hidden, part, d_logits, d_token_out, nullptr, nullptr, stream));
+    return ok();
+}
+
+// Allocation-free lm_head argmax: the block partials of the argmax live in a
+// file-scope device array (one copy per GPU, held until the process ends)
+// instead of the caller's workspace. Host code never passes `scratch` itself
+// (in host code the name is a stand-in, not a device address): the device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+constexpr int kNoAllocPartials = 65536;  // u64 argmax keys: vocabularies up to 262137 rows
+static __device__ __align__(256) unsigned long long scratch[kNoAllocPartials];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static unsigned long long* g_scratch_ptr[kMaxDevices] = {};
+
+static vlm_status scratch_for_current_device(unsigned long long** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(VLM_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(VLM_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+        g_scratch_ptr[dev] = (unsigned long long*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return VLM_OK;
+}
+
+vlm_status vlm_lmhead_argmax_noalloc(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
+                                     const float* d_x_row, int32_t* d_token_out, float* d_logits,
+                                     hipStream_t stream) {
+    vlm_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->vocab < 1) return fail(VLM_ERR_SHAPE, "model has no lm_head table (vocab 0)");
+    if (lmhead_partials_max(desc->vocab) > kNoAllocPartials)
+        return fail(VLM_ERR_UNSUPPORTED, "vocab %d needs %d argmax partials; the allocation-free scratch holds %d",
+                    desc->vocab, lmhead_partials_max(desc->vocab), kNoAllocPartials);
+    if (!d_final_norm || !d_table || !aligned16(d_table) || !d_x_row || !d_token_out)
+        return fail(VLM_ERR_ARG, "NULL or misaligned pointer");
+    unsigned long long* part = nullptr;
+    if ((s = scratch_for_current_device(&part))) return s;
     HIP_TRY(launch_lmhead_argmax(desc->dtype, d_table, d_x_row, d_final_norm, desc->norm_eps, desc->vocab,
                                  desc->hidden, part, d_logits, d_token_out, nullptr, nullptr, stream));
     return ok();

@@ -79,6 +79,7 @@ _SIG = {
     "vlm_prefill": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _I, _I, _P, _P, _I, C.POINTER(Mask), _I, _P,
                          _P, C.c_size_t, _P]),
     "vlm_lmhead_argmax": (_I, [C.POINTER(ModelDesc), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "vlm_lmhead_argmax_noalloc": (_I, [C.POINTER(ModelDesc), _P, _P, _P, _P, _P, _P]),
     "vlm_lmhead_argmax_rows": (_I, [C.POINTER(ModelDesc), _P, _P, _P, _I, _P, _P, _P, C.c_size_t, _P]),
     "vlm_verify_commit": (_I, [_P, _I, C.POINTER(_I), _I, _P, _P, C.POINTER(_I), C.POINTER(_I)]),
     "vlm_decode_step": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P,

@@ -282,6 +282,21 @@ vlm_status vlm_lmhead_argmax(const vlm_model_desc* desc, const void* d_final_nor
                              const float* d_x_row, int32_t* d_token_out, float* d_logits, void* d_ws,
                              size_t ws_bytes, hipStream_t stream);
 
+/* vlm_lmhead_argmax without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, kernels and results as
+ * vlm_lmhead_argmax; the argmax block partials live in a library-owned device
+ * array of 65536 u64 keys (512 KiB per GPU the library runs on, held until the
+ * process ends), so the vocabulary is limited to 262137 rows
+ * (VLM_ERR_UNSUPPORTED beyond, nothing enqueued). No hipMalloc, hipFree or
+ * other allocating call is made. Every call on one GPU shares that array:
+ * calls that overlap on one GPU (other streams or threads) race and must be
+ * serialized by the caller. The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) with that device current. */
+vlm_status vlm_lmhead_argmax_noalloc(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
+                                     const float* d_x_row, int32_t* d_token_out, float* d_logits,
+                                     hipStream_t stream);
+
 /* Multi-token verify head ([HyOCR15] §3.8: the target model checks a drafted
  * block in one causal forward). Rows d_x [S][H] fp32 (hidden rows after the
  * last layer, e.g. of a vlm_prefill over the block at pos0 = cache length):

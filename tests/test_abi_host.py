@@ -170,3 +170,21 @@ def test_merger_validation():
     assert N.lib().vlm_vit_merger_workspace_bytes(C.byref(m), 1287, C.byref(n)) == N.VLM_ERR_SHAPE
     N.call("vlm_vit_merger_workspace_bytes", C.byref(m), 1288, C.byref(n))
     assert n.value >= 1288 * 1152 * 4 + 322 * 4608 * 4
+
+
+def test_noalloc_lmhead_rejects_vocab_beyond_scratch_before_device_work():
+    d = desc(vocab=300000, dtype=N.VLM_BF16)
+    fake = C.c_void_p(256)
+    st = N.lib().vlm_lmhead_argmax_noalloc(C.byref(d), fake, fake, fake, fake, None, None)
+    assert st == N.VLM_ERR_UNSUPPORTED and "scratch" in N.last_error()
+
+
+def test_verify_commit_and_status_argument_checks():
+    assert N.lib().vlm_verify_commit(None, 0, None, 1, None, None, None, None) == N.VLM_ERR_ARG
+    assert N.lib().vlm_kv_status(None, None, None) == N.VLM_ERR_ARG
+    assert N.lib().vlm_token_status(None, None, None) == N.VLM_ERR_ARG
+    d = desc(vocab=0)
+    fake = C.c_void_p(256)
+    tok = C.c_void_p(512)
+    assert N.lib().vlm_lmhead_argmax_rows(C.byref(d), fake, fake, fake, 4, tok, None, fake, 1 << 20, None) == \
+        N.VLM_ERR_SHAPE
