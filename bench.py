@@ -79,10 +79,11 @@ def kernel_bytes(cfg, name, t=None):
     E = 2 if cfg.dtype == "bf16" else 4
     H, F, qd = cfg.hidden, cfg.ffn, cfg.n_q_heads * cfg.head_dim
     if name == "attn":
-        from decoder_prefill_decode_amd.csrc_info import decode_splits
+        from decoder_prefill_decode_amd.csrc_info import decode_plan, partial_stride
         kvd = cfg.n_kv_heads * cfg.head_dim
+        nsplit = decode_plan(cfg.capacity, t)[0]
         return 2 * kvd * t * E + 2 * kvd * E + cfg.qkv_rows * 4 + \
-            cfg.n_q_heads * decode_splits(cfg.capacity) * (cfg.head_dim + 2) * 4
+            cfg.n_q_heads * nsplit * partial_stride(cfg.head_dim) * 4
     if name == "lmhead":
         return cfg.vocab * H * E + H * 4
     if name == "qkv":
@@ -171,7 +172,7 @@ def time_kernel(run, name, launches):
 
     def go(n):
         N.call("vlm_launch_kernel", C.byref(m.desc), m.layers, ptr(m.final_norm), ptr(m.embed), run.kv.handle,
-               ptr(run.cos), ptr(run.sin), which, n, ptr(x), ptr(run.ws), run.ws.numel(), stream())
+               ptr(run.cos), ptr(run.sin), run.cos.shape[0], which, n, ptr(x), ptr(run.ws), run.ws.numel(), stream())
     go(10)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()

@@ -975,10 +975,19 @@ vlm_status vlm_vit_merger(const vlm_merger* m, const float* d_x, int32_t N, cons
 }
 
 // =============================================================================== measurement
+vlm_status vlm_decode_split_plan(int32_t capacity, int32_t t, int32_t* nsplit, int32_t* chunk) {
+    if (!nsplit || !chunk) return fail(VLM_ERR_ARG, "NULL pointer");
+    if (capacity < 1 || t < 0 || t >= capacity) return fail(VLM_ERR_SHAPE, "t %d outside [0, %d)", t, capacity);
+    const DecSplitPlan p = attn_decode_plan(capacity, t);
+    *nsplit = p.nsplit;
+    *chunk = p.chunk;
+    return ok();
+}
+
 vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_final_norm,
                              const void* d_table, vlm_kv* kv, const float* d_cos, const float* d_sin,
-                             int32_t which, int32_t n_launches, const float* d_x_row, void* d_ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             int32_t table_rows, int32_t which, int32_t n_launches, const float* d_x_row, void* d_ws,
+                             size_t ws_bytes, hipStream_t stream) {
     vlm_status s = check_desc(desc);
     if (s) return s;
     if (desc->block_kind != VLM_BLOCK_DECODER) return fail(VLM_ERR_ARG, "decoder (GQA) kernels only");
@@ -995,6 +1004,8 @@ vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_laye
         if (!kv || !d_cos || !d_sin) return fail(VLM_ERR_ARG, "attention needs the KV cache and RoPE tables");
         if (memcmp(&kv->desc, desc, sizeof(*desc)) != 0) return fail(VLM_ERR_ARG, "KV cache bound to another model");
         if (kv->len >= kv->capacity) return fail(VLM_ERR_CAPACITY, "cache full");
+        if (kv->len >= table_rows)
+            return fail(VLM_ERR_CAPACITY, "position %d beyond the RoPE table rows %d", kv->len, table_rows);
     }
     Ws w;
     if ((s = check_ws(desc, 1, d_ws, ws_bytes, &w))) return s;

@@ -90,8 +90,9 @@ _SIG = {
     "vlm_gather_rows": (_I, [_P, _I, _P, _I, _I, _P, _P]),
     "vlm_vit_merger": (_I, [C.POINTER(Merger), _P, _I, _P, _P, _P, C.c_size_t, _P]),
     "vlm_vit_merger_workspace_bytes": (_I, [C.POINTER(Merger), _I, C.POINTER(C.c_size_t)]),
-    "vlm_launch_kernel": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _I, _I, _P, _P, C.c_size_t,
-                               _P]),
+    "vlm_decode_split_plan": (_I, [_I, _I, C.POINTER(_I), C.POINTER(_I)]),
+    "vlm_launch_kernel": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _I, _I, _I, _P, _P,
+                               C.c_size_t, _P]),
 }
 VLM_KERNEL_LMHEAD, VLM_KERNEL_QKV, VLM_KERNEL_O, VLM_KERNEL_GATE_UP, VLM_KERNEL_DOWN, VLM_KERNEL_ATTN = range(6)
 

@@ -425,6 +425,13 @@ vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sam
                              int32_t* d_token_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
+/* Host-only: the split plan of the decode attention at position t in a window
+ * of `capacity` slots, as vlm_decode_step launches it (the slots [0, tb) of
+ * t's band of 64 positions, tb the band's end or the capacity, in *nsplit
+ * splits of *chunk slots; *nsplit <= 32). For accounting (bytes a launch
+ * reads) and tests; no device work. */
+vlm_status vlm_decode_split_plan(int32_t capacity, int32_t t, int32_t* nsplit, int32_t* chunk);
+
 /* Measurement helper: enqueues n_launches back-to-back launches of one kernel
  * of the decode step, exactly as vlm_decode_step launches it, cycling over the
  * layers so that consecutive launches read different weights. Inputs come from
@@ -432,9 +439,10 @@ vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sam
  * outputs go to the workspace only, except VLM_KERNEL_ATTN, which (like a
  * decode step) writes the new token's K/V into slot t = current length of
  * `kv` and reads slots 0..t; the length does not change. `kv`, d_cos and
- * d_sin are needed for VLM_KERNEL_ATTN only (else may be NULL). Used to time
- * one kernel with events on `stream`, and under a profiler, without the rest
- * of the step. */
+ * d_sin ([table_rows][d]) are needed for VLM_KERNEL_ATTN only, which requires
+ * length < table_rows (else VLM_ERR_CAPACITY); otherwise they may be NULL.
+ * Used to time one kernel with events on `stream`, and under a profiler,
+ * without the rest of the step. */
 typedef enum {
     VLM_KERNEL_LMHEAD = 0,   /* final RMSNorm + lm_head GEMV + block argmax partials */
     VLM_KERNEL_QKV = 1,      /* RMSNorm + fused QKV GEMV */
@@ -445,8 +453,8 @@ typedef enum {
 } vlm_kernel_id;
 vlm_status vlm_launch_kernel(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_final_norm,
                              const void* d_table, vlm_kv* kv, const float* d_cos, const float* d_sin,
-                             int32_t which, int32_t n_launches, const float* d_x_row, void* d_ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             int32_t table_rows, int32_t which, int32_t n_launches, const float* d_x_row,
+                             void* d_ws, size_t ws_bytes, hipStream_t stream);
 
 /* Thread-local description of the last error. */
 const char* vlm_last_error(void);

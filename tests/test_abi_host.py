@@ -188,3 +188,15 @@ def test_verify_commit_and_status_argument_checks():
     tok = C.c_void_p(512)
     assert N.lib().vlm_lmhead_argmax_rows(C.byref(d), fake, fake, fake, 4, tok, None, fake, 1 << 20, None) == \
         N.VLM_ERR_SHAPE
+
+
+def test_host_split_plan_mirror_matches_library():
+    """decoder_prefill_decode_amd.csrc_info.decode_plan (the bench's byte accounting) equals the
+    library's planner at every band of the 36-layer stack's window and of a long tiny one."""
+    from decoder_prefill_decode_amd.csrc_info import decode_plan
+    ns, ch = C.c_int32(), C.c_int32()
+    for cap in (64, 1024, 1152, 2048, 2100):
+        for t in list(range(0, cap, 37)) + [cap - 1]:
+            N.call("vlm_decode_split_plan", cap, t, C.byref(ns), C.byref(ch))
+            assert (ns.value, ch.value) == decode_plan(cap, t), (cap, t)
+            assert ns.value <= 32 and ns.value * ch.value >= min(cap, (t // 64 + 1) * 64) > t
