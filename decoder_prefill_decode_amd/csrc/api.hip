@@ -111,6 +111,7 @@ int mla_a_cols(const vlm_model_desc* d) { return is_mla(d) ? d->q_lora_rank + d-
 struct Ws {
     size_t h, qkv, q, kv, o, a, gpart, gpart_floats, xrow, qkvrow, qrow, part, orow, arow, rope, lm;
     size_t ma, mqa, mc, marow;  // MLA: down-projection output, normed q / kv latents (rows), its decode row
+    size_t logits;              // decode step's logits row for the sampler (vocab floats)
     size_t total;
 };
 
@@ -145,6 +146,7 @@ Ws ws_layout(const vlm_model_desc* d, int max_rows) {
     w.mqa = take(is_mla(d) ? R * d->q_lora_rank * E : 0);
     w.mc = take(is_mla(d) ? R * d->kv_lora_rank * E : 0);
     w.marow = take((size_t)mla_a_cols(d) * 4);
+    w.logits = take(d->vocab > 0 ? (size_t)d->vocab * 4 : 0);
     w.total = off;
     return w;
 }
@@ -205,11 +207,16 @@ struct GraphKey {
     int32_t* hist;
     void* ws;
     size_t ws_bytes;
+    bool sampled = false;  // the sampler instead of the argmax ends each step
+    SampleParams sp{};
+    const float* uniform = nullptr;
     bool operator==(const GraphKey& o) const {
         return memcmp(&desc, &o.desc, sizeof(desc)) == 0 && layers.size() == o.layers.size() &&
                memcmp(layers.data(), o.layers.data(), layers.size() * sizeof(vlm_layer)) == 0 && embed == o.embed &&
                fnorm == o.fnorm && table == o.table && tok == o.tok && cos == o.cos && sin == o.sin &&
-               table_rows == o.table_rows && hist == o.hist && ws == o.ws && ws_bytes == o.ws_bytes;
+               table_rows == o.table_rows && hist == o.hist && ws == o.ws && ws_bytes == o.ws_bytes &&
+               sampled == o.sampled && uniform == o.uniform && sp.temperature == o.sp.temperature &&
+               sp.top_k == o.sp.top_k && sp.top_p == o.sp.top_p && sp.penalty == o.sp.penalty;
     }
 };
 
@@ -678,10 +685,8 @@ vlm_status vlm_verify_commit(vlm_kv* kv, int32_t pos0, const int32_t* h_draft, i
 }
 
 // =============================================================================== sampling
-vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sampling* h_params,
-                             const int32_t* d_context_ids, int32_t n_context, const float* d_uniform,
-                             int32_t* d_token_out, hipStream_t stream) {
-    if (!h_params || !d_logits || !d_uniform || !d_token_out) return fail(VLM_ERR_ARG, "NULL pointer");
+static vlm_status check_sampling(const vlm_sampling* h_params, int vocab, SampleParams* out) {
+    if (!h_params) return fail(VLM_ERR_ARG, "sampling parameters NULL");
     if (vocab < 1 || vocab > kSampleVocabMax) return fail(VLM_ERR_SHAPE, "vocab %d not in [1, %d]", vocab, kSampleVocabMax);
     const vlm_sampling& p = *h_params;
     if (!(p.temperature > 0.f) || !std::isfinite(p.temperature))
@@ -690,8 +695,18 @@ vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sam
     if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(VLM_ERR_ARG, "top_p must be in (0, 1]");
     if (!(p.repetition_penalty > 0.f) || !std::isfinite(p.repetition_penalty))
         return fail(VLM_ERR_ARG, "repetition_penalty must be > 0");
+    *out = SampleParams{p.temperature, p.top_k, p.top_p, p.repetition_penalty};
+    return VLM_OK;
+}
+
+vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sampling* h_params,
+                             const int32_t* d_context_ids, int32_t n_context, const float* d_uniform,
+                             int32_t* d_token_out, hipStream_t stream) {
+    if (!h_params || !d_logits || !d_uniform || !d_token_out) return fail(VLM_ERR_ARG, "NULL pointer");
+    SampleParams sp;
+    vlm_status s = check_sampling(h_params, vocab, &sp);
+    if (s) return s;
     if (n_context < 0 || (n_context > 0 && !d_context_ids)) return fail(VLM_ERR_ARG, "context ids");
-    SampleParams sp{p.temperature, p.top_k, p.top_p, p.repetition_penalty};
     HIP_TRY(launch_sample_logits(d_logits, vocab, sp, d_context_ids, n_context, d_uniform, d_token_out, stream));
     return ok();
 }
@@ -700,7 +715,8 @@ vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sam
 static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L, const void* embed, const void* fnorm,
                                  const void* table, vlm_kv* kv, const int32_t* tok_in, const float* x_in,
                                  const float* cosv, const float* sinv, int32_t* tok_out, float* x_out, int32_t* hist,
-                                 void* ws, const Ws& w, const DecSplitPlan& plan, hipStream_t st) {
+                                 void* ws, const Ws& w, const DecSplitPlan& plan, hipStream_t st,
+                                 const SampleParams* samp = nullptr, const float* uniform = nullptr) {
     const int dt = desc->dtype, H = desc->hidden, F = desc->ffn, nq = desc->n_q_heads, nkv = desc->n_kv_heads;
     const int hd = desc->head_dim, dv = vdim(desc), QKV = qkv_rows(desc), W = kv->capacity;
     const bool mla = is_mla(desc);
@@ -774,7 +790,13 @@ static vlm_status enqueue_decode(const vlm_model_desc* desc, const vlm_layer* L,
         HIP_TRY(launch_gemv(dt, Pro::Plain, Epi::Resid, g, st));
     }
     if (x_out) HIP_TRY(launch_copy_f32(x, x_out, H, st));
-    if (table) {
+    if (table && samp) {  // logits row, then the sampler commits the token (context: the history)
+        auto* lm = (unsigned long long*)P(ws, w.lm);
+        float* lg = (float*)P(ws, w.logits);
+        HIP_TRY(launch_lmhead_argmax(dt, table, x, fnorm, desc->norm_eps, desc->vocab, H, lm, lg, nullptr, nullptr,
+                                     nullptr, st));
+        HIP_TRY(launch_sample_step(lg, desc->vocab, *samp, hist, uniform, tok_out, kv->dlen(), st));
+    } else if (table) {
         auto* lm = (unsigned long long*)P(ws, w.lm);
         HIP_TRY(launch_lmhead_argmax(dt, table, x, fnorm, desc->norm_eps, desc->vocab, H, lm, nullptr, tok_out, hist,
                                      kv->dlen(), st));
@@ -827,16 +849,13 @@ vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers
     return ok();
 }
 
-vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
-                           const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
-                           const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
-                           int32_t n_steps, void* d_ws, size_t ws_bytes, hipStream_t stream) {
-    if (n_steps < 0) return fail(VLM_ERR_SHAPE, "n_steps %d < 0", n_steps);
-    Ws w;
-    vlm_status s = check_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos, d_sin,
-                                table_rows, d_token_io, d_ws, ws_bytes, n_steps, &w);
-    if (s) return s;
-    if (!d_table) return fail(VLM_ERR_ARG, "decode loop needs the lm_head table");
+// Captures one step per band of positions into a HIP graph (before any launch) and launches
+// n_steps of them; samp == nullptr: greedy argmax head, else the sampler with draws `uniform`.
+static vlm_status decode_loop_impl(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                                   const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
+                                   const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
+                                   int32_t n_steps, void* d_ws, size_t ws_bytes, const Ws& w, const SampleParams* samp,
+                                   const float* uniform, hipStream_t stream) {
     if (n_steps == 0) return ok();
     GraphKey key;
     key.desc = *desc;
@@ -844,6 +863,9 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
     key.embed = d_embed; key.fnorm = d_final_norm; key.table = d_table; key.tok = d_token_io;
     key.cos = d_cos; key.sin = d_sin; key.table_rows = table_rows; key.hist = d_token_hist;
     key.ws = d_ws; key.ws_bytes = ws_bytes;
+    key.sampled = samp != nullptr;
+    if (samp) key.sp = *samp;
+    key.uniform = uniform;
     if (!kv->has_key || !(kv->key == key)) {
         kv->drop_graph();
         kv->key = key;
@@ -862,7 +884,8 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
         if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
         HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
         vlm_status es = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos,
-                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, plan, kv->cap_stream);
+                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, plan, kv->cap_stream, samp,
+                                       uniform);
         hipGraph_t graph = nullptr;
         hipError_t ee = hipStreamEndCapture(kv->cap_stream, &graph);
         if (es) {
@@ -885,6 +908,38 @@ vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers
         kv->len += 1;  // the launched step advances the device length
     }
     return ok();
+}
+
+vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                           const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
+                           const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
+                           int32_t n_steps, void* d_ws, size_t ws_bytes, hipStream_t stream) {
+    if (n_steps < 0) return fail(VLM_ERR_SHAPE, "n_steps %d < 0", n_steps);
+    Ws w;
+    vlm_status s = check_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos, d_sin,
+                                table_rows, d_token_io, d_ws, ws_bytes, n_steps, &w);
+    if (s) return s;
+    if (!d_table) return fail(VLM_ERR_ARG, "decode loop needs the lm_head table");
+    return decode_loop_impl(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, d_cos, d_sin, table_rows,
+                            d_token_hist, n_steps, d_ws, ws_bytes, w, nullptr, nullptr, stream);
+}
+
+vlm_status vlm_decode_loop_sampled(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                                   const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
+                                   const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
+                                   const vlm_sampling* h_params, const float* d_uniform, int32_t n_steps, void* d_ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    if (n_steps < 0) return fail(VLM_ERR_SHAPE, "n_steps %d < 0", n_steps);
+    Ws w;
+    vlm_status s = check_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos, d_sin,
+                                table_rows, d_token_io, d_ws, ws_bytes, n_steps, &w);
+    if (s) return s;
+    if (!d_table) return fail(VLM_ERR_ARG, "decode loop needs the lm_head table");
+    if (!d_token_hist || !d_uniform) return fail(VLM_ERR_ARG, "the sampled loop needs the token history and draws");
+    SampleParams sp;
+    if ((s = check_sampling(h_params, desc->vocab, &sp))) return s;
+    return decode_loop_impl(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, d_cos, d_sin, table_rows,
+                            d_token_hist, n_steps, d_ws, ws_bytes, w, &sp, d_uniform, stream);
 }
 
 // =============================================================================== vision helpers

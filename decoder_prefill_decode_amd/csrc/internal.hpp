@@ -163,6 +163,11 @@ constexpr int kSampleVocabMax = 1 << 19;
 struct SampleParams { float temperature; int top_k; float top_p; float penalty; };
 hipError_t launch_sample_logits(const float* logits, int V, const SampleParams& p, const int32_t* ctx, int nctx,
                                 const float* u, int32_t* out, hipStream_t st);
+// The sampler as the last kernel of a decode step at position t = kv_len[0] (the cache header):
+// context hist[0..t], draw u[t + 1]; the token goes to out[0] and hist[t + 1], the length to t + 1
+// (a step with no token is not committed and flags the header, as launch_argmax_final does).
+hipError_t launch_sample_step(const float* logits, int V, const SampleParams& p, int32_t* hist, const float* u,
+                              int32_t* out, int32_t* kv_len, hipStream_t st);
 
 // Final RMSNorm + lm_head GEMV + argmax. Writes per-block argmax keys to
 // `partials` (lmhead_partials_max(V) entries) and the logits when non-null.

@@ -30,11 +30,27 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
     return __uint_as_float(u);
 }
 
+// Decode-step form (kv_len != null, the cache header): position t = kv_len[0]; the context is
+// ctx[0..t] (the token history: prompt ids, then every token fed so far), the draw uptr[t + 1];
+// the token goes to out[0] and ctx[t + 1] and the length becomes t + 1; a step with no token
+// (-1) is not committed and sets the header's non-finite flag, as the greedy head does.
+__device__ __forceinline__ void sample_commit(int32_t tok, int32_t* out, int32_t* hist, int32_t* kv_len) {
+    out[0] = tok;
+    if (!kv_len) return;
+    const int t = kv_len[0];
+    if (tok >= 0) {
+        hist[t + 1] = tok;
+        kv_len[0] = t + 1;
+    } else if (kv_len[1] == 0) {
+        kv_len[1] = 1;
+        kv_len[2] = t;
+    }
+}
+
 __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const float* __restrict__ logits, int V,
-                                                                       SampleParams sp,
-                                                                       const int32_t* __restrict__ ctx, int nctx,
+                                                                       SampleParams sp, int32_t* ctx, int nctx,
                                                                        const float* __restrict__ uptr,
-                                                                       int32_t* __restrict__ out) {
+                                                                       int32_t* __restrict__ out, int32_t* kv_len) {
     __shared__ uint32_t bits[kSampleVocabMax / 32];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t ckey[kSampleCand];
@@ -44,6 +60,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
     __shared__ uint32_t s_prefix, s_krem, s_count, s_bad;
     const int tid = threadIdx.x;
     const int nw = (V + 31) / 32;
+    if (kv_len) {  // decode-step form: context and draw follow the device length
+        const int t = kv_len[0];
+        nctx = t + 1;
+        uptr += t + 1;
+    }
     for (int i = tid; i < nw; i += kSampleThreads) bits[i] = 0u;
     if (tid == 0) {
         s_prefix = 0u;
@@ -92,7 +113,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
         __syncthreads();
     }
     if (s_bad) {  // a non-finite logit: no token (the argmax path reports it the same way)
-        if (tid == 0) out[0] = -1;
+        if (tid == 0) sample_commit(-1, out, ctx, kv_len);
         return;
     }
     const uint32_t kth = s_prefix;
@@ -111,7 +132,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
     __syncthreads();
     const int n = (int)s_count;
     if (n > kSampleCand) {  // more ties at the k-th value than slots
-        if (tid == 0) out[0] = -1;
+        if (tid == 0) sample_commit(-1, out, ctx, kv_len);
         return;
     }
     int np2 = 1;
@@ -188,12 +209,19 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
         if (cval[i] > target && before <= target) atomicMin(&s_prefix, (uint32_t)i);
     }
     __syncthreads();
-    if (tid == 0) out[0] = cidx[s_prefix];
+    if (tid == 0) sample_commit(cidx[s_prefix], out, ctx, kv_len);
 }
 
 hipError_t launch_sample_logits(const float* logits, int V, const SampleParams& p, const int32_t* ctx, int nctx,
                                 const float* u, int32_t* out, hipStream_t st) {
-    sample_logits_kernel<<<1, kSampleThreads, 0, st>>>(logits, V, p, ctx, nctx, u, out);
+    sample_logits_kernel<<<1, kSampleThreads, 0, st>>>(logits, V, p, const_cast<int32_t*>(ctx), nctx, u, out,
+                                                       nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_sample_step(const float* logits, int V, const SampleParams& p, int32_t* hist, const float* u,
+                              int32_t* out, int32_t* kv_len, hipStream_t st) {
+    sample_logits_kernel<<<1, kSampleThreads, 0, st>>>(logits, V, p, hist, 0, u, out, kv_len);
     return hipGetLastError();
 }
 

@@ -86,6 +86,8 @@ _SIG = {
                              _P, C.c_size_t, _P]),
     "vlm_decode_loop": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P,
                              C.c_size_t, _P]),
+    "vlm_decode_loop_sampled": (_I, [C.POINTER(ModelDesc), C.POINTER(Layer), _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                     C.POINTER(Sampling), _P, _I, _P, C.c_size_t, _P]),
     "vlm_vit_window_index": (_I, [_I, _I, _I, _I, C.POINTER(_I), C.POINTER(_I), C.POINTER(_I), C.POINTER(_I)]),
     "vlm_gather_rows": (_I, [_P, _I, _P, _I, _I, _P, _P]),
     "vlm_vit_merger": (_I, [C.POINTER(Merger), _P, _I, _P, _P, _P, C.c_size_t, _P]),

@@ -119,6 +119,27 @@ class DecoderRun:
         torch.cuda.current_stream().synchronize()
         return ctx[S:].cpu().numpy().astype(np.int64)
 
+    def generate_sampled_loop(self, n, temperature, top_k, top_p, penalty, u):
+        """generate_sampled with every decode step (layers, lm_head, sampler) replayed from HIP graphs
+        (vlm_decode_loop_sampled): the first token is sampled from the last prompt row, the history
+        holds the prompt ids and the tokens so far, draw i is u[i]. Returns the n + 1 ids (host)."""
+        from .runtime import decode_loop_sampled, sample_logits
+        cfg = self.cfg
+        S, V = cfg.seq, cfg.vocab
+        hist = torch.full((cfg.capacity + 1,), -2, dtype=torch.int32, device="cuda")
+        hist[:S].copy_(self.ids_dev)
+        ud = torch.zeros(cfg.capacity + 1, dtype=torch.float32, device="cuda")
+        ud[S:S + n + 1].copy_(torch.from_numpy(np.ascontiguousarray(u, np.float32)))
+        logits = torch.empty(V, dtype=torch.float32, device="cuda")
+        scratch = torch.empty(1, dtype=torch.int32, device="cuda")
+        self.model.lmhead_argmax(self.x[S - 1], scratch, self.ws, logits)
+        sample_logits(logits, temperature, top_k, top_p, penalty, hist[:S], ud[S:S + 1], hist[S:S + 1])
+        self.tok.copy_(hist[S:S + 1])
+        decode_loop_sampled(self.model, self.kv, self.cos, self.sin, self.ws, self.tok, n, hist,
+                            N.Sampling(temperature, top_k, top_p, penalty), ud)
+        self.kv.status()
+        return hist[S:S + n + 1].cpu().numpy().astype(np.int64)
+
     def decode_forced(self, ids):
         """Teacher-forced greedy steps: step i feeds ids[i] (host ints) and records
         the token the GPU picks next; returns those picks (host)."""

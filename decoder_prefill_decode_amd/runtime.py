@@ -151,6 +151,13 @@ class Model:
                ptr(ws), ws.numel(), stream())
 
 
+def decode_loop_sampled(model, kv, cos, sin, ws, token_io, n_steps, hist, params, uniform):
+    """vlm_decode_loop_sampled: n_steps graph-captured steps ending in the sampler (params: N.Sampling)."""
+    N.call("vlm_decode_loop_sampled", C.byref(model.desc), model.layers, ptr(model.embed), ptr(model.final_norm),
+           ptr(model.embed), kv.handle, ptr(token_io), ptr(cos), ptr(sin), cos.shape[0], ptr(hist), C.byref(params),
+           ptr(uniform), n_steps, ptr(ws), ws.numel(), stream())
+
+
 class KVCache:
     """Caller-owned KV buffer bound to a library handle."""
 

@@ -399,7 +399,7 @@ vlm_status vlm_vit_merger_workspace_bytes(const vlm_merger* m, int32_t N, size_t
 /* ------------------------------------------------------------------------- */
 /* Sampling instead of the greedy argmax ([MNN] §4.1: temperature, top_k,
  * top_p, softmax, draw; repeat penalty on tokens already in the context;
- * [HyOCR15] §3.5 generation options). On one fp32 logits row d_logits [vocab]
+ * [HyOCR15] §3.6 generation options). On one fp32 logits row d_logits [vocab]
  * (e.g. the d_logits output of vlm_lmhead_argmax), in this order:
  *   x_i = logits_i; for i in the context: x_i = x_i > 0 ? x_i / r : x_i * r;
  *   x_i /= temperature; keep the x_i >= the top_k-th largest (ties kept);
@@ -423,6 +423,25 @@ typedef struct {
 vlm_status vlm_sample_logits(const float* d_logits, int32_t vocab, const vlm_sampling* h_params,
                              const int32_t* d_context_ids, int32_t n_context, const float* d_uniform,
                              int32_t* d_token_out, hipStream_t stream);
+
+/* vlm_decode_loop with the sampler in place of the greedy argmax ([MNN] §4.1;
+ * [HyOCR15] §3.6 generation options): every captured step ends with the
+ * lm_head logits row (workspace) and the sampler above, whose context is the
+ * token history d_token_hist[0..t] and whose draw is d_uniform[t + 1], t the
+ * step's position (the device length), so the graphs replay unchanged from
+ * step to step. Before the call the caller fills d_token_hist[0..len) with the
+ * ids of the cached positions (the prompt; the penalty treats them as context)
+ * and d_token_hist[len] = d_token_io[0] (the token fed first); each step writes
+ * its token to d_token_io[0] and d_token_hist[t + 1]. d_uniform holds at least
+ * len + n_steps + 1 draws in [0, 1). A step whose sampler returns no token
+ * (non-finite logits, or more than 2048 values tied at the top_k-th) writes -1
+ * and is not committed (vlm_kv_status reports it). Parameter checks as in
+ * vlm_sample_logits; the other requirements as in vlm_decode_loop. */
+vlm_status vlm_decode_loop_sampled(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
+                                   const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
+                                   const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
+                                   const vlm_sampling* h_params, const float* d_uniform, int32_t n_steps, void* d_ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host-only: the split plan of the decode attention at position t in a window

@@ -97,3 +97,39 @@ def test_sampled_generation_matches_oracle(cfg_name):
             print(f"{cfg_name}: sampled ids agree up to step {i} (boundary case {near:.1e})")
             return
     print(f"{cfg_name}: sampled ids {[int(i) for i in got]} agree with the oracle")
+
+
+@pytest.mark.parametrize("cfg_name", ["c1", "c_mla"])
+def test_sampled_graph_loop_equals_eager_steps_and_oracle(cfg_name):
+    """vlm_decode_loop_sampled (the sampler inside every captured step, context and draw indexed by
+    the device length) gives the same ids as the eager sampled generation, and the oracle's (as in
+    the eager test above); the cache advances by one slot per step."""
+    from decoder_prefill_decode_amd import pipeline
+    from oracle import decoder as od
+    cfg = vs.scaled(vs.C1 if cfg_name == "c1" else vs.C_MLA, decode_steps=10)
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    T, k, p, r = 1.6, 64, 0.95, 1.3
+    u = vs.sampling_case(20, 2, 0, n_draws=cfg.decode_steps + 1)["u"]
+    a = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    a.prefill()
+    eager = [int(i) for i in a.generate_sampled(cfg.decode_steps, T, k, p, r, u)]
+    b = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    b.prefill()
+    loop = [int(i) for i in b.generate_sampled_loop(cfg.decode_steps, T, k, p, r, u)]
+    assert loop == eager
+    assert b.kv.len() == cfg.seq + cfg.decode_steps and int(b.kv.device_len()[0]) == cfg.seq + cfg.decode_steps
+    infos = []
+
+    def sampler(lg, ctx, i):
+        tok, info = osm.sample_token(lg, ctx, T, k, p, r, float(u[i]))
+        infos.append(info)
+        return tok
+
+    ref = od.run_decoder(cfg, glob, layers, sampler=sampler)
+    for i, (g, e) in enumerate(zip(loop, ref["ids"])):
+        if g != e:
+            near = min(infos[i].get("topk_gap", np.inf), infos[i].get("topp_margin", np.inf), infos[i]["cdf_margin"])
+            assert near < 1e-4, f"step {i}: GPU {g} != oracle {e}, nearest boundary {near}"
+            break
+    print(f"{cfg_name}: graph-loop sampled ids {loop}")
