@@ -35,16 +35,27 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return b;
 }
 
+// (tile, K split) of this block: the remap runs over the whole grid (blocks are dealt to the XCDs
+// in launch order, x fastest), so each XCD takes a contiguous run of (tile, split) work with the
+// tiles of one split together: the M tiles that read the same weight columns share an L2. (With
+// the split taken from blockIdx.y the M tiles of one column block fell on different XCDs and the
+// split down projection fetched 2.7x its weight bytes from memory.) Any bijection is correct.
+__device__ __forceinline__ void gemm_work(int ntiles, int* tile, int* split) {
+    const int w = xcd_remap(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    *tile = w % ntiles;
+    *split = w / ntiles;
+}
+
 // Epilogue of one wavefront's (TM*32) x (TN*32) accumulator tile at output
 // rows m0 + wm*WM, columns n0 + wn*WN. C layout of a 32x32 block: lane owns
 // column l32 and rows (r/4)*8 + h*4 + r%4, r = 0..15.
 template <class T, int WM, int WN, int TM, int TN, Epi EPI, bool SPLIT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, f32x16 (&acc)[TM][TN], int m0, int n0, int wm,
-                                              int wn, int h, int l32) {
+                                              int wn, int h, int l32, int split) {
     const int M = a.M, N = a.N;
     const T* bias = (const T*)a.bias;
     if constexpr (SPLIT) {  // raw partial sums; splitk_reduce_kernel applies the epilogue
-        float* part = a.part + (size_t)blockIdx.y * M * N;
+        float* part = a.part + (size_t)split * M * N;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int n = n0 + wn * WN + j * 32 + l32;
@@ -117,7 +128,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
     const int M = a.M, N = a.N, K = a.K;
     const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
-    const int tile = xcd_remap(blockIdx.x, mt * nt);
+    int tile, split;
+    gemm_work(mt * nt, &tile, &split);
     const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int wm = w / 2, wn = w % 2, h = lane / 32, l32 = lane % 32;
@@ -161,11 +173,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    // split-K: blockIdx.y selects a contiguous range of K stages
+    // split-K: the block's split selects a contiguous range of K stages
     int kt0 = 0, nk = (K + BK - 1) / BK;
     if constexpr (SPLIT) {
         const int per = (nk + gridDim.y - 1) / gridDim.y;
-        kt0 = blockIdx.y * per;
+        kt0 = split * per;
         nk = max(0, min(nk, kt0 + per) - kt0);
     }
     gload(kt0);
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         __syncthreads();
     }
 
-    gemm_epilogue<T, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32);
+    gemm_epilogue<T, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32, split);
 }
 
 // ------------------------------------------------- bf16, direct-to-LDS pipeline
@@ -276,7 +288,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
 
     const int M = a.M, N = a.N, K = a.K;
     const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
-    const int tile = xcd_remap(blockIdx.x, mt * nt);
+    int tile, split;
+    gemm_work(mt * nt, &tile, &split);
     const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int wm = w / WGN, wn = w % WGN, h = lane / 32, l32 = lane % 32;
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     int kt0 = 0, nk = nk_all;
     if constexpr (SPLIT) {
         const int per = (nk + gridDim.y - 1) / gridDim.y;
-        kt0 = blockIdx.y * per;
+        kt0 = split * per;
         nk = max(0, min(nk, kt0 + per) - kt0);
     }
     // one K stage of both tiles into LDS stage ST: instruction i of wavefront w fills RPI rows (1 KiB).
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
         }
     }
 #undef VLM_LDS_STAGE
-    gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32);
+    gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32, split);
 }
 
 // Sums the split partials in split order (deterministic) and applies the epilogue.
