@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4_llama_4b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-decode-steps", type=int, default=128)
+    ap.add_argument("--cpu-decode-steps", type=int, default=32)
     ap.add_argument("--kernel-only", default=None,
                     help="launch one decode kernel (lmhead, qkv, o, gate_up, down, attn) --launches times, then "
                          "one plain copy of --copy-mib MiB (reference for HBM counters), and exit")

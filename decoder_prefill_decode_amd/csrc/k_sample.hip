@@ -1,7 +1,7 @@
 // Next-token sampling on the logits row: repetition penalty, temperature,
 // top-k, top-p, softmax and an inverse-CDF draw with a caller-supplied
 // uniform number (MNN llm_demo Omni article §4.1; HunyuanOCR v1.5 ncnn port
-// §3.5 for the generation options).
+// §3.6 for the generation options).
 //
 // One block of 1024 threads; the vocabulary streams from L2 a few times:
 //  1. the context ids become a bitmap in LDS (membership in one read);

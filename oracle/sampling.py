@@ -11,8 +11,8 @@ Sources (page title, section):
            tokens after the cumulative probability passes the threshold become
            -inf), then softmax and a draw (or the maximum); a repeat penalty acts
            on tokens already in the context during the same post-processing.
-  [HyOCR15] HunyuanOCR v1.5 ncnn port, §3.5 (generation options: temperature,
-           top_p / top_k, repetition penalty, sample or not) and §6 (unit tests
+  [HyOCR15] HunyuanOCR v1.5 ncnn port, §3.6 (generation options: temperature,
+           top_p / top_k, repetition penalty, sample or not) and §4 (unit tests
            cover the repetition penalty).
 
 Readings where the pages are silent (listed with the design notes):

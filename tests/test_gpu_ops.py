@@ -187,7 +187,7 @@ def test_truncate_then_redecode_is_deterministic(mods):
 
 # ---------------------------------------------------------------- vision tower
 def test_vit_tower_and_merger_scaled_bf16(mods):
-    """bf16 storage, fp32 accumulation (the Mixed policy of the HunyuanOCR v1.5 port, §3.6), with the
+    """bf16 storage, fp32 accumulation (the Mixed policy of the HunyuanOCR v1.5 port, §3.7), with the
     72-wide heads zero-padded to the 16-wide MFMA steps inside the attention kernel."""
     _, pipeline, _ = mods
     cfg = vs.scaled_vit(vs.C5, n_layers=3, full_layers=(1,), dtype="bf16")

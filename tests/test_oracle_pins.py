@@ -323,7 +323,7 @@ def _softmax(z):
 
 
 def test_sampling_repetition_penalty_worked_example():
-    """HunyuanOCR v1.5 port §3.5/§6 name the penalty; reading: x/r for x > 0, x*r otherwise, once per id."""
+    """HunyuanOCR v1.5 port §3.6/§4 name the penalty; reading: x/r for x > 0, x*r otherwise, once per id."""
     got = osm.penalize([2.0, -1.0, 0.5, 3.0], [0, 1, 1], 2.0)
     assert np.array_equal(got, [1.0, -2.0, 0.5, 3.0])
 
