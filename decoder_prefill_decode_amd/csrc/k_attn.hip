@@ -45,28 +45,37 @@ constexpr float kLog2e = 1.4426950408889634f;
 // returns their count; all threads of the block take part.
 // Under a segment mask: true when every query row of this wavefront (lane % 32 -> row q0 + lane % 32)
 // and every key of the tile [key0, key0 + BKEY) lie in one and the same segment, so the tile needs no
-// per-element test. Wavefront-uniform.
+// per-element test. `sg` holds the tile's segment ids, staged in LDS with its K/V. Wavefront-uniform.
 template <int BKEY>
-__device__ __forceinline__ bool segment_tile_full(const int32_t* seg, int seg_q, bool row_ok, int key0, int nkeys) {
+__device__ __forceinline__ bool segment_tile_full(const int* sg, int seg_q, bool row_ok, int key0, int nkeys) {
     const int s0 = __builtin_amdgcn_readfirstlane(seg_q);
-    const int lane = threadIdx.x % kWave;
-    const int key = key0 + lane % BKEY;
-    const bool key_ok = key < nkeys && seg[min(key, nkeys - 1)] == s0;
+    const int kl = (threadIdx.x % kWave) % BKEY;
+    const bool key_ok = key0 + kl < nkeys && sg[kl] == s0;
     return __all(row_ok && seg_q == s0 && key_ok);
 }
 
-constexpr int kSegMaxTiles = 512;
+// The ids of the block's query rows and of up to NT * kSegKeysPerThread keys are requested in one
+// round trip (indices clamped, no load under a branch); longer key ranges read the rest in a loop.
+constexpr int kSegMaxTiles = 512, kSegKeysPerThread = 8;
 template <int NT, int BKEY>
 __device__ int segment_tiles(const int32_t* seg, int row0, int nrows, int S, int nkeys, int nkt, short* list,
                              unsigned char* flag, int* lohi) {
     const int tid = threadIdx.x;
+    const int rv = seg[min(row0 + min(tid, nrows - 1), S - 1)];
+    int kv[kSegKeysPerThread];
+#pragma unroll
+    for (int i = 0; i < kSegKeysPerThread; i++) kv[i] = seg[min(tid + NT * i, nkeys - 1)];
     if (tid == 0) {
         lohi[0] = 0x7fffffff;
         lohi[1] = (int)0x80000000;
     }
     for (int t = tid; t < nkt; t += NT) flag[t] = 0;
     __syncthreads();
-    for (int r = tid; r < nrows; r += NT)
+    if (tid < nrows && row0 + tid < S) {
+        atomicMin(lohi, rv);
+        atomicMax(lohi + 1, rv);
+    }
+    for (int r = tid + NT; r < nrows; r += NT)  // blocks of more than NT rows
         if (row0 + r < S) {
             const int sv = seg[row0 + r];
             atomicMin(lohi, sv);
@@ -74,7 +83,12 @@ __device__ int segment_tiles(const int32_t* seg, int row0, int nrows, int S, int
         }
     __syncthreads();
     const int lo = lohi[0], hi = lohi[1];
-    for (int k = tid; k < nkeys; k += NT) {
+#pragma unroll
+    for (int i = 0; i < kSegKeysPerThread; i++) {
+        const int k = tid + NT * i;
+        if (k < nkeys && kv[i] >= lo && kv[i] <= hi) flag[k / BKEY] = 1;
+    }
+    for (int k = tid + NT * kSegKeysPerThread; k < nkeys; k += NT) {
         const int sv = seg[k];
         if (sv >= lo && sv <= hi) flag[k / BKEY] = 1;
     }
@@ -175,7 +189,11 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
     // consecutive dwords.
     constexpr int TCH = (BKEY * CH + 255) / 256;        // 16-byte chunks of the K tile per thread
     constexpr int NVP = (BKEY / 2) * CHV, VP = (NVP + 255) / 256;  // (key pair, chunk) items of the V tile
-    auto request = [&](int kt, u32x4 (&kreg)[TCH], u32x4 (&vreg)[VP][2]) {
+    // the segment ids of a tile's keys travel with its K/V: requested with them (every thread, key
+    // tid % BKEY), stored to LDS by the first BKEY threads
+    __shared__ int segs[MASK == VLM_MASK_SEGMENT_ID ? 2 : 1][MASK == VLM_MASK_SEGMENT_ID ? BKEY : 1];
+    auto request = [&](int kt, u32x4 (&kreg)[TCH], u32x4 (&vreg)[VP][2], int& sreg) {
+        if constexpr (MASK == VLM_MASK_SEGMENT_ID) sreg = a.seg[min(kt * BKEY + tid % BKEY, a.nkeys - 1)];
 #pragma unroll
         for (int i = 0; i < TCH; i++) {
             const int c = min(tid + 256 * i, BKEY * CH - 1), r = c / CH, d0 = (c % CH) * 8;
@@ -192,8 +210,10 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
             }
         }
     };
-    auto stage = [&](int kt, int buf, const u32x4 (&kreg)[TCH], const u32x4 (&vreg)[VP][2]) {
+    auto stage = [&](int kt, int buf, const u32x4 (&kreg)[TCH], const u32x4 (&vreg)[VP][2], int sreg) {
         const int key0 = kt * BKEY;
+        if constexpr (MASK == VLM_MASK_SEGMENT_ID)
+            if (tid < BKEY) segs[buf][tid] = sreg;
         bf16_t* kd = Ks + buf * KSZ;
         bf16_t* vd = Vt + buf * VSZ;
 #pragma unroll
@@ -220,15 +240,16 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
         }
     };
     u32x4 kA[TCH], vA[VP][2], kB[TCH], vB[VP][2];
-    if (nvis > 0) request(tile_at(0), kA, vA);
-    if (nvis > 1) request(tile_at(1), kB, vB);
+    int sA = 0, sB = 0;
+    if (nvis > 0) request(tile_at(0), kA, vA, sA);
+    if (nvis > 1) request(tile_at(1), kB, vB, sB);
     for (int kt2 = 0; kt2 < nvis; kt2 += 2) {
-        stage(tile_at(kt2), 0, kA, vA);
-        if (kt2 + 1 < nvis) stage(tile_at(kt2 + 1), 1, kB, vB);
+        stage(tile_at(kt2), 0, kA, vA, sA);
+        if (kt2 + 1 < nvis) stage(tile_at(kt2 + 1), 1, kB, vB, sB);
         __syncthreads();
         // the next pair is in flight during this pair's MFMAs
-        if (kt2 + 2 < nvis) request(tile_at(kt2 + 2), kA, vA);
-        if (kt2 + 3 < nvis) request(tile_at(kt2 + 3), kB, vB);
+        if (kt2 + 2 < nvis) request(tile_at(kt2 + 2), kA, vA, sA);
+        if (kt2 + 3 < nvis) request(tile_at(kt2 + 3), kB, vB, sB);
         const int kv = kt2 + kpar;  // position in the visit order
         const int key0 = (kv < nvis ? tile_at(kv) : 0) * BKEY;
         const bf16_t* const Kw = Ks + kpar * KSZ;
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
                          (MASK == VLM_MASK_CAUSAL_ID && key0 + BKEY - 1 <= a.pos0 + q0)) &&
                         key0 + BKEY <= a.nkeys;
             if constexpr (MASK == VLM_MASK_SEGMENT_ID)
-                full = segment_tile_full<BKEY>(a.seg, seg_q, qrow < S, key0, a.nkeys);
+                full = segment_tile_full<BKEY>(segs[kpar], seg_q, qrow < S, key0, a.nkeys);
             float mt = -INFINITY;
             // wavefront-uniform: one scalar branch per tile (the segment mask keeps the test per
             // element: its two loop bodies together would spill)
@@ -278,7 +299,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
                     }
                     bool vis = key < a.nkeys;
                     if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
-                    if (MASK == VLM_MASK_SEGMENT_ID) vis = vis && qrow < S && a.seg[key] == seg_q;
+                    if (MASK == VLM_MASK_SEGMENT_ID) vis = vis && qrow < S && segs[kpar][key - key0] == seg_q;
                     if (MASK == VLM_MASK_ADDITIVE_ID && vis && qrow < S)
                         s += a.add[(size_t)qrow * a.ld_add + key] * kLog2e;
                     s = vis ? s : -INFINITY;
@@ -430,9 +451,12 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     if constexpr (MASK == VLM_MASK_SEGMENT_ID)
         if (listed) nvis = segment_tiles<256, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
 
+    __shared__ int segs[MASK == VLM_MASK_SEGMENT_ID ? BKEY : 1];  // the tile's segment ids
     for (int kv = 0; kv < nvis; kv++) {
         const int kt = listed ? (int)tlist[kv] : kv;
         const int key0 = kt * BKEY;
+        if constexpr (MASK == VLM_MASK_SEGMENT_ID)
+            if (tid < BKEY) segs[tid] = a.seg[min(key0 + tid, a.nkeys - 1)];
         for (int c = tid; c < BKEY * CH; c += 256) {
             const int r = c / CH, d0 = (c % CH) * 4;
             const int key = key0 + r;
@@ -463,7 +487,7 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
             }
             bool full = false;  // segment mask: the whole tile lies in this wavefront's one segment
             if constexpr (MASK == VLM_MASK_SEGMENT_ID)
-                full = segment_tile_full<BKEY>(a.seg, seg_q, qrow < S, key0, a.nkeys);
+                full = segment_tile_full<BKEY>(segs, seg_q, qrow < S, key0, a.nkeys);
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
@@ -473,7 +497,7 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                     float s = sacc[kb][r] * scale;
                     bool vis = key < a.nkeys;
                     if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
-                    if (MASK == VLM_MASK_SEGMENT_ID) vis = full || (vis && qrow < S && a.seg[key] == seg_q);
+                    if (MASK == VLM_MASK_SEGMENT_ID) vis = full || (vis && qrow < S && segs[key - key0] == seg_q);
                     if (MASK == VLM_MASK_ADDITIVE_ID && vis && qrow < S)
                         s += a.add[(size_t)qrow * a.ld_add + key] * kLog2e;
                     s = vis ? s : -INFINITY;
