@@ -104,15 +104,18 @@ __device__ int segment_tiles(const int32_t* seg, int row0, int nrows, int S, int
 }
 
 // ============================================================== prefill, bf16
-// A block covers 64 query rows of one head with 4 wavefronts: wavefronts
-// w and w+2 own the same 32 rows and take alternate 64-key tiles (a pair of
-// tiles is staged per iteration), which halves the sequential key chain of
-// the longest (last, causal) row block; their (m, l, O) merge through LDS at
-// the end.
+// A block covers 64 query rows of one head with 2 * KP wavefronts: wavefronts
+// w, w + 2, ... own the same 32 rows and take every KP-th 64-key tile (KP
+// tiles are staged per iteration), which divides the sequential key chain of
+// the longest (last, causal) row block by KP; their (m, l, O) merge through
+// LDS at the end. KP = 2 (4 wavefronts, two blocks per CU for heads up to 80
+// wide) or KP = 4 (8 wavefronts, one block per CU: used when the grid has no
+// more blocks than CUs, where two blocks per CU would leave half the wavefront
+// slots empty).
 // DQ: width of q and k rows, DV: width of v and output rows (equal except for expanded MLA).
-template <int DQ, int DV, int MASK>
-__global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnArgs a) {
-    constexpr int BQ = 64, BKEY = 64;
+template <int DQ, int DV, int MASK, int KP>
+__global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_prefill_bf16(AttnArgs a) {
+    constexpr int BQ = 64, BKEY = 64, NT = 128 * KP;
     // a q/k width that is not a multiple of 16 (72) is zero-padded to DK * 16 in the K tile and
     // the q fragments, which leaves every dot product unchanged
     constexpr int DK = (DQ + 15) / 16, NB = (DV + 31) / 32, DP = NB * 32, DQP = DK * 16;
@@ -120,10 +123,10 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
     constexpr int CH = DQ / 8, CHV = DV / 8;  // 16-byte chunks per key / value row
     constexpr int KSZ = BKEY * LDK, VSZ = DP * LDV;                 // elements of one K / V^T tile
     constexpr int MRG = NB * 16 + 2;                                // floats per lane in the final merge
-    constexpr int TILE_BYTES = 2 * (KSZ + VSZ) * 2, MRG_BYTES = 2 * 64 * MRG * 4;
+    constexpr int TILE_BYTES = KP * (KSZ + VSZ) * 2, MRG_BYTES = (KP - 1) * 2 * 64 * MRG * 4;
     __shared__ __attribute__((aligned(16))) unsigned char sm[TILE_BYTES > MRG_BYTES ? TILE_BYTES : MRG_BYTES];
-    bf16_t* const Ks = reinterpret_cast<bf16_t*>(sm);   // [2][KSZ]
-    bf16_t* const Vt = Ks + 2 * KSZ;                     // [2][VSZ]
+    bf16_t* const Ks = reinterpret_cast<bf16_t*>(sm);   // [KP][KSZ]
+    bf16_t* const Vt = Ks + KP * KSZ;                    // [KP][VSZ]
 
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, hh = lane / 32, l32 = lane % 32;
     const int rg = w & 1, kpar = w >> 1;  // row group, key-tile parity
@@ -135,15 +138,14 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
     const bf16_t* Kg = (const bf16_t*)a.k + (size_t)g * a.ldkv * DQ;
     const bf16_t* Vg = (const bf16_t*)a.v + (size_t)g * a.ldkv * DV;
 
-    for (int i = tid; i < (DP - DV) * LDV; i += 256) {
-        Vt[DV * LDV + i] = 0;
-        Vt[VSZ + DV * LDV + i] = 0;
-    }
-    if constexpr (DQP > DQ) {  // pad columns of both K tiles (the stages write columns < DQ only)
-        for (int i = tid; i < BKEY * (DQP - DQ); i += 256) {
+    for (int i = tid; i < (DP - DV) * LDV; i += NT)
+#pragma unroll
+        for (int b = 0; b < KP; b++) Vt[b * VSZ + DV * LDV + i] = 0;
+    if constexpr (DQP > DQ) {  // pad columns of every K tile (the stages write columns < DQ only)
+        for (int i = tid; i < BKEY * (DQP - DQ); i += NT) {
             const int r = i / (DQP - DQ), c = DQ + i % (DQP - DQ);
-            Ks[r * LDK + c] = 0;
-            Ks[KSZ + r * LDK + c] = 0;
+#pragma unroll
+            for (int b = 0; b < KP; b++) Ks[b * KSZ + r * LDK + c] = 0;
         }
     }
 
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
     __shared__ int tlohi[3];
     const bool listed = MASK == VLM_MASK_SEGMENT_ID && nkt <= kSegMaxTiles;
     if constexpr (MASK == VLM_MASK_SEGMENT_ID)
-        if (listed) nvis = segment_tiles<256, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
+        if (listed) nvis = segment_tiles<NT, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
     auto tile_at = [&](int i) { return listed ? (int)tlist[i] : i; };
 
     // K/V tile kt+1 is requested into registers (unconditional, key index clamped; keys past nkeys
@@ -187,22 +189,22 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
     // (coalesced 16-byte row pieces into the row-major K tile); V is fetched as key pairs so that
     // each transposed LDS store writes two keys of one dimension as a dword, 32 lanes to 32
     // consecutive dwords.
-    constexpr int TCH = (BKEY * CH + 255) / 256;        // 16-byte chunks of the K tile per thread
-    constexpr int NVP = (BKEY / 2) * CHV, VP = (NVP + 255) / 256;  // (key pair, chunk) items of the V tile
+    constexpr int TCH = (BKEY * CH + NT - 1) / NT;        // 16-byte chunks of the K tile per thread
+    constexpr int NVP = (BKEY / 2) * CHV, VP = (NVP + NT - 1) / NT;  // (key pair, chunk) items of the V tile
     // the segment ids of a tile's keys travel with its K/V: requested with them (every thread, key
     // tid % BKEY), stored to LDS by the first BKEY threads
-    __shared__ int segs[MASK == VLM_MASK_SEGMENT_ID ? 2 : 1][MASK == VLM_MASK_SEGMENT_ID ? BKEY : 1];
+    __shared__ int segs[MASK == VLM_MASK_SEGMENT_ID ? KP : 1][MASK == VLM_MASK_SEGMENT_ID ? BKEY : 1];
     auto request = [&](int kt, u32x4 (&kreg)[TCH], u32x4 (&vreg)[VP][2], int& sreg) {
         if constexpr (MASK == VLM_MASK_SEGMENT_ID) sreg = a.seg[min(kt * BKEY + tid % BKEY, a.nkeys - 1)];
 #pragma unroll
         for (int i = 0; i < TCH; i++) {
-            const int c = min(tid + 256 * i, BKEY * CH - 1), r = c / CH, d0 = (c % CH) * 8;
+            const int c = min(tid + NT * i, BKEY * CH - 1), r = c / CH, d0 = (c % CH) * 8;
             const int key = min(kt * BKEY + r, a.nkeys - 1);
             kreg[i] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * DQ + d0);
         }
 #pragma unroll
         for (int i = 0; i < VP; i++) {
-            const int pi = min(tid + 256 * i, NVP - 1), kp = pi % (BKEY / 2), d0 = (pi / (BKEY / 2)) * 8;
+            const int pi = min(tid + NT * i, NVP - 1), kp = pi % (BKEY / 2), d0 = (pi / (BKEY / 2)) * 8;
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 const int key = min(kt * BKEY + 2 * kp + u, a.nkeys - 1);
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
         bf16_t* vd = Vt + buf * VSZ;
 #pragma unroll
         for (int i = 0; i < TCH; i++) {
-            const int c = tid + 256 * i;
+            const int c = tid + NT * i;
             if (c < BKEY * CH) {
                 const int r = c / CH, d0 = (c % CH) * 8;
                 *reinterpret_cast<u32x4*>(kd + r * LDK + d0) = key0 + r < a.nkeys ? kreg[i] : u32x4{0, 0, 0, 0};
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
         }
 #pragma unroll
         for (int i = 0; i < VP; i++) {
-            const int pi = tid + 256 * i, kp = pi % (BKEY / 2), d0 = (pi / (BKEY / 2)) * 8;
+            const int pi = tid + NT * i, kp = pi % (BKEY / 2), d0 = (pi / (BKEY / 2)) * 8;
             if (pi >= NVP) break;
             const u32x4 v0 = key0 + 2 * kp < a.nkeys ? vreg[i][0] : u32x4{0, 0, 0, 0};
             const u32x4 v1 = key0 + 2 * kp + 1 < a.nkeys ? vreg[i][1] : u32x4{0, 0, 0, 0};
@@ -239,17 +241,22 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
             }
         }
     };
-    u32x4 kA[TCH], vA[VP][2], kB[TCH], vB[VP][2];
-    int sA = 0, sB = 0;
-    if (nvis > 0) request(tile_at(0), kA, vA, sA);
-    if (nvis > 1) request(tile_at(1), kB, vB, sB);
-    for (int kt2 = 0; kt2 < nvis; kt2 += 2) {
-        stage(tile_at(kt2), 0, kA, vA, sA);
-        if (kt2 + 1 < nvis) stage(tile_at(kt2 + 1), 1, kB, vB, sB);
+    u32x4 kr[KP][TCH], vr[KP][VP][2];
+    int sr[KP];
+#pragma unroll
+    for (int b = 0; b < KP; b++) {
+        sr[b] = 0;
+        if (b < nvis) request(tile_at(b), kr[b], vr[b], sr[b]);
+    }
+    for (int kt2 = 0; kt2 < nvis; kt2 += KP) {
+#pragma unroll
+        for (int b = 0; b < KP; b++)
+            if (kt2 + b < nvis) stage(tile_at(kt2 + b), b, kr[b], vr[b], sr[b]);
         __syncthreads();
-        // the next pair is in flight during this pair's MFMAs
-        if (kt2 + 2 < nvis) request(tile_at(kt2 + 2), kA, vA, sA);
-        if (kt2 + 3 < nvis) request(tile_at(kt2 + 3), kB, vB, sB);
+        // the next KP tiles are in flight during these tiles' MFMAs
+#pragma unroll
+        for (int b = 0; b < KP; b++)
+            if (kt2 + KP + b < nvis) request(tile_at(kt2 + KP + b), kr[b], vr[b], sr[b]);
         const int kv = kt2 + kpar;  // position in the visit order
         const int key0 = (kv < nvis ? tile_at(kv) : 0) * BKEY;
         const bf16_t* const Kw = Ks + kpar * KSZ;
@@ -365,9 +372,10 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
         }
         __syncthreads();
     }
-    // merge the two key-parity halves of each row group: wavefronts 2, 3 hand (m, l, O) to 0, 1
-    float* mb = reinterpret_cast<float*>(sm) + (size_t)(rg * 64 + lane) * MRG;
-    if (kpar == 1) {
+    // merge the KP key parities of each row group: wavefronts 2, 3, ... hand (m, l, O) to 0, 1
+    float* const mbase = reinterpret_cast<float*>(sm);
+    if (kpar > 0) {
+        float* mb = mbase + (size_t)(((kpar - 1) * 2 + rg) * 64 + lane) * MRG;
         mb[0] = m;
         mb[1] = l;
 #pragma unroll
@@ -376,8 +384,10 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
             for (int r = 0; r < 16; r++) mb[2 + nb * 16 + r] = oacc[nb][r];
     }
     __syncthreads();
-    if (kpar == 1) return;
-    {
+    if (kpar > 0) return;
+#pragma unroll
+    for (int pp = 1; pp < KP; pp++) {
+        const float* mb = mbase + (size_t)(((pp - 1) * 2 + rg) * 64 + lane) * MRG;
         const float m2 = mb[0], l2 = mb[1];
         const float mn = fmaxf(m, m2);
         const float fa = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
@@ -387,6 +397,7 @@ __global__ __launch_bounds__(256, DQ <= 80 ? 2 : 1) void attn_prefill_bf16(AttnA
         for (int nb = 0; nb < NB; nb++)
 #pragma unroll
             for (int r = 0; r < 16; r++) oacc[nb][r] = oacc[nb][r] * fa + mb[2 + nb * 16 + r] * fb;
+        m = mn;
     }
     if (qrow < S) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -556,12 +567,27 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     }
 }
 
+static int attn_cus() {
+    static const int v = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        return n;
+    }();
+    return v;
+}
+
 template <int DQ, int DV, int MASK>
 static hipError_t run_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.S + 127) / 128, a.nq);
     if (dtype == 1) {
         if constexpr (DQ % 8 == 0 && DV % 8 == 0) {
-            attn_prefill_bf16<DQ, DV, MASK><<<dim3((a.S + 63) / 64, a.nq), 256, 0, st>>>(a);
+            const dim3 g64((a.S + 63) / 64, a.nq);
+            bool kp4 = false;  // one block per CU anyway: 8 wavefronts, 4 key parities (LDS: heads up to 128)
+            if constexpr (DQ <= 128) kp4 = (int)(g64.x * g64.y) <= attn_cus();
+            if constexpr (DQ <= 128)
+                if (kp4) attn_prefill_bf16<DQ, DV, MASK, 4><<<g64, 512, 0, st>>>(a);
+            if (!kp4) attn_prefill_bf16<DQ, DV, MASK, 2><<<g64, 256, 0, st>>>(a);
         } else {
             return hipErrorInvalidValue;
         }
