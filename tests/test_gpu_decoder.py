@@ -93,6 +93,34 @@ def test_c1_eager_steps_equal_graph_loop(rt):
         assert np.array_equal(ka[:, :T], kb[:, :T]) and np.array_equal(va[:, :T], vb[:, :T])
 
 
+def test_graph_replays_between_eager_work_equal_eager_steps(rt):
+    """bf16 4B-class layer shape: graph-loop calls of 4, 4 and 6 steps with eager decode steps, a cache
+    status read and unrelated eager GPU work (a torch reduction over another buffer, synchronized)
+    between the replays give bitwise the ids and cache slots of 16 eager steps."""
+    pipeline, _ = rt
+    cfg = vs.scaled(vs.C4, n_layers=2, vocab=4096, seq=40, n_img=8, img_start=8, decode_steps=16, capacity=128,
+                    name="c4_2layer_replays")
+    glob, layers = make(cfg)
+    a = gpu_run(pipeline, cfg, glob, layers)
+    a.prefill()
+    ids_a = [int(a.first_token()[0])]
+    scratch = torch.randn(1 << 20, device="cuda")
+    for n, loop in ((4, True), (2, False), (4, True), (0, False), (6, True)):
+        ids_a += [int(i) for i in a.decode(n, loop=loop)]
+        a.kv.status()
+        assert torch.isfinite(scratch.sum()).item()   # eager work on the same device between the replays
+        torch.cuda.synchronize()
+    b = gpu_run(pipeline, cfg, glob, layers)
+    b.prefill()
+    ids_b = [int(b.first_token()[0])] + [int(i) for i in b.decode(cfg.decode_steps, loop=False)]
+    assert ids_a == ids_b
+    T = cfg.seq + cfg.decode_steps
+    for l in range(cfg.n_layers):
+        ka, va = kv_host(a, l)
+        kb, vb = kv_host(b, l)
+        assert np.array_equal(ka[:, :T], kb[:, :T]) and np.array_equal(va[:, :T], vb[:, :T])
+
+
 def test_embed_inject_bit_exact(rt):
     pipeline, _ = rt
     cfg = vs.C1
