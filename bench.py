@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--vit-dtype", default="f32", choices=("f32", "bf16"),
                     help="storage type of the vision tower (c5_vit_27l only)")
+    ap.add_argument("--next-rows", action="store_true",
+                    help="time the widened rows instead of the step: the verify head and a block verify against "
+                         "one-token decode, the sampler and the sampled graph loop, the expanded-MLA stack, and "
+                         "the vision tower feeding the decoder prefill; prints one JSON line and exits")
     ap.add_argument("--traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --kernel-only run "
                          "into profiles/traffic.json and exit")
@@ -363,6 +367,127 @@ def vit_main(args, cfg):
     print(json.dumps(out))
 
 
+def next_rows_main(args):
+    """Measurement of the widened rows on the 36-layer stack (HIP events on torch's current stream, the
+    stream every call runs on): verify head (one pass over the lm_head table for a block of rows),
+    block verify (chunked prefill of the block + verify head + commit) against the same number of
+    one-token decode steps, the sampler on one logits row and the sampled graph loop against the
+    greedy loop, the expanded-MLA stack (prefill and decode step), and the vision tower whose merged
+    rows feed the decoder prefill."""
+    import numpy as np
+    import torch
+
+    import vlm_synth as vs
+    from decoder_prefill_decode_amd import native as N
+    from decoder_prefill_decode_amd.pipeline import DecoderRun, VitRun
+    from decoder_prefill_decode_amd.runtime import decode_loop_sampled, sample_logits
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us per call
+
+    out = {"mode": "next_rows", "n_gpus": 1, "data": "synthetic"}
+    cfg = vs.ALL_CONFIGS["c4_llama_4b"]
+    glob = vs.decoder_globals(cfg)
+    run = DecoderRun(cfg, lambda l: vs.decoder_layer_weights(cfg, l), glob)
+    E, V, H, K = 2, cfg.vocab, cfg.hidden, 8
+    run.prefill()
+    run.first_token(check=False)
+    ids = [int(run.tok[0])] + [int(t) for t in run.decode(K)]      # a greedy block to draft from
+    # verify head alone: K rows, one pass over the table
+    rows = run.x[:K].clone()
+    pred = torch.empty(K, dtype=torch.int32, device="cuda")
+    logits = torch.empty((K, V), dtype=torch.float32, device="cuda")
+    us = timed(lambda: run.model.lmhead_argmax_rows(rows, pred, run.ws, logits), 20)
+    b = V * H * E + K * V * 4 + K * H * 4
+    out["verify_head"] = {"rows": K, "us": round(us, 2), "bytes": b, "gbs": round(b / us * 1e-3, 1),
+                          "hbm_frac": round(b / us * 1e-3 / PEAK_HBM_GBS, 4)}
+    # block verify of K drafted tokens (all accepted) against K one-token decode steps from the same length
+    L0 = cfg.seq
+    def verify():
+        run.kv.truncate(L0)
+        run.verify_block(ids[:K])
+    def one_token():
+        run.kv.truncate(L0)
+        run.tok.fill_(ids[0])
+        run.decode(K)
+    vu, du = timed(verify, 5), timed(one_token, 5)
+    out["block_verify"] = {"block": K, "verify_us": round(vu, 1), "decode_steps_us": round(du, 1),
+                           "speedup": round(du / vu, 2)}
+    # sampler on one logits row, context = the prompt ids
+    lg = logits[0].contiguous()
+    ctx = run.ids_dev
+    u = torch.full((1,), 0.37, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    su = timed(lambda: sample_logits(lg, 0.8, 50, 0.9, 1.1, ctx, u, tok), 50)
+    out["sampler"] = {"vocab": V, "top_k": 50, "top_p": 0.9, "context": int(ctx.numel()), "us": round(su, 2)}
+    n = 64
+    hist = torch.full((cfg.capacity + 1,), -2, dtype=torch.int32, device="cuda")
+    hist[:L0].copy_(ctx)
+    ud = torch.from_numpy(np.random.default_rng(7).random(cfg.capacity + 1).astype(np.float32)).to("cuda")
+    prm = N.Sampling(0.8, 50, 0.9, 1.1)
+    def greedy():
+        run.kv.truncate(L0)
+        run.tok.fill_(ids[0])
+        run.decode(n)
+    def sampled():  # fixed buffers: the captured graphs are reused from call to call
+        run.kv.truncate(L0)
+        run.tok.fill_(ids[0])
+        hist[L0:L0 + 1].fill_(ids[0])
+        decode_loop_sampled(run.model, run.kv, run.cos, run.sin, run.ws, run.tok, n, hist, prm, ud)
+        run.kv.status()
+    gu, smu = timed(greedy, 3), timed(sampled, 3)
+    out["sampled_loop"] = {"steps": n, "greedy_tok_s": round(n / (gu * 1e-6), 1),
+                           "sampled_tok_s": round(n / (smu * 1e-6), 1), "sampled_us_per_token_extra":
+                           round((smu - gu) / n, 2)}
+    del run, logits, rows
+    torch.cuda.empty_cache()
+    # expanded MLA stack (the layer shape the parity tests cover), bf16
+    mcfg = vs.scaled(vs.C_MLA, dtype=vs.BF16, name="c_mla_small_bf16")
+    mglob = vs.decoder_globals(mcfg)
+    mrun = DecoderRun(mcfg, lambda l: vs.decoder_layer_weights(mcfg, l), mglob)
+    def mla_prefill():
+        mrun.reset()
+        mrun.prefill()
+    pu = timed(mla_prefill, 10)
+    mrun.reset()
+    mrun.prefill()
+    mrun.first_token(check=False)
+    def mla_decode():
+        mrun.kv.truncate(mcfg.seq)
+        mrun.tok.fill_(1)
+        mrun.decode(mcfg.decode_steps)
+    mu = timed(mla_decode, 5)
+    out["mla_stack"] = {"config": f"{mcfg.n_layers} layers, hidden {mcfg.hidden}, {mcfg.n_q_heads} heads, "
+                                  f"K {mcfg.head_dim} / V {mcfg.v_head_dim}, latent {mcfg.kv_lora_rank}, bf16",
+                        "prefill_rows": mcfg.seq, "prefill_us": round(pu, 1),
+                        "decode_us_per_token": round(mu / mcfg.decode_steps, 1)}
+    del mrun
+    torch.cuda.empty_cache()
+    # vision tower (bf16 storage) -> 36-layer decoder prefill with its merged rows injected
+    vcfg = vs.scaled_vit(vs.C5, dtype=vs.BF16, name="c5_vit_27l_bf16")
+    vglob = vs.vit_globals(vcfg)
+    vrun = VitRun(vcfg, lambda l: vs.vit_layer_weights(vcfg, l), vglob)
+    drun = DecoderRun(cfg, lambda l: vs.decoder_layer_weights(cfg, l), glob)
+    def chain():
+        drun.img = vrun.run()
+        drun.reset()
+        drun.prefill()
+        drun.first_token(check=False)
+    tower = timed(lambda: vrun.run(), 5)
+    cu = timed(chain, 5)
+    out["vision_to_decoder"] = {"tower_ms": round(tower * 1e-3, 3), "tower_plus_prefill_ms": round(cu * 1e-3, 3),
+                                "image_rows": cfg.n_img, "prompt_rows": cfg.seq}
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.traffic:
@@ -382,6 +507,9 @@ def main():
     from decoder_prefill_decode_amd.pipeline import DecoderRun
     from decoder_prefill_decode_amd.runtime import causal_mask as pipeline_causal
 
+    if args.next_rows:
+        next_rows_main(args)
+        return
     cfg = vs.ALL_CONFIGS[args.config]
     if isinstance(cfg, vs.VitConfig):
         vit_main(args, cfg)

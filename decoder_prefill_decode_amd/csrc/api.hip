@@ -646,11 +646,13 @@ vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_fina
     Ws w;
     if ((s = check_ws(desc, S, d_ws, ws_bytes, &w))) return s;
     float* logits = d_logits;
-    if (!logits) {
-        if ((size_t)S * desc->vocab > w.gpart_floats)
-            return fail(VLM_ERR_WORKSPACE, "%d rows x vocab %d logits exceed the workspace scratch; pass d_logits",
-                        S, desc->vocab);
-        logits = (float*)P(d_ws, w.gpart);
+    if (!logits) {  // right after the S normalised rows (the only other region this call uses)
+        const size_t off = w.h + al256((size_t)S * desc->hidden * esize(desc->dtype));
+        const size_t need = off + (size_t)S * desc->vocab * 4;
+        if (need > ws_bytes)
+            return fail(VLM_ERR_WORKSPACE, "%d rows x vocab %d logits need %zu workspace bytes, got %zu; pass d_logits",
+                        S, desc->vocab, need, ws_bytes);
+        logits = (float*)P(d_ws, off);
     }
     if (S == 0) return ok();
     const int dt = desc->dtype, H = desc->hidden;

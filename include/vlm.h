@@ -303,9 +303,10 @@ vlm_status vlm_lmhead_argmax_noalloc(const vlm_model_desc* desc, const void* d_f
  * final RMSNorm of each row, logits against the [V][H] table in one pass over
  * the table (an MFMA GEMM), then d_tokens_out[r] = argmax of row r (lowest
  * index on ties; -1 for a non-finite row). d_logits [S][V] fp32 receives the
- * logits when non-NULL; with NULL they live in the workspace, which must then
- * hold S * V floats of split scratch (else VLM_ERR_WORKSPACE; the workspace of
- * vlm_workspace_bytes(desc, max_rows >= S) is also required for the rows). */
+ * logits when non-NULL; with NULL they live in the workspace after the S
+ * normalised rows, which then needs 256-aligned S * H * dtype-size bytes plus
+ * S * V * 4 bytes (else VLM_ERR_WORKSPACE, nothing enqueued); the workspace of
+ * vlm_workspace_bytes(desc, max_rows >= S) is required in any case. */
 vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
                                   const float* d_x, int32_t S, int32_t* d_tokens_out, float* d_logits, void* d_ws,
                                   size_t ws_bytes, hipStream_t stream);

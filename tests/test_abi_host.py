@@ -190,6 +190,21 @@ def test_verify_commit_and_status_argument_checks():
         N.VLM_ERR_SHAPE
 
 
+def test_verify_head_logits_scratch_is_checked_against_the_workspace_bytes():
+    """With no logits buffer the verify head keeps S x V fp32 logits in the workspace, after the S
+    normalised rows, and checks that against the caller's workspace size (a vocabulary of 128256
+    does not fit the S-row layout's own split scratch)."""
+    d = desc(vocab=128256)
+    n = C.c_size_t()
+    N.call("vlm_workspace_bytes", C.byref(d), 8, C.byref(n))
+    need = 8 * 256 * 4 + 8 * 128256 * 4          # rows (already 256-aligned) + logits
+    assert n.value < need
+    fake = C.c_void_p(256)
+    tok = C.c_void_p(512)
+    st = N.lib().vlm_lmhead_argmax_rows(C.byref(d), fake, fake, fake, 8, tok, None, fake, n.value, None)
+    assert st == N.VLM_ERR_WORKSPACE and str(need) in N.last_error()
+
+
 def test_host_split_plan_mirror_matches_library():
     """decoder_prefill_decode_amd.csrc_info.decode_plan (the bench's byte accounting) equals the
     library's planner at every band of the 36-layer stack's window and of a long tiny one."""

@@ -88,3 +88,26 @@ def test_draft_accept_commit_reproduces_greedy_decode(env, k, wrong):
         kb, vb = (t[:, :T].cpu().numpy() for t in sp.kv.kv(l))
         assert rel(kb, ka) <= 1e-4 and rel(vb, va) <= 1e-4
     print(f"block {k}: {N + 1} greedy ids reproduced in {blocks} verify passes")
+
+
+def test_verify_head_without_logits_buffer_beyond_the_split_scratch():
+    """The verify head with its logits in the workspace, for a vocabulary wider than four times every row
+    width of the stack (16384 > 4 x 1536 on the tiny stack): picks equal the argmax of the oracle's block
+    logits, row for row."""
+    from decoder_prefill_decode_amd import pipeline
+    cfg = vs.scaled(vs.C1, vocab=16384, decode_steps=8, name="c1_vocab16k")
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    block = [int(i) for i in np.random.default_rng(3).integers(0, cfg.vocab - 1, size=8)]
+    want = [int(np.argmax(r)) for r in od.block_logits(cfg, glob, layers, block)]
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.prefill()
+    pos0 = run.kv.len()
+    ids = torch.tensor(block, dtype=torch.int32, device="cuda")
+    xb = torch.empty((len(block), cfg.hidden), dtype=torch.float32, device="cuda")
+    run.model.embed_ids(ids, xb)
+    run.model.prefill(xb, pos0, run.cos, run.sin, pipeline.causal_mask(), run.kv, run.ws)
+    pred = torch.empty(len(block), dtype=torch.int32, device="cuda")
+    run.model.lmhead_argmax_rows(xb, pred, run.ws)      # no logits buffer
+    assert [int(p) for p in pred.cpu()] == want
+
