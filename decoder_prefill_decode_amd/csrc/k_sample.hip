@@ -3,13 +3,18 @@
 // uniform number (MNN llm_demo Omni article §4.1; HunyuanOCR v1.5 ncnn port
 // §3.6 for the generation options).
 //
-// One block of 1024 threads; the vocabulary streams from L2 a few times:
+// One block of 1024 threads; the vocabulary streams from L2 two to four times:
 //  1. the context ids become a bitmap in LDS (membership in one read);
-//  2. the k-th largest processed value is found by a 4-pass radix select on
-//     order-preserving 32-bit keys (LDS histograms of 256 bins);
-//  3. the values >= that one (ties kept) are gathered into LDS, sorted by
-//     (value descending, id ascending) with a bitonic sort;
-//  4. softmax over the sorted candidates, a block scan gives the cumulative
+//  2. radix select on order-preserving 32-bit keys with 11-, 11- and 10-bit
+//     digits (LDS histograms of 2048 bins, a parallel suffix scan finds the
+//     bin holding the k-th largest): as soon as every value at or above that
+//     bin's lower bound fits the 2048 candidate slots they are gathered (one
+//     or two histogram passes for ordinary logits), else the next digit is
+//     resolved. (One 8-bit top digit would put nearly every logit in one or
+//     two bins, and their LDS atomics would serialise on one address.)
+//  3. the candidates are sorted by (value descending, id ascending) with a
+//     bitonic sort; those at or above the k-th value are kept (ties kept);
+//  4. softmax over the kept candidates, a block scan gives the cumulative
 //     sums: top-p keeps the prefix whose preceding mass is below top_p * Z,
 //     and the draw takes the first kept token whose cumulative sum exceeds
 //     u times the kept mass.
@@ -24,6 +29,8 @@ namespace vlm {
 
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleCand = 2 * kSampleMaxK;  // candidate slots (ties at the k-th value included)
+constexpr int kSampleBins = 2048;             // histogram bins of an 11-bit digit
+constexpr int kSampleBatch = 8;               // logits each thread requests together
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
     const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -52,12 +59,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
                                                                        const float* __restrict__ uptr,
                                                                        int32_t* __restrict__ out, int32_t* kv_len) {
     __shared__ uint32_t bits[kSampleVocabMax / 32];
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[kSampleBins];
     __shared__ uint32_t ckey[kSampleCand];
     __shared__ int32_t cidx[kSampleCand];
     __shared__ float cval[kSampleCand];
     __shared__ float red[kSampleThreads / kWave];
-    __shared__ uint32_t s_prefix, s_krem, s_count, s_bad;
+    __shared__ uint32_t redu[kSampleThreads / kWave];
+    __shared__ uint32_t s_prefix, s_krem, s_count, s_bad, s_bin, s_above, s_inbin;
     const int tid = threadIdx.x;
     const int nw = (V + 31) / 32;
     if (kv_len) {  // decode-step form: context and draw follow the device length
@@ -79,65 +87,106 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
     }
     __syncthreads();
     const float inv_t = 1.0f / sp.temperature, r = sp.penalty;
-    auto value = [&](int i) -> float {
-        float x = logits[i];
-        if ((bits[i >> 5] >> (i & 31)) & 1u) x = x > 0.f ? x / r : x * r;
-        return x * inv_t;
-    };
 
-    // (2) radix select of the k-th largest key, most significant byte first
-    uint32_t mask = 0u;
-    for (int pass = 0; pass < 4; pass++) {
-        const int shift = 24 - 8 * pass;
-        for (int b = tid; b < 256; b += kSampleThreads) hist[b] = 0u;
+    // (2) radix select: digits of 11, 11 and 10 bits, most significant first. The prefix of the
+    // resolved digits is `prefix` under `mask`; `above` values lie strictly above the prefix bin.
+    const uint32_t need0 = s_krem;
+    uint32_t prefix = 0u, mask = 0u, above = 0u, lower = 0u;
+    bool gathered = false;
+    for (int pass = 0; pass < 3 && !gathered; pass++) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+        for (int b = tid; b < kSampleBins; b += kSampleThreads) hist[b] = 0u;
         __syncthreads();
-        const uint32_t prefix = s_prefix;
-        for (int i = tid; i < V; i += kSampleThreads) {
-            const float x = value(i);
-            if (pass == 0 && !isfinite(x)) s_bad = 1u;
-            const uint32_t k = ordered_key(x);
-            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t need = s_krem, cum = 0u;
-            int b = 255;
-            for (; b > 0; b--) {
-                if (cum + hist[b] >= need) break;
-                cum += hist[b];
+        // values in batches of kSampleBatch per thread, requested together (indices clamped)
+        for (int i0 = tid; i0 < V; i0 += kSampleThreads * kSampleBatch) {
+            float xv[kSampleBatch];
+#pragma unroll
+            for (int u = 0; u < kSampleBatch; u++) xv[u] = logits[min(i0 + u * kSampleThreads, V - 1)];
+#pragma unroll
+            for (int u = 0; u < kSampleBatch; u++) {
+                const int i = i0 + u * kSampleThreads;
+                if (i >= V) break;
+                float x = xv[u];
+                if ((bits[i >> 5] >> (i & 31)) & 1u) x = x > 0.f ? x / r : x * r;
+                x *= inv_t;
+                if (pass == 0 && !isfinite(x)) s_bad = 1u;
+                const uint32_t k = ordered_key(x);
+                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
             }
-            s_krem = need - cum;
-            s_prefix = prefix | ((uint32_t)b << shift);
         }
-        mask |= 255u << shift;
+        __syncthreads();
+        // suffix scan over the bins (highest first): thread t holds bins top - 2t and top - 2t - 1
+        const uint32_t need = need0 - above;
+        const int top = (int)dmask;
+        const int j0 = top - 2 * tid, j1 = j0 - 1;
+        const uint32_t c0 = j0 >= 0 ? hist[j0] : 0u, c1 = j1 >= 0 ? hist[j1] : 0u;
+        const uint32_t pair = c0 + c1;
+        const int lane = tid % kWave, w = tid / kWave;
+        uint32_t sc = pair;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t o = __shfl_up(sc, off, kWave);
+            if (lane >= off) sc += o;
+        }
+        if (lane == kWave - 1) redu[w] = sc;
+        __syncthreads();
+        uint32_t base = 0u;
+        for (int q = 0; q < w; q++) base += redu[q];
+        const uint32_t excl = base + sc - pair;
+        if (j0 >= 0 && excl < need && need <= excl + c0) {
+            s_bin = (uint32_t)j0;
+            s_above = excl;
+            s_inbin = c0;
+        } else if (j1 >= 0 && excl + c0 < need && need <= excl + pair) {
+            s_bin = (uint32_t)j1;
+            s_above = excl + c0;
+            s_inbin = c1;
+        }
+        __syncthreads();
+        if (s_bad) break;
+        prefix |= s_bin << shift;
+        mask |= dmask << shift;
+        above += s_above;
+        lower = prefix;  // keys >= lower: every value above the prefix bin and the bin itself
+        gathered = above + s_inbin <= (uint32_t)kSampleCand || pass == 2;
         __syncthreads();
     }
     if (s_bad) {  // a non-finite logit: no token (the argmax path reports it the same way)
         if (tid == 0) sample_commit(-1, out, ctx, kv_len);
         return;
     }
-    const uint32_t kth = s_prefix;
 
-    // (3) gather the values >= the k-th one, then sort by (value desc, id asc)
-    for (int i = tid; i < V; i += kSampleThreads) {
-        const uint32_t k = ordered_key(value(i));
-        if (k >= kth) {
-            const uint32_t slot = atomicAdd(&s_count, 1u);
-            if (slot < (uint32_t)kSampleCand) {
-                ckey[slot] = k;
-                cidx[slot] = i;
+    // (3) gather the values with key >= lower (the k-th largest is among them), sort by (value desc,
+    // id asc), keep those >= the k-th value (ties kept)
+    for (int i0 = tid; i0 < V; i0 += kSampleThreads * kSampleBatch) {
+        float xv[kSampleBatch];
+#pragma unroll
+        for (int u = 0; u < kSampleBatch; u++) xv[u] = logits[min(i0 + u * kSampleThreads, V - 1)];
+#pragma unroll
+        for (int u = 0; u < kSampleBatch; u++) {
+            const int i = i0 + u * kSampleThreads;
+            if (i >= V) break;
+            float x = xv[u];
+            if ((bits[i >> 5] >> (i & 31)) & 1u) x = x > 0.f ? x / r : x * r;
+            const uint32_t k = ordered_key(x * inv_t);
+            if (k >= lower) {
+                const uint32_t slot = atomicAdd(&s_count, 1u);
+                if (slot < (uint32_t)kSampleCand) {
+                    ckey[slot] = k;
+                    cidx[slot] = i;
+                }
             }
         }
     }
     __syncthreads();
-    const int n = (int)s_count;
-    if (n > kSampleCand) {  // more ties at the k-th value than slots
+    const int ngath = (int)s_count;
+    if (ngath > kSampleCand) {  // more ties at the k-th value than slots
         if (tid == 0) sample_commit(-1, out, ctx, kv_len);
         return;
     }
     int np2 = 1;
-    while (np2 < n) np2 <<= 1;
-    for (int i = n + tid; i < np2; i += kSampleThreads) {
+    while (np2 < ngath) np2 <<= 1;
+    for (int i = ngath + tid; i < np2; i += kSampleThreads) {
         ckey[i] = 0u;
         cidx[i] = 0x7fffffff;
     }
@@ -161,6 +210,14 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
             __syncthreads();
         }
     }
+    // the k-th largest key is ckey[need0 - 1]; the kept candidates are the prefix of keys >= it
+    const uint32_t kth = ckey[need0 - 1];
+    if (tid == 0) s_count = (uint32_t)ngath;
+    __syncthreads();
+    for (int i = tid; i < ngath; i += kSampleThreads)
+        if (ckey[i] < kth) atomicMin(&s_count, (uint32_t)i);
+    __syncthreads();
+    const int n = (int)s_count;
 
     // (4) softmax over the sorted candidates; inclusive scan of the weights
     const float m = key_to_float(ckey[0]);
