@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libvlm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "k_misc.hip", "k_gemm.hip", "k_gemv.hip", "k_attn.hip", "k_sample.hip"]
+SOURCES = ["api.hip", "k_misc.hip", "k_gemm.hip", "k_gemv.hip", "k_attn.hip", "k_sample.hip", "k_gemm_small.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions stay off: the compiler would otherwise form

@@ -119,6 +119,15 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(b.lo, b.hi);
 }
 
+// LDS destination of global_load_lds (direct global-to-LDS loads).
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int V>
+__device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(V), other counters untouched (gfx9 encoding)
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+
 // Block-wide sum for blockDim.x == NT (multiple of 64); `red` holds NT/64 floats.
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {

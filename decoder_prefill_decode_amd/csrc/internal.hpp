@@ -42,6 +42,14 @@ struct GemmArgs {
 
 // dtype: 0 = f32, 1 = bf16 (vlm_dtype values)
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t st);
+// bf16 projections of M <= 16 rows (StoreF32, Resid, SwiGLU; no bias or row map, K % 8 == 0):
+// a weight stream reusing each load for every row; launch_gemm takes it whenever
+// gemm_small_fits() (a residual or a split projection needs a.part for its fp32 partials).
+bool gemm_small_fits(int dtype, Epi epi, const GemmArgs& a);
+hipError_t launch_gemm_small(Epi epi, const GemmArgs& a, hipStream_t st);
+// The split-K reduction of a bf16 GEMM whose fp32 partials [splits][M][N] are in a.part (Resid with
+// a.norm_out also writes the row norm when it fits, as the prefill GEMM's reduction does).
+hipError_t launch_split_reduce(Epi epi, const GemmArgs& a, int splits, hipStream_t st);
 
 // Operand of a decode projection: RMSNorm of fp32 x, or a plain model-type vector (PlainLds: the
 // same operand, staged once per block in LDS; chosen inside launch_gemv for long rows).

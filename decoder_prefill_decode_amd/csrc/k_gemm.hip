@@ -247,13 +247,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 // when K is not a multiple of BK, the last stage's loads past K are clamped to
 // the row's last chunk and those columns are zeroed in LDS (A and B rows)
 // before any wavefront reads the stage.
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int V>
-__device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(V), other counters untouched (gfx9 encoding)
-    static_assert(V >= 0 && V < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
-}
 __device__ __forceinline__ void wait_lgkm0() {  // s_waitcnt lgkmcnt(0), other counters untouched
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
@@ -701,8 +694,19 @@ static hipError_t dispatch_epi(Epi epi, const GemmArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_split_reduce(Epi epi, const GemmArgs& a, int splits, hipStream_t st) {
+    switch (epi) {
+        case Epi::StoreF32: return run_reduce<bf16_t, Epi::StoreF32>(a, splits, st);
+        case Epi::Resid: return run_reduce<bf16_t, Epi::Resid>(a, splits, st);
+        case Epi::SwiGLU: return run_reduce<bf16_t, Epi::SwiGLU>(a, splits, st);
+        default: break;
+    }
+    return hipErrorNotSupported;
+}
+
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t st) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    if (gemm_small_fits(dtype, epi, a)) return launch_gemm_small(epi, a, st);
     return dtype == 1 ? dispatch_epi<bf16_t>(epi, a, st) : dispatch_epi<float>(epi, a, st);
 }
 

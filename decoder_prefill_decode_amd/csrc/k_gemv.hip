@@ -574,28 +574,64 @@ __global__ __launch_bounds__(1024) void argmax_final_kernel(const unsigned long 
 
 // Row-wise argmax of a logits matrix (the multi-token verify head): block r
 // scans row r with the same u64 keys (largest logit, lowest index; -1 when the
-// row holds a non-finite value).
+// row holds a non-finite value). Each thread requests U 16-byte chunks of the
+// row (indices clamped) before it compares any of them, so a 128256-entry row
+// takes four memory round trips instead of one per element.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+    return isfinite(v) ? (((unsigned long long)ordered_key(v)) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n)
+                       : ~0ull;
+}
+
 __global__ __launch_bounds__(1024) void argmax_rows_kernel(const float* __restrict__ logits, int V, int ld,
                                                            int32_t* __restrict__ out) {
-    __shared__ unsigned long long sm[1024 / kWave];
+    constexpr int U = 8, NT = 1024;
+    __shared__ unsigned long long sm[NT / kWave];
     const float* row = logits + (size_t)blockIdx.x * ld;
+    const int tid = threadIdx.x;
     unsigned long long best = 0ull;
-    for (int n = threadIdx.x; n < V; n += 1024) {
-        const float v = row[n];
-        const unsigned long long key = isfinite(v)
-            ? (((unsigned long long)ordered_key(v)) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n)
-            : ~0ull;
-        best = key > best ? key : best;
+    int tail = 0;  // first element the scalar loop covers
+    if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+        const int nv = V / 4;
+        for (int c0 = 0; c0 < nv; c0 += NT * U) {
+            f32x4 r[U];
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                r[u] = *reinterpret_cast<const f32x4*>(row + 4 * (size_t)min(c0 + tid + NT * u, nv - 1));
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int c = c0 + tid + NT * u;
+                if (c < nv)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const unsigned long long key = argmax_key(r[u][e], 4 * c + e);
+                        best = key > best ? key : best;
+                    }
+            }
+        }
+        tail = 4 * nv;
+    }
+    for (int n0 = tail; n0 < V; n0 += NT * U) {
+        float r[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) r[u] = row[min(n0 + tid + NT * u, V - 1)];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int n = n0 + tid + NT * u;
+            if (n < V) {
+                const unsigned long long key = argmax_key(r[u], n);
+                best = key > best ? key : best;
+            }
+        }
     }
     for (int off = kWave / 2; off > 0; off >>= 1) {
         const unsigned long long o = __shfl_xor(best, off);
         best = o > best ? o : best;
     }
-    if (threadIdx.x % kWave == 0) sm[threadIdx.x / kWave] = best;
+    if (tid % kWave == 0) sm[tid / kWave] = best;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         unsigned long long b = sm[0];
-        for (int i = 1; i < 1024 / kWave; i++) b = sm[i] > b ? sm[i] : b;
+        for (int i = 1; i < NT / kWave; i++) b = sm[i] > b ? sm[i] : b;
         out[blockIdx.x] = b == ~0ull ? -1 : (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
     }
 }

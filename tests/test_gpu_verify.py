@@ -111,3 +111,67 @@ def test_verify_head_without_logits_buffer_beyond_the_split_scratch():
     run.model.lmhead_argmax_rows(xb, pred, run.ws)      # no logits buffer
     assert [int(p) for p in pred.cpu()] == want
 
+
+
+# ------------------------------------------------------------- bf16: projections of a few rows
+BF16_CHUNKS = [
+    vs.scaled(vs.C4, n_layers=2, vocab=4096, seq=60, n_img=20, img_start=8, decode_steps=0, capacity=96,
+              name="c4_2layer_bf16_chunks"),
+    vs.scaled(vs.C3, n_layers=2, vocab=4096, seq=60, n_img=20, img_start=8, decode_steps=0, capacity=96,
+              name="c3_2layer_bf16_chunks"),
+]
+
+
+@pytest.mark.parametrize("cfg", BF16_CHUNKS, ids=lambda c: c.name)
+def test_few_row_chunks_bf16_match_oracle(cfg):
+    """bf16 chunked prefill in blocks of 1, 7 and 16 rows after a 36-row prefill (the blocks take the
+    few-row projections: K split over 4, 8 and 16 wavefronts across the two layer shapes): hidden rows
+    and both layers' K/V against the oracle's one-shot prefill within the 2e-2 bf16 gate."""
+    from decoder_prefill_decode_amd import pipeline
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    ref = od.run_decoder(cfg, glob, layers, steps=0)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.embed_inject()
+    for p0, s in ((0, 36), (36, 1), (37, 7), (44, 16)):
+        run.model.prefill(run.x[p0:p0 + s], p0, run.cos, run.sin, [pipeline.causal_mask()], run.kv, run.ws)
+    assert run.kv.len() == cfg.seq
+    x = run.x.cpu().numpy()
+    assert rel(x[36:], ref["prefill_x"][36:]) <= 2e-2
+    assert rel(x, ref["prefill_x"]) <= 2e-2
+    for l in range(cfg.n_layers):
+        k, v = (t[:, :cfg.seq].float().cpu().numpy() for t in run.kv.kv(l))
+        assert rel(k, ref["k_cache"][l][:, :cfg.seq]) <= 2e-2
+        assert rel(v, ref["v_cache"][l][:, :cfg.seq]) <= 2e-2
+
+
+def test_verify_head_bf16_matches_causal_forward():
+    """bf16 4B-class shape: an 8-row verify block (few-row projections and the few-row lm_head) against
+    the oracle's causal forward over prompt + block: logits within 2e-2, and every row whose top-2
+    margin exceeds the oracle's own noise floor (float32 instead of exact sums) picks the oracle's id."""
+    from decoder_prefill_decode_amd import pipeline
+    cfg = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=60, n_img=20, img_start=8, decode_steps=8, capacity=96,
+                    name="c4_2layer_bf16_verify")
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    block = [int(i) for i in np.random.default_rng(5).integers(0, cfg.vocab - 1, size=8)]
+    want = od.block_logits(cfg, glob, layers, block)
+    floor = float(np.abs(want - od.block_logits(cfg, glob, layers, block, prec=od.BF16_F32SUM)).max())
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.prefill()
+    pos0 = run.kv.len()
+    ids = torch.tensor(block, dtype=torch.int32, device="cuda")
+    xb = torch.empty((len(block), cfg.hidden), dtype=torch.float32, device="cuda")
+    run.model.embed_ids(ids, xb)
+    run.model.prefill(xb, pos0, run.cos, run.sin, pipeline.causal_mask(), run.kv, run.ws)
+    pred = torch.empty(len(block), dtype=torch.int32, device="cuda")
+    logits = torch.empty((len(block), cfg.vocab), dtype=torch.float32, device="cuda")
+    run.model.lmhead_argmax_rows(xb, pred, run.ws, logits)
+    lg = logits.cpu().numpy()
+    assert rel(lg, want) <= 2e-2
+    top2 = np.sort(want, axis=1)[:, -2:]
+    decided = [i for i in range(len(block)) if top2[i, 1] - top2[i, 0] > floor]
+    print(f"verify head bf16: max logit error {np.abs(lg - want).max():.3e}, noise floor {floor:.3e}, "
+          f"{len(decided)}/{len(block)} rows decided")
+    assert [int(pred[i]) for i in decided] == [int(np.argmax(want[i])) for i in decided]
+    assert [int(p) for p in pred.cpu()] == [int(np.argmax(r)) for r in lg]
