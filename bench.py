@@ -65,6 +65,11 @@ def parse():
                     help="time the widened rows instead of the step: the verify head and a block verify against "
                          "one-token decode, the sampler and the sampled graph loop, the expanded-MLA stack, and "
                          "the vision tower feeding the decoder prefill; prints one JSON line and exits")
+    ap.add_argument("--verify-blocks", type=int, default=0, metavar="N",
+                    help="after the prompt's prefill and 8 greedy steps, verify that greedy block N times "
+                         "(chunked prefill of 8 rows, verify head, commit; the cache trimmed back each time), "
+                         "print one JSON line with the time per block and exit (the run the verify kernel "
+                         "traces are taken on)")
     ap.add_argument("--traffic", nargs=3, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV"), default=None,
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --kernel-only run "
                          "into profiles/traffic.json and exit")
@@ -367,6 +372,36 @@ def vit_main(args, cfg):
     print(json.dumps(out))
 
 
+def verify_blocks_main(args):
+    """N verify passes of one 8-token greedy block on the configured stack (HIP events on torch's
+    current stream, the stream every call runs on)."""
+    import torch
+
+    import vlm_synth as vs
+    from decoder_prefill_decode_amd.pipeline import DecoderRun
+
+    cfg = vs.ALL_CONFIGS[args.config]
+    run = DecoderRun(cfg, lambda l: vs.decoder_layer_weights(cfg, l), vs.decoder_globals(cfg))
+    run.prefill()
+    run.first_token(check=False)
+    ids = [int(run.tok[0])] + [int(t) for t in run.decode(8)]
+
+    def verify():
+        run.kv.truncate(cfg.seq)
+        return run.verify_block(ids[:8])
+    verify()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.verify_blocks):
+        toks, _ = verify()
+    e1.record()
+    e1.synchronize()
+    print(json.dumps({"mode": "verify_blocks", "config": cfg.name, "block": 8, "blocks": args.verify_blocks,
+                      "us_per_block": round(e0.elapsed_time(e1) * 1e3 / args.verify_blocks, 1),
+                      "accepted": len(toks) - 1}))
+
+
 def next_rows_main(args):
     """Measurement of the widened rows on the 36-layer stack (HIP events on torch's current stream, the
     stream every call runs on): verify head (one pass over the lm_head table for a block of rows),
@@ -509,6 +544,9 @@ def main():
 
     if args.next_rows:
         next_rows_main(args)
+        return
+    if args.verify_blocks:
+        verify_blocks_main(args)
         return
     cfg = vs.ALL_CONFIGS[args.config]
     if isinstance(cfg, vs.VitConfig):

@@ -532,6 +532,7 @@ vlm_status vlm_prefill(const vlm_model_desc* desc, const vlm_layer* h_layers, fl
         at.q = qb; at.ldq = S; at.k = kd; at.v = vd; at.ldkv = ldkv; at.out = ob;
         at.S = S; at.nq = nq; at.nkv = nkv; at.d = hd; at.dv = dv; at.pos0 = pos0; at.nkeys = pos0 + S;
         at.mask_kind = mk.kind; at.add = mk.add; at.ld_add = mk.ld_add; at.seg = mk.seg;
+        at.part = gpart; at.part_cap = w.gpart_floats;  // free between the QKV and O projections
         HIP_TRY(launch_attn_prefill(dt, at, stream));
         // O projection + residual; a split-K reduction also writes the post-attention norm of the rows
         int fused = 0;

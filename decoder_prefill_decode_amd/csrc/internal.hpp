@@ -123,6 +123,12 @@ struct AttnArgs {
     int S, nq, nkv, d, pos0, nkeys;
     int mask_kind; const float* add; int ld_add; const int32_t* seg;
     int dv = 0;
+    // fp32 scratch for a few-row launch (bf16, causal or no mask, nq/nkv * S <= 64): the key tiles
+    // split over blocks, each writing (o, m, l) partials that the decode merge kernel combines.
+    // Null (or too small): the row-tiled kernel runs instead.
+    float* part = nullptr;
+    size_t part_cap = 0;  // floats at part
+    int split_tiles = 0;  // set by the launcher: 64-key tiles per block of the few-row launch
 };
 hipError_t launch_attn_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 

@@ -113,7 +113,12 @@ __device__ int segment_tiles(const int32_t* seg, int row0, int nrows, int S, int
 // more blocks than CUs, where two blocks per CU would leave half the wavefront
 // slots empty).
 // DQ: width of q and k rows, DV: width of v and output rows (equal except for expanded MLA).
-template <int DQ, int DV, int MASK, int KP>
+// PACK (a few query rows, causal or no mask): the block's 64 rows are the (query head, row) pairs
+// of one KV head (blockIdx.y), row r = local head r / S, row r % S, so the KV head's keys are read
+// once for all its query heads; blockIdx.x takes a.split_tiles key tiles, and the block writes
+// unnormalised (o, m, l) partials [(row * nq + head) * gridDim.x + split][DV + 4] to a.part for
+// the decode merge kernel.
+template <int DQ, int DV, int MASK, int KP, bool PACK = false>
 __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_prefill_bf16(AttnArgs a) {
     constexpr int BQ = 64, BKEY = 64, NT = 128 * KP;
     // a q/k width that is not a multiple of 16 (72) is zero-padded to DK * 16 in the K tile and
@@ -130,10 +135,12 @@ __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_
 
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, hh = lane / 32, l32 = lane % 32;
     const int rg = w & 1, kpar = w >> 1;  // row group, key-tile parity
-    const int hq = blockIdx.y, g = hq / (a.nq / a.nkv);
-    const int q0 = blockIdx.x * BQ + rg * 32;
-    const int qrow = q0 + l32;
-    const int S = a.S;
+    const int S = a.S, G = a.nq / a.nkv;
+    // PACK: lane row r = q0 + l32 is query row r % S of head g * G + r / S (valid below G * S)
+    const int hq = PACK ? blockIdx.y * G + min((rg * 32 + l32) / S, G - 1) : blockIdx.y, g = hq / G;
+    const int q0 = PACK ? rg * 32 : blockIdx.x * BQ + rg * 32;
+    const int qrow = PACK ? (q0 + l32) % S : q0 + l32;  // the lane's query row (position pos0 + qrow)
+    const bool qvalid = PACK ? q0 + l32 < G * S : qrow < S;
     const bf16_t* Q = (const bf16_t*)a.q + (size_t)hq * a.ldq * DQ;
     const bf16_t* Kg = (const bf16_t*)a.k + (size_t)g * a.ldkv * DQ;
     const bf16_t* Vg = (const bf16_t*)a.v + (size_t)g * a.ldkv * DV;
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_
     bf16x8 Qf[DK];
 #pragma unroll
     for (int kk = 0; kk < DK; kk++) {
-        if (qrow < S && kk * 16 + hh * 8 < DQ) {
+        if (qvalid && kk * 16 + hh * 8 < DQ) {
             Qf[kk] = *reinterpret_cast<const bf16x8*>(Q + (size_t)qrow * DQ + kk * 16 + hh * 8);
         } else {
 #pragma unroll
@@ -168,21 +175,23 @@ __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_
     const float scale = kLog2e / sqrtf((float)DQ);
 
     int kend = a.nkeys;
-    if (MASK == VLM_MASK_CAUSAL_ID) {
+    if (MASK == VLM_MASK_CAUSAL_ID && !PACK) {
         const int last = min(S, (int)(blockIdx.x + 1) * BQ) - 1;
         kend = min(kend, a.pos0 + last + 1);
     }
     const int seg_q = (MASK == VLM_MASK_SEGMENT_ID && qrow < S) ? a.seg[qrow] : 0;
     const int nkt = (kend + BKEY - 1) / BKEY;
     // tiles visited, in order: all of them, or under a segment mask those that can hold a visible key
-    int nvis = nkt;
+    // (PACK: this block's a.split_tiles tiles)
+    const int tfirst = PACK ? (int)blockIdx.x * a.split_tiles : 0;
+    int nvis = PACK ? max(0, min(nkt, tfirst + a.split_tiles) - tfirst) : nkt;
     __shared__ short tlist[MASK == VLM_MASK_SEGMENT_ID ? kSegMaxTiles : 1];
     __shared__ unsigned char tflag[MASK == VLM_MASK_SEGMENT_ID ? kSegMaxTiles : 1];
     __shared__ int tlohi[3];
     const bool listed = MASK == VLM_MASK_SEGMENT_ID && nkt <= kSegMaxTiles;
     if constexpr (MASK == VLM_MASK_SEGMENT_ID)
         if (listed) nvis = segment_tiles<NT, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
-    auto tile_at = [&](int i) { return listed ? (int)tlist[i] : i; };
+    auto tile_at = [&](int i) { return listed ? (int)tlist[i] : tfirst + i; };
 
     // K/V tile kt+1 is requested into registers (unconditional, key index clamped; keys past nkeys
     // are zeroed when stored) while tile kt runs on the matrix cores. K chunks are spread along rows
@@ -262,7 +271,10 @@ __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_
         const bf16_t* const Kw = Ks + kpar * KSZ;
         const bf16_t* const Vw = Vt + kpar * VSZ;
         bool active = kv < nvis;
-        if (MASK == VLM_MASK_CAUSAL_ID) active = active && key0 <= a.pos0 + q0 + 31;
+        // the row group's lowest and highest query rows (PACK: rows 0 .. S - 1 of each head)
+        const int qlo = PACK ? 0 : q0, qhi = PACK ? S - 1 : q0 + 31;
+        if (PACK) active = active && q0 < G * S;
+        if (MASK == VLM_MASK_CAUSAL_ID) active = active && key0 <= a.pos0 + qhi;
         if (active) {
             f32x16 sacc[2];
 #pragma unroll
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_
             }
             // a tile every key of which is visible to every query row of this wavefront skips the mask
             bool full = (MASK == VLM_MASK_NONE_ID ||
-                         (MASK == VLM_MASK_CAUSAL_ID && key0 + BKEY - 1 <= a.pos0 + q0)) &&
+                         (MASK == VLM_MASK_CAUSAL_ID && key0 + BKEY - 1 <= a.pos0 + qlo)) &&
                         key0 + BKEY <= a.nkeys;
             if constexpr (MASK == VLM_MASK_SEGMENT_ID)
                 full = segment_tile_full<BKEY>(segs[kpar], seg_q, qrow < S, key0, a.nkeys);
@@ -398,6 +410,23 @@ __global__ __launch_bounds__(128 * KP, (DQ <= 80 && KP == 2) ? 2 : 1) void attn_
 #pragma unroll
             for (int r = 0; r < 16; r++) oacc[nb][r] = oacc[nb][r] * fa + mb[2 + nb * 16 + r] * fb;
         m = mn;
+    }
+    if constexpr (PACK) {
+        if (qvalid) {
+            float* pr = a.part + ((size_t)(qrow * a.nq + hq) * gridDim.x + blockIdx.x) * (DV + 4);
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int n = nb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
+                    if (n < DV) pr[n] = oacc[nb][r];
+                }
+            if (hh == 0) {
+                pr[DV] = m;
+                pr[DV + 1] = l;
+            }
+        }
+        return;
     }
     if (qrow < S) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -577,10 +606,40 @@ static int attn_cus() {
     return v;
 }
 
+// A few query rows (bf16, causal or no mask, the rows of all query heads of a KV head in one
+// 64-row tile): blocks over (key-tile range, KV head) writing partials, then the decode merge
+// kernel (partial row (row, head) = decode "head" row * nq + head, so it writes [S][nq][DV]).
+// The row-tiled launch would give each query head its own block reading the KV head's keys, with
+// at most S of its 64 rows in use. Returns hipErrorNotSupported when the launch does not apply.
+template <int DQ, int DV, int MASK>
+static hipError_t run_prefill_few(const AttnArgs& a, hipStream_t st) {
+    if constexpr ((MASK == VLM_MASK_CAUSAL_ID || MASK == VLM_MASK_NONE_ID) && DQ % 8 == 0 && DV % 8 == 0 &&
+                  (DV == 64 || DV == 80 || DV == 128)) {
+        const char* e = getenv("VLM_FEW_ROWS");  // bit 1 clear: the row-tiled kernel for every row count
+        if ((e && !(atoi(e) & 2)) || !a.part || a.nkv < 1 || a.nq % a.nkv != 0) return hipErrorNotSupported;
+        if ((a.nq / a.nkv) * a.S > 64) return hipErrorNotSupported;
+        const int ntiles = (a.nkeys + 63) / 64;
+        if (ntiles < 1) return hipErrorNotSupported;
+        const int tps = std::max(2, (ntiles + kDecMaxSplits - 1) / kDecMaxSplits);
+        const int nsplit = (ntiles + tps - 1) / tps;
+        if ((size_t)a.S * a.nq * nsplit * (DV + 4) > a.part_cap) return hipErrorNotSupported;
+        AttnArgs b = a;
+        b.split_tiles = tps;
+        attn_prefill_bf16<DQ, DV, MASK, 2, true><<<dim3(nsplit, a.nkv), 256, 0, st>>>(b);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        return launch_attn_combine(1, a.part, a.S * a.nq, nsplit, DV, a.out, st);
+    } else {
+        return hipErrorNotSupported;
+    }
+}
+
 template <int DQ, int DV, int MASK>
 static hipError_t run_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.S + 127) / 128, a.nq);
     if (dtype == 1) {
+        const hipError_t fe = run_prefill_few<DQ, DV, MASK>(a, st);
+        if (fe != hipErrorNotSupported) return fe;
         if constexpr (DQ % 8 == 0 && DV % 8 == 0) {
             const dim3 g64((a.S + 63) / 64, a.nq);
             bool kp4 = false;  // one block per CU anyway: 8 wavefronts, 4 key parities (LDS: heads up to 128)

@@ -152,8 +152,10 @@ static RowsPlan rows_plan(const GemmArgs& a) {
 }
 
 bool gemm_small_fits(int dtype, Epi epi, const GemmArgs& a) {
-    const char* e = getenv("VLM_FEW_ROWS");  // 0 keeps the prefill GEMM for every row count (read per call)
-    if (e && atoi(e) == 0) return false;
+    // VLM_FEW_ROWS (read per call): bit 0 = these projections, bit 1 = the few-row attention
+    // launch; unset = both, 0 = the prefill kernels for every row count
+    const char* e = getenv("VLM_FEW_ROWS");
+    if (e && !(atoi(e) & 1)) return false;
     if (dtype != 1 || a.M < 1 || a.M > kRowsMaxM || a.K < 8 || a.K % 8 != 0) return false;
     if (a.bias || a.rowmap) return false;
     if (epi != Epi::StoreF32 && epi != Epi::Resid && epi != Epi::SwiGLU) return false;

@@ -175,3 +175,31 @@ def test_verify_head_bf16_matches_causal_forward():
           f"{len(decided)}/{len(block)} rows decided")
     assert [int(pred[i]) for i in decided] == [int(np.argmax(want[i])) for i in decided]
     assert [int(p) for p in pred.cpu()] == [int(np.argmax(r)) for r in lg]
+
+
+@pytest.mark.parametrize("base", BF16_CHUNKS, ids=lambda c: c.name)
+def test_few_row_attention_equals_row_tiled_attention(base, monkeypatch):
+    """One bf16 layer, chunks of 1, 5, 8 and 16 rows at positions past a 150-row prefill (three to
+    five 64-key tiles, causal): the few-row attention launch (the query heads of a KV head packed
+    into one tile, key tiles split over blocks, merged by the decode merge kernel) against the
+    row-tiled prefill attention on the same q, k and v (the projections are the few-row ones in
+    both runs). The two differ only in summation order, so the layer outputs agree to 1e-3 of
+    their scale, while a key seen past its row's position moves them by ~1e-2."""
+    from decoder_prefill_decode_amd import pipeline
+    cfg = vs.scaled(base, n_layers=1, seq=180, n_img=40, img_start=20, capacity=256, name=base.name + "_1layer")
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, 0)]
+    outs = []
+    for flag in ("3", "1"):
+        monkeypatch.setenv("VLM_FEW_ROWS", flag)
+        run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+        run.embed_inject()
+        p0 = 150
+        run.model.prefill(run.x[:p0], 0, run.cos, run.sin, [pipeline.causal_mask()], run.kv, run.ws)
+        for s in (1, 5, 8, 16):
+            run.model.prefill(run.x[p0:p0 + s], p0, run.cos, run.sin, [pipeline.causal_mask()], run.kv, run.ws)
+            p0 += s
+        outs.append(run.x[150:p0].cpu().numpy().copy())
+    err = rel(outs[0], outs[1])
+    print(f"{cfg.name}: few-row vs row-tiled attention, layer output max rel diff {err:.2e}")
+    assert err <= 1e-3
