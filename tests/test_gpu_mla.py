@@ -88,3 +88,25 @@ def test_mla_bf16_end_to_end(pipeline):
     forced = [tok0] + list(run.decode_forced(ref["ids"][:-1]))
     print(f"mla bf16: first-token logit err {np.abs(lg - ref['logits0']).max():.2e}")
     check_ids("mla bf16", free, forced, ref["ids"], ref["margins"], ref["floor"])
+
+
+def test_mla_bf16_few_row_chunks_match_oracle(pipeline):
+    """bf16 expanded-MLA stack prefilled in chunks of 16, 1, 7 and 8 rows after a 16-row first chunk
+    (every projection of the chunks, the latent ones with K = 512 included, on the few-row path, and the
+    attention of 1-16 query rows per head on the few-row launch): hidden rows and the K/V caches against
+    the oracle's one-shot prefill within the 2e-2 bf16 gate."""
+    cfg = vs.scaled(vs.C_MLA, dtype="bf16", decode_steps=0)
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers, steps=0)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.embed_inject()
+    p0 = 0
+    for s in (16, 16, 1, 7, 8):
+        s = min(s, cfg.seq - p0)
+        run.model.prefill(run.x[p0:p0 + s], p0, run.cos, run.sin, [pipeline.causal_mask()], run.kv, run.ws)
+        p0 += s
+    if p0 < cfg.seq:
+        run.model.prefill(run.x[p0:cfg.seq], p0, run.cos, run.sin, [pipeline.causal_mask()], run.kv, run.ws)
+    assert run.kv.len() == cfg.seq
+    assert rel(run.x.cpu().numpy(), ref["prefill_x"]) <= TOL["bf16"]
+    check_caches(run, ref, cfg, cfg.seq, TOL["bf16"])
