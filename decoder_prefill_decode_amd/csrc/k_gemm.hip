@@ -240,10 +240,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 // register staging. A stage holds BK (64 or 32) bf16 of each tile row; one
 // load instruction fills 1 KiB, i.e. 8 rows of 64 or 16 rows of 32. Chunk c
 // (16 bytes) of row r is stored at chunk position c ^ swz(r) of that row, so
-// the MFMA operand reads (32 rows, one chunk) spread over the LDS banks:
-// swz(r) = r & 7 for 128-byte rows, (r >> 1) & 3 for 64-byte rows (two rows
-// share one 128-byte bank window). Lane L therefore fetches row L / CPR and
-// chunk (L % CPR) ^ swz(L / CPR) (CPR = chunks per row). Requires K % 8 == 0:
+// the MFMA operand reads (32 rows, one chunk) spread over the LDS banks
+// (lds_swz below). Lane L of load instruction i therefore fetches tile row
+// i * RPI + L / CPR and chunk (L % CPR) ^ swz(that row) (CPR = chunks per
+// row). Requires K % 8 == 0:
 // when K is not a multiple of BK, the last stage's loads past K are clamped to
 // the row's last chunk and those columns are zeroed in LDS (A and B rows)
 // before any wavefront reads the stage.
@@ -264,8 +264,14 @@ __device__ __forceinline__ void wait_stages(int k) {
     }
 }
 
+// The LDS of gfx950 serves a 16-byte read of 16 lanes at once from 64 four-byte banks (256 bytes),
+// so the 16 rows of one chunk column must cover every bank: with 128-byte rows, even and odd rows
+// fall in opposite bank halves and (r >> 1) & 7 spreads each half's 8 rows over its 8 chunk slots;
+// with 64-byte rows, r % 4 picks the bank quarter and (r >> 2) & 3 the slot. (r & 7 on 128-byte
+// rows put rows r and r + 8 on the same banks: half of the GEMMs' LDS cycles were conflict stalls.)
+// Both have a period of 16 rows.
 template <int BK>
-__device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
+__device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 
 // WGM x WGN wavefronts per block, each owning a (BM/WGM) x (BN/WGN) sub-tile.
 template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
@@ -291,13 +297,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
 
     // this lane's source row/chunk in each of the wave's load instructions (rows past M / N are clamped:
     // their products land in output rows / columns the epilogue never stores)
-    const int lr = lane / CPR, lc = (lane % CPR) ^ lds_swz<BK>(lr);  // RPI is a multiple of 8: swz(lr) = swz(row)
+    // (the chunk depends on the tile row, whose swizzle has a period of 16 rows: with 8-row load
+    // instructions it alternates between instructions)
+    const int lr = lane / CPR;
     const bf16_t* ga[AI];
     const bf16_t* gb[BI];
+    int lca[AI], lcb[BI];
 #pragma unroll
-    for (int i = 0; i < AI; i++) ga[i] = A + (size_t)min(m0 + (w * AI + i) * RPI + lr, M - 1) * K;
+    for (int i = 0; i < AI; i++) {
+        ga[i] = A + (size_t)min(m0 + (w * AI + i) * RPI + lr, M - 1) * K;
+        lca[i] = (lane % CPR) ^ lds_swz<BK>((w * AI + i) * RPI + lr);
+    }
 #pragma unroll
-    for (int i = 0; i < BI; i++) gb[i] = B + (size_t)min(n0 + (w * BI + i) * RPI + lr, N - 1) * K;
+    for (int i = 0; i < BI; i++) {
+        gb[i] = B + (size_t)min(n0 + (w * BI + i) * RPI + lr, N - 1) * K;
+        lcb[i] = (lane % CPR) ^ lds_swz<BK>((w * BI + i) * RPI + lr);
+    }
     const int kmax = K - 8;  // last 16-byte chunk of a row: loads of the tail stage are clamped to it
 
     f32x16 acc[TM][TN];
@@ -317,13 +332,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     }
     // one K stage of both tiles into LDS stage ST: instruction i of wavefront w fills RPI rows (1 KiB).
     // (The source pointer is passed as const void*: the host pass silently drops the kernel otherwise.)
+#define VLM_LDS_KC(KOFF, LC) (TAIL ? min((KOFF) + (LC) * 8, kmax) : (KOFF) + (LC) * 8)
 #define VLM_LDS_STAGE(KOFF, ST)                                                                              \
     do {                                                                                                     \
-        const int kc_ = TAIL ? min((KOFF) + lc * 8, kmax) : (KOFF) + lc * 8;                                 \
         _Pragma("unroll") for (int i = 0; i < AI; i++) __builtin_amdgcn_global_load_lds(                     \
-            (const void*)(ga[i] + kc_), (lds_void*)((ST) + (w * AI + i) * 512), 16, 0, 0);                   \
+            (const void*)(ga[i] + VLM_LDS_KC(KOFF, lca[i])), (lds_void*)((ST) + (w * AI + i) * 512), 16, 0, 0); \
         _Pragma("unroll") for (int i = 0; i < BI; i++) __builtin_amdgcn_global_load_lds(                     \
-            (const void*)(gb[i] + kc_), (lds_void*)((ST) + BM * BK + (w * BI + i) * 512), 16, 0, 0);         \
+            (const void*)(gb[i] + VLM_LDS_KC(KOFF, lcb[i])), (lds_void*)((ST) + BM * BK + (w * BI + i) * 512), \
+            16, 0, 0);                                                                                       \
     } while (0)
     // the last stage (global index nk_all - 1) of a K that is not a multiple of BK: zero its columns
     // ktail..BK-1 in every A and B row once they have landed (callers hold a barrier on both sides)
@@ -396,6 +412,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
         }
     }
 #undef VLM_LDS_STAGE
+#undef VLM_LDS_KC
     gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32, split);
 }
 
