@@ -182,13 +182,18 @@ static hipError_t rows_launch(const GemmArgs& a, const RowsPlan& p, float* out, 
     return hipGetLastError();
 }
 
-// Rows per wavefront: 2 (4 with 16 operand rows, so the operand reads per weight byte stay low);
-// SwiGLU two (gate, up) pairs.
+// Rows per wavefront: 2, or 4 with 16 operand rows or at least kRowsWideN rows (a block restages
+// its M operand rows for every 4 * NR weight rows, so wide projections such as the verify head's
+// table pass keep those L2 reads below the weight bytes); SwiGLU two (gate, up) pairs.
+constexpr int kRowsWideN = 16384;
 template <bool SWIGLU, int KCH>
 static hipError_t rows_mr(const GemmArgs& a, const RowsPlan& p, float* out, int ldo, hipStream_t st) {
+    const bool wide = SWIGLU || a.N >= kRowsWideN;
     switch (p.mr) {
-        case 4: return rows_launch<SWIGLU, SWIGLU ? 4 : 2, KCH, 4>(a, p, out, ldo, st);
-        case 8: return rows_launch<SWIGLU, SWIGLU ? 4 : 2, KCH, 8>(a, p, out, ldo, st);
+        case 4: return wide ? rows_launch<SWIGLU, 4, KCH, 4>(a, p, out, ldo, st)
+                            : rows_launch<SWIGLU, 2, KCH, 4>(a, p, out, ldo, st);
+        case 8: return wide ? rows_launch<SWIGLU, 4, KCH, 8>(a, p, out, ldo, st)
+                            : rows_launch<SWIGLU, 2, KCH, 8>(a, p, out, ldo, st);
         default: return rows_launch<SWIGLU, 4, KCH, 16>(a, p, out, ldo, st);
     }
 }
