@@ -203,3 +203,37 @@ def test_few_row_attention_equals_row_tiled_attention(base, monkeypatch):
     err = rel(outs[0], outs[1])
     print(f"{cfg.name}: few-row vs row-tiled attention, layer output max rel diff {err:.2e}")
     assert err <= 1e-3
+
+
+def test_few_row_tails_bf16_match_oracle():
+    """bf16 Qwen3 layer shape with a 4101-entry vocabulary (the verify head's table rows end 5 rows into
+    a 16-row block) and chunks of 3, 12 and 2 rows (operand rows padded to 4 and 16): hidden rows and
+    K/V against the oracle's one-shot prefill, and the head over the last chunk's rows against the
+    oracle's causal forward, all within the 2e-2 bf16 gate."""
+    from decoder_prefill_decode_amd import pipeline
+    cfg = vs.scaled(vs.C3, n_layers=1, vocab=4101, seq=37, n_img=8, img_start=4, decode_steps=0, capacity=64,
+                    name="c3_1layer_bf16_tails")
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, 0)]
+    ref = od.run_decoder(cfg, glob, layers, steps=0)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.embed_inject()
+    p0 = 0
+    for s in (20, 3, 12, 2):
+        run.model.prefill(run.x[p0:p0 + s], p0, run.cos, run.sin, [pipeline.causal_mask()], run.kv, run.ws)
+        p0 += s
+    assert p0 == cfg.seq and run.kv.len() == cfg.seq
+    assert rel(run.x.cpu().numpy(), ref["prefill_x"]) <= 2e-2
+    k, v = (t[:, :cfg.seq].float().cpu().numpy() for t in run.kv.kv(0))
+    assert rel(k, ref["k_cache"][0][:, :cfg.seq]) <= 2e-2 and rel(v, ref["v_cache"][0][:, :cfg.seq]) <= 2e-2
+    # head over rows 20..36 (17 rows: the row-tiled head) and over the last 12-row chunk (the few-row head)
+    for r0 in (20, 23):
+        rows = run.x[r0:r0 + (cfg.seq - r0 if r0 == 20 else 12)].contiguous()
+        S = rows.shape[0]
+        pred = torch.empty(S, dtype=torch.int32, device="cuda")
+        logits = torch.empty((S, cfg.vocab), dtype=torch.float32, device="cuda")
+        run.model.lmhead_argmax_rows(rows, pred, run.ws, logits)
+        want = np.stack([od.lm_head_logits(ref["prefill_x"][r0 + i], glob["final_norm"], glob["embed"], cfg.eps, od.BF16)
+                         for i in range(S)])
+        assert rel(logits.cpu().numpy(), want) <= 2e-2
+        assert [int(p) for p in pred.cpu()] == [int(np.argmax(r)) for r in logits.cpu().numpy()]
