@@ -371,12 +371,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
         for (int j = 0; j < TN; j++)
             fb[j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ lds_swz<BK>(rb[j])) * 8));
     };
+    // a wavefront issuing its MFMA burst runs at raised priority, so the arbiter favours it over the
+    // other wavefronts' load issue and LDS reads (prefill 0.9% faster over 5 A/B pairs on the 36-layer
+    // stack, results unchanged)
     auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int j = 0; j < TN; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
     };
     // Software pipeline: the fragments of step kk+1 are read while the MFMAs of step kk run, and
     // the first step of stage kt+1 is read (after its wait and barrier) before the last MFMAs of
