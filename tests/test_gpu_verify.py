@@ -237,3 +237,47 @@ def test_few_row_tails_bf16_match_oracle():
                          for i in range(S)])
         assert rel(logits.cpu().numpy(), want) <= 2e-2
         assert [int(p) for p in pred.cpu()] == [int(np.argmax(r)) for r in logits.cpu().numpy()]
+
+
+def test_graph_loop_continues_after_verify_commits():
+    """fp32 4B-class layer shape (2 layers), a 160-slot window: verify commits interleaved with graph-loop
+    decoding, the device length moving by several positions per commit and once across the 128 band
+    boundary inside a verify block (prompt 100, verify 6 with a wrong draft at offset 2, 20 graph-loop steps,
+    verify 8 all correct, 10 graph-loop steps): the 41 tokens are the oracle's greedy ids and the caches
+    equal a one-token decode's (1e-4)."""
+    from decoder_prefill_decode_amd import pipeline
+    cfg = vs.scaled(vs.C4, n_layers=2, vocab=8192, seq=100, n_img=30, img_start=16, decode_steps=44, capacity=160,
+                    dtype="f32", name="c4_2layer_f32_verify_loop")
+    glob = vs.decoder_globals(cfg)
+    layers = [vs.decoder_layer_weights(cfg, l) for l in range(cfg.n_layers)]
+    ids = [int(i) for i in od.run_decoder(cfg, glob, layers)["ids"]]
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    run.prefill()
+    gen = [int(run.first_token()[0])]
+
+    def verify(k, wrong=()):
+        i0 = len(gen) - 1
+        draft = [gen[-1]] + ids[i0 + 1:i0 + k]
+        for off in wrong:
+            draft[off] = (draft[off] + 1) % (cfg.vocab - 1)
+        toks, nxt = run.verify_block(draft)
+        gen.extend(toks)
+        run.tok.fill_(nxt)
+
+    verify(6, wrong=(2,))
+    assert run.kv.len() == cfg.seq + 2
+    gen.extend(int(t) for t in run.decode(20, loop=True))
+    verify(8)
+    assert run.kv.len() == cfg.seq + 30 > 128
+    gen.extend(int(t) for t in run.decode(10, loop=True))
+    assert len(gen) == 41 and gen == ids[:41]
+    ar = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    ar.prefill()
+    ar.first_token()
+    ar.decode(40, loop=False)
+    T = run.kv.len()
+    assert T == ar.kv.len() == cfg.seq + 40
+    for l in range(cfg.n_layers):
+        ka, va = (t[:, :T].cpu().numpy() for t in ar.kv.kv(l))
+        kb, vb = (t[:, :T].cpu().numpy() for t in run.kv.kv(l))
+        assert rel(kb, ka) <= 1e-4 and rel(vb, va) <= 1e-4
