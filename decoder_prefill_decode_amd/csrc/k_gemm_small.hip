@@ -72,6 +72,8 @@ __global__ __launch_bounds__(kRowsNW * 64) void gemv_rows_kernel(GemmArgs a, int
         __builtin_amdgcn_global_load_lds((const void*)(A + (size_t)min(m, M - 1) * K + k),
                                          (lds_void*)(xs + (size_t)m * KCH * 64 + 64 * j), 16, 0, 0);
     }
+    // the operand loads stay ahead of the weight loads: the wait below counts on their issue order
+    __builtin_amdgcn_sched_barrier(0);
     // (2) this wavefront's weight rows
     const int wave = blockIdx.x * NW + w;
     int rows[NR];
