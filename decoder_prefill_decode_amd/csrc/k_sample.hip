@@ -5,13 +5,16 @@
 //
 // One block of 1024 threads; the vocabulary streams from L2 two to four times:
 //  1. the context ids become a bitmap in LDS (membership in one read);
-//  2. radix select on order-preserving 32-bit keys with 11-, 11- and 10-bit
-//     digits (LDS histograms of 2048 bins, a parallel suffix scan finds the
-//     bin holding the k-th largest): as soon as every value at or above that
-//     bin's lower bound fits the 2048 candidate slots they are gathered (one
-//     or two histogram passes for ordinary logits), else the next digit is
-//     resolved. (One 8-bit top digit would put nearly every logit in one or
-//     two bins, and their LDS atomics would serialise on one address.)
+//  2. for top-k up to 256, a threshold from the threads' maxima (step (2)
+//     below): two passes (maxima, gather) when the values at or above it
+//     fit the candidate slots, as they do for ordinary logits;
+//  2'. else radix select on order-preserving 32-bit keys with 11-, 11- and
+//     10-bit digits (LDS histograms of 2048 bins, a parallel suffix scan
+//     finds the bin holding the k-th largest): as soon as every value at or
+//     above that bin's lower bound fits the 2048 candidate slots they are
+//     gathered, else the next digit is resolved. (One 8-bit top digit would
+//     put nearly every logit in one or two bins, and their LDS atomics would
+//     serialise on one address.)
 //  3. the candidates are sorted by (value descending, id ascending) with a
 //     bitonic sort; those at or above the k-th value are kept (ties kept);
 //  4. softmax over the kept candidates, a block scan gives the cumulative
@@ -31,6 +34,7 @@ constexpr int kSampleThreads = 1024;
 constexpr int kSampleCand = 2 * kSampleMaxK;  // candidate slots (ties at the k-th value included)
 constexpr int kSampleBins = 2048;             // histogram bins of an 11-bit digit
 constexpr int kSampleBatch = 8;               // logits each thread requests together
+constexpr int kSamplePreK = 256;              // top-k up to which the threshold of step (2) is tried
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
     const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -88,37 +92,43 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
     __syncthreads();
     const float inv_t = 1.0f / sp.temperature, r = sp.penalty;
 
-    // (2) radix select: digits of 11, 11 and 10 bits, most significant first. The prefix of the
-    // resolved digits is `prefix` under `mask`; `above` values lie strictly above the prefix bin.
-    const uint32_t need0 = s_krem;
-    uint32_t prefix = 0u, mask = 0u, above = 0u, lower = 0u;
-    bool gathered = false;
-    for (int pass = 0; pass < 3 && !gathered; pass++) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-        for (int b = tid; b < kSampleBins; b += kSampleThreads) hist[b] = 0u;
-        __syncthreads();
-        // values in batches of kSampleBatch per thread, requested together (indices clamped)
-        for (int i0 = tid; i0 < V; i0 += kSampleThreads * kSampleBatch) {
-            float xv[kSampleBatch];
+    // One pass over the row: f(i, key) for every value, key = the order-preserving bits of the value
+    // after the penalty (context ids) and the temperature. A lane takes 4 consecutive values per load
+    // (they share one context-bitmap word) and requests kSampleBatch loads together; values are
+    // bounds-checked per 4 and a non-finite value sets s_bad once per thread (one CU does all the
+    // arithmetic of the row, so the instructions per value set the pass time). A row that is not
+    // 16-byte aligned, and the last V % 4 values, take one value per load.
+    const int nv = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 ? V / 4 : 0;
+    auto for_keys = [&](auto&& f, auto&& stop) __attribute__((always_inline)) {
+        bool bad = false;
+        auto proc = [&](int i, float x, uint32_t in_ctx) __attribute__((always_inline)) {
+            if (in_ctx) x = x > 0.f ? x / r : x * r;
+            x *= inv_t;
+            bad |= !isfinite(x);
+            f(i, ordered_key(x));
+        };
+        for (int c0 = tid; c0 < nv; c0 += kSampleThreads * kSampleBatch) {
+            if (stop()) break;  // a gather past its slots: the pass's result is discarded anyway
+            f32x4 xv[kSampleBatch];
 #pragma unroll
-            for (int u = 0; u < kSampleBatch; u++) xv[u] = logits[min(i0 + u * kSampleThreads, V - 1)];
+            for (int u = 0; u < kSampleBatch; u++)
+                xv[u] = *reinterpret_cast<const f32x4*>(logits + 4 * (size_t)min(c0 + u * kSampleThreads, nv - 1));
 #pragma unroll
             for (int u = 0; u < kSampleBatch; u++) {
-                const int i = i0 + u * kSampleThreads;
-                if (i >= V) break;
-                float x = xv[u];
-                if ((bits[i >> 5] >> (i & 31)) & 1u) x = x > 0.f ? x / r : x * r;
-                x *= inv_t;
-                if (pass == 0 && !isfinite(x)) s_bad = 1u;
-                const uint32_t k = ordered_key(x);
-                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+                const int c = c0 + u * kSampleThreads;
+                if (c < nv) {
+                    const uint32_t word = bits[c >> 3] >> ((4 * c) & 31);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) proc(4 * c + e, xv[u][e], (word >> e) & 1u);
+                }
             }
         }
-        __syncthreads();
-        // suffix scan over the bins (highest first): thread t holds bins top - 2t and top - 2t - 1
-        const uint32_t need = need0 - above;
-        const int top = (int)dmask;
+        for (int i = 4 * nv + tid; i < V; i += kSampleThreads) proc(i, logits[i], (bits[i >> 5] >> (i & 31)) & 1u);
+        if (bad) s_bad = 1u;
+    };
+    // suffix scan over the bins of `hist` (highest first) for the bin holding the need-th largest:
+    // thread t holds bins top - 2t and top - 2t - 1; the result goes to s_bin, s_above, s_inbin
+    auto scan_bins = [&](uint32_t need, int top) __attribute__((always_inline)) {
         const int j0 = top - 2 * tid, j1 = j0 - 1;
         const uint32_t c0 = j0 >= 0 ? hist[j0] : 0u, c1 = j1 >= 0 ? hist[j1] : 0u;
         const uint32_t pair = c0 + c1;
@@ -143,32 +153,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
             s_inbin = c1;
         }
         __syncthreads();
-        if (s_bad) break;
-        prefix |= s_bin << shift;
-        mask |= dmask << shift;
-        above += s_above;
-        lower = prefix;  // keys >= lower: every value above the prefix bin and the bin itself
-        gathered = above + s_inbin <= (uint32_t)kSampleCand || pass == 2;
-        __syncthreads();
-    }
-    if (s_bad) {  // a non-finite logit: no token (the argmax path reports it the same way)
-        if (tid == 0) sample_commit(-1, out, ctx, kv_len);
-        return;
-    }
-
-    // (3) gather the values with key >= lower (the k-th largest is among them), sort by (value desc,
-    // id asc), keep those >= the k-th value (ties kept)
-    for (int i0 = tid; i0 < V; i0 += kSampleThreads * kSampleBatch) {
-        float xv[kSampleBatch];
-#pragma unroll
-        for (int u = 0; u < kSampleBatch; u++) xv[u] = logits[min(i0 + u * kSampleThreads, V - 1)];
-#pragma unroll
-        for (int u = 0; u < kSampleBatch; u++) {
-            const int i = i0 + u * kSampleThreads;
-            if (i >= V) break;
-            float x = xv[u];
-            if ((bits[i >> 5] >> (i & 31)) & 1u) x = x > 0.f ? x / r : x * r;
-            const uint32_t k = ordered_key(x * inv_t);
+    };
+    // gather the values with key >= lower into the candidate slots (s_count may end above the slots)
+    auto gather = [&](uint32_t lower) __attribute__((always_inline)) {
+        for_keys([&](int i, uint32_t k) __attribute__((always_inline)) {
             if (k >= lower) {
                 const uint32_t slot = atomicAdd(&s_count, 1u);
                 if (slot < (uint32_t)kSampleCand) {
@@ -176,9 +164,73 @@ __global__ __launch_bounds__(kSampleThreads) void sample_logits_kernel(const flo
                     cidx[slot] = i;
                 }
             }
+        }, [&]() __attribute__((always_inline)) { return *(volatile uint32_t*)&s_count > (uint32_t)kSampleCand; });
+        __syncthreads();
+    };
+    const uint32_t need0 = s_krem;
+    bool gathered = false;
+
+    // (2) a threshold from the threads' maxima: thread t's largest key over the values it reads is a
+    // value of the row, so the lower bound of the (11-bit top digit) bin holding the need0-th largest
+    // of those maxima has at least need0 values at or above it. When those fit the candidate slots
+    // (an ordinary top-k of logits: a few dozen to a few hundred values) one pass computing the maxima
+    // and one gathering replace the histogram passes below, whose LDS atomics collide on the few bins
+    // that hold most logits.
+    if (need0 <= (uint32_t)kSamplePreK) {
+        uint32_t kmax = 0u;
+        bool owns = false;
+        for_keys([&](int, uint32_t k) __attribute__((always_inline)) {
+            kmax = max(kmax, k);
+            owns = true;
+        }, []() { return false; });
+        for (int b = tid; b < kSampleBins; b += kSampleThreads) hist[b] = 0u;
+        if (tid == 0) s_above = 0u;  // here: the number of maxima
+        __syncthreads();
+        if (owns) {
+            atomicAdd(&hist[kmax >> 21], 1u);
+            atomicAdd(&s_above, 1u);
+        }
+        __syncthreads();
+        if (need0 <= s_above && !s_bad) {  // uniform
+            scan_bins(need0, kSampleBins - 1);
+            gather(s_bin << 21);
+            gathered = s_count <= (uint32_t)kSampleCand;
+            __syncthreads();
+            if (!gathered && tid == 0) s_count = 0u;  // too many at or above the threshold: select below
+            __syncthreads();
         }
     }
-    __syncthreads();
+
+    // (2') radix select: digits of 11, 11 and 10 bits, most significant first. The prefix of the
+    // resolved digits is `prefix` under `mask`; `above` values lie strictly above the prefix bin.
+    uint32_t prefix = 0u, mask = 0u, above = 0u, lower = 0u;
+    bool resolved = gathered;
+    for (int pass = 0; pass < 3 && !resolved && !s_bad; pass++) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+        for (int b = tid; b < kSampleBins; b += kSampleThreads) hist[b] = 0u;
+        __syncthreads();
+        for_keys([&](int, uint32_t k) __attribute__((always_inline)) {
+            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+        }, []() { return false; });
+        __syncthreads();
+        if (s_bad) break;
+        scan_bins(need0 - above, (int)dmask);
+        prefix |= s_bin << shift;
+        mask |= dmask << shift;
+        above += s_above;
+        lower = prefix;  // keys >= lower: every value above the prefix bin and the bin itself
+        resolved = above + s_inbin <= (uint32_t)kSampleCand || pass == 2;
+        __syncthreads();
+    }
+    if (s_bad) {  // a non-finite logit: no token (the argmax path reports it the same way)
+        if (tid == 0) sample_commit(-1, out, ctx, kv_len);
+        return;
+    }
+
+    // (3) gather the values with key >= lower (the k-th largest is among them) unless the threshold
+    // of (2) already did, sort by (value desc, id asc), keep those >= the k-th value (ties kept)
+    if (!gathered) gather(lower);
     const int ngath = (int)s_count;
     if (ngath > kSampleCand) {  // more ties at the k-th value than slots
         if (tid == 0) sample_commit(-1, out, ctx, kv_len);
