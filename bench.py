@@ -79,7 +79,7 @@ def parse():
 KERNELS = ["lmhead", "qkv", "o", "gate_up", "down", "attn"]
 # name fragments of each kernel in a --kernel-only run (the copy kernels are told apart by name too)
 KERNEL_NAME = {"lmhead": "Epi)5", "qkv": "Epi)0", "o": "Epi)1", "gate_up": "Epi)2", "down": "Epi)1",
-               "attn": "attn_decode_fused"}
+               "attn": "attn_decode_"}  # the vector-ALU (fused), matrix-core (mfma) or MLA decode attention
 
 
 def kernel_bytes(cfg, name, t=None):

@@ -28,6 +28,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -713,15 +714,15 @@ constexpr int kDecSteps = 8;  // key steps requested in one batch (fewer for 4 o
 // stack's shape at 624 valid slots: 4 wavefronts x 32 splits 5.1 us,
 // 8 x 16 5.6 us, 2 x 64 5.8 us.)
 // VLM_DEC_SPLITS (1..kDecMaxSplits) caps the splits, for tuning. Measured on
-// the 36-layer stack (positions 512..767): a cap of 32 gives 465.8 ms per
-// 256-token decode, 16 467.1 ms, 48 and 64 (with a 64-split maximum) 473.5 ms.
+// the 36-layer stack (positions 512..767), vector-ALU form: a cap of 32 gives
+// 465.8 ms per 256-token decode, 16 467.1 ms, 48 and 64 (with a 64-split
+// maximum) 473.5 ms; matrix-core form (one box): 32 454.6 ms, 16 453.9 ms,
+// 8 458.9 ms, 4 466.9 ms.
+// Read at every plan, so a process can compare plans (a graph keeps the plan it was captured with).
 static int dec_split_cap() {
-    static int v = [] {
-        const char* e = getenv("VLM_DEC_SPLITS");
-        const int n = e ? atoi(e) : 32;
-        return n < 1 ? 1 : (n > kDecMaxSplits ? kDecMaxSplits : n);
-    }();
-    return v;
+    const char* e = getenv("VLM_DEC_SPLITS");
+    const int n = e ? atoi(e) : 32;
+    return n < 1 ? 1 : (n > kDecMaxSplits ? kDecMaxSplits : n);
 }
 
 DecSplitPlan attn_decode_plan(int capacity, int t) {
@@ -1013,6 +1014,269 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
     }
 }
 
+// ============================================================== decode, bf16 on the matrix cores
+// The work of attn_decode_fused_kernel<bf16_t, D, G, 4> (one block of four
+// wavefronts per (KV head g, split sp): rotation of the group's q heads and
+// of the new k / v, the owner's write of slot t, one (o, m, l) partial per
+// query head) with the products of each 16-key tile on the matrix cores. The
+// group's query heads are the 16 columns of the products (G of them used):
+//   S^T[16 keys][16 heads] = K tile . q^T      v_mfma_f32_16x16x32_bf16, ceil(D/32) steps;
+//   V tile in the operand layout of P . V: the product of the tile with 0/1
+//     columns of the identity, exact in fp32   v_mfma_f32_16x16x32_bf16, one per 16 dims;
+//   O[16 heads][16 dims] += P . V               v_mfma_f32_16x16x16bf16_1k, P = hi + lo in bf16.
+// In these 16x16 layouts lane l holds column l % 16 and rows 4 (l / 16) .. +3
+// of a result, and row l % 16 with contraction indices 8 (l / 16) .. +7 (x32)
+// or 4 (l / 16) .. +3 (x16) of an operand, so the rows of S^T a lane holds (4
+// keys for the lane's head) are already the lane's part of the P operand.
+// Wavefront w scores the tiles w, w + 4, ... of the split, kDecMfmaNT at a
+// time, with an online softmax across its batches; the four wavefronts merge
+// through LDS as in the other form.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int G, int NW, int NT>
+__global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(DecAttnArgs a) {
+    typedef bf16_t T;
+    constexpr int KS = (D + 31) / 32, DB = D / 16, PS = D + 4;
+    constexpr int NI = (G + 2 + NW - 1) / NW;  // rotation items (G q heads, k, v) per wavefront
+    static_assert(D % 16 == 0 && G <= 16, "16-dim blocks, at most 16 query heads per KV head");
+    __shared__ float qs[G][D];
+    __shared__ __attribute__((aligned(16))) T knew[D];
+    __shared__ __attribute__((aligned(16))) T vnew[D];
+    __shared__ float sm_m[NW][G], sm_l[NW][G];
+    __shared__ float sm_o[NW][G][D];
+    const int g = blockIdx.x, sp = blockIdx.y;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, l16 = lane % 16, grp = lane / 16;
+    const int chunk = a.chunk;
+    const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
+    const int ntile = kend > k0 ? (kend - k0 + 15) / 16 : 0;
+    const int nmine = ntile > w ? (ntile - w + NW - 1) / NW : 0;  // this wavefront's tiles (uniform)
+    const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
+    const T* Vg = (const T*)a.vc + (size_t)g * a.W * D;
+    const int jl = max(kend - 1, 0);  // a valid slot for clamped requests
+
+    // (1) K/V rows of the first batch: lane l loads key l % 16 of a tile, dims
+    // 32 ks + 8 (l / 16) .. +7 (clamped to the last 8 dims past D: those lanes'
+    // products meet zero q entries and zero identity entries)
+    u32x4 kr[NT][KS], vr[NT][KS];
+    auto request = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < NT; b++) {
+            if (i0 + b < nmine) {  // uniform over the wavefront
+                const int j = min(k0 + (w + NW * (i0 + b)) * 16 + l16, jl);
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const int d = min(32 * ks + 8 * grp, D - 8);
+                    kr[b][ks] = *reinterpret_cast<const u32x4*>(Kg + (size_t)j * D + d);
+                    vr[b][ks] = *reinterpret_cast<const u32x4*>(Vg + (size_t)j * D + d);
+                }
+            }
+        }
+    };
+    request(0);
+    const int half = D / 2, sd = D / a.segments, sh = sd / 2;
+    const bool on = lane < half;
+    const int lp = on ? lane : 0;
+    const int i0 = (lp / sh) * sd + lp % sh, i1 = i0 + sh;
+    const int r0 = a.interleave ? (lp / sh) * sd + 2 * (lp % sh) : i0, r1 = a.interleave ? r0 + 1 : i1;
+    const int n0 = a.norm_after ? i0 : r0, n1 = a.norm_after ? i1 : r1;
+    float x0[NI], x1[NI], g0[NI], g1[NI];
+#pragma unroll
+    for (int ii = 0; ii < NI; ii++) {
+        const int it = min(w + ii * NW, G + 1);
+        const bool isq = it < G, isk = it == G;
+        const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
+        const float* src = a.qkv + (size_t)row * D;
+        const T* gn = (const T*)(isq ? a.qn : a.kn);
+        const T* gp = (it <= G && gn) ? gn : (const T*)a.kc;  // any valid address when unused
+        x0[ii] = src[it <= G ? r0 : i0];
+        x1[ii] = src[it <= G ? r1 : i1];
+        g0[ii] = Elt<T>::ld(gp, n0);
+        g1[ii] = Elt<T>::ld(gp, n1);
+    }
+    const float c0 = a.rope[i0], c1 = a.rope[i1], s0 = a.rope[D + i0], s1 = a.rope[D + i1];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) the valid range, then QK-Norm + RoPE of q (G heads) and of the owner's new k / v
+    const int t = a.len[0];
+    const int k1 = min(t + 1, kend);
+    const bool own = k0 <= t && t < kend;
+#pragma unroll
+    for (int ii = 0; ii < NI; ii++) {
+        const int it = w + ii * NW;
+        if (it >= G + (own ? 2 : 0)) continue;  // uniform per wavefront
+        const bool isq = it < G, isk = it == G;
+        const bool rot = isq || isk, norm = rot && (isq ? a.qn : a.kn) != nullptr;
+        float y0 = on ? x0[ii] : 0.f, y1 = on ? x1[ii] : 0.f;
+        if (norm && !a.norm_after) {
+            const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
+            y0 = y0 * r * g0[ii];
+            y1 = y1 * r * g1[ii];
+        }
+        if (rot) {
+            const float z0 = y0 * c0 - y1 * s0;
+            const float z1 = y1 * c1 + y0 * s1;
+            y0 = z0;
+            y1 = z1;
+        }
+        if (norm && a.norm_after) {
+            const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
+            y0 = y0 * r * g0[ii];
+            y1 = y1 * r * g1[ii];
+        }
+        if (!on) continue;
+        if (isq) {
+            qs[it][i0] = Elt<T>::rnd(y0);
+            qs[it][i1] = Elt<T>::rnd(y1);
+        } else {
+            T* cache = (T*)(isk ? a.kc : a.vc) + ((size_t)g * a.W + t) * D;
+            T* lds = isk ? knew : vnew;
+            Elt<T>::st(lds, i0, y0);
+            Elt<T>::st(lds, i1, y1);
+            Elt<T>::st(cache, i0, y0);
+            Elt<T>::st(cache, i1, y1);
+        }
+    }
+    __syncthreads();
+
+    // q^T operand (lane l: head l % 16, dims 32 ks + 8 (l / 16) .. +7; zero past G or D)
+    // and the two identity operands (column j of half h selects dim 16 h + j of a 32-dim step)
+    bf16x8 qb[KS], ib[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const int d = 32 * ks + 8 * grp + e;
+            const float v = (l16 < G && d < D) ? qs[l16 < G ? l16 : 0][d < D ? d : 0] : 0.f;
+            qb[ks][e] = __builtin_bit_cast(__bf16, f2bf(v));
+        }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            ib[h][e] = __builtin_bit_cast(__bf16, (bf16_t)(8 * grp + e == l16 + 16 * h ? 0x3f80 : 0));
+    const float scale = kLog2e / sqrtf((float)D);
+    float mrun = -INFINITY, lpart = 0.f;  // per head l % 16 (replicated over the four lanes of a head)
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // (3) this wavefront's tiles, NT per batch
+    for (int b0 = 0; b0 < nmine; b0 += NT) {
+        if (b0 > 0) request(b0);
+        float s[NT][4];
+#pragma unroll
+        for (int b = 0; b < NT; b++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) s[b][r] = -INFINITY;
+            if (b0 + b >= nmine) continue;  // uniform
+            const int kt = k0 + (w + NW * (b0 + b)) * 16;
+            const int ka = kt + l16;  // the key this lane loaded
+            if (ka == t) {  // the new slot: this token's rotated k and v
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const int d = min(32 * ks + 8 * grp, D - 8);
+                    kr[b][ks] = *reinterpret_cast<const u32x4*>(knew + d);
+                    vr[b][ks] = *reinterpret_cast<const u32x4*>(vnew + d);
+                }
+            }
+            if (ka >= k1) {  // clamped or past t: arbitrary bits; weight 0 must not meet NaN
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) vr[b][ks] = u32x4{0, 0, 0, 0};
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[b][ks]), qb[ks], acc, 0,
+                                                              0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; r++) s[b][r] = kt + 4 * grp + r < k1 ? acc[r] * scale : -INFINITY;
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NT; b++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) mb = fmaxf(mb, s[b][r]);
+        {
+            const LanePair p16 = swap16(mb);
+            mb = fmaxf(p16.lo, p16.hi);
+            const LanePair p32 = swap32(mb);
+            mb = fmaxf(p32.lo, p32.hi);
+        }
+        const float mn = fmaxf(mrun, mb);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        // arguments are <= 0 (or -inf): the bare v_exp_f32 needs no range reduction
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mu);
+        mrun = mn;
+        lpart *= alpha;
+        if (b0 > 0) {  // rows of oacc are heads 4 (l / 16) + r: their factors from lanes 4 (l / 16) + r
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float f = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+                for (int db = 0; db < DB; db++) oacc[db][r] *= f;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NT; b++) {
+            if (b0 + b >= nmine) continue;  // uniform
+            s16x4 phi, plo;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float p = __builtin_amdgcn_exp2f(s[b][r] - mu);
+                lpart += p;
+                const bf16_t h = f2bf(p);
+                phi[r] = (short)h;
+                plo[r] = (short)f2bf(p - bf2f(h));
+            }
+#pragma unroll
+            for (int db = 0; db < DB; db++) {
+                const f32x4 vt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, vr[b][db / 2]), ib[db % 2], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                s16x4 vb;
+#pragma unroll
+                for (int r = 0; r < 4; r++) vb[r] = (short)(__float_as_uint(vt[r]) >> 16);  // exact: bf16 values
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, oacc[db], 0, 0, 0);
+            }
+        }
+    }
+    {
+        const LanePair p16 = swap16(lpart);
+        lpart = p16.lo + p16.hi;
+        const LanePair p32 = swap32(lpart);
+        lpart = p32.lo + p32.hi;
+    }
+    if (grp == 0 && l16 < G) {
+        sm_m[w][l16] = mrun;
+        sm_l[w][l16] = lpart;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int hd = 4 * grp + r;
+        if (hd < G)
+#pragma unroll
+            for (int db = 0; db < DB; db++) sm_o[w][hd][16 * db + l16] = oacc[db][r];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * (D + 2); idx += NW * kWave) {
+        const int gg = idx / (D + 2), e = idx % (D + 2);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < NW; q++) mx = fmaxf(mx, sm_m[q][gg]);
+        float v = 0.f;
+        if (e == D) {
+            v = mx;
+        } else {
+#pragma unroll
+            for (int q = 0; q < NW; q++) {
+                const float f = mx == -INFINITY ? 0.f : exp2f(sm_m[q][gg] - mx);
+                v += f * (e < D ? sm_o[q][gg][e] : sm_l[q][gg]);
+            }
+        }
+        a.partial[((size_t)(g * G + gg) * a.nsplit + sp) * PS + e] = v;
+    }
+}
+
 // Merge of the split partials: one wavefront per 64 columns of a query head's
 // output row (a block per head). Lane s holds the statistics (m, l) of split
 // s; every lane requests its column of the NS >= nsplit launched splits' o rows
@@ -1049,9 +1313,26 @@ __global__ __launch_bounds__(64 * ((D + 63) / 64)) void attn_combine_fast_kernel
     if (e < D) Elt<T>::st(out, (size_t)h * D + e, v);
 }
 
+// VLM_DEC_MFMA=0 keeps bf16 decode attention on the vector-ALU form (for comparison; read at
+// every launch, a captured graph keeps the form it was captured with).
+static bool dec_mfma_on() {
+    const char* e = getenv("VLM_DEC_MFMA");
+    return !(e && atoi(e) == 0);
+}
+
 template <class T, int D>
 static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
     const dim3 grid(a.nkv, a.nsplit);
+    if constexpr (std::is_same<T, bf16_t>::value && D % 16 == 0) {
+        const int G = a.nq / a.nkv;
+        if (dec_mfma_on() && G >= 4) {  // for 1-2 heads per KV head the vector-ALU form is faster
+            switch (G) {
+                case 4: attn_decode_mfma_kernel<D, 4, 4, 2><<<grid, 256, 0, st>>>(a); return hipGetLastError();
+                case 8: attn_decode_mfma_kernel<D, 8, 4, 2><<<grid, 256, 0, st>>>(a); return hipGetLastError();
+                default: break;
+            }
+        }
+    }
     switch (a.nq / a.nkv) {
         case 1: attn_decode_fused_kernel<T, D, 1, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;
         case 2: attn_decode_fused_kernel<T, D, 2, kDecWaves><<<grid, kDecWaves * 64, 0, st>>>(a); break;

@@ -86,3 +86,55 @@ def test_bf16_head80_stack_interleave(pipeline):
     forced = [tok0] + list(run.decode_forced(ref["ids"][:-1]))
     print(f"head80 variants: first-token logit err {np.abs(lg - ref['logits0']).max():.2e}")
     check_ids("head80 variants", free, forced, ref["ids"], ref["margins"], ref["floor"])
+
+
+# (head_dim, n_q_heads, n_kv_heads): groups of 8 and 4 query heads per KV head at widths 64, 80, 128
+GROUP_SHAPES = [(64, 16, 2), (80, 32, 4), (128, 16, 4), (64, 8, 2)]
+
+
+def group_stack(hd, nq, nkv):
+    """One bf16 layer with a 180-row prompt (its last 16-key tile ragged) and 24 decode steps that
+    cross the split plan's band boundary at position 192."""
+    return vs.scaled(vs.C2_BF16, hidden=512, n_q_heads=nq, n_kv_heads=nkv, head_dim=hd, ffn=1024, seq=180,
+                     decode_steps=24, capacity=256)
+
+
+@pytest.mark.parametrize("hd,nq,nkv", GROUP_SHAPES, ids=["d64_g8", "d80_g8", "d128_g4", "d64_g4"])
+def test_bf16_decode_groups_of_4_and_8(pipeline, hd, nq, nkv):
+    """bf16 decode with 4 or 8 query heads per KV head (scored on the matrix cores): prefill rows,
+    decode hidden rows and both caches against the oracle at the bf16 gate."""
+    cfg = group_stack(hd, nq, nkv)
+    glob, layers = make(cfg)
+    ref = od.run_decoder(cfg, glob, layers)
+    run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+    x = run.prefill()
+    assert rel(x.cpu().numpy(), ref["prefill_x"]) <= TOL["bf16"]
+    out = run.decode_hidden(run.dec_x).cpu().numpy()
+    assert rel(out, ref["decode_x"]) <= TOL["bf16"]
+    check_caches(run, ref, cfg, cfg.seq + cfg.decode_steps, TOL["bf16"])
+
+
+@pytest.mark.parametrize("splits", [32, 1], ids=["plan", "one_split"])
+@pytest.mark.parametrize("hd,nq,nkv", GROUP_SHAPES[:3], ids=["d64_g8", "d80_g8", "d128_g4"])
+def test_matrix_core_decode_attention_equals_vector_form(pipeline, monkeypatch, hd, nq, nkv, splits):
+    """The matrix-core decode attention (VLM_DEC_MFMA unset) against the vector-ALU form
+    (VLM_DEC_MFMA=0) on the same prompt and steps: caches bitwise equal (both write the same rotated
+    k / v), hidden rows within 1e-3 (P enters the P.V products as a bf16 hi + lo pair). One split
+    gives each wavefront 3-4 tiles, two batches, so the online rescale between batches runs."""
+    cfg = group_stack(hd, nq, nkv)
+    glob, layers = make(cfg)
+    monkeypatch.setenv("VLM_DEC_SPLITS", str(splits))
+    outs, caches = [], []
+    for form in ("1", "0"):
+        monkeypatch.setenv("VLM_DEC_MFMA", form)
+        run = pipeline.DecoderRun(cfg, lambda l: layers[l], glob)
+        run.prefill()
+        outs.append(run.decode_hidden(run.dec_x).cpu().numpy())
+        caches.append(kv_host(run, 0))
+        del run
+    T = cfg.seq + cfg.decode_steps
+    for a, b in zip(caches[0], caches[1]):
+        assert np.array_equal(a[:, :T], b[:, :T])
+    err = rel(outs[0], outs[1])
+    print(f"d{hd} g{nq // nkv} splits {splits}: matrix-core vs vector form {err:.2e}")
+    assert err <= 1e-3
