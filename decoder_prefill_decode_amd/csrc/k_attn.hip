@@ -1015,10 +1015,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
 }
 
 // ============================================================== decode, bf16 on the matrix cores
-// The work of attn_decode_fused_kernel<bf16_t, D, G, 4> (one block of four
-// wavefronts per (KV head g, split sp): rotation of the group's q heads and
-// of the new k / v, the owner's write of slot t, one (o, m, l) partial per
-// query head) with the products of each 16-key tile on the matrix cores. The
+// The work of attn_decode_fused_kernel<bf16_t, D, G, 4> (one block per (KV
+// head g, split sp): rotation of the group's q heads and of the new k / v,
+// the owner's write of slot t, one (o, m, l) partial per query head), in
+// blocks of NW wavefronts, with the products of each 16-key tile on the matrix
+// cores. The
 // group's query heads are the 16 columns of the products (G of them used):
 //   S^T[16 keys][16 heads] = K tile . q^T      v_mfma_f32_16x16x32_bf16, ceil(D/32) steps;
 //   V tile in the operand layout of P . V: the product of the tile with 0/1
@@ -1028,9 +1029,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
 // of a result, and row l % 16 with contraction indices 8 (l / 16) .. +7 (x32)
 // or 4 (l / 16) .. +3 (x16) of an operand, so the rows of S^T a lane holds (4
 // keys for the lane's head) are already the lane's part of the P operand.
-// Wavefront w scores the tiles w, w + 4, ... of the split, kDecMfmaNT at a
-// time, with an online softmax across its batches; the four wavefronts merge
-// through LDS as in the other form.
+// Wavefront w scores the tiles w, w + NW, ... of the split, NT at a time,
+// with an online softmax across its batches; the wavefronts merge through LDS
+// as in the other form.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int G, int NW, int NT>
@@ -1325,10 +1326,12 @@ static hipError_t fused_group(const DecAttnArgs& a, hipStream_t st) {
     const dim3 grid(a.nkv, a.nsplit);
     if constexpr (std::is_same<T, bf16_t>::value && D % 16 == 0) {
         const int G = a.nq / a.nkv;
-        if (dec_mfma_on() && G >= 4) {  // for 1-2 heads per KV head the vector-ALU form is faster
+        // for 1-2 heads per KV head the vector-ALU form is faster; eight wavefronts rotate the q, k,
+        // v rows one each (36-layer stack: 2 wavefronts 454.3, 4 453.5, 8 452.4 ms per 256 tokens)
+        if (dec_mfma_on() && G >= 4) {
             switch (G) {
-                case 4: attn_decode_mfma_kernel<D, 4, 4, 2><<<grid, 256, 0, st>>>(a); return hipGetLastError();
-                case 8: attn_decode_mfma_kernel<D, 8, 4, 2><<<grid, 256, 0, st>>>(a); return hipGetLastError();
+                case 4: attn_decode_mfma_kernel<D, 4, 8, 2><<<grid, 512, 0, st>>>(a); return hipGetLastError();
+                case 8: attn_decode_mfma_kernel<D, 8, 8, 2><<<grid, 512, 0, st>>>(a); return hipGetLastError();
                 default: break;
             }
         }
