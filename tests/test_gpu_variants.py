@@ -89,7 +89,7 @@ def test_bf16_head80_stack_interleave(pipeline):
 
 
 # (head_dim, n_q_heads, n_kv_heads): groups of 8 and 4 query heads per KV head at widths 64, 80, 128
-GROUP_SHAPES = [(64, 16, 2), (80, 32, 4), (128, 16, 4), (64, 8, 2)]
+GROUP_SHAPES = [(64, 16, 2), (80, 32, 4), (128, 16, 4), (64, 8, 2), (128, 32, 4)]
 
 
 def group_stack(hd, nq, nkv):
@@ -99,7 +99,7 @@ def group_stack(hd, nq, nkv):
                      decode_steps=24, capacity=256)
 
 
-@pytest.mark.parametrize("hd,nq,nkv", GROUP_SHAPES, ids=["d64_g8", "d80_g8", "d128_g4", "d64_g4"])
+@pytest.mark.parametrize("hd,nq,nkv", GROUP_SHAPES, ids=["d64_g8", "d80_g8", "d128_g4", "d64_g4", "d128_g8"])
 def test_bf16_decode_groups_of_4_and_8(pipeline, hd, nq, nkv):
     """bf16 decode with 4 or 8 query heads per KV head (scored on the matrix cores): prefill rows,
     decode hidden rows and both caches against the oracle at the bf16 gate."""
