@@ -210,13 +210,14 @@ struct GraphKey {
     bool sampled = false;  // the sampler instead of the argmax ends each step
     SampleParams sp{};
     const float* uniform = nullptr;
+    int steps = 1;  // decode steps in a band's multi-step graph
     bool operator==(const GraphKey& o) const {
         return memcmp(&desc, &o.desc, sizeof(desc)) == 0 && layers.size() == o.layers.size() &&
                memcmp(layers.data(), o.layers.data(), layers.size() * sizeof(vlm_layer)) == 0 && embed == o.embed &&
                fnorm == o.fnorm && table == o.table && tok == o.tok && cos == o.cos && sin == o.sin &&
                table_rows == o.table_rows && hist == o.hist && ws == o.ws && ws_bytes == o.ws_bytes &&
                sampled == o.sampled && uniform == o.uniform && sp.temperature == o.sp.temperature &&
-               sp.top_k == o.sp.top_k && sp.top_p == o.sp.top_p && sp.penalty == o.sp.penalty;
+               sp.top_k == o.sp.top_k && sp.top_p == o.sp.top_p && sp.penalty == o.sp.penalty && steps == o.steps;
     }
 };
 
@@ -227,9 +228,10 @@ struct vlm_kv {
     size_t bytes;
     int len;  // host mirror
     hipStream_t cap_stream = nullptr;
-    // one decode-step graph per band of positions (the attention split plan changes from band to band)
-    std::vector<hipGraph_t> graph;
-    std::vector<hipGraphExec_t> exec;
+    // per band of positions (the attention split plan changes from band to band): a graph of one
+    // decode step (graph, exec) and one of kDecGraphSteps steps (graphk, execk)
+    std::vector<hipGraph_t> graph, graphk;
+    std::vector<hipGraphExec_t> exec, execk;
     bool has_key = false;
     GraphKey key;
     int32_t* dlen() const { return (int32_t*)buf; }
@@ -238,12 +240,16 @@ struct vlm_kv {
     char* kptr(int l) const { return (char*)buf + kHeader + (size_t)l * layer_bytes(); }
     char* vptr(int l) const { return kptr(l) + k_bytes(); }
     void drop_graph() {
-        for (hipGraphExec_t e : exec)
-            if (e) hipGraphExecDestroy(e);
-        for (hipGraph_t g : graph)
-            if (g) hipGraphDestroy(g);
+        for (auto* v : {&exec, &execk})
+            for (hipGraphExec_t e : *v)
+                if (e) hipGraphExecDestroy(e);
+        for (auto* v : {&graph, &graphk})
+            for (hipGraph_t g : *v)
+                if (g) hipGraphDestroy(g);
         exec.clear();
+        execk.clear();
         graph.clear();
+        graphk.clear();
         has_key = false;
     }
 };
@@ -852,8 +858,19 @@ vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers
     return ok();
 }
 
-// Captures one step per band of positions into a HIP graph (before any launch) and launches
-// n_steps of them; samp == nullptr: greedy argmax head, else the sampler with draws `uniform`.
+// Decode steps captured into one graph for the launches inside a band (VLM_DEC_GRAPH_STEPS, read per
+// call; 1 = one step per launch). Each graph launch costs the GPU a few microseconds more than a
+// kernel boundary inside a graph: 8 steps per launch took the 36-layer stack's 256-token decode
+// 451.9 -> 450.7 ms (4: 450.9) and the 28-layer stack's 128 tokens 88.0 -> 87.2 ms.
+static int dec_graph_steps() {
+    const char* e = getenv("VLM_DEC_GRAPH_STEPS");
+    const int n = e ? atoi(e) : 8;
+    return n < 1 ? 1 : (n > kDecBand ? kDecBand : n);
+}
+
+// Captures the steps of each band of positions into HIP graphs (before any launch: one step, and
+// dec_graph_steps() steps) and launches n_steps of them; samp == nullptr: greedy argmax head, else
+// the sampler with draws `uniform`.
 static vlm_status decode_loop_impl(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
                                    const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,
                                    const float* d_cos, const float* d_sin, int32_t table_rows, int32_t* d_token_hist,
@@ -869,26 +886,31 @@ static vlm_status decode_loop_impl(const vlm_model_desc* desc, const vlm_layer* 
     key.sampled = samp != nullptr;
     if (samp) key.sp = *samp;
     key.uniform = uniform;
+    const int K = dec_graph_steps();
+    key.steps = K;
     if (!kv->has_key || !(kv->key == key)) {
         kv->drop_graph();
         kv->key = key;
         kv->has_key = true;
     }
     // the graphs of the bands the steps pass through, captured before any launch
+    vlm_status s = VLM_OK;
     const int b0 = attn_decode_plan(kv->capacity, kv->len).band;
     const int b1 = attn_decode_plan(kv->capacity, kv->len + n_steps - 1).band;
     if ((int)kv->exec.size() <= b1) {
         kv->exec.resize(b1 + 1, nullptr);
         kv->graph.resize(b1 + 1, nullptr);
+        kv->execk.resize(b1 + 1, nullptr);
+        kv->graphk.resize(b1 + 1, nullptr);
     }
-    for (int b = b0; b <= b1; b++) {
-        if (kv->exec[b]) continue;
+    auto capture = [&](int b, int steps, hipGraph_t* g_out, hipGraphExec_t* e_out) -> vlm_status {
         const DecSplitPlan plan = attn_decode_plan(kv->capacity, b * kDecBand);
         if (!kv->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&kv->cap_stream, hipStreamNonBlocking));
         HIP_TRY(hipStreamBeginCapture(kv->cap_stream, hipStreamCaptureModeThreadLocal));
-        vlm_status es = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos,
-                                       d_sin, d_token_io, nullptr, d_token_hist, d_ws, w, plan, kv->cap_stream, samp,
-                                       uniform);
+        vlm_status es = VLM_OK;
+        for (int i = 0; i < steps && !es; i++)  // each step reads the length the one before it advanced
+            es = enqueue_decode(desc, h_layers, d_embed, d_final_norm, d_table, kv, d_token_io, nullptr, d_cos, d_sin,
+                                d_token_io, nullptr, d_token_hist, d_ws, w, plan, kv->cap_stream, samp, uniform);
         hipGraph_t graph = nullptr;
         hipError_t ee = hipStreamEndCapture(kv->cap_stream, &graph);
         if (es) {
@@ -902,13 +924,23 @@ static vlm_status decode_loop_impl(const vlm_model_desc* desc, const vlm_layer* 
             hipGraphDestroy(graph);
             return fail(VLM_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ie));
         }
-        kv->graph[b] = graph;
-        kv->exec[b] = exec;
+        *g_out = graph;
+        *e_out = exec;
+        return VLM_OK;
+    };
+    for (int b = b0; b <= b1; b++) {
+        if (!kv->exec[b] && (s = capture(b, 1, &kv->graph[b], &kv->exec[b]))) return s;
+        if (K > 1 && !kv->execk[b] && (s = capture(b, K, &kv->graphk[b], &kv->execk[b]))) return s;
     }
-    for (int i = 0; i < n_steps; i++) {
-        const hipError_t le = hipGraphLaunch(kv->exec[attn_decode_plan(kv->capacity, kv->len).band], stream);
+    for (int i = 0; i < n_steps;) {
+        const int band = attn_decode_plan(kv->capacity, kv->len).band;
+        // K steps in one launch when they all stay in this band (one split plan)
+        const bool many = K > 1 && n_steps - i >= K && kv->len % kDecBand + K <= kDecBand;
+        const hipError_t le = hipGraphLaunch(many ? kv->execk[band] : kv->exec[band], stream);
         if (le != hipSuccess) return fail(VLM_ERR_HIP, "graph launch at position %d: %s", kv->len, hipGetErrorString(le));
-        kv->len += 1;  // the launched step advances the device length
+        const int adv = many ? K : 1;
+        kv->len += adv;  // the launched steps advance the device length
+        i += adv;
     }
     return ok();
 }

@@ -344,12 +344,13 @@ vlm_status vlm_decode_step(const vlm_model_desc* desc, const vlm_layer* h_layers
                            size_t ws_bytes, hipStream_t stream);
 
 /* n_steps greedy decode steps with each step's token feeding the next
- * (d_token_io is read and written by every step). One step is captured into a
- * HIP graph per band of 64 positions (the decode attention's split layout
- * follows the band), before the first launch of the call; the graphs are
- * cached on the kv handle and dropped when any argument changes. Each step is
- * then one graph launch on `stream`, and the host never synchronises inside
- * the loop. Requires vocab > 0 and length + n_steps <= min(capacity,
+ * (d_token_io is read and written by every step). Per band of 64 positions
+ * (the decode attention's split layout follows the band) one step and 8
+ * consecutive steps are captured into HIP graphs, before the first launch of
+ * the call; the graphs are cached on the kv handle and dropped when any
+ * argument changes. Eight steps that stay inside one band are one graph launch
+ * on `stream`, the others one launch each, and the host never synchronises
+ * inside the loop. Requires vocab > 0 and length + n_steps <= min(capacity,
  * table_rows). */
 vlm_status vlm_decode_loop(const vlm_model_desc* desc, const vlm_layer* h_layers, const void* d_embed,
                            const void* d_final_norm, const void* d_table, vlm_kv* kv, int32_t* d_token_io,

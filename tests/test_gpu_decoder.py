@@ -121,6 +121,28 @@ def test_graph_replays_between_eager_work_equal_eager_steps(rt):
         assert np.array_equal(ka[:, :T], kb[:, :T]) and np.array_equal(va[:, :T], vb[:, :T])
 
 
+def test_multi_step_graphs_equal_one_step_graphs(rt, monkeypatch):
+    """bf16 4B-class layer shape, 37 graph-loop steps from position 43: two 8-step launches, five
+    single steps up to the band boundary at 64, two more 8-step launches and five single steps at
+    the end. Launching 8 steps per graph inside a band (the default) and one step per graph
+    (VLM_DEC_GRAPH_STEPS=1) give bitwise the same ids and cache slots."""
+    pipeline, _ = rt
+    cfg = vs.scaled(vs.C4, n_layers=2, vocab=4096, seq=43, n_img=8, img_start=8, decode_steps=37, capacity=128,
+                    name="c4_2layer_graph_steps")
+    glob, layers = make(cfg)
+    runs = []
+    for steps in ("8", "1"):
+        monkeypatch.setenv("VLM_DEC_GRAPH_STEPS", steps)
+        r = gpu_run(pipeline, cfg, glob, layers)
+        r.prefill()
+        ids = [int(r.first_token()[0])] + [int(i) for i in r.decode(cfg.decode_steps, loop=True)]
+        runs.append((ids, [kv_host(r, l) for l in range(cfg.n_layers)]))
+    assert runs[0][0] == runs[1][0]
+    T = cfg.seq + cfg.decode_steps
+    for (ka, va), (kb, vb) in zip(runs[0][1], runs[1][1]):
+        assert np.array_equal(ka[:, :T], kb[:, :T]) and np.array_equal(va[:, :T], vb[:, :T])
+
+
 def test_embed_inject_bit_exact(rt):
     pipeline, _ = rt
     cfg = vs.C1
