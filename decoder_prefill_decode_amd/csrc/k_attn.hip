@@ -736,79 +736,53 @@ DecSplitPlan attn_decode_plan(int capacity, int t) {
     return p;
 }
 
+// The rotation phase of a decode attention block for KV head g, shared by both
+// forms: wavefront w takes the items w, w + NW, ... of (the G q heads of the
+// group, the new k, the new v); lane i < D/2 holds rotation pair i. load()
+// requests the projections, norm gains and the RoPE row of position t (staged
+// once per token by the embed kernel): no address depends on the device
+// length, so nothing waits for it. apply() runs QK-Norm + RoPE, leaves the
+// rounded q heads in qs and, in the block owning slot t, the new k / v in
+// knew / vnew and in the cache.
 template <class T, int D, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs a) {
-    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16, KSTEP = NW * 4;
-    constexpr int PS = D + 4;  // partial row: o[D], m, l, pad
-    constexpr int NB = G <= 2 ? kDecSteps : (G == 4 ? kDecSteps / 2 : kDecSteps / 4);  // steps per batch
-    constexpr int NI = (G + 2 + NW - 1) / NW;  // rotation items (G q heads, k, v) per wavefront
-    __shared__ float qs[G][D];
-    __shared__ __attribute__((aligned(16))) T knew[D];
-    __shared__ __attribute__((aligned(16))) T vnew[D];
-    // LDS merge: one (m, l, o) partial per 16-lane quarter (NQ = NW * 4 of them) for groups of 4+
-    // query heads whose partials fit (the register merge there costs 2 * G * 8 permlane swaps per
-    // lane); otherwise the quarters merge in registers first and one partial per wavefront is stored
-    constexpr bool QMERGE = G >= 4 && NW * 4 * G * D * 4 <= 48 * 1024;
-    constexpr int NQ = QMERGE ? NW * 4 : NW;
-    __shared__ float sm_m[NQ][G], sm_l[NQ][G];
-    __shared__ float sm_o[NQ][G][D];
-    const int g = blockIdx.x, sp = blockIdx.y;
-    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
-    const int chunk = a.chunk;
-    const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
-    const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;  // key steps of the slot range
-    const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
-    const T* Vg = (const T*)a.vc + (size_t)g * a.W * D;
-    const int jl = max(kend - 1, 0);  // a valid slot for clamped requests
-
-    // (1) K/V rows of the first batch, then the projections to rotate
-    u32x4 kr[NB][CPL], vr[NB][CPL];
-    const int jw = k0 + w * 4 + kq;  // this quarter's key in step 0
-    auto request = [&](int s0) {
-#pragma unroll
-        for (int b = 0; b < NB; b++) {
-            if (s0 + b < nst) {  // uniform over the block
-                const int j = min(jw + (s0 + b) * KSTEP, jl);
-#pragma unroll
-                for (int c = 0; c < CPL; c++) {
-                    const int ch = min(sub + 16 * c, CH - 1);
-                    kr[b][c] = *reinterpret_cast<const u32x4*>(Kg + (size_t)j * D + ch * VEC);
-                    vr[b][c] = *reinterpret_cast<const u32x4*>(Vg + (size_t)j * D + ch * VEC);
-                }
-            }
-        }
-    };
-    request(0);
-    const int half = D / 2, sd = D / a.segments, sh = sd / 2;
-    const bool on = lane < half;
-    const int lp = on ? lane : 0;
-    const int i0 = (lp / sh) * sd + lp % sh, i1 = i0 + sh;
-    // inputs of a rotated head: the adjacent pair for interleaved RoPE (V keeps i0, i1)
-    const int r0 = a.interleave ? (lp / sh) * sd + 2 * (lp % sh) : i0, r1 = a.interleave ? r0 + 1 : i1;
-    // gain index: input order if the norm runs before the rotation, output order after it
-    const int n0 = a.norm_after ? i0 : r0, n1 = a.norm_after ? i1 : r1;
+struct DecRotation {
+    static constexpr int NI = (G + 2 + NW - 1) / NW;  // items per wavefront
     float x0[NI], x1[NI], g0[NI], g1[NI];
-#pragma unroll
-    for (int ii = 0; ii < NI; ii++) {
-        const int it = min(w + ii * NW, G + 1);
-        const bool isq = it < G, isk = it == G;
-        const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
-        const float* src = a.qkv + (size_t)row * D;
-        const T* gn = (const T*)(isq ? a.qn : a.kn);
-        const T* gp = (it <= G && gn) ? gn : (const T*)a.kc;  // any valid address when unused
-        x0[ii] = src[it <= G ? r0 : i0];
-        x1[ii] = src[it <= G ? r1 : i1];
-        g0[ii] = Elt<T>::ld(gp, n0);
-        g1[ii] = Elt<T>::ld(gp, n1);
-    }
-    const float c0 = a.rope[i0], c1 = a.rope[i1], s0 = a.rope[D + i0], s1 = a.rope[D + i1];
-    __builtin_amdgcn_sched_barrier(0);
+    float c0, c1, s0, s1;
+    int i0, i1;
+    bool on;
 
-    // (2) the valid range, then QK-Norm + RoPE of q (G heads) and of the owner's new k / v
-    const int t = a.len[0];
-    const int k1 = min(t + 1, kend);
-    const bool own = k0 <= t && t < kend;
-    {
+    __device__ __forceinline__ void load(const DecAttnArgs& a, int g, int w, int lane) {
+        const int half = D / 2, sd = D / a.segments, sh = sd / 2;
+        on = lane < half;
+        const int lp = on ? lane : 0;
+        i0 = (lp / sh) * sd + lp % sh;
+        i1 = i0 + sh;
+        // inputs of a rotated head: the adjacent pair for interleaved RoPE (V keeps i0, i1)
+        const int r0 = a.interleave ? (lp / sh) * sd + 2 * (lp % sh) : i0, r1 = a.interleave ? r0 + 1 : i1;
+        // gain index: input order if the norm runs before the rotation, output order after it
+        const int n0 = a.norm_after ? i0 : r0, n1 = a.norm_after ? i1 : r1;
+#pragma unroll
+        for (int ii = 0; ii < NI; ii++) {
+            const int it = min(w + ii * NW, G + 1);
+            const bool isq = it < G, isk = it == G;
+            const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
+            const float* src = a.qkv + (size_t)row * D;
+            const T* gn = (const T*)(isq ? a.qn : a.kn);
+            const T* gp = (it <= G && gn) ? gn : (const T*)a.kc;  // any valid address when unused
+            x0[ii] = src[it <= G ? r0 : i0];
+            x1[ii] = src[it <= G ? r1 : i1];
+            g0[ii] = Elt<T>::ld(gp, n0);
+            g1[ii] = Elt<T>::ld(gp, n1);
+        }
+        c0 = a.rope[i0];
+        c1 = a.rope[i1];
+        s0 = a.rope[D + i0];
+        s1 = a.rope[D + i1];
+    }
+
+    __device__ __forceinline__ void apply(const DecAttnArgs& a, int g, int w, int t, bool own, float (*qs)[D],
+                                          T* knew, T* vnew) {
 #pragma unroll
         for (int ii = 0; ii < NI; ii++) {
             const int it = w + ii * NW;
@@ -846,6 +820,59 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs 
             }
         }
     }
+};
+
+template <class T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_fused_kernel(DecAttnArgs a) {
+    constexpr int VEC = 16 / sizeof(T), CH = D / VEC, CPL = (CH + 15) / 16, KSTEP = NW * 4;
+    constexpr int PS = D + 4;  // partial row: o[D], m, l, pad
+    constexpr int NB = G <= 2 ? kDecSteps : (G == 4 ? kDecSteps / 2 : kDecSteps / 4);  // steps per batch
+    __shared__ float qs[G][D];
+    __shared__ __attribute__((aligned(16))) T knew[D];
+    __shared__ __attribute__((aligned(16))) T vnew[D];
+    // LDS merge: one (m, l, o) partial per 16-lane quarter (NQ = NW * 4 of them) for groups of 4+
+    // query heads whose partials fit (the register merge there costs 2 * G * 8 permlane swaps per
+    // lane); otherwise the quarters merge in registers first and one partial per wavefront is stored
+    constexpr bool QMERGE = G >= 4 && NW * 4 * G * D * 4 <= 48 * 1024;
+    constexpr int NQ = QMERGE ? NW * 4 : NW;
+    __shared__ float sm_m[NQ][G], sm_l[NQ][G];
+    __shared__ float sm_o[NQ][G][D];
+    const int g = blockIdx.x, sp = blockIdx.y;
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, sub = lane % 16, kq = lane / 16;
+    const int chunk = a.chunk;
+    const int k0 = sp * chunk, kend = min(a.W, k0 + chunk);
+    const int nst = kend > k0 ? (kend - k0 + KSTEP - 1) / KSTEP : 0;  // key steps of the slot range
+    const T* Kg = (const T*)a.kc + (size_t)g * a.W * D;
+    const T* Vg = (const T*)a.vc + (size_t)g * a.W * D;
+    const int jl = max(kend - 1, 0);  // a valid slot for clamped requests
+
+    // (1) K/V rows of the first batch, then the projections to rotate
+    u32x4 kr[NB][CPL], vr[NB][CPL];
+    const int jw = k0 + w * 4 + kq;  // this quarter's key in step 0
+    auto request = [&](int s0) {
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            if (s0 + b < nst) {  // uniform over the block
+                const int j = min(jw + (s0 + b) * KSTEP, jl);
+#pragma unroll
+                for (int c = 0; c < CPL; c++) {
+                    const int ch = min(sub + 16 * c, CH - 1);
+                    kr[b][c] = *reinterpret_cast<const u32x4*>(Kg + (size_t)j * D + ch * VEC);
+                    vr[b][c] = *reinterpret_cast<const u32x4*>(Vg + (size_t)j * D + ch * VEC);
+                }
+            }
+        }
+    };
+    request(0);
+    DecRotation<T, D, G, NW> rot;
+    rot.load(a, g, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) the valid range, then QK-Norm + RoPE of q (G heads) and of the owner's new k / v
+    const int t = a.len[0];
+    const int k1 = min(t + 1, kend);
+    const bool own = k0 <= t && t < kend;
+    rot.apply(a, g, w, t, own, qs, knew, vnew);
     __syncthreads();
 
     float qf[G][CPL][VEC];
@@ -1038,7 +1065,6 @@ template <int D, int G, int NW, int NT>
 __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(DecAttnArgs a) {
     typedef bf16_t T;
     constexpr int KS = (D + 31) / 32, DB = D / 16, PS = D + 4;
-    constexpr int NI = (G + 2 + NW - 1) / NW;  // rotation items (G q heads, k, v) per wavefront
     static_assert(D % 16 == 0 && G <= 16, "16-dim blocks, at most 16 query heads per KV head");
     __shared__ float qs[G][D];
     __shared__ __attribute__((aligned(16))) T knew[D];
@@ -1074,69 +1100,15 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(DecAttnArgs a
         }
     };
     request(0);
-    const int half = D / 2, sd = D / a.segments, sh = sd / 2;
-    const bool on = lane < half;
-    const int lp = on ? lane : 0;
-    const int i0 = (lp / sh) * sd + lp % sh, i1 = i0 + sh;
-    const int r0 = a.interleave ? (lp / sh) * sd + 2 * (lp % sh) : i0, r1 = a.interleave ? r0 + 1 : i1;
-    const int n0 = a.norm_after ? i0 : r0, n1 = a.norm_after ? i1 : r1;
-    float x0[NI], x1[NI], g0[NI], g1[NI];
-#pragma unroll
-    for (int ii = 0; ii < NI; ii++) {
-        const int it = min(w + ii * NW, G + 1);
-        const bool isq = it < G, isk = it == G;
-        const int row = isq ? g * G + it : (isk ? a.nq + g : a.nq + a.nkv + g);
-        const float* src = a.qkv + (size_t)row * D;
-        const T* gn = (const T*)(isq ? a.qn : a.kn);
-        const T* gp = (it <= G && gn) ? gn : (const T*)a.kc;  // any valid address when unused
-        x0[ii] = src[it <= G ? r0 : i0];
-        x1[ii] = src[it <= G ? r1 : i1];
-        g0[ii] = Elt<T>::ld(gp, n0);
-        g1[ii] = Elt<T>::ld(gp, n1);
-    }
-    const float c0 = a.rope[i0], c1 = a.rope[i1], s0 = a.rope[D + i0], s1 = a.rope[D + i1];
+    DecRotation<T, D, G, NW> rot;
+    rot.load(a, g, w, lane);
     __builtin_amdgcn_sched_barrier(0);
 
     // (2) the valid range, then QK-Norm + RoPE of q (G heads) and of the owner's new k / v
     const int t = a.len[0];
     const int k1 = min(t + 1, kend);
     const bool own = k0 <= t && t < kend;
-#pragma unroll
-    for (int ii = 0; ii < NI; ii++) {
-        const int it = w + ii * NW;
-        if (it >= G + (own ? 2 : 0)) continue;  // uniform per wavefront
-        const bool isq = it < G, isk = it == G;
-        const bool rot = isq || isk, norm = rot && (isq ? a.qn : a.kn) != nullptr;
-        float y0 = on ? x0[ii] : 0.f, y1 = on ? x1[ii] : 0.f;
-        if (norm && !a.norm_after) {
-            const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
-            y0 = y0 * r * g0[ii];
-            y1 = y1 * r * g1[ii];
-        }
-        if (rot) {
-            const float z0 = y0 * c0 - y1 * s0;
-            const float z1 = y1 * c1 + y0 * s1;
-            y0 = z0;
-            y1 = z1;
-        }
-        if (norm && a.norm_after) {
-            const float r = rsqrtf(wave_sum(y0 * y0 + y1 * y1) / (float)D + a.eps);
-            y0 = y0 * r * g0[ii];
-            y1 = y1 * r * g1[ii];
-        }
-        if (!on) continue;
-        if (isq) {
-            qs[it][i0] = Elt<T>::rnd(y0);
-            qs[it][i1] = Elt<T>::rnd(y1);
-        } else {
-            T* cache = (T*)(isk ? a.kc : a.vc) + ((size_t)g * a.W + t) * D;
-            T* lds = isk ? knew : vnew;
-            Elt<T>::st(lds, i0, y0);
-            Elt<T>::st(lds, i1, y1);
-            Elt<T>::st(cache, i0, y0);
-            Elt<T>::st(cache, i1, y1);
-        }
-    }
+    rot.apply(a, g, w, t, own, qs, knew, vnew);
     __syncthreads();
 
     // q^T operand (lane l: head l % 16, dims 32 ks + 8 (l / 16) .. +7; zero past G or D)
