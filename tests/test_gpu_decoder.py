@@ -291,6 +291,10 @@ EDGE = [
     # bf16 4B-class layer shape, ragged prompt with no image rows
     vs.scaled(vs.C4, n_layers=2, vocab=4096, seq=77, n_img=0, img_start=0, decode_steps=6, capacity=96,
               name="c4_s77"),
+    # bf16 4B-class layer shape (the matrix-core decode attention): a 90-slot window, not a multiple of
+    # the 16-key tile, filled to its last slot (the last split's tile reaches past the window)
+    vs.scaled(vs.C4, n_layers=2, vocab=4096, seq=70, n_img=10, img_start=8, decode_steps=20, capacity=90,
+              name="c4_window90_full"),
 ]
 
 
