@@ -652,15 +652,20 @@ vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_fina
         return fail(VLM_ERR_ARG, "NULL or misaligned pointer");
     Ws w;
     if ((s = check_ws(desc, S, d_ws, ws_bytes, &w))) return s;
+    // after the S normalised rows (the only other regions this call uses): the logits when the caller
+    // passes none, then the row argmax's partial keys
     float* logits = d_logits;
-    if (!logits) {  // right after the S normalised rows (the only other region this call uses)
-        const size_t off = w.h + al256((size_t)S * desc->hidden * esize(desc->dtype));
-        const size_t need = off + (size_t)S * desc->vocab * 4;
-        if (need > ws_bytes)
-            return fail(VLM_ERR_WORKSPACE, "%d rows x vocab %d logits need %zu workspace bytes, got %zu; pass d_logits",
-                        S, desc->vocab, need, ws_bytes);
+    size_t off = w.h + al256((size_t)S * desc->hidden * esize(desc->dtype));
+    if (!logits) {
         logits = (float*)P(d_ws, off);
+        off += al256((size_t)S * desc->vocab * 4);
     }
+    const size_t need = off + (size_t)S * argmax_rows_pieces(desc->vocab) * 8;
+    if (need > ws_bytes)
+        return fail(VLM_ERR_WORKSPACE, "%d rows x vocab %d %sneed %zu workspace bytes, got %zu%s", S, desc->vocab,
+                    d_logits ? "argmax keys " : "logits and argmax keys ", need, ws_bytes,
+                    d_logits ? "" : "; pass d_logits");
+    auto* keys = (unsigned long long*)P(d_ws, off);
     if (S == 0) return ok();
     const int dt = desc->dtype, H = desc->hidden;
     void* hbuf = P(d_ws, w.h);
@@ -668,7 +673,7 @@ vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_fina
     GemmArgs g{};
     g.A = hbuf; g.B = d_table; g.out = logits; g.M = S; g.N = desc->vocab; g.K = H; g.ldo = desc->vocab;
     HIP_TRY(launch_gemm(dt, Epi::StoreF32, g, stream));
-    HIP_TRY(launch_argmax_rows(logits, S, desc->vocab, desc->vocab, d_tokens_out, stream));
+    HIP_TRY(launch_argmax_rows(logits, S, desc->vocab, desc->vocab, d_tokens_out, keys, stream));
     return ok();
 }
 

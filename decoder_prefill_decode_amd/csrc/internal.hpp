@@ -76,7 +76,11 @@ hipError_t launch_argmax_final(const unsigned long long* partials, int nblocks, 
                                int32_t* kv_len, hipStream_t st);
 
 // out[r] = argmax of logits row r (r < S, row stride ld; lowest index on ties, -1 for a non-finite row).
-hipError_t launch_argmax_rows(const float* logits, int S, int V, int ld, int32_t* out, hipStream_t st);
+// Row argmax of S logits rows (row r at logits + r * ld): argmax_rows_pieces(V) blocks per row write
+// partial keys to part [S][argmax_rows_pieces(V)], then one wavefront per row reduces them.
+int argmax_rows_pieces(int V);
+hipError_t launch_argmax_rows(const float* logits, int S, int V, int ld, int32_t* out, unsigned long long* part,
+                              hipStream_t st);
 
 // Row norms producing the GEMM operand (model type): RMSNorm (shift == null, layer == false)
 // or LayerNorm (layer == true, shift may be null).

@@ -575,56 +575,50 @@ __global__ __launch_bounds__(1024) void argmax_final_kernel(const unsigned long 
     }
 }
 
-// Row-wise argmax of a logits matrix (the multi-token verify head): block r
-// scans row r with the same u64 keys (largest logit, lowest index; -1 when the
-// row holds a non-finite value). Each thread requests U 16-byte chunks of the
-// row (indices clamped) before it compares any of them, so a 128256-entry row
-// takes four memory round trips instead of one per element.
+// Row-wise argmax of a logits matrix (the multi-token verify head) in two launches, with the
+// u64 keys of the lm_head (largest logit, lowest index; ~0 for a non-finite value, which wins and
+// gives -1): block (b, r) scans piece b of row r, `piece` consecutive entries (a multiple of 4),
+// and writes its best key to part[r * gridDim.x + b]; one wavefront per row then takes the
+// largest of the row's keys. (One block per row left 8 CUs to scan a 128256-entry row each:
+// 16.6 us for 8 rows.) Each thread requests U 16-byte chunks (indices clamped) before it
+// compares any of them.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
     return isfinite(v) ? (((unsigned long long)ordered_key(v)) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n)
                        : ~0ull;
 }
 
-__global__ __launch_bounds__(1024) void argmax_rows_kernel(const float* __restrict__ logits, int V, int ld,
-                                                           int32_t* __restrict__ out) {
-    constexpr int U = 8, NT = 1024;
+__global__ __launch_bounds__(256) void argmax_rows_part_kernel(const float* __restrict__ logits, int V, int ld,
+                                                               int piece, unsigned long long* __restrict__ part) {
+    constexpr int U = 4, NT = 256;
     __shared__ unsigned long long sm[NT / kWave];
-    const float* row = logits + (size_t)blockIdx.x * ld;
-    const int tid = threadIdx.x;
-    unsigned long long best = 0ull;
-    int tail = 0;  // first element the scalar loop covers
-    if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {
-        const int nv = V / 4;
+    const float* row = logits + (size_t)blockIdx.y * ld;
+    const int tid = threadIdx.x, n0 = blockIdx.x * piece, n1 = min(V, n0 + piece);
+    unsigned long long best = 0ull;  // below every key
+    int tail = n0;                   // first element the scalar loop covers
+    if (n1 > n0 && (reinterpret_cast<uintptr_t>(row + n0) & 15) == 0) {
+        const int nv = (n1 - n0) / 4;
+        const float* base = row + n0;
         for (int c0 = 0; c0 < nv; c0 += NT * U) {
             f32x4 r[U];
 #pragma unroll
             for (int u = 0; u < U; u++)
-                r[u] = *reinterpret_cast<const f32x4*>(row + 4 * (size_t)min(c0 + tid + NT * u, nv - 1));
+                r[u] = *reinterpret_cast<const f32x4*>(base + 4 * (size_t)min(c0 + tid + NT * u, nv - 1));
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int c = c0 + tid + NT * u;
                 if (c < nv)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const unsigned long long key = argmax_key(r[u][e], 4 * c + e);
+                        const unsigned long long key = argmax_key(r[u][e], n0 + 4 * c + e);
                         best = key > best ? key : best;
                     }
             }
         }
-        tail = 4 * nv;
+        tail = n0 + 4 * nv;
     }
-    for (int n0 = tail; n0 < V; n0 += NT * U) {
-        float r[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) r[u] = row[min(n0 + tid + NT * u, V - 1)];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int n = n0 + tid + NT * u;
-            if (n < V) {
-                const unsigned long long key = argmax_key(r[u], n);
-                best = key > best ? key : best;
-            }
-        }
+    for (int n = tail + tid; n < n1; n += NT) {
+        const unsigned long long key = argmax_key(row[n], n);
+        best = key > best ? key : best;
     }
     for (int off = kWave / 2; off > 0; off >>= 1) {
         const unsigned long long o = __shfl_xor(best, off);
@@ -634,14 +628,32 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const float* __restri
     __syncthreads();
     if (tid == 0) {
         unsigned long long b = sm[0];
+#pragma unroll
         for (int i = 1; i < NT / kWave; i++) b = sm[i] > b ? sm[i] : b;
-        out[blockIdx.x] = b == ~0ull ? -1 : (int32_t)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+        part[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = b;
     }
 }
 
-hipError_t launch_argmax_rows(const float* logits, int S, int V, int ld, int32_t* out, hipStream_t st) {
+__global__ __launch_bounds__(64) void argmax_rows_final_kernel(const unsigned long long* __restrict__ part, int nb,
+                                                               int32_t* __restrict__ out) {
+    const int lane = threadIdx.x;
+    unsigned long long best = lane < nb ? part[(size_t)blockIdx.x * nb + lane] : 0ull;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off);
+        best = o > best ? o : best;
+    }
+    if (lane == 0) out[blockIdx.x] = best == ~0ull ? -1 : (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+}
+
+int argmax_rows_pieces(int V) { return V / 2048 < 1 ? 1 : (V / 2048 > 32 ? 32 : V / 2048); }
+
+hipError_t launch_argmax_rows(const float* logits, int S, int V, int ld, int32_t* out, unsigned long long* part,
+                              hipStream_t st) {
     if (S <= 0) return hipSuccess;
-    argmax_rows_kernel<<<S, 1024, 0, st>>>(logits, V, ld, out);
+    const int nb = argmax_rows_pieces(V);
+    const int piece = 4 * ((V + 4 * nb - 1) / (4 * nb));
+    argmax_rows_part_kernel<<<dim3(nb, S), 256, 0, st>>>(logits, V, ld, piece, part);
+    argmax_rows_final_kernel<<<S, kWave, 0, st>>>(part, nb, out);
     return hipGetLastError();
 }
 

@@ -304,9 +304,12 @@ vlm_status vlm_lmhead_argmax_noalloc(const vlm_model_desc* desc, const void* d_f
  * the table (an MFMA GEMM), then d_tokens_out[r] = argmax of row r (lowest
  * index on ties; -1 for a non-finite row). d_logits [S][V] fp32 receives the
  * logits when non-NULL; with NULL they live in the workspace after the S
- * normalised rows, which then needs 256-aligned S * H * dtype-size bytes plus
- * S * V * 4 bytes (else VLM_ERR_WORKSPACE, nothing enqueued); the workspace of
- * vlm_workspace_bytes(desc, max_rows >= S) is required in any case. */
+ * normalised rows. The argmax then keeps S * P u64 partial keys after that,
+ * P = min(32, max(1, V / 2048)) pieces per row. The workspace must hold
+ * 256-aligned S * H * dtype-size bytes, then (without d_logits) 256-aligned
+ * S * V * 4 bytes, then the keys (else VLM_ERR_WORKSPACE, nothing enqueued);
+ * the workspace of vlm_workspace_bytes(desc, max_rows >= S) is required in
+ * any case. */
 vlm_status vlm_lmhead_argmax_rows(const vlm_model_desc* desc, const void* d_final_norm, const void* d_table,
                                   const float* d_x, int32_t S, int32_t* d_tokens_out, float* d_logits, void* d_ws,
                                   size_t ws_bytes, hipStream_t stream);

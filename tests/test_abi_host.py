@@ -192,12 +192,13 @@ def test_verify_commit_and_status_argument_checks():
 
 def test_verify_head_logits_scratch_is_checked_against_the_workspace_bytes():
     """With no logits buffer the verify head keeps S x V fp32 logits in the workspace, after the S
-    normalised rows, and checks that against the caller's workspace size (a vocabulary of 128256
-    does not fit the S-row layout's own split scratch)."""
+    normalised rows, then the row argmax's partial keys (32 u64 per row at this vocabulary), and
+    checks that against the caller's workspace size (a vocabulary of 128256 does not fit the S-row
+    layout's own split scratch)."""
     d = desc(vocab=128256)
     n = C.c_size_t()
     N.call("vlm_workspace_bytes", C.byref(d), 8, C.byref(n))
-    need = 8 * 256 * 4 + 8 * 128256 * 4          # rows (already 256-aligned) + logits
+    need = 8 * 256 * 4 + 8 * 128256 * 4 + 8 * 32 * 8   # rows, logits (both already 256-aligned), keys
     assert n.value < need
     fake = C.c_void_p(256)
     tok = C.c_void_p(512)

@@ -126,6 +126,43 @@ def test_lmhead_argmax_ties_and_nonfinite(mods, dtype):
     assert int(tok[0]) == -1
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lmhead_argmax_rows_ties_pieces_and_nonfinite(mods, dtype):
+    """The verify head's row argmax (partial keys over pieces of each row, then one reduction per
+    row) on 5 rows of a 70001-entry table, so the last piece of every row is ragged:
+    - row 0 ties the table rows 1234 and 60000, which lie in different pieces: the lowest index wins;
+    - row 3's unique maximum is the table's last row;
+    - row 2 holds a NaN, which gives -1.
+    Every token equals numpy's first-maximum argmax of the logits the call returns."""
+    _, _, rt = mods
+    V, H, S = 70001, 256, 5
+    m = _head_model(rt, V, H, dtype)
+    rng = np.random.default_rng(4)
+    E = vs.to_bf16_values(rng.standard_normal((V, H)).astype(np.float32) * 0.02)
+    alt = np.where(np.arange(H) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    E[1234] = E[60000] = 0.5
+    E[V - 1] = 0.5 * alt
+    m.set_table(E, np.ones(H, np.float32))
+    ws = m.workspace(S)
+    xr = rng.standard_normal((S, H)).astype(np.float32)
+    xr[0] = 0.3
+    xr[3] = alt
+    x = torch.from_numpy(xr).to("cuda")
+    x[2, 11] = float("nan")
+    tok = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    logits = torch.empty((S, V), dtype=torch.float32, device="cuda")
+    m.lmhead_argmax_rows(x, tok, ws, logits)
+    got = [int(t) for t in tok.cpu()]
+    lg = logits.cpu().numpy()
+    assert got[0] == 1234 and got[2] == -1 and got[3] == V - 1
+    for r in (0, 1, 3, 4):
+        assert got[r] == int(np.argmax(lg[r])), r
+    tok2 = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    ws2 = torch.empty(ws.numel() + S * (H + V) * 4 + (1 << 16), dtype=torch.uint8, device="cuda")
+    m.lmhead_argmax_rows(x, tok2, ws2)     # logits kept in the workspace: the same picks
+    assert [int(t) for t in tok2.cpu()] == got
+
+
 def test_lmhead_full_vocab_matches_oracle(mods):
     _, _, rt = mods
     cfg = vs.C3
