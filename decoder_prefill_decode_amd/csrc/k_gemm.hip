@@ -19,6 +19,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -270,20 +271,25 @@ __device__ __forceinline__ void wait_stages(int k) {
 // with 64-byte rows, r % 4 picks the bank quarter and (r >> 2) & 3 the slot. (r & 7 on 128-byte
 // rows put rows r and r + 8 on the same banks: half of the GEMMs' LDS cycles were conflict stalls.)
 // Both have a period of 16 rows.
-template <int BK>
-__device__ __forceinline__ int lds_swz(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+template <int CPR>
+__device__ __forceinline__ int lds_swz(int r) { return CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 
 // WGM x WGN wavefronts per block, each owning a (BM/WGM) x (BN/WGN) sub-tile.
-template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
+// T = float: a stage holds 32 floats of each row (the same 128 bytes as 64 bf16); each 16-byte
+// operand read feeds four v_mfma_f32_32x32x2f32 steps, in which the lanes of half h contribute
+// column 8q + 4h + e (step e of column quad q; the same permutation on A and B leaves the
+// contraction unchanged).
+template <class T, int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
-    static_assert(BK == 64 || BK == 32, "stage depth");
+    constexpr int VEC = 16 / sizeof(T), LDI = 1024 / sizeof(T);  // elements per 16-byte chunk / load instruction
+    static_assert(BK * sizeof(T) == 128 || BK * sizeof(T) == 64, "stage depth: 128- or 64-byte rows");
     constexpr int NW = WGM * WGN, WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
-    constexpr int CPR = BK / 8, RPI = 64 / CPR;  // 16-byte chunks per row, rows per load instruction
+    constexpr int CPR = BK / VEC, RPI = 64 / CPR;  // 16-byte chunks per row, rows per load instruction
     constexpr int AI = BM / (RPI * NW), BI = BN / (RPI * NW);  // load instructions per wave per stage
     static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN && TM >= 1 && TN >= 1, "tile / wavefront grid");
     constexpr int LPS = AI + BI, STAGE = (BM + BN) * BK;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
+    T* smem = reinterpret_cast<T*>(smem_raw);
 
     const int M = a.M, N = a.N, K = a.K;
     const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
@@ -292,28 +298,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int wm = w / WGN, wn = w % WGN, h = lane / 32, l32 = lane % 32;
-    const bf16_t* A = (const bf16_t*)a.A;
-    const bf16_t* B = (const bf16_t*)a.B;
+    const T* A = (const T*)a.A;
+    const T* B = (const T*)a.B;
 
     // this lane's source row/chunk in each of the wave's load instructions (rows past M / N are clamped:
     // their products land in output rows / columns the epilogue never stores)
     // (the chunk depends on the tile row, whose swizzle has a period of 16 rows: with 8-row load
     // instructions it alternates between instructions)
     const int lr = lane / CPR;
-    const bf16_t* ga[AI];
-    const bf16_t* gb[BI];
+    const T* ga[AI];
+    const T* gb[BI];
     int lca[AI], lcb[BI];
 #pragma unroll
     for (int i = 0; i < AI; i++) {
         ga[i] = A + (size_t)min(m0 + (w * AI + i) * RPI + lr, M - 1) * K;
-        lca[i] = (lane % CPR) ^ lds_swz<BK>((w * AI + i) * RPI + lr);
+        lca[i] = (lane % CPR) ^ lds_swz<CPR>((w * AI + i) * RPI + lr);
     }
 #pragma unroll
     for (int i = 0; i < BI; i++) {
         gb[i] = B + (size_t)min(n0 + (w * BI + i) * RPI + lr, N - 1) * K;
-        lcb[i] = (lane % CPR) ^ lds_swz<BK>((w * BI + i) * RPI + lr);
+        lcb[i] = (lane % CPR) ^ lds_swz<CPR>((w * BI + i) * RPI + lr);
     }
-    const int kmax = K - 8;  // last 16-byte chunk of a row: loads of the tail stage are clamped to it
+    const int kmax = K - VEC;  // last 16-byte chunk of a row: loads of the tail stage are clamped to it
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -332,23 +338,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     }
     // one K stage of both tiles into LDS stage ST: instruction i of wavefront w fills RPI rows (1 KiB).
     // (The source pointer is passed as const void*: the host pass silently drops the kernel otherwise.)
-#define VLM_LDS_KC(KOFF, LC) (TAIL ? min((KOFF) + (LC) * 8, kmax) : (KOFF) + (LC) * 8)
+#define VLM_LDS_KC(KOFF, LC) (TAIL ? min((KOFF) + (LC) * VEC, kmax) : (KOFF) + (LC) * VEC)
 #define VLM_LDS_STAGE(KOFF, ST)                                                                              \
     do {                                                                                                     \
         _Pragma("unroll") for (int i = 0; i < AI; i++) __builtin_amdgcn_global_load_lds(                     \
-            (const void*)(ga[i] + VLM_LDS_KC(KOFF, lca[i])), (lds_void*)((ST) + (w * AI + i) * 512), 16, 0, 0); \
+            (const void*)(ga[i] + VLM_LDS_KC(KOFF, lca[i])), (lds_void*)((ST) + (w * AI + i) * LDI), 16, 0, 0); \
         _Pragma("unroll") for (int i = 0; i < BI; i++) __builtin_amdgcn_global_load_lds(                     \
-            (const void*)(gb[i] + VLM_LDS_KC(KOFF, lcb[i])), (lds_void*)((ST) + BM * BK + (w * BI + i) * 512), \
+            (const void*)(gb[i] + VLM_LDS_KC(KOFF, lcb[i])), (lds_void*)((ST) + BM * BK + (w * BI + i) * LDI), \
             16, 0, 0);                                                                                       \
     } while (0)
     // the last stage (global index nk_all - 1) of a K that is not a multiple of BK: zero its columns
     // ktail..BK-1 in every A and B row once they have landed (callers hold a barrier on both sides)
-    auto zero_tail = [&](int kt_local, bf16_t* st) {
+    auto zero_tail = [&](int kt_local, T* st) {
         if (!TAIL || ktail == BK || kt0 + kt_local != nk_all - 1) return;  // uniform
-        const int c0 = ktail / 8;
+        const int c0 = ktail / VEC;
         for (int idx = tid; idx < (BM + BN) * CPR; idx += NW * kWave) {
             const int r = idx / CPR, c = idx % CPR;
-            if (c >= c0) *reinterpret_cast<u32x4*>(st + r * BK + ((c ^ lds_swz<BK>(r)) * 8)) = u32x4{0, 0, 0, 0};
+            if (c >= c0) *reinterpret_cast<u32x4*>(st + r * BK + ((c ^ lds_swz<CPR>(r)) * VEC)) = u32x4{0, 0, 0, 0};
         }
         __syncthreads();
     };
@@ -361,26 +367,37 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     for (int i = 0; i < TM; i++) ra[i] = wm * WM + i * 32 + l32;
 #pragma unroll
     for (int j = 0; j < TN; j++) rb[j] = BM + wn * WN + j * 32 + l32;
-    constexpr int KS = BK / 16;  // 16-wide MFMA steps per stage
-    auto read_frags = [&](const bf16_t* st, int kk, bf16x8* fa, bf16x8* fb) {
+    constexpr int KS = BK / (2 * VEC);  // fragment steps per stage (one 16-byte read per operand row and half)
+    using Frag = typename std::conditional<sizeof(T) == 2, bf16x8, f32x4>::type;
+    auto read_frags = [&](const T* st, int kk, Frag* fa, Frag* fb) {
         const int c = kk * 2 + h;
 #pragma unroll
         for (int i = 0; i < TM; i++)
-            fa[i] = *reinterpret_cast<const bf16x8*>(st + ra[i] * BK + ((c ^ lds_swz<BK>(ra[i])) * 8));
+            fa[i] = *reinterpret_cast<const Frag*>(st + ra[i] * BK + ((c ^ lds_swz<CPR>(ra[i])) * VEC));
 #pragma unroll
         for (int j = 0; j < TN; j++)
-            fb[j] = *reinterpret_cast<const bf16x8*>(st + rb[j] * BK + ((c ^ lds_swz<BK>(rb[j])) * 8));
+            fb[j] = *reinterpret_cast<const Frag*>(st + rb[j] * BK + ((c ^ lds_swz<CPR>(rb[j])) * VEC));
     };
     // a wavefront issuing its MFMA burst runs at raised priority, so the arbiter favours it over the
     // other wavefronts' load issue and LDS reads (prefill 0.9% faster over 5 A/B pairs on the 36-layer
     // stack, results unchanged)
-    auto mfmas = [&](const bf16x8* fa, const bf16x8* fb) {
+    auto mfmas = [&](const Frag* fa, const Frag* fb) {
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+            for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int j = 0; j < TN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][e], fb[j][e], acc[i][j], 0, 0, 0);
+        }
         __builtin_amdgcn_s_setprio(0);
     };
     // Software pipeline: the fragments of step kk+1 are read while the MFMAs of step kk run, and
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     // stage kt, so LDS reads overlap the matrix cores within each wavefront. (Reading a whole
     // stage's fragments before its first MFMA measured 5-12% slower on the prefill shapes.)
     {
-        bf16x8 fa[2][TM], fb[2][TN];
+        Frag fa[2][TM], fb[2][TN];
         if (nk > 0) {
             wait_stages<LPS, P - 2>(nk - 1);
             __builtin_amdgcn_s_barrier();
@@ -398,7 +415,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
             read_frags(smem, 0, fa[0], fb[0]);
         }
         for (int kt = 0; kt < nk; kt++) {
-            const bf16_t* st = smem + (kt % P) * STAGE;
+            const T* st = smem + (kt % P) * STAGE;
 #pragma unroll
             for (int kk = 0; kk < KS - 1; kk++) {
                 read_frags(st, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
@@ -418,7 +435,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_lds_kernel(GemmArgs a) {
     }
 #undef VLM_LDS_STAGE
 #undef VLM_LDS_KC
-    gemm_epilogue<bf16_t, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32, split);
+    gemm_epilogue<T, WM, WN, TM, TN, EPI, SPLIT>(a, acc, m0, n0, wm, wn, h, l32, split);
 }
 
 // Sums the split partials in split order (deterministic) and applies the epilogue.
@@ -571,21 +588,21 @@ static hipError_t run_gemm(const GemmArgs& a, int splits, hipStream_t st) {
     return run_reduce<T, EPI>(a, splits, st);
 }
 
-template <int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
+template <class T, int BM, int BN, int P, int WGM, int WGN, Epi EPI, bool SPLIT, int BK, bool TAIL>
 static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
     const int mt = (a.M + BM - 1) / BM, nt = (a.N + BN - 1) / BN;
-    const size_t smem = (size_t)P * (BM + BN) * BK * sizeof(bf16_t);
+    const size_t smem = (size_t)P * (BM + BN) * BK * sizeof(T);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK, TAIL>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_lds_kernel<T, BM, BN, P, WGM, WGN, EPI, SPLIT, BK, TAIL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    gemm_lds_kernel<BM, BN, P, WGM, WGN, EPI, SPLIT, BK, TAIL><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
+    gemm_lds_kernel<T, BM, BN, P, WGM, WGN, EPI, SPLIT, BK, TAIL><<<dim3(mt * nt, SPLIT ? splits : 1), WGM * WGN * 64, smem, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
-    return run_reduce<bf16_t, EPI>(a, splits, st);
+    return run_reduce<T, EPI>(a, splits, st);
 }
 
 // Tile and K-split choice of the direct-to-LDS kernel from a per-CU feed model.
@@ -642,8 +659,8 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
         if (a.K % 8 == 0 && a.K >= 64) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
             const LdsPlan pl = plan_lds(a, EPI == Epi::SwiGLU);
 #define VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, T_)                                            \
-    return pl.sp > 1 ? run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, true, BK_, T_>(a, pl.sp, st)     \
-                     : run_gemm_lds<BM_, BN_, P_, GM_, GN_, EPI, false, BK_, T_>(a, 1, st)
+    return pl.sp > 1 ? run_gemm_lds<bf16_t, BM_, BN_, P_, GM_, GN_, EPI, true, BK_, T_>(a, pl.sp, st)     \
+                     : run_gemm_lds<bf16_t, BM_, BN_, P_, GM_, GN_, EPI, false, BK_, T_>(a, 1, st)
 #define VLM_RUN_LDS(BM_, BN_, P_, GM_, GN_, BK_)                                                   \
     do {                                                                                          \
         if (a.K % BK_ != 0) VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, true);                     \
@@ -692,6 +709,27 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
                 bbn = c.bn;
                 bsp = sp;
             }
+        }
+    }
+    // fp32 rows of 16-byte chunks (K % 4 == 0): the same tile and split on the direct-to-LDS ring of
+    // 32-float stages (128x128 in 2 stages, 64x128 in 3, 64x64 in 4; four wavefronts of 2 x 2);
+    // VLM_F32_LDS=0 keeps the register-staged kernel (read per call, for comparison)
+    if constexpr (sizeof(T) == 4) {
+        const char* ev = getenv("VLM_F32_LDS");
+        if (a.K % 4 == 0 && a.K >= 32 && !(ev && atoi(ev) == 0)) {
+#define VLM_RUN_LDS32_T(BM_, BN_, P_, T_)                                                           \
+    return bsp > 1 ? run_gemm_lds<float, BM_, BN_, P_, 2, 2, EPI, true, 32, T_>(a, bsp, st)          \
+                   : run_gemm_lds<float, BM_, BN_, P_, 2, 2, EPI, false, 32, T_>(a, 1, st)
+#define VLM_RUN_LDS32(BM_, BN_, P_)                                                                 \
+    do {                                                                                            \
+        if (a.K % 32 != 0) VLM_RUN_LDS32_T(BM_, BN_, P_, true);                                     \
+        VLM_RUN_LDS32_T(BM_, BN_, P_, false);                                                       \
+    } while (0)
+            if (bbm == 128) VLM_RUN_LDS32(128, 128, 2);
+            if (bbn == 128) VLM_RUN_LDS32(64, 128, 3);
+            if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS32(64, 64, 4);
+#undef VLM_RUN_LDS32
+#undef VLM_RUN_LDS32_T
         }
     }
 #define VLM_RUN_REG(BM_, BN_)                                                                  \
