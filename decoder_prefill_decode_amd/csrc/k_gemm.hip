@@ -684,6 +684,21 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
 #undef VLM_RUN_LDS_T
         }
     }
+    // fp32 rows of 16-byte chunks (K % 4 == 0): the direct-to-LDS ring of 32-float stages with 64x64
+    // tiles in 4 stages (64x128 in 3 for SwiGLU, whose wavefront tiles hold whole gate/up column
+    // pairs; four wavefronts of 2 x 2), one block per tile and no K split. Measured on the vision
+    // tower (M 1288; N 1152-4304; K 1152-4304), ms per pass: 16.4 (4 or 3 stages; 2: 16.5), with a
+    // K split of up to 2 16.8, with the register-staged plan's tiles 17.6 (its splits too: 18.0),
+    // 64x128 18.1, 128x128 24.0; the register-staged kernel 20.8. VLM_F32_LDS=0 keeps the
+    // register-staged kernel (read per call, for comparison).
+    if constexpr (sizeof(T) == 4) {
+        const char* ev = getenv("VLM_F32_LDS");
+        if (a.K % 4 == 0 && a.K >= 32 && !(ev && atoi(ev) == 0)) {
+            constexpr int BN32 = EPI == Epi::SwiGLU ? 128 : 64, P32 = EPI == Epi::SwiGLU ? 3 : 4;
+            if (a.K % 32 != 0) return run_gemm_lds<float, 64, BN32, P32, 2, 2, EPI, false, 32, true>(a, 1, st);
+            return run_gemm_lds<float, 64, BN32, P32, 2, 2, EPI, false, 32, false>(a, 1, st);
+        }
+    }
     // register-staged kernel (f32, or bf16 with K % 8 != 0): tile and K split from a per-CU work
     // model fitted on the vision tower's shapes (M 322-1288, N 1152-4608, K 1152-4608, f32):
     // a CU runs ceil(blocks / 256) blocks one after another at a rate set by the tile shape, and a
@@ -709,27 +724,6 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
                 bbn = c.bn;
                 bsp = sp;
             }
-        }
-    }
-    // fp32 rows of 16-byte chunks (K % 4 == 0): the same tile and split on the direct-to-LDS ring of
-    // 32-float stages (128x128 in 2 stages, 64x128 in 3, 64x64 in 4; four wavefronts of 2 x 2);
-    // VLM_F32_LDS=0 keeps the register-staged kernel (read per call, for comparison)
-    if constexpr (sizeof(T) == 4) {
-        const char* ev = getenv("VLM_F32_LDS");
-        if (a.K % 4 == 0 && a.K >= 32 && !(ev && atoi(ev) == 0)) {
-#define VLM_RUN_LDS32_T(BM_, BN_, P_, T_)                                                           \
-    return bsp > 1 ? run_gemm_lds<float, BM_, BN_, P_, 2, 2, EPI, true, 32, T_>(a, bsp, st)          \
-                   : run_gemm_lds<float, BM_, BN_, P_, 2, 2, EPI, false, 32, T_>(a, 1, st)
-#define VLM_RUN_LDS32(BM_, BN_, P_)                                                                 \
-    do {                                                                                            \
-        if (a.K % 32 != 0) VLM_RUN_LDS32_T(BM_, BN_, P_, true);                                     \
-        VLM_RUN_LDS32_T(BM_, BN_, P_, false);                                                       \
-    } while (0)
-            if (bbm == 128) VLM_RUN_LDS32(128, 128, 2);
-            if (bbn == 128) VLM_RUN_LDS32(64, 128, 3);
-            if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS32(64, 64, 4);
-#undef VLM_RUN_LDS32
-#undef VLM_RUN_LDS32_T
         }
     }
 #define VLM_RUN_REG(BM_, BN_)                                                                  \
