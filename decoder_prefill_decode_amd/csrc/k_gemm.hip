@@ -613,7 +613,8 @@ static hipError_t run_gemm_lds(const GemmArgs& a, int splits, hipStream_t st) {
 // lone block per CU, "two" when two blocks share it), plus, for a K split,
 // 3 us and the fp32 partials written and re-read by the reduce (~4 GB/ms).
 // The constants come from timing every candidate on the decoder prefill
-// shapes (M 512-560; K 1024-9728); the model picks within ~6% of the fastest.
+// shapes (M 512-560; K 1024-9728) with two-stage rings for the 128-row tiles
+// and three for 64x128; the model picks within ~6% of the fastest.
 // The 256x192 SwiGLU tile (eight 32x192 wavefront tiles, so each wavefront
 // holds whole gate/up pairs) covers N = 19456 in 204 blocks instead of 152:
 // gate/up of the 36-layer stack 78.5 -> 71.7 us (four 64x192 wavefront tiles,
@@ -656,7 +657,7 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
     auto tiles = [&](int bm, int bn) { return (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
     const int nk = (a.K + GemmTraits<T>::BK - 1) / GemmTraits<T>::BK;
     if constexpr (sizeof(T) == 2) {
-        if (a.K % 8 == 0 && a.K >= 64) {  // direct-to-LDS pipeline; <= 72 KiB of LDS stages: two blocks per CU
+        if (a.K % 8 == 0 && a.K >= 64) {  // direct-to-LDS pipeline; rings of at most 144 KiB (one block per CU)
             const LdsPlan pl = plan_lds(a, EPI == Epi::SwiGLU);
 #define VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, T_)                                            \
     return pl.sp > 1 ? run_gemm_lds<bf16_t, BM_, BN_, P_, GM_, GN_, EPI, true, BK_, T_>(a, pl.sp, st)     \
@@ -666,6 +667,15 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
         if (a.K % BK_ != 0) VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, true);                     \
         VLM_RUN_LDS_T(BM_, BN_, P_, GM_, GN_, BK_, false);                                        \
     } while (0)
+            // The 128-row tiles keep 2 stages in flight instead of 1 (a ring of 3), 64x128 tiles 4
+            // instead of 2 (a ring of 5): on M 512-1288 a stage waits on the L2 round trip, not on the
+            // matrix cores, so more bytes in flight feed the CU faster. bf16 vision tower 4.70 -> 4.46 ms
+            // per pass, prefill of the 36-layer stack 6.83 -> 6.57 ms, of the 28-layer stack 2.82 ->
+            // 2.66 ms; one stage more again (128x128 in 4, 64x128 in 6) gained nothing. Only the depth
+            // of the ring differs, so the products are bitwise those of the shallow ring, which
+            // VLM_LDS_DEEP=0 selects (read per call, for comparison).
+            const char* dv = getenv("VLM_LDS_DEEP");
+            const bool deep = !(dv && atoi(dv) == 0);
             if constexpr (EPI == Epi::SwiGLU)
                 if (pl.bm == 256 && pl.bn == 192) VLM_RUN_LDS(256, 192, 2, 8, 1, 64);
             // an unsplit 128x256 plan whose blocks fit one round as 128x192 tiles takes those (eight
@@ -673,12 +683,23 @@ static hipError_t pick_tile(const GemmArgs& a, hipStream_t st) {
             // vision tower's fc1 (N 4304: 187 -> 253 blocks) and QKV (N 3456: 154 -> 198), bf16 tower
             // 5.05 -> 4.83 ms per pass (a four-wavefront 64x96 form: 5.07 ms)
             if constexpr (EPI != Epi::SwiGLU)
-                if (pl.bm == 128 && pl.bn == 256 && pl.sp == 1 && tiles(128, 192) <= 256)
+                if (pl.bm == 128 && pl.bn == 256 && pl.sp == 1 && tiles(128, 192) <= 256) {
+                    if (deep) VLM_RUN_LDS(128, 192, 3, 4, 2, 64);
                     VLM_RUN_LDS(128, 192, 2, 4, 2, 64);
+                }
             if (pl.bm == 256) VLM_RUN_LDS(256, 256, 2, 4, 2, 64);
-            if (pl.bm == 128 && pl.bn == 256) VLM_RUN_LDS(128, 256, 2, 2, 4, 64);
-            if (pl.bm == 128) VLM_RUN_LDS(128, 128, 2, 2, 2, 64);
-            if (pl.bn == 128) VLM_RUN_LDS(64, 128, 3, 2, 2, 64);
+            if (pl.bm == 128 && pl.bn == 256) {
+                if (deep) VLM_RUN_LDS(128, 256, 3, 2, 4, 64);
+                VLM_RUN_LDS(128, 256, 2, 2, 4, 64);
+            }
+            if (pl.bm == 128) {
+                if (deep) VLM_RUN_LDS(128, 128, 3, 2, 2, 64);
+                VLM_RUN_LDS(128, 128, 2, 2, 2, 64);
+            }
+            if (pl.bn == 128) {
+                if (deep) VLM_RUN_LDS(64, 128, 5, 2, 2, 64);
+                VLM_RUN_LDS(64, 128, 3, 2, 2, 64);
+            }
             if constexpr (EPI != Epi::SwiGLU) VLM_RUN_LDS(64, 64, 4, 2, 2, 64);
 #undef VLM_RUN_LDS
 #undef VLM_RUN_LDS_T

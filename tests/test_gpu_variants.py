@@ -138,3 +138,28 @@ def test_matrix_core_decode_attention_equals_vector_form(pipeline, monkeypatch, 
     err = rel(outs[0], outs[1])
     print(f"d{hd} g{nq // nkv} splits {splits}: matrix-core vs vector form {err:.2e}")
     assert err <= 1e-3
+
+
+def test_deep_gemm_ring_equals_two_stage_ring(pipeline, monkeypatch):
+    """The prefill GEMMs' deeper LDS rings (default) against the shallow ones (VLM_LDS_DEEP=0) on
+    the tile shapes that take them: a 2-layer bf16 vision tower at full width (128x192 QKV and fc1,
+    64x128 O, 128x256 split fc2; one window and one full-attention layer) and a one-layer prefill at
+    the 36-layer stack's width (64x128 QKV, 128x128 split O, 128x256 split down). Only the number of
+    stages in flight differs, so the outputs are bitwise equal."""
+    vcfg = vs.scaled_vit(vs.C5, dtype=vs.BF16, n_layers=2, full_layers=(1,), name="c5_vit_2l_bf16")
+    vglob = vs.vit_globals(vcfg)
+    dcfg = vs.scaled(vs.C4, n_layers=1, vocab=4096, name="c4_1l")
+    glob, layers = make(dcfg)
+    outs = {}
+    for deep in ("1", "0"):
+        monkeypatch.setenv("VLM_LDS_DEEP", deep)
+        run = pipeline.VitRun(vcfg, lambda l: vs.vit_layer_weights(vcfg, l), vglob)
+        v = run.run().cpu().numpy()
+        del run
+        drun = pipeline.DecoderRun(dcfg, lambda l: layers[l], glob)
+        x = drun.prefill().cpu().numpy()
+        del drun
+        outs[deep] = (v, x)
+    assert np.isfinite(outs["1"][0]).all() and np.isfinite(outs["1"][1]).all()
+    assert np.array_equal(outs["1"][0], outs["0"][0])
+    assert np.array_equal(outs["1"][1], outs["0"][1])
