@@ -503,10 +503,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int spli
 // summation order of norm_rows_reg_kernel, so the normalised row is bitwise the
 // one a separate norm launch would write). x[m] += sum of the partials (split
 // order) + bias, then norm_out[m] = norm(x[m]).
+// SM >= splits partial planes and NPT >= N / 256 columns per thread are requested (clamped indices),
+// so both are sized to the launch: with 8 planes and 8 columns for a 4-split, 1152-column row, 96
+// loads per thread went out for 20 distinct values (vision tower fc2 reduction 15.4 us).
 constexpr int kReduceNormMaxSplits = 8;
-template <class T, bool LAYER, int NPT>
+template <class T, bool LAYER, int NPT, int SM>
 __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs a, int splits) {
-    constexpr int SM = kReduceNormMaxSplits;
     __shared__ float red[4];
     const int m = blockIdx.x, N = a.N, tid = threadIdx.x;
     const size_t MN = (size_t)a.M * N;
@@ -571,17 +573,26 @@ static hipError_t run_reduce(const GemmArgs& a, int splits, hipStream_t st) {
     if constexpr (EPI == Epi::Resid) {
         if (a.norm_out && a.norm_gain && a.N <= 4096 && splits <= kReduceNormMaxSplits) {
             const int npt = (a.N + 255) / 256;
-#define VLM_RED_NORM(NPT_)                                                                                \
-    do {                                                                                                  \
-        if (a.norm_layer) splitk_reduce_norm_kernel<T, true, NPT_><<<a.M, 256, 0, st>>>(a, splits);       \
-        else splitk_reduce_norm_kernel<T, false, NPT_><<<a.M, 256, 0, st>>>(a, splits);                   \
+#define VLM_RED_NORM_S(NPT_, SM_)                                                                              \
+    do {                                                                                                       \
+        if (a.norm_layer) splitk_reduce_norm_kernel<T, true, NPT_, SM_><<<a.M, 256, 0, st>>>(a, splits);       \
+        else splitk_reduce_norm_kernel<T, false, NPT_, SM_><<<a.M, 256, 0, st>>>(a, splits);                   \
+    } while (0)
+#define VLM_RED_NORM(NPT_)                                  \
+    do {                                                    \
+        if (splits <= 2) VLM_RED_NORM_S(NPT_, 2);           \
+        else if (splits <= 4) VLM_RED_NORM_S(NPT_, 4);      \
+        else VLM_RED_NORM_S(NPT_, kReduceNormMaxSplits);    \
     } while (0)
             if (npt <= 2) VLM_RED_NORM(2);
             else if (npt <= 4) VLM_RED_NORM(4);
+            else if (npt <= 5) VLM_RED_NORM(5);
             else if (npt <= 8) VLM_RED_NORM(8);
+            else if (npt <= 10) VLM_RED_NORM(10);
             else if (npt <= 12) VLM_RED_NORM(12);
             else VLM_RED_NORM(16);
 #undef VLM_RED_NORM
+#undef VLM_RED_NORM_S
             const hipError_t e = hipGetLastError();
             if (e == hipSuccess && a.fused_norm) *a.fused_norm = 1;
             return e;
