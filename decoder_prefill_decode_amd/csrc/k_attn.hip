@@ -449,8 +449,10 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     constexpr int NB = (DV + 31) / 32, DP = NB * 32;
     constexpr int LDK = DQ + 4, LDV = DP + 4;
     constexpr int CH = DQ / 4, CHV = DV / 4;
-    __shared__ __attribute__((aligned(16))) float Ks[BKEY * LDK];
-    __shared__ __attribute__((aligned(16))) float Vs[BKEY * LDV];
+    // two K / V tile buffers: tile kv + 1 is requested into registers while tile kv runs on the
+    // matrix cores, and stored into the other buffer after it (one barrier per tile)
+    __shared__ __attribute__((aligned(16))) float Ks[2][BKEY * LDK];
+    __shared__ __attribute__((aligned(16))) float Vs[2][BKEY * LDV];
 
     const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave, hh = lane / 32, l32 = lane % 32;
     const int hq = blockIdx.y, g = hq / (a.nq / a.nkv);
@@ -462,7 +464,9 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     const float* Vg = (const float*)a.v + (size_t)g * a.ldkv * DV;
 
     if constexpr (DP > DV) {
-        for (int i = tid; i < BKEY * (DP - DV); i += 256) Vs[(i / (DP - DV)) * LDV + DV + i % (DP - DV)] = 0.f;
+        for (int i = tid; i < BKEY * (DP - DV); i += 256)
+#pragma unroll
+            for (int b = 0; b < 2; b++) Vs[b][(i / (DP - DV)) * LDV + DV + i % (DP - DV)] = 0.f;
     }
 
     float Qf[DQ / 2];
@@ -492,27 +496,54 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
     if constexpr (MASK == VLM_MASK_SEGMENT_ID)
         if (listed) nvis = segment_tiles<256, BKEY>(a.seg, blockIdx.x * BQ, BQ, S, a.nkeys, nkt, tlist, tflag, tlohi);
 
-    __shared__ int segs[MASK == VLM_MASK_SEGMENT_ID ? BKEY : 1];  // the tile's segment ids
-    for (int kv = 0; kv < nvis; kv++) {
-        const int kt = listed ? (int)tlist[kv] : kv;
+    __shared__ int segs[2][MASK == VLM_MASK_SEGMENT_ID ? BKEY : 1];  // the tiles' segment ids
+    auto tile_at = [&](int i) { return listed ? (int)tlist[i] : i; };
+    // K / V chunks of a tile: requested unconditionally (indices clamped), keys past nkeys zeroed when
+    // stored; the segment ids travel with them
+    constexpr int KCH = (BKEY * CH + 255) / 256, VCH = (BKEY * CHV + 255) / 256;
+    f32x4 kreg[KCH], vreg[VCH];
+    int sreg = 0;
+    auto request = [&](int kt) {
+        const int key0 = kt * BKEY;
+        if constexpr (MASK == VLM_MASK_SEGMENT_ID) sreg = a.seg[min(key0 + tid % BKEY, a.nkeys - 1)];
+#pragma unroll
+        for (int i = 0; i < KCH; i++) {
+            const int c = min(tid + 256 * i, BKEY * CH - 1), r = c / CH, d0 = (c % CH) * 4;
+            kreg[i] = *reinterpret_cast<const f32x4*>(Kg + (size_t)min(key0 + r, a.nkeys - 1) * DQ + d0);
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; i++) {
+            const int c = min(tid + 256 * i, BKEY * CHV - 1), r = c / CHV, d0 = (c % CHV) * 4;
+            vreg[i] = *reinterpret_cast<const f32x4*>(Vg + (size_t)min(key0 + r, a.nkeys - 1) * DV + d0);
+        }
+    };
+    auto stage = [&](int kt, int buf) {
         const int key0 = kt * BKEY;
         if constexpr (MASK == VLM_MASK_SEGMENT_ID)
-            if (tid < BKEY) segs[tid] = a.seg[min(key0 + tid, a.nkeys - 1)];
-        for (int c = tid; c < BKEY * CH; c += 256) {
-            const int r = c / CH, d0 = (c % CH) * 4;
-            const int key = key0 + r;
-            f32x4 kv = {0.f, 0.f, 0.f, 0.f};
-            if (key < a.nkeys) kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)key * DQ + d0);
-            *reinterpret_cast<f32x4*>(Ks + r * LDK + d0) = kv;
+            if (tid < BKEY) segs[buf][tid] = sreg;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < KCH; i++) {
+            const int c = tid + 256 * i, r = c / CH, d0 = (c % CH) * 4;
+            if (c < BKEY * CH) *reinterpret_cast<f32x4*>(&Ks[buf][r * LDK + d0]) = key0 + r < a.nkeys ? kreg[i] : zero;
         }
-        for (int c = tid; c < BKEY * CHV; c += 256) {
-            const int r = c / CHV, d0 = (c % CHV) * 4;
-            const int key = key0 + r;
-            f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-            if (key < a.nkeys) vv = *reinterpret_cast<const f32x4*>(Vg + (size_t)key * DV + d0);
-            *reinterpret_cast<f32x4*>(Vs + r * LDV + d0) = vv;
+#pragma unroll
+        for (int i = 0; i < VCH; i++) {
+            const int c = tid + 256 * i, r = c / CHV, d0 = (c % CHV) * 4;
+            if (c < BKEY * CHV) *reinterpret_cast<f32x4*>(&Vs[buf][r * LDV + d0]) = key0 + r < a.nkeys ? vreg[i] : zero;
         }
-        __syncthreads();
+    };
+    if (nvis > 0) {
+        request(tile_at(0));
+        stage(tile_at(0), 0);
+    }
+    __syncthreads();
+    for (int kv = 0; kv < nvis; kv++) {
+        const int buf = kv & 1;
+        const int key0 = tile_at(kv) * BKEY;
+        if (kv + 1 < nvis) request(tile_at(kv + 1));
+        const float* const Kb = Ks[buf];
+        const float* const Vb = Vs[buf];
         bool active = true;
         if (MASK == VLM_MASK_CAUSAL_ID) active = key0 <= a.pos0 + q0 + 31;
         if (active) {
@@ -521,14 +552,14 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
             for (int kb = 0; kb < KB; kb++) {
 #pragma unroll
                 for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
-                const float* kr = Ks + (kb * 32 + l32) * LDK + hh;
+                const float* kr = Kb + (kb * 32 + l32) * LDK + hh;
 #pragma unroll
                 for (int kk = 0; kk < DQ / 2; kk++)
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[kk * 2], Qf[kk], sacc[kb], 0, 0, 0);
             }
             bool full = false;  // segment mask: the whole tile lies in this wavefront's one segment
             if constexpr (MASK == VLM_MASK_SEGMENT_ID)
-                full = segment_tile_full<BKEY>(segs, seg_q, qrow < S, key0, a.nkeys);
+                full = segment_tile_full<BKEY>(segs[buf], seg_q, qrow < S, key0, a.nkeys);
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < KB; kb++)
@@ -538,7 +569,7 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
                     float s = sacc[kb][r] * scale;
                     bool vis = key < a.nkeys;
                     if (MASK == VLM_MASK_CAUSAL_ID) vis = vis && key <= a.pos0 + qrow;
-                    if (MASK == VLM_MASK_SEGMENT_ID) vis = full || (vis && qrow < S && segs[key - key0] == seg_q);
+                    if (MASK == VLM_MASK_SEGMENT_ID) vis = full || (vis && qrow < S && segs[buf][key - key0] == seg_q);
                     if (MASK == VLM_MASK_ADDITIVE_ID && vis && qrow < S)
                         s += a.add[(size_t)qrow * a.ld_add + key] * kLog2e;
                     s = vis ? s : -INFINITY;
@@ -576,12 +607,14 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int kl = kb * 32 + (r / 4) * 8 + hh * 4 + (r % 4);
-                    const float* vr = Vs + kl * LDV + l32;
+                    const float* vr = Vb + kl * LDV + l32;
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++)
                         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[nb * 32], sacc[kb][r], oacc[nb], 0, 0, 0);
                 }
         }
+        // the other buffer was last read in the previous iteration, before its closing barrier
+        if (kv + 1 < nvis) stage(tile_at(kv + 1), buf ^ 1);
         __syncthreads();
     }
     if (qrow < S) {
